@@ -1,0 +1,227 @@
+"""Python face of the CPU oracle for Invariant Bit Packing.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU
+baseline of the benchmark use this module; the product library never does.
+The arithmetic lives in ``ibp_oracle.c`` (plain bit-serial C, see its
+header for the method's source and the readings of it); this file only
+compiles it with gcc, loads it with ctypes and moves numpy arrays in and out.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ibp_oracle.c")
+_LIB = os.path.join(_HERE, "libibp_oracle.so")
+
+GCC_CMD = ["gcc", "-O2", "-std=gnu11", "-Wall", "-Wextra", "-shared", "-fPIC",
+           _SRC, "-o", _LIB]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle shared object (gcc, no GPU headers).
+
+    IBP_ORACLE_LIB names another build of the same source (the pin tests use
+    it to run deliberately broken copies of the oracle)."""
+    override = os.environ.get("IBP_ORACLE_LIB")
+    if override:
+        return override
+    if force or not os.path.exists(_LIB) or \
+            os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        subprocess.run(GCC_CMD, check=True)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        L = ctypes.CDLL(build())
+        u8p = ctypes.POINTER(ctypes.c_uint8)
+        u64p = ctypes.POINTER(ctypes.c_uint64)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        u64, u32, c_uint, c_int = (ctypes.c_uint64, ctypes.c_uint32,
+                                   ctypes.c_uint, ctypes.c_int)
+        L.orc_pext.restype = u64
+        L.orc_pext.argtypes = [u64, u64]
+        L.orc_pdep.restype = u64
+        L.orc_pdep.argtypes = [u64, u64]
+        L.orc_build_metadata.restype = c_int
+        L.orc_build_metadata.argtypes = [u8p, u64, c_uint, u32, u64p, u64p, u64p]
+        L.orc_stored_bytes.restype = u64
+        L.orc_stored_bytes.argtypes = [u64, u64, c_int]
+        L.orc_compress_row.restype = c_int
+        L.orc_compress_row.argtypes = [u8p, u64, c_uint, u64, u64, u8p, u64p,
+                                       ctypes.POINTER(c_int)]
+        L.orc_decompress_row.restype = c_int
+        L.orc_decompress_row.argtypes = [u8p, u64, c_uint, u64, u64, c_int, u8p]
+        L.orc_compress_table.restype = c_int
+        L.orc_compress_table.argtypes = [u8p, u64, u64, c_uint, u64, u64, u8p,
+                                         u64p, u64p]
+        L.orc_gather_decompress.restype = c_int
+        L.orc_gather_decompress.argtypes = [u8p, u64p, u64, u64, c_uint, u64,
+                                            u64, i64p, u64, u8p]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray, ct):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ct))
+
+
+def _bytes2d(x: np.ndarray) -> np.ndarray:
+    """View a 2-D array of any dtype as [rows, row_bytes] uint8."""
+    x = np.ascontiguousarray(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    return x.reshape(x.shape[0], -1).view(np.uint8)
+
+
+@dataclass(frozen=True)
+class Metadata:
+    width_bits: int
+    mask: int
+    bitval: int
+    t_ppm: int
+
+    @property
+    def invariant_bits(self) -> int:
+        return bin(self.mask).count("1")
+
+
+def t_to_ppm(t: float) -> int:
+    """Threshold T as an integer number of parts per million."""
+    return int(round(t * 1_000_000))
+
+
+def pext(x: int, m: int) -> int:
+    return int(lib().orc_pext(x, m))
+
+
+def pdep(v: int, m: int) -> int:
+    return int(lib().orc_pdep(v, m))
+
+
+def build_metadata(sample: np.ndarray, width_bits: int = 32, t: float = 0.9,
+                   t_ppm: int | None = None, n_blocks: int | None = None):
+    """Mask/Bitval over the blocks of ``sample`` (read as a flat bit string).
+
+    Returns (Metadata, ones) where ones[b] counts the sample blocks with bit b
+    set.  ``n_blocks`` defaults to every whole block of the buffer.
+    """
+    raw = np.ascontiguousarray(sample).reshape(-1).view(np.uint8)
+    if n_blocks is None:
+        n_blocks = raw.size * 8 // width_bits
+    ppm = t_to_ppm(t) if t_ppm is None else int(t_ppm)
+    ones = np.zeros(64, np.uint64)
+    mask = ctypes.c_uint64()
+    bitval = ctypes.c_uint64()
+    buf = raw if raw.size else np.zeros(1, np.uint8)
+    rc = lib().orc_build_metadata(_p(buf, ctypes.c_uint8), n_blocks, width_bits,
+                                  ppm, _p(ones, ctypes.c_uint64),
+                                  ctypes.byref(mask), ctypes.byref(bitval))
+    if rc:
+        raise ValueError(f"orc_build_metadata failed: {rc}")
+    md = Metadata(width_bits, int(mask.value), int(bitval.value), ppm)
+    return md, ones[:width_bits].copy()
+
+
+def stored_bytes(row_bytes: int, c_bits: int, flag: int) -> int:
+    return int(lib().orc_stored_bytes(row_bytes, c_bits, int(flag)))
+
+
+def compress(md: Metadata, x: np.ndarray):
+    """Compress a table (rows = first axis).  Returns (slots, flags, row_bits).
+
+    slots: uint8 [n_rows, row_bytes]; flags: uint64 [ceil(n_rows/64)];
+    row_bits: uint64 [n_rows] (C of every row, raw rows included).
+    """
+    src = _bytes2d(x)
+    n_rows, row_bytes = src.shape
+    slots = np.zeros((n_rows, row_bytes), np.uint8)
+    flags = np.zeros(max(1, (n_rows + 63) // 64), np.uint64)
+    row_bits = np.zeros(max(1, n_rows), np.uint64)
+    rc = lib().orc_compress_table(
+        _p(src, ctypes.c_uint8) if n_rows else None, n_rows, row_bytes,
+        md.width_bits, md.mask, md.bitval,
+        _p(slots, ctypes.c_uint8) if n_rows else None,
+        _p(flags, ctypes.c_uint64), _p(row_bits, ctypes.c_uint64))
+    if rc:
+        raise ValueError(f"orc_compress_table failed: {rc}")
+    return slots, flags[:(n_rows + 63) // 64], row_bits[:n_rows]
+
+
+def compress_row(md: Metadata, row: np.ndarray):
+    """One row -> (slot bytes, C, flag)."""
+    r = np.ascontiguousarray(row).reshape(-1).view(np.uint8)
+    slot = np.zeros_like(r)
+    c = ctypes.c_uint64()
+    f = ctypes.c_int()
+    rc = lib().orc_compress_row(_p(r, ctypes.c_uint8), r.size, md.width_bits,
+                                md.mask, md.bitval, _p(slot, ctypes.c_uint8),
+                                ctypes.byref(c), ctypes.byref(f))
+    if rc:
+        raise ValueError(f"orc_compress_row failed: {rc}")
+    return slot, int(c.value), int(f.value)
+
+
+def decompress_row(md: Metadata, slot: np.ndarray, flag: int) -> np.ndarray:
+    s = np.ascontiguousarray(slot).reshape(-1).view(np.uint8)
+    out = np.zeros_like(s)
+    rc = lib().orc_decompress_row(_p(s, ctypes.c_uint8), s.size, md.width_bits,
+                                  md.mask, md.bitval, int(flag),
+                                  _p(out, ctypes.c_uint8))
+    if rc:
+        raise ValueError(f"orc_decompress_row failed: {rc}")
+    return out
+
+
+def gather_decompress(md: Metadata, slots: np.ndarray, flags: np.ndarray,
+                      ids: np.ndarray) -> np.ndarray:
+    """out[i] = decompressed row ids[i] (uint8 [n_ids, row_bytes])."""
+    s = _bytes2d(slots)
+    n_rows, row_bytes = s.shape
+    ids = np.ascontiguousarray(ids, dtype=np.int64).reshape(-1)
+    fl = np.ascontiguousarray(flags, dtype=np.uint64)
+    if fl.size == 0:
+        fl = np.zeros(1, np.uint64)
+    out = np.zeros((ids.size, row_bytes), np.uint8)
+    if ids.size == 0:
+        return out
+    rc = lib().orc_gather_decompress(
+        _p(s, ctypes.c_uint8), _p(fl, ctypes.c_uint64), n_rows, row_bytes,
+        md.width_bits, md.mask, md.bitval, _p(ids, ctypes.c_int64), ids.size,
+        _p(out, ctypes.c_uint8))
+    if rc:
+        raise ValueError(f"orc_gather_decompress failed: {rc}")
+    return out
+
+
+def decompress(md: Metadata, slots: np.ndarray, flags: np.ndarray) -> np.ndarray:
+    n_rows = _bytes2d(slots).shape[0]
+    return gather_decompress(md, slots, flags, np.arange(n_rows, dtype=np.int64))
+
+
+def image_bytes_equal(slots_a: np.ndarray, slots_b: np.ndarray,
+                      flags: np.ndarray, row_bits: np.ndarray) -> np.ndarray:
+    """Per-row equality of two images over the bytes that belong to the image.
+
+    Returns a bool array; bytes of a compressed slot past its padded stream
+    are ignored.
+    """
+    a, b = _bytes2d(slots_a), _bytes2d(slots_b)
+    n_rows, row_bytes = a.shape
+    ok = np.empty(n_rows, bool)
+    for r in range(n_rows):
+        f = int((int(flags[r >> 6]) >> (r & 63)) & 1)
+        nb = stored_bytes(row_bytes, int(row_bits[r]), f)
+        ok[r] = np.array_equal(a[r, :nb], b[r, :nb])
+    return ok
