@@ -1,0 +1,354 @@
+"""Benchmark of IBP decompression on one MI355X.
+
+Default workload: sparse GNN features, a 1,048,576 x 512 fp32 table (2 GiB,
+entries 1.0 with probability 0.01) compressed with Invariant Bit Packing,
+then gather-decompressed in batches of 65,536 uniform random row ids.  One
+step = one gather-decompress launch over one batch (8 batches, 8 output
+buffers of 128 MiB rotated so that neither L2 nor the 256 MiB MALL holds the
+output).  Metadata building and compression run once before the timed region
+(the method builds metadata once and compresses a table once; both are
+timed and reported separately).
+
+Prints one JSON line (rank 0):
+  value      = GB/s of uncompressed output over the timed steps
+  roofline   = algorithmic bytes of one launch / its mean duration (HIP
+               events on the launch stream) against the 8 TB/s HBM peak
+  cpu_baseline = the CPU oracle's gather over a bounded sample, all threads
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "IBP decompress GB/s (uncompressed out), % of HBM roofline; compression ratio"
+HBM_PEAK_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SRC = os.path.join(ROOT, "lossless_bit_level_amd", "csrc", "ibp.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- workloads --
+
+class Workload:
+    """tables: list of numpy arrays (rows on axis 0); steps: list of
+    (table index, ids or None); sample_for_metadata: numpy array."""
+
+    def __init__(self, name, desc, tables, steps, sample, n_out_bytes):
+        self.name, self.desc, self.tables, self.steps = name, desc, tables, steps
+        self.sample = sample
+        self.n_out_bytes = n_out_bytes
+
+
+def make_workload(name: str) -> Workload:
+    import synthetic as syn
+    if name == "sparse_gnn":
+        x = syn.sparse_gnn_rows()
+        ids = syn.uniform_ids(syn.SPARSE_GNN_ROWS, 8, 65536)
+        return Workload(name, "sparse GNN features 1048576 x 512 fp32, gather 8 x 65536 "
+                        "uniform ids", [x], [(0, b) for b in ids], x, 65536 * 2048)
+    if name in ("dense_gnn", "dlrm_emb"):
+        if name == "dense_gnn":
+            x = syn.dense_gnn_rows()
+            ids = syn.zipf_ids(syn.DENSE_GNN_ROWS, 8, 65536)
+            desc = "dense GNN features 2097152 x 256 fp32 N(0,0.25)"
+        else:
+            x = syn.dlrm_emb_rows()
+            ids = syn.zipf_ids(syn.DLRM_EMB_ROWS, 8, 65536, seed=2)
+            desc = "DLRM embedding 4194304 x 128 fp32 U(-0.05,0.05)"
+        return Workload(name, desc + ", gather 8 x 65536 Zipf(1.05) ids", [x],
+                        [(0, b) for b in ids], x, 65536 * x.shape[1] * 4)
+    if name == "llm_kv":
+        x = syn.llm_kv_pages()
+        ids = syn.kv_page_ids()
+        return Workload(name, "LLM KV cache [16,32,4096,128] bf16, 4 KiB pages, gather "
+                        "8 x 16384 page ids", [x], [(0, b) for b in ids], x, 16384 * 4096)
+    if name == "llm_weights":
+        tables = [syn.llm_weight(layer, j) for layer in (0, 1) for j in range(7)]
+        steps = [(t, None) for t in range(len(tables))]
+        return Workload(name, "LLM weights bf16, 4 x [4096,4096] + 3 x [4096,14336] per "
+                        "layer, full decompress per matrix (2 resident layers)", tables,
+                        steps, tables[0], None)
+    raise SystemExit(f"unknown workload {name}")
+
+
+# ----------------------------------------------------------- helpers ----
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only
+    if it was taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"decode_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not h or not t or h.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def stored_bytes_per_row(row_bits: np.ndarray, row_bytes: int) -> np.ndarray:
+    n = row_bytes // 4
+    c = row_bits.astype(np.int64)
+    comp = c < 32 * n
+    return np.where(comp, 4 * ((c + 31) // 32), row_bytes)
+
+
+def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
+    """Time the CPU oracle's gather-decompress on a bounded sample of the same
+    workload: the rows the first ids of the gather batches reference are
+    compressed by the oracle (untimed), then the oracle's gather over those
+    ids is timed on every allowed core (one contiguous id range per thread)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from oracle import oracle as orc
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    md_o = orc.Metadata(32, int(md.mask), int(md.bitval), int(md.t_ppm))
+    t_idx, ids0 = wl.steps[0]
+    table = wl.tables[t_idx]
+    S = table.nbytes // table.shape[0]
+    if ids0 is None:
+        ids0 = np.arange(table.shape[0], dtype=np.int64)
+    else:  # the gather batches back to back
+        ids0 = np.concatenate([ids for ti, ids in wl.steps if ti == t_idx])
+    # calibrate on 64 rows, size the sample for ~target_core_s core-seconds
+    probe = np.unique(ids0[:64])
+    local = table[probe]
+    slots, flags, _ = orc.compress(md_o, local)
+    t0 = time.perf_counter()
+    orc.gather_decompress(md_o, slots, flags, np.arange(len(probe)))
+    per_row = (time.perf_counter() - t0) / len(probe)
+    n_ids = int(min(len(ids0), max(threads * 64, target_core_s / max(per_row, 1e-9))))
+    ids = ids0[:n_ids]
+    uniq, inv = np.unique(ids, return_inverse=True)
+    src = table[uniq]
+    parts = np.array_split(np.arange(len(uniq)), threads)
+    with ThreadPoolExecutor(threads) as ex:   # oracle compress of the sample rows
+        res = list(ex.map(lambda p: orc.compress(md_o, src[p]), parts))
+    slots = np.concatenate([r[0] for r in res])
+    flag_bits = np.concatenate([[(int(r[1][i >> 6]) >> (i & 63)) & 1 for i in range(len(p))]
+                                for r, p in zip(res, parts)]).astype(np.uint8)
+    pad = np.zeros(((len(uniq) + 63) // 64) * 64, np.uint8)
+    pad[:len(uniq)] = flag_bits
+    flags = np.packbits(pad, bitorder="little").view(np.uint64)
+    id_parts = np.array_split(inv.astype(np.int64), threads)
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        outs = list(ex.map(lambda p: orc.gather_decompress(md_o, slots, flags, p), id_parts))
+    dt = time.perf_counter() - t0
+    out = np.concatenate(outs)
+    assert np.array_equal(out, table[ids].reshape(len(ids), -1).view(np.uint8))
+    return {"value": round(n_ids * S / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {n_ids} ids of the gather batches ({n_ids * S / 2**20:.1f} MiB out), "
+                      f"bit-serial C oracle, {threads} threads, {dt:.2f} s wall"}
+
+
+# --------------------------------------------------------------- main ----
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="sparse_gnn",
+                    choices=["sparse_gnn", "dense_gnn", "dlrm_emb", "llm_weights", "llm_kv"])
+    ap.add_argument("--source", default="device", choices=["device", "host"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the IBP path here is single-GPU "
+              "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lossless_bit_level_amd import ibp
+    ibp.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    wl = make_workload(args.workload)
+    log(f"workload {wl.name}: generated in {time.perf_counter() - t_gen:.1f} s")
+
+    tables_g = [torch.from_numpy(t.reshape(t.shape[0], -1).view(np.uint8)).to(dev)
+                for t in wl.tables]
+    S = tables_g[0].shape[1]
+    stream = torch.cuda.current_stream()
+
+    # metadata (first min(N, 2^24) blocks) and compression, timed apart
+    samp = torch.from_numpy(wl.sample.reshape(-1).view(np.uint8)).to(dev)
+    n_blocks = min(samp.numel() // 4, 1 << 24)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks)
+    meta_ms = (time.perf_counter() - t0) * 1e3
+    del samp
+    images = []
+    comp_ms = 0.0
+    raw_bytes = stored = 0
+    bits_total = 0
+    for tg in tables_g:
+        ibp.ibp_compress(md, tg)              # warm
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        slots, flags, rb = ibp.ibp_compress(md, tg)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        comp_ms += e0.elapsed_time(e1)
+        rbn = rb.cpu().numpy()[:tg.shape[0]]
+        sb = stored_bytes_per_row(rbn, S)
+        images.append((slots, flags, sb))
+        raw_bytes += tg.numel()
+        stored += int(sb.sum())
+        bits_total += int(np.minimum(rbn.astype(np.int64), 8 * S).sum())
+    comp_GBps = raw_bytes / (comp_ms / 1e3) / 1e9
+    log(f"metadata {md} in {meta_ms:.1f} ms; compress {comp_ms:.2f} ms ({comp_GBps:.0f} GB/s); "
+        f"ratio {raw_bytes / stored:.4f}")
+
+    if args.source == "host":
+        host_images = []
+        for slots, flags, sb in images:
+            h = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+            h.copy_(slots)
+            host_images.append((h, flags, sb))
+        images = host_images
+    del tables_g
+
+    # per-step launch plan: (image index, ids tensor or None, output buffer)
+    plan = []
+    outs = []
+    for i, (ti, ids) in enumerate(wl.steps):
+        n_out = len(ids) if ids is not None else wl.tables[ti].shape[0]
+        outs.append(torch.empty((n_out, S if ids is not None else
+                                 wl.tables[ti].nbytes // wl.tables[ti].shape[0]),
+                                dtype=torch.uint8, device=dev))
+        idg = torch.from_numpy(np.ascontiguousarray(ids)).to(dev) if ids is not None else None
+        plan.append((ti, idg, outs[-1], ids))
+
+    def algo_bytes(ti, ids):
+        slots, flags, sb = images[ti]
+        if ids is None:
+            n = wl.tables[ti].shape[0]
+            return int(sb.sum()) + wl.tables[ti].nbytes + 8 * ((n + 63) // 64)
+        return int(sb[ids].sum()) + len(ids) * S + 8 * len(ids) + \
+            8 * len(np.unique(ids >> 6))
+
+    plan_bytes = [algo_bytes(ti, ids) for ti, _, _, ids in plan]
+    plan_out = [o.numel() for _, _, o, _ in plan]
+
+    def launch(k):
+        ti, idg, out, _ = plan[k % len(plan)]
+        slots, flags, _ = images[ti]
+        if idg is None:
+            ibp.ibp_decompress(md, slots, flags, out=out)
+        else:
+            ibp.ibp_gather_decompress(md, slots, flags, idg, out=out)
+
+    for k in range(args.warmup):
+        launch(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record(stream)
+        launch(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    out_bytes = sum(plan_out[k % len(plan)] for k in range(K))
+    a_bytes = sum(plan_bytes[k % len(plan)] for k in range(K)) / K
+    value = out_bytes / wall / 1e9
+    mean_launch_s = float(launch_ms.mean()) / 1e3
+    achieved = a_bytes / mean_launch_s / 1e9
+
+    # correctness spot check of the timed path against the source rows
+    ti, idg, out, ids = plan[(K - 1) % len(plan)]
+    src = wl.tables[ti].reshape(wl.tables[ti].shape[0], -1).view(np.uint8)
+    pick = np.random.default_rng(0).integers(0, out.shape[0], 256)
+    got = out[torch.from_numpy(pick).to(dev)].cpu().numpy()
+    want = src[ids[pick]] if ids is not None else src[pick]
+    if not np.array_equal(got, want):
+        raise SystemExit("bench: decompressed rows differ from the source table")
+
+    if args.source == "host":
+        # host-link ceiling: pinned host -> device copy of 1 GiB
+        h = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+        d = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        d.copy_(h, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(3):
+            d.copy_(h, non_blocking=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        link = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
+        link_read = a_bytes - np.mean(plan_out)   # bytes that cross the link per launch
+        roof = {"bound": "host_link", "achieved": round(link_read / mean_launch_s / 1e9, 2),
+                "peak": round(link, 2), "unit": "GB/s",
+                "frac": round(link_read / mean_launch_s / 1e9 / link, 4), "traffic": None,
+                "peak_note": "measured pinned host->device hipMemcpy ceiling, 1 GiB"}
+    else:
+        traffic = traffic_from_profiles(wl.name)
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic}
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "desc": wl.desc, "source": args.source,
+                   "row_bytes": S, "parallelism": "none (1 GPU)"},
+        "compression_ratio": round(raw_bytes / stored, 4),
+        "compression_ratio_bits": round(raw_bytes * 8 / bits_total, 4),
+        "metadata": {"mask": f"0x{md.mask:08X}", "bitval": f"0x{md.bitval:08X}",
+                     "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
+        "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1)},
+        "kernel": {"name": "decode_kernel", "mean_launch_us": round(mean_launch_s * 1e6, 3),
+                   "min_launch_us": round(float(launch_ms.min()) * 1e3, 3),
+                   "algorithmic_bytes_per_launch": int(a_bytes),
+                   "source_sha256_16": kernel_source_hash()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, md)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

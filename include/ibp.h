@@ -1,0 +1,170 @@
+/*
+ * ibp.h -- C ABI of libibp, Invariant Bit Packing on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method source, cited as [IBP]: the explainer page "Reducing the GPU Memory
+ * Bottleneck with Lossless Compression for ML -- Extended" (Kamath,
+ * Krishnamurthy, Canini, Peter), section "Methodology: Invariant Bit Packing
+ * (IBP)" with its three phases Preprocessing, Compression and Decompression,
+ * and section "System integration".
+ *
+ * Data model
+ * ----------
+ * A table is n_rows rows of row_bytes (= S) bytes, row r at byte r*S.  The
+ * unit the page calls a tensor is a row here.  A row is cut into n = S/4
+ * blocks of W = 32 bits (block k = little-endian 32-bit word k; a bf16 row
+ * packs two elements per block).  One ibp_metadata (Mask/Bitval) covers the
+ * whole table.
+ *
+ * Compressed image
+ * ----------------
+ * slots: n_rows slots of S bytes each (the fixed-size buffers of [IBP]
+ * System integration), slot r at byte r*S.  flags: ceil(n_rows/64) uint64
+ * words, bit (r & 63) of word r >> 6 set when row r is stored compressed
+ * (the GPU-side bitmask of [IBP] System integration); unused high bits of
+ * the last word are 0.
+ *   flag 0: the slot holds the S raw bytes.
+ *   flag 1: the slot's first ceil(C/32) little-endian 32-bit words hold the
+ *           row stream of C bits, zero padded; later slot bytes are not part
+ *           of the image and are neither written nor read.
+ * Row stream: bits [0, n) are the participation bits, bit k = 1 when block
+ * k was stripped ([IBP] Compression); then the payloads of blocks 0..n-1 in
+ * order, each least significant bit first at the running bit cursor, no
+ * alignment.  A stripped payload is the block's non-invariant bits in
+ * ascending position order (W - p bits, p = popcount(Mask)); any other
+ * payload is the whole block (W bits).  So C = n + n*W - p*m for a row with
+ * m stripped blocks, and payload k starts at bit n + k*W - p*(number of
+ * stripped blocks before k).  A row is stored compressed iff C < n*W.
+ *
+ * Memory, ownership, streams
+ * --------------------------
+ * The caller allocates and owns every buffer.  Device pointers are HIP
+ * device memory; `sample` and `slots` may also be pinned host memory mapped
+ * for the device (pass the pointer ibp_host_device_pointer returns), which
+ * the kernels then read across the host link without a staging copy
+ * ([IBP] Compression and Decompression use zero-copy access to host memory).
+ * All buffers must be 16-byte aligned and row_bytes a multiple of 4.
+ * ibp_compress, ibp_decompress and ibp_gather_decompress only enqueue work on
+ * `stream` (a hipStream_t, NULL = the null stream) and return at once; they
+ * allocate nothing, copy nothing on the host and never synchronise.
+ * ibp_build_metadata is synchronous.  The library keeps no state between
+ * calls apart from the last HIP error code of the calling thread.
+ *
+ * Errors
+ * ------
+ * Every entry point validates its arguments on the host before it enqueues
+ * anything; a negative status means nothing was enqueued.  IBP_ERR_HIP means
+ * a HIP call or launch failed; ibp_last_hip_error() gives its hipError_t.
+ * Row ids outside [0, n_rows) are a precondition violation: they are not
+ * checked on the device.
+ */
+#ifndef IBP_H_
+#define IBP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define IBP_OK 0
+#define IBP_ERR_INVALID_ARGUMENT (-1) /* null pointer, overflow, t_ppm > 1e6, bad metadata */
+#define IBP_ERR_UNSUPPORTED (-2)      /* block width other than 32, row too long */
+#define IBP_ERR_LAYOUT (-3)           /* row_bytes not a multiple of 4, misaligned pointer */
+#define IBP_ERR_EMPTY (-4)            /* empty sample */
+#define IBP_ERR_HIP (-5)              /* HIP API or launch failure */
+
+/* Largest row ibp_compress accepts (the row's stream is assembled in LDS). */
+#define IBP_MAX_COMPRESS_ROW_BYTES 98304u
+
+/* The fixed-size global metadata of [IBP] Preprocessing: one Mask/Bitval
+ * pair for every block of the data set, 32 bytes, built once and reused. */
+typedef struct ibp_metadata {
+    uint32_t width_bits;     /* W; this library: 32 */
+    uint32_t invariant_bits; /* p = popcount(mask) */
+    uint64_t mask;           /* bit b set <=> block bit b is invariant; bits >= W are 0 */
+    uint64_t bitval;         /* values of the invariant bits; (bitval & ~mask) == 0 */
+    uint32_t t_ppm;          /* threshold T in parts per million (0.9 -> 900000) */
+    uint32_t reserved;       /* 0 */
+} ibp_metadata;
+
+/*
+ * [IBP] Preprocessing, host half.  From per-bit one-counts over n_blocks
+ * sample blocks: for each bit b < width_bits, the majority value (ties give
+ * 0) is invariant when 1e6 * majority_count >= t_ppm * n_blocks, compared in
+ * exact integers.  ones: width_bits host counters.  Pure host code; lets
+ * counts from several devices or passes be summed before thresholding.
+ * Errors: INVALID_ARGUMENT (null, ones[b] > n_blocks, t_ppm > 1e6),
+ * UNSUPPORTED (width not 32), EMPTY (n_blocks == 0).
+ */
+int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
+                             uint32_t width_bits, uint32_t t_ppm,
+                             ibp_metadata *out);
+
+/*
+ * [IBP] Preprocessing.  Counts the ones of every bit position over the
+ * n_blocks 32-bit blocks at `sample` (device memory or mapped pinned host
+ * memory, 16-byte aligned) on the GPU, then applies the threshold rule of
+ * ibp_metadata_from_counts.  out: host struct.  out_ones: optional host
+ * array of width_bits counters.  SYNCHRONOUS: waits for `stream`.  Uses a
+ * 256-byte device buffer of its own for the counters for the duration of
+ * the call.
+ */
+int ibp_build_metadata(const void *sample, uint64_t n_blocks,
+                       uint32_t width_bits, uint32_t t_ppm, ibp_metadata *out,
+                       uint64_t *out_ones, void *stream);
+
+/*
+ * [IBP] Compression, out of place.  src: n_rows x row_bytes device table.
+ * Writes the image (slots, flags) described above and, when row_bits is not
+ * NULL, row_bits[r] = C of row r (also for rows stored raw).  slots may be
+ * device memory or mapped pinned host memory.  Asynchronous on `stream`.
+ * row_bytes <= IBP_MAX_COMPRESS_ROW_BYTES.  Equal inputs give equal bytes.
+ */
+int ibp_compress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
+                 const void *src, void *slots, uint64_t *flags,
+                 uint32_t *row_bits, void *stream);
+
+/*
+ * [IBP] Decompression of the whole table: dst row r = row r restored.
+ * slots: device memory or mapped pinned host memory; flags, dst: device.
+ * Asynchronous on `stream`.
+ */
+int ibp_decompress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
+                   const void *slots, const uint64_t *flags, void *dst,
+                   void *stream);
+
+/*
+ * Gather-decompress: dst row i = row row_ids[i] restored, for i < n_ids, in
+ * id order; duplicate ids are allowed.  The fetch of a feature / embedding /
+ * KV page by index that the page's GNN, DLRM and LLM integrations perform
+ * ([IBP] Decompression; System integration).  row_ids: device int64 array.
+ * n_ids == 0 is a no-op.  Asynchronous on `stream`.
+ */
+int ibp_gather_decompress(const ibp_metadata *md, uint64_t n_rows,
+                          uint64_t row_bytes, const void *slots,
+                          const uint64_t *flags, const int64_t *row_ids,
+                          uint64_t n_ids, void *dst, void *stream);
+
+/* (n_rows + 63) / 64: the number of uint64 words of a flag bitmap. */
+uint64_t ibp_flag_words(uint64_t n_rows);
+
+/*
+ * Device-visible address of pinned host memory (hipHostMalloc'd, e.g. a
+ * torch pin_memory tensor), for zero-copy sample/slots arguments.
+ * Errors: INVALID_ARGUMENT on null, IBP_ERR_HIP when the memory is not
+ * mapped for the current device.
+ */
+int ibp_host_device_pointer(const void *host_ptr, void **device_ptr);
+
+/* Static description of a status code. */
+const char *ibp_status_string(int status);
+
+/* hipError_t behind the calling thread's last IBP_ERR_HIP (0 if none). */
+int ibp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IBP_H_ */

@@ -1,0 +1,663 @@
+// libibp: Invariant Bit Packing for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// Method source, cited as [IBP]: the explainer page "Reducing the GPU Memory
+// Bottleneck with Lossless Compression for ML -- Extended" (Kamath,
+// Krishnamurthy, Canini, Peter), section "Methodology: Invariant Bit Packing
+// (IBP)" (phases Preprocessing, Compression, Decompression) and section
+// "System integration" (fixed-size buffers, GPU bitmask of compressed rows).
+// The image format is specified in include/ibp.h.
+//
+// Everything here is integer bit work bound by HBM (or by the host link for a
+// pinned image); nothing is a contraction, so no MFMA.  Design for wave64:
+//   * a 64-block chunk of a row maps to one wave, one block per lane;
+//   * the participation bits of the chunk are one 64-bit header word, so the
+//     offset of each lane's payload is a closed-form prefix count:
+//     v_mbcnt_lo/hi over the header word plus a scalar carry (s_bcnt1) --
+//     the wave prefix scan of the per-block bit lengths, which take only the
+//     two values 1 + W - p and 1 + W;
+//   * the compressed stream of a row segment is fetched by the wave with
+//     coalesced 16-byte loads into a wave-private LDS window, and each lane
+//     pulls its payload out of two LDS words with one funnel shift;
+//   * invariant bits go back in with a run decomposition of ~Mask
+//     (v_bfe_u32 + v_lshl_or_b32 per run) and an OR with Bitval; the run
+//     count is a template parameter for the common masks;
+//   * workgroup ids are remapped so that consecutive tasks land on the same
+//     XCD (each of the 8 XCDs has its own L2).
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ibp.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlockThreads = 256;
+constexpr int kWavesPerBlock = kBlockThreads / kWave;
+constexpr uint32_t kSegBlocks = 1024;          // blocks per decode task
+constexpr uint32_t kSegLdsWords = kSegBlocks + 8;
+constexpr uint64_t kMaxRowBytes = 1ull << 26;  // bit offsets fit 32 bits, counts 24
+constexpr int kMaxRuns = 16;                   // runs of ~Mask for W = 32
+constexpr uint32_t kMaxGrid = 1u << 24;
+
+// Run decomposition of the kept (non-invariant) bit positions ~Mask.  Run j
+// is a maximal stretch of kept block bits; `place[j]` is its mask in the
+// block, `shift[j]` how far it moves between block and payload (its block
+// position minus the number of kept bits below it, always >= 0).  Then
+//   extract:  payload = OR_j ((x & place[j]) >> shift[j])
+//   deposit:  block   = OR_j ((v << shift[j]) & place[j])
+// two VALU ops per run either way.
+struct Runs {
+  uint32_t n;
+  uint32_t shift[kMaxRuns];
+  uint32_t place[kMaxRuns];
+};
+
+struct Codec {
+  uint32_t mask;
+  uint32_t bitval;
+  uint32_t p;       // invariant bits
+  uint32_t n;       // blocks per row
+  Runs runs;
+};
+
+// Parallel bit extract by ~Mask: [IBP] Compression strips the invariant bits
+// and closes the gaps.
+template <int NR>
+__device__ __forceinline__ uint32_t extract_kept(uint32_t x, const Runs& rs) {
+  uint32_t v = 0;
+  if constexpr (NR >= 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) v |= (x & rs.place[j]) >> rs.shift[j];
+  } else {
+    for (uint32_t j = 0; j < rs.n; ++j) v |= (x & rs.place[j]) >> rs.shift[j];
+  }
+  return v;
+}
+
+// Parallel bit deposit by ~Mask, ORed onto `base`: [IBP] Decompression puts
+// the stored bits back around the invariant positions (base = Bitval).
+template <int NR>
+__device__ __forceinline__ uint32_t deposit_kept(uint32_t v, const Runs& rs, uint32_t base) {
+  uint32_t x = base;
+  if constexpr (NR >= 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) x |= (v << rs.shift[j]) & rs.place[j];
+  } else {
+    for (uint32_t j = 0; j < rs.n; ++j) x |= (v << rs.shift[j]) & rs.place[j];
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Number of set bits of the 64-bit word (hi:lo) strictly below this lane.
+__device__ __forceinline__ uint32_t bits_below_lane(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+}
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    uint32_t t = __shfl_up(v, d, kWave);
+    if (lane >= (uint32_t)d) v += t;
+  }
+  return v;
+}
+
+// Make this wave's LDS writes visible to its own later LDS reads (one wave
+// executes its LDS instructions in order; this stops compiler reordering).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroups are handed to the 8 XCDs round robin; renumber them so that
+// logical neighbours (segments of one row, rows of one batch) share an XCD
+// and its L2.  A bijection on [0, G).
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t g) {
+  const uint32_t x = 8;
+  uint32_t q = g / x, r = g % x, xcd = b % x, idx = b / x;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+
+// One block per lane: pull the payload at bit `rel` of the LDS window out of
+// two words with a funnel shift; a stripped block (its bit set in the 64-bit
+// chunk header, used directly as a lane mask) gets its invariant bits back.
+template <int NR>
+__device__ __forceinline__ uint32_t decode_block(const uint32_t* lds, uint32_t rel,
+                                                 uint32_t h_lo, uint32_t h_hi,
+                                                 const Codec& cd) {
+  const uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
+  const uint32_t w0 = lds[wi];
+  const uint32_t w1 = lds[wi + 1];
+  const uint32_t v = __builtin_amdgcn_alignbit(w1, w0, rel & 31u);
+  const uint32_t dep = deposit_kept<NR>(v, cd.runs, cd.bitval);
+  const bool stripped =
+      __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+  return stripped ? dep : v;
+}
+
+// ------------------------------------------------------------ kernels --
+
+__global__ void fill_u64_kernel(unsigned long long* p, uint64_t n, unsigned long long v) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (uint64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// [IBP] Preprocessing, device half: per-bit one counts over the sample.  Each
+// wave ballots bit b of its 64 blocks and accumulates the popcount in a
+// scalar register; one atomic per bit and wave at the end.
+__global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
+    const uint32_t* __restrict__ sample, uint64_t n_blocks,
+    unsigned long long* __restrict__ counts) {
+  const uint32_t lane = lane_id();
+  const uint64_t gwave = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+  const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
+  uint64_t acc[32];
+#pragma unroll
+  for (int b = 0; b < 32; ++b) acc[b] = 0;
+  for (uint64_t base = gwave * kWave; base < n_blocks; base += nwaves * kWave) {
+    uint64_t k = base + lane;
+    uint32_t x = k < n_blocks ? sample[k] : 0u;
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+      acc[b] += __popcll(__ballot((x >> b) & 1u));
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int b = 0; b < 32; ++b)
+      if (acc[b]) atomicAdd(&counts[b], (unsigned long long)acc[b]);
+  }
+}
+
+// [IBP] Compression, one workgroup per row.  The row's stream is assembled
+// in LDS: header words from per-chunk ballots, a workgroup scan of the chunk
+// match counts, then every lane ORs its payload (<= 2 words) into place with
+// LDS atomics (OR commutes, so the bytes do not depend on timing), and the
+// finished words are written out with coalesced stores.  A row whose stream
+// would not be shorter than the raw row is copied raw.
+template <int NR, uint32_t MAXW>
+__global__ __launch_bounds__(kBlockThreads) void compress_kernel(
+    Codec cd, uint64_t n_rows, const uint32_t* __restrict__ src,
+    uint32_t* __restrict__ slots, unsigned long long* __restrict__ flags,
+    uint32_t* __restrict__ row_bits, int vec) {
+  __shared__ uint32_t buf[MAXW + 4];
+  __shared__ uint32_t chunk_pre[MAXW / kWave + 1];
+  __shared__ uint32_t total_m;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t n = cd.n;
+  const uint32_t nchunks = (n + kWave - 1) / kWave;
+
+  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const uint32_t* x_row = src + row * n;
+    uint32_t* s_row = slots + row * n;
+
+    for (uint32_t j = threadIdx.x; j < n + 4; j += kBlockThreads) buf[j] = 0;
+    __syncthreads();
+
+    // header bits and per-chunk match counts
+    for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {
+      uint32_t k = c * kWave + lane;
+      bool valid = k < n;
+      uint32_t x = valid ? x_row[k] : 0u;
+      bool match = valid && ((x & cd.mask) == cd.bitval);
+      unsigned long long h = __ballot(match);
+      if (lane == 0) {
+        chunk_pre[c] = (uint32_t)__popcll(h);
+        buf[2 * c] = (uint32_t)h;
+        buf[2 * c + 1] = (uint32_t)(h >> 32);
+      }
+    }
+    __syncthreads();
+
+    // exclusive scan of the chunk counts
+    if (wave == 0) {
+      uint32_t carry = 0;
+      for (uint32_t b0 = 0; b0 < nchunks; b0 += kWave) {
+        uint32_t c = b0 + lane;
+        uint32_t v = c < nchunks ? chunk_pre[c] : 0u;
+        uint32_t inc = wave_inclusive_scan(v, lane);
+        if (c < nchunks) chunk_pre[c] = carry + inc - v;
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
+      if (lane == 0) total_m = carry;
+    }
+    __syncthreads();
+
+    const uint32_t m = total_m;
+    const uint32_t c_bits = n + 32u * n - cd.p * m;
+    const bool flag = c_bits < 32u * n;
+
+    if (!flag) {
+      if (vec) {
+        const uint4* a = reinterpret_cast<const uint4*>(x_row);
+        uint4* o = reinterpret_cast<uint4*>(s_row);
+        for (uint32_t j = threadIdx.x; j < n / 4; j += kBlockThreads) o[j] = a[j];
+      } else {
+        for (uint32_t j = threadIdx.x; j < n; j += kBlockThreads) s_row[j] = x_row[j];
+      }
+    } else {
+      for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {
+        uint32_t k = c * kWave + lane;
+        bool valid = k < n;
+        uint32_t x = valid ? x_row[k] : 0u;
+        bool match = valid && ((x & cd.mask) == cd.bitval);
+        unsigned long long h = __ballot(match);
+        uint32_t pre = chunk_pre[c] + bits_below_lane((uint32_t)h, (uint32_t)(h >> 32));
+        if (valid) {
+          uint32_t off = n + 32u * k - cd.p * pre;
+          uint32_t len = match ? 32u - cd.p : 32u;
+          uint32_t pay = match ? extract_kept<NR>(x, cd.runs) : x;
+          if (len) {
+            uint32_t sh = off & 31u, wi = off >> 5;
+            atomicOr(&buf[wi], pay << sh);
+            if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t nw = (c_bits + 31u) >> 5;
+      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+    __syncthreads();
+  }
+}
+
+// [IBP] Decompression.  One wave per task = (output row, segment of up to
+// kSegBlocks blocks).  For a compressed row the wave
+//   1. counts the stripped blocks before its segment (popcount of header
+//      words) and inside it,
+//   2. fetches the segment's stream words [a/32, ceil(b/32)) into its LDS
+//      window with coalesced 16-byte loads,
+//   3. per 64-block chunk: header word -> per-lane bit offset (mbcnt + carry)
+//      -> two LDS words -> funnel shift -> deposit + Bitval -> store.
+// A raw row is a straight copy.
+template <bool GATHER, int NR>
+__global__ __launch_bounds__(kBlockThreads) void decode_kernel(
+    Codec cd, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t* __restrict__ dst, int vec) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint32_t n = cd.n;
+
+  const uint32_t g = gridDim.x;
+  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+    const uint64_t task = wg * kWavesPerBlock + wave;
+    if (task >= n_tasks) break;
+    const uint64_t i = task / nseg;
+    const uint32_t s = (uint32_t)(task - i * nseg);
+    const uint64_t id = GATHER ? (uint64_t)ids[i] : i;
+    uint32_t* out = dst + i * n;
+    const uint32_t lo = s * kSegBlocks;
+    const uint32_t hi = min(n, lo + kSegBlocks);
+    if (GATHER && id >= n_rows) {  // an id outside the table gives a zero row
+      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = 0u;
+      continue;
+    }
+    const uint32_t* src = slots + id * n;
+    const bool flag = (flags[id >> 6] >> (id & 63)) & 1ull;
+
+    if (!flag) {
+      if (vec) {
+        const uint4* a = reinterpret_cast<const uint4*>(src);
+        uint4* o = reinterpret_cast<uint4*>(out);
+        for (uint32_t j = lo / 4 + lane; j < hi / 4; j += kWave) o[j] = a[j];
+      } else {
+        for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = src[j];
+      }
+      continue;
+    }
+
+    // stripped blocks before the segment: header words [0, lo/32) (all header)
+    uint32_t carry = 0;
+    if (lo) {
+      uint32_t acc = 0;
+      for (uint32_t t = lane; t < lo / 32; t += kWave) acc += __popc(src[t]);
+      carry = uniform(wave_sum(acc));
+    }
+    // the segment's header words, one per lane; bits at or past n belong to
+    // the payloads and are cleared
+    const uint32_t hw_n = (hi - lo + 31) / 32;
+    uint32_t hw = 0;
+    if (lane < hw_n) {
+      uint32_t t = lo / 32 + lane;
+      hw = src[t];
+      uint32_t valid_bits = min(32u, hi - 32u * t);
+      if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
+    }
+    const uint32_t m_seg = uniform(wave_sum(__popc(hw)));
+
+    // stream bit range of the segment's payloads, and its LDS window
+    // (for an image that ibp_compress wrote, wb <= ceil(C/32) <= n; the
+    // clamps only keep a corrupt header from reading past the slot)
+    const uint32_t a = n + 32u * lo - cd.p * carry;
+    const uint32_t b = n + 32u * hi - cd.p * (carry + m_seg);
+    const uint32_t wb = min((b + 31u) >> 5, n);
+    const uint32_t wa = min(a >> 5, wb);
+    uint32_t base;
+    if (vec) {
+      base = wa & ~3u;
+      const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
+      uint4* l4 = reinterpret_cast<uint4*>(lds);
+      const uint32_t n4 = (wb - base + 3u) / 4u;
+      for (uint32_t j = lane; j < n4; j += kWave) l4[j] = g4[j];
+    } else {
+      base = wa;
+      for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+    }
+    wave_lds_sync();
+
+    // u = bit offset, relative to the LDS window, of the payload of the
+    // chunk's first block; lane l's payload starts 32*l - p*(stripped blocks
+    // of the chunk below l) further on.
+    uint32_t u = n + 32u * lo - cd.p * carry - 32u * base;
+    const uint32_t l32 = lane * 32u;
+    const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
+    uint32_t k0 = lo;
+    for (; k0 < full_hi; k0 += kWave) {
+      const uint32_t q = (k0 - lo) / 32;
+      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+      const uint32_t rel = u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi));
+      uint32_t* o = out + k0;
+      o[lane] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+      u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+    }
+    if (k0 < hi) {  // ragged end of the row (n not a multiple of 64)
+      const uint32_t q = (k0 - lo) / 32;
+      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+      const bool valid = k0 + lane < hi;
+      const uint32_t rel = valid ? u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi)) : 0u;
+      const uint32_t x = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+      if (valid) out[k0 + lane] = x;
+    }
+    wave_lds_sync();
+  }
+}
+
+// ------------------------------------------------------------- host ----
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return IBP_ERR_HIP;
+}
+
+int popcount32(uint64_t x) {
+  int c = 0;
+  for (; x; x &= x - 1) ++c;
+  return c;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_metadata(const ibp_metadata* md) {
+  if (!md) return IBP_ERR_INVALID_ARGUMENT;
+  if (md->width_bits != 32) return IBP_ERR_UNSUPPORTED;
+  if ((md->mask >> 32) != 0 || (md->bitval & ~md->mask) != 0 ||
+      (int)md->invariant_bits != popcount32(md->mask) || md->t_ppm > 1000000u)
+    return IBP_ERR_INVALID_ARGUMENT;
+  return IBP_OK;
+}
+
+int check_rows(uint64_t n_rows, uint64_t row_bytes) {
+  if (row_bytes == 0 || row_bytes % 4 != 0) return IBP_ERR_LAYOUT;
+  if (row_bytes > kMaxRowBytes) return IBP_ERR_UNSUPPORTED;
+  if (n_rows > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
+  return IBP_OK;
+}
+
+Codec make_codec(const ibp_metadata* md, uint64_t row_bytes) {
+  Codec cd{};
+  cd.mask = (uint32_t)md->mask;
+  cd.bitval = (uint32_t)md->bitval;
+  cd.p = md->invariant_bits;
+  cd.n = (uint32_t)(row_bytes / 4);
+  const uint32_t keep = ~cd.mask;
+  uint32_t at = 0, nr = 0;
+  for (uint32_t b = 0; b < 32;) {
+    if (!((keep >> b) & 1u)) { ++b; continue; }
+    uint32_t e = b;
+    while (e < 32 && ((keep >> e) & 1u)) ++e;
+    const uint32_t len = e - b;
+    cd.runs.shift[nr] = b - at;
+    cd.runs.place[nr] = (len == 32 ? ~0u : ((1u << len) - 1u)) << b;
+    ++nr;
+    at += len;
+    b = e;
+  }
+  cd.runs.n = nr;
+  return cd;
+}
+
+uint32_t grid_for(uint64_t work_groups) {
+  return (uint32_t)(work_groups < kMaxGrid ? work_groups : kMaxGrid);
+}
+
+template <int NR, uint32_t MAXW>
+void launch_compress_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
+                       uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
+  hipLaunchKernelGGL((compress_kernel<NR, MAXW>), dim3(grid_for(n_rows)),
+                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,
+                     (uint32_t*)slots, (unsigned long long*)flags, row_bits, vec);
+}
+
+template <int NR>
+void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
+                        uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
+  // LDS window tiers: the whole row stream (<= n words) lives in LDS
+  if (cd.n <= 1024)
+    launch_compress_t<NR, 1024>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else if (cd.n <= 4096)
+    launch_compress_t<NR, 4096>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else if (cd.n <= 8192)
+    launch_compress_t<NR, 8192>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else
+    launch_compress_t<NR, IBP_MAX_COMPRESS_ROW_BYTES / 4>(cd, n_rows, src, slots, flags,
+                                                          row_bits, vec, st);
+}
+
+template <bool GATHER, int NR>
+void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
+                     const int64_t* ids, uint64_t n_rows, uint64_t n_out, void* dst, int vec,
+                     hipStream_t st) {
+  const uint32_t nseg = (cd.n + kSegBlocks - 1) / kSegBlocks;
+  const uint64_t n_tasks = n_out * nseg;
+  const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((decode_kernel<GATHER, NR>), dim3(grid_for(wgs)),
+                     dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
+                     (const unsigned long long*)flags, ids, n_rows, n_tasks, nseg,
+                     (uint32_t*)dst, vec);
+}
+
+template <bool GATHER>
+void launch_decode(const Codec& cd, const void* slots, const uint64_t* flags,
+                   const int64_t* ids, uint64_t n_rows, uint64_t n_out, void* dst, int vec,
+                   hipStream_t st) {
+  switch (cd.runs.n) {
+    case 0: launch_decode_t<GATHER, 0>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    case 1: launch_decode_t<GATHER, 1>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    case 2: launch_decode_t<GATHER, 2>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    case 3: launch_decode_t<GATHER, 3>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    case 4: launch_decode_t<GATHER, 4>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    default: launch_decode_t<GATHER, -1>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+  }
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ C ABI ----
+
+extern "C" {
+
+uint64_t ibp_flag_words(uint64_t n_rows) { return n_rows / 64 + (n_rows % 64 ? 1 : 0); }
+
+int ibp_last_hip_error(void) { return g_last_hip; }
+
+const char* ibp_status_string(int status) {
+  switch (status) {
+    case IBP_OK: return "ok";
+    case IBP_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case IBP_ERR_UNSUPPORTED: return "unsupported block width or row size";
+    case IBP_ERR_LAYOUT: return "bad layout (row_bytes not a multiple of 4, or misaligned pointer)";
+    case IBP_ERR_EMPTY: return "empty sample";
+    case IBP_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+int ibp_metadata_from_counts(const uint64_t* ones, uint64_t n_blocks, uint32_t width_bits,
+                             uint32_t t_ppm, ibp_metadata* out) {
+  if (!ones || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
+  if (width_bits != 32) return IBP_ERR_UNSUPPORTED;
+  if (n_blocks == 0) return IBP_ERR_EMPTY;
+  uint64_t mask = 0, bitval = 0;
+  for (uint32_t b = 0; b < width_bits; ++b) {
+    if (ones[b] > n_blocks) return IBP_ERR_INVALID_ARGUMENT;
+    const uint64_t zeros = n_blocks - ones[b];
+    const bool one_wins = ones[b] > zeros;  // a tie records 0
+    const unsigned __int128 count = one_wins ? ones[b] : zeros;
+    if (count * 1000000u >= (unsigned __int128)n_blocks * t_ppm) {
+      mask |= 1ull << b;
+      if (one_wins) bitval |= 1ull << b;
+    }
+  }
+  out->width_bits = width_bits;
+  out->invariant_bits = (uint32_t)popcount32(mask);
+  out->mask = mask;
+  out->bitval = bitval;
+  out->t_ppm = t_ppm;
+  out->reserved = 0;
+  return IBP_OK;
+}
+
+int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bits,
+                       uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
+                       void* stream) {
+  if (!sample || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
+  if (width_bits != 32) return IBP_ERR_UNSUPPORTED;
+  if (n_blocks == 0) return IBP_ERR_EMPTY;
+  if (!aligned(sample, 4)) return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  unsigned long long* d_counts = nullptr;
+  hipError_t e = hipMalloc((void**)&d_counts, 32 * sizeof(unsigned long long));
+  if (e != hipSuccess) return hip_fail(e);
+  uint64_t ones[32];
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(64), 0, st, d_counts, 32ull, 0ull);
+  const uint64_t waves = (n_blocks + kWave - 1) / kWave;
+  uint64_t wgs = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (wgs > 2048) wgs = 2048;
+  hipLaunchKernelGGL(count_ones_kernel, dim3((uint32_t)wgs), dim3(kBlockThreads), 0, st,
+                     (const uint32_t*)sample, n_blocks, d_counts);
+  e = hipGetLastError();
+  if (e == hipSuccess) e = hipMemcpyAsync(ones, d_counts, sizeof(ones), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  hipError_t ef = hipFree(d_counts);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  if (out_ones)
+    for (int b = 0; b < 32; ++b) out_ones[b] = ones[b];
+  return ibp_metadata_from_counts(ones, n_blocks, width_bits, t_ppm, out);
+}
+
+int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, const void* src,
+                 void* slots, uint64_t* flags, uint32_t* row_bits, void* stream) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  rc = check_rows(n_rows, row_bytes);
+  if (rc) return rc;
+  if (row_bytes > IBP_MAX_COMPRESS_ROW_BYTES) return IBP_ERR_UNSUPPORTED;
+  if (n_rows == 0) return IBP_OK;
+  if (!src || !slots || !flags) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(src, 4) || !aligned(slots, 4) || !aligned(flags, 8) ||
+      (row_bits && !aligned(row_bits, 4)))
+    return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  const Codec cd = make_codec(md, row_bytes);
+  const int vec = row_bytes % 16 == 0 && aligned(src, 16) && aligned(slots, 16);
+  const uint64_t fw = ibp_flag_words(n_rows);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
+                     (unsigned long long*)flags, fw, 0ull);
+  switch (cd.runs.n) {
+    case 0: launch_compress_nr<0>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+    case 1: launch_compress_nr<1>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+    case 2: launch_compress_nr<2>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+    case 3: launch_compress_nr<3>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+    case 4: launch_compress_nr<4>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+    default: launch_compress_nr<-1>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                         const void* slots, const uint64_t* flags, const int64_t* ids,
+                         uint64_t n_out, void* dst, void* stream, bool gather) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  rc = check_rows(n_rows, row_bytes);
+  if (rc) return rc;
+  if (n_out > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
+  if (n_out == 0) return IBP_OK;
+  if (n_rows == 0 || !slots || !flags || !dst || (gather && !ids))
+    return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(slots, 4) || !aligned(dst, 4) || !aligned(flags, 8) ||
+      (gather && !aligned(ids, 8)))
+    return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  const Codec cd = make_codec(md, row_bytes);
+  const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
+  if (gather)
+    launch_decode<true>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st);
+  else
+    launch_decode<false>(cd, slots, flags, nullptr, n_rows, n_out, dst, vec, st);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+int ibp_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                   const void* slots, const uint64_t* flags, void* dst, void* stream) {
+  return decode_common(md, n_rows, row_bytes, slots, flags, nullptr, n_rows, dst, stream,
+                       false);
+}
+
+int ibp_gather_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                          const void* slots, const uint64_t* flags, const int64_t* row_ids,
+                          uint64_t n_ids, void* dst, void* stream) {
+  return decode_common(md, n_rows, row_bytes, slots, flags, row_ids, n_ids, dst, stream,
+                       true);
+}
+
+int ibp_host_device_pointer(const void* host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr) return IBP_ERR_INVALID_ARGUMENT;
+  hipError_t e = hipHostGetDevicePointer(device_ptr, const_cast<void*>(host_ptr), 0);
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+}  // extern "C"

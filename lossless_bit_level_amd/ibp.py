@@ -1,0 +1,203 @@
+"""Thin ctypes binding of libibp (include/ibp.h), same names as the C ABI.
+
+Argument marshalling only: every step of compression and decompression runs
+in the HIP kernels of libibp.so.  PyTorch supplies device memory and the
+current HIP stream.  If libibp.so has not been built this module raises on
+first use; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libibp.so")
+
+IBP_OK = 0
+IBP_ERR_INVALID_ARGUMENT = -1
+IBP_ERR_UNSUPPORTED = -2
+IBP_ERR_LAYOUT = -3
+IBP_ERR_EMPTY = -4
+IBP_ERR_HIP = -5
+IBP_MAX_COMPRESS_ROW_BYTES = 98304
+
+
+class ibp_metadata(ctypes.Structure):
+    _fields_ = [("width_bits", ctypes.c_uint32),
+                ("invariant_bits", ctypes.c_uint32),
+                ("mask", ctypes.c_uint64),
+                ("bitval", ctypes.c_uint64),
+                ("t_ppm", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
+
+    def __repr__(self):
+        return (f"ibp_metadata(W={self.width_bits}, p={self.invariant_bits}, "
+                f"mask=0x{self.mask:08X}, bitval=0x{self.bitval:08X}, "
+                f"t_ppm={self.t_ppm})")
+
+
+class IBPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = f"{fn}: {status_string(status)} ({status})"
+        if status == IBP_ERR_HIP:
+            msg += f", hipError {lib().ibp_last_hip_error()}"
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libibp.so (built in-tree by lossless_bit_level_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is missing: build it with "
+                "`python -m lossless_bit_level_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, u64, u32, i32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int
+        mdp = ctypes.POINTER(ibp_metadata)
+        L.ibp_metadata_from_counts.argtypes = [vp, u64, u32, u32, mdp]
+        L.ibp_build_metadata.argtypes = [vp, u64, u32, u32, mdp, vp, vp]
+        L.ibp_compress.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp]
+        L.ibp_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, vp]
+        L.ibp_gather_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp]
+        L.ibp_flag_words.argtypes = [u64]
+        L.ibp_flag_words.restype = u64
+        L.ibp_host_device_pointer.argtypes = [vp, ctypes.POINTER(vp)]
+        L.ibp_status_string.argtypes = [i32]
+        L.ibp_status_string.restype = ctypes.c_char_p
+        L.ibp_last_hip_error.argtypes = []
+        for f in ("ibp_metadata_from_counts", "ibp_build_metadata", "ibp_compress",
+                  "ibp_decompress", "ibp_gather_decompress", "ibp_host_device_pointer",
+                  "ibp_last_hip_error"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ibp_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != IBP_OK:
+        raise IBPError(fn, status)
+
+
+def _stream(stream) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dptr(t: torch.Tensor) -> int:
+    """Device-visible address of a CUDA tensor or of a pinned host tensor."""
+    if t.is_cuda:
+        return t.data_ptr()
+    if t.is_pinned():
+        return ibp_host_device_pointer(t)
+    raise ValueError("tensor must be on the GPU or in pinned host memory")
+
+
+def _rows(t: torch.Tensor):
+    """(n_rows, row_bytes) of a tensor whose first axis is the row axis."""
+    if t.dim() == 0:
+        raise ValueError("need at least one dimension")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    n_rows = t.shape[0]
+    row_bytes = (t.numel() // n_rows) * t.element_size() if n_rows else \
+        int(torch.tensor(t.shape[1:]).prod().item()) * t.element_size()
+    return n_rows, row_bytes
+
+
+def ibp_flag_words(n_rows: int) -> int:
+    return int(lib().ibp_flag_words(n_rows))
+
+
+def ibp_host_device_pointer(t: torch.Tensor) -> int:
+    dev = ctypes.c_void_p()
+    _check("ibp_host_device_pointer",
+           lib().ibp_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(dev)))
+    return int(dev.value)
+
+
+def ibp_metadata_from_counts(ones, n_blocks: int, t_ppm: int = 900000,
+                             width_bits: int = 32) -> ibp_metadata:
+    arr = (ctypes.c_uint64 * width_bits)(*[int(v) for v in ones])
+    md = ibp_metadata()
+    _check("ibp_metadata_from_counts",
+           lib().ibp_metadata_from_counts(arr, n_blocks, width_bits, t_ppm, ctypes.byref(md)))
+    return md
+
+
+def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 32,
+                       n_blocks: int | None = None, t_ppm: int | None = None,
+                       stream=None):
+    """Mask/Bitval over the 32-bit blocks of `sample` (GPU or pinned host).
+
+    Returns (ibp_metadata, ones) with ones a list of the per-bit counts.
+    Synchronous."""
+    if n_blocks is None:
+        n_blocks = sample.numel() * sample.element_size() * 8 // width_bits
+    ppm = int(round(t * 1_000_000)) if t_ppm is None else int(t_ppm)
+    md = ibp_metadata()
+    ones = (ctypes.c_uint64 * width_bits)()
+    _check("ibp_build_metadata",
+           lib().ibp_build_metadata(_dptr(sample), n_blocks, width_bits, ppm,
+                                    ctypes.byref(md), ones, _stream(stream)))
+    return md, list(ones)
+
+
+def ibp_compress(md: ibp_metadata, src: torch.Tensor, slots: torch.Tensor | None = None,
+                 flags: torch.Tensor | None = None, row_bits: torch.Tensor | None = None,
+                 want_row_bits: bool = True, stream=None):
+    """Compress the rows of `src` (first axis = rows).  Returns
+    (slots uint8 [n_rows, row_bytes], flags int64 [flag words], row_bits
+    int32 [n_rows] or None).  Asynchronous on the current stream."""
+    n_rows, row_bytes = _rows(src)
+    dev = src.device
+    if slots is None:
+        slots = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device=dev)
+    if flags is None:
+        flags = torch.empty(max(1, ibp_flag_words(n_rows)), dtype=torch.int64, device=dev)
+    if row_bits is None and want_row_bits:
+        row_bits = torch.empty(max(1, n_rows), dtype=torch.int32, device=dev)
+    _check("ibp_compress",
+           lib().ibp_compress(ctypes.byref(md), n_rows, row_bytes, _dptr(src), _dptr(slots),
+                              flags.data_ptr(),
+                              row_bits.data_ptr() if row_bits is not None else None,
+                              _stream(stream)))
+    return slots, flags, row_bits
+
+
+def ibp_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                   out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Restore every row; `out` defaults to uint8 [n_rows, row_bytes] on the GPU."""
+    n_rows, row_bytes = _rows(slots)
+    if out is None:
+        out = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device="cuda")
+    _check("ibp_decompress",
+           lib().ibp_decompress(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
+                                flags.data_ptr(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def ibp_gather_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                          row_ids: torch.Tensor, out: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """out[i] = restored row row_ids[i] (row_ids: int64 on the GPU)."""
+    n_rows, row_bytes = _rows(slots)
+    if row_ids.dtype != torch.int64 or not row_ids.is_cuda:
+        raise ValueError("row_ids must be an int64 GPU tensor")
+    n_ids = row_ids.numel()
+    if out is None:
+        out = torch.empty((n_ids, row_bytes), dtype=torch.uint8, device="cuda")
+    _check("ibp_gather_decompress",
+           lib().ibp_gather_decompress(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
+                                       flags.data_ptr(), row_ids.data_ptr(), n_ids,
+                                       out.data_ptr(), _stream(stream)))
+    return out

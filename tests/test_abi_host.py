@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+* libibp.so loads and exports every function include/ibp.h declares;
+* argument validation returns the documented status before anything is
+  enqueued (these calls never reach HIP);
+* the host half of the metadata step (ibp_metadata_from_counts) agrees with
+  the oracle's rule on the oracle's own counts.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+import synthetic as syn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "lossless_bit_level_amd", "libibp.so")
+HEADER = os.path.join(ROOT, "include", "ibp.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
+                                reason="libibp.so not built (run __graft_entry__.build())")
+
+
+@pytest.fixture(scope="module")
+def ibp():
+    from lossless_bit_level_amd import ibp as b
+    return b
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ibp_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"ibp_build_metadata", "ibp_compress", "ibp_decompress",
+            "ibp_gather_decompress"} <= set(names)
+    L = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_flag_words_and_status_strings(ibp):
+    assert [ibp.ibp_flag_words(n) for n in (0, 1, 63, 64, 65, 128, 129)] == \
+        [0, 1, 1, 1, 2, 2, 3]
+    for s in (0, -1, -2, -3, -4, -5):
+        assert ibp.status_string(s) and ibp.status_string(s) != "unknown status"
+    assert ibp.status_string(7) == "unknown status"
+
+
+def _md(ibp, mask=0x7C000000, bitval=0x3C000000, w=32, p=None):
+    md = ibp.ibp_metadata()
+    md.width_bits, md.mask, md.bitval, md.t_ppm = w, mask, bitval, 900000
+    md.invariant_bits = bin(mask).count("1") if p is None else p
+    return md
+
+
+def test_validation_before_enqueue(ibp):
+    L = ibp.lib()
+    md = _md(ibp)
+    byref = ctypes.byref
+    fake = 0x10000  # never dereferenced: every call below fails validation
+    # null metadata / bad metadata
+    assert L.ibp_compress(None, 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(_md(ibp, w=16)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_compress(byref(_md(ibp, bitval=0x1)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(_md(ibp, p=3)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(_md(ibp, mask=1 << 40, bitval=0)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    # layout
+    assert L.ibp_compress(byref(md), 4, 6, fake, fake, fake, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_compress(byref(md), 4, 0, fake, fake, fake, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_compress(byref(md), 4, 16, fake + 2, fake, fake, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_compress(byref(md), 4, 16, fake, fake, fake + 4, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_compress(byref(md), 4, ibp.IBP_MAX_COMPRESS_ROW_BYTES + 4, fake, fake, fake, None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_compress(byref(md), 4, 16, None, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(md), 1 << 62, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    # empty work is a no-op that needs no pointers
+    assert L.ibp_compress(byref(md), 0, 16, None, None, None, None, None) == ibp.IBP_OK
+    assert L.ibp_gather_decompress(byref(md), 10, 16, fake, fake, fake, 0, fake, None) == ibp.IBP_OK
+    assert L.ibp_decompress(byref(md), 0, 16, None, None, None, None) == ibp.IBP_OK
+    # decode validation
+    assert L.ibp_decompress(byref(md), 4, 16, None, fake, fake, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_gather_decompress(byref(md), 4, 16, fake, fake, None, 3, fake, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_gather_decompress(byref(md), 0, 16, fake, fake, fake, 3, fake, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_gather_decompress(byref(md), 4, 16, fake, fake, fake + 4, 3, fake, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_gather_decompress(byref(md), 4, 1 << 27, fake, fake, fake, 3, fake, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_gather_decompress(byref(md), 4, 16, fake, fake, fake, 1 << 61, fake, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    # metadata build
+    out = ibp.ibp_metadata()
+    assert L.ibp_build_metadata(fake, 0, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_EMPTY
+    assert L.ibp_build_metadata(fake, 10, 16, 900000, byref(out), None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_build_metadata(fake, 10, 32, 1000001, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_build_metadata(None, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_build_metadata(fake + 1, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_host_device_pointer(None, byref(ctypes.c_void_p())) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_last_hip_error() == 0
+
+
+@pytest.mark.parametrize("t_ppm", [0, 500000, 500001, 900000, 999999, 1000000])
+def test_metadata_from_counts_matches_oracle(ibp, t_ppm):
+    rng = np.random.default_rng(t_ppm)
+    samples = [syn.tiny_dense()[:256], syn.sparse_gnn_rows(0, 64),
+               rng.integers(0, 2**32, 4096, dtype=np.uint64).astype(np.uint32),
+               np.array([0x80000001, 0x80000001, 0x00000001, 0xFFFFFFFF], np.uint32)]
+    for x in samples:
+        md_o, ones = orc.build_metadata(x, 32, t_ppm=t_ppm)
+        md = ibp.ibp_metadata_from_counts(ones, x.nbytes // 4, t_ppm=t_ppm)
+        assert (md.mask, md.bitval, md.invariant_bits, md.t_ppm) == \
+            (md_o.mask, md_o.bitval, md_o.invariant_bits, t_ppm)
+
+
+def test_metadata_from_counts_rejects(ibp):
+    L = ibp.lib()
+    ones = (ctypes.c_uint64 * 32)(*([5] * 32))
+    out = ibp.ibp_metadata()
+    assert L.ibp_metadata_from_counts(ones, 4, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_metadata_from_counts(ones, 0, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_EMPTY
+    assert L.ibp_metadata_from_counts(ones, 8, 64, 900000, ctypes.byref(out)) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_metadata_from_counts(None, 8, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_INVALID_ARGUMENT

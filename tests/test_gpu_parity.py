@@ -1,0 +1,361 @@
+"""GPU parity: libibp's HIP kernels against the CPU oracle, byte for byte.
+
+Small cases compare everything (metadata, per-bit counts, flags, row_bits,
+every image byte that belongs to the image, every decompressed byte).  The
+full-size workloads run in the launch configuration the benchmark times and
+compare sampled rows with the oracle plus properties that hold at any size
+(closed-form row sizes, round trip against the source table).
+"""
+import numpy as np
+import pytest
+
+from oracle import oracle as orc
+import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def ibp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from lossless_bit_level_amd import ibp as b
+    b.lib()
+    return b
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_gpu(x: np.ndarray) -> torch.Tensor:
+    x = np.ascontiguousarray(x)
+    return torch.from_numpy(x.reshape(x.shape[0], -1).view(np.uint8)).cuda()
+
+
+def omd(md) -> orc.Metadata:
+    return orc.Metadata(32, int(md.mask), int(md.bitval), int(md.t_ppm))
+
+
+def gmd(ibp, mask, bitval, t_ppm=900000):
+    md = ibp.ibp_metadata()
+    md.width_bits, md.mask, md.bitval, md.t_ppm = 32, mask, bitval, t_ppm
+    md.invariant_bits = bin(mask).count("1")
+    return md
+
+
+def flags_np(flags: torch.Tensor, n_rows: int) -> np.ndarray:
+    return flags.cpu().numpy().view(np.uint64)[:(n_rows + 63) // 64]
+
+
+def assert_image_equal(slots_g, flags_g, rb_g, slots_o, flags_o, rb_o, rows=None):
+    """Flags, row_bits and the image bytes of every (or the listed) row."""
+    n_rows, S = slots_o.shape
+    assert np.array_equal(flags_g, flags_o)
+    assert np.array_equal(rb_g.astype(np.uint64), rb_o)
+    rows = range(n_rows) if rows is None else rows
+    for r in rows:
+        f = int((int(flags_o[r >> 6]) >> (r & 63)) & 1)
+        nb = orc.stored_bytes(S, int(rb_o[r]), f)
+        if not np.array_equal(slots_g[r, :nb], slots_o[r, :nb]):
+            diff = np.nonzero(slots_g[r, :nb] != slots_o[r, :nb])[0]
+            raise AssertionError(f"row {r}: {diff.size} bytes differ, first at {diff[0]}")
+
+
+# --------------------------------------------------------------- metadata --
+
+META_CASES = {
+    "tiny_dense": lambda: syn.tiny_dense(),
+    "sparse_gnn": lambda: syn.sparse_gnn_rows(0, 2048),
+    "dense_gnn": lambda: syn.dense_gnn_rows(0, 4096),
+    "dlrm_emb": lambda: syn.dlrm_emb_rows(0, 8192),
+    "llm_weights": lambda: syn.llm_weight(0, 4, rows=slice(0, 64)),
+    "llm_kv": lambda: syn.llm_kv_batch(0, seq=256),
+    "ragged_random": lambda: np.random.default_rng(5).integers(
+        0, 2**32, 100_003, dtype=np.uint64).astype(np.uint32),
+}
+
+
+@pytest.mark.parametrize("name", list(META_CASES))
+def test_metadata_parity(ibp, name):
+    x = META_CASES[name]()
+    say(f"metadata {name} blocks={x.nbytes // 4}")
+    for t_ppm in (900000, 500000, 1000000):
+        md_o, ones_o = orc.build_metadata(x, 32, t_ppm=t_ppm)
+        md_g, ones_g = ibp.ibp_build_metadata(to_gpu(x.reshape(-1)[None]), t_ppm=t_ppm)
+        assert np.array_equal(np.array(ones_g, np.uint64), ones_o)
+        assert (md_g.mask, md_g.bitval) == (md_o.mask, md_o.bitval)
+        assert md_g.invariant_bits == md_o.invariant_bits
+
+
+def test_metadata_pinned_host_sample(ibp):
+    x = syn.tiny_dense()
+    host = torch.from_numpy(x.reshape(-1).view(np.uint8).copy()).pin_memory()
+    md_g, ones_g = ibp.ibp_build_metadata(host)
+    md_o, ones_o = orc.build_metadata(x, 32)
+    assert np.array_equal(np.array(ones_g, np.uint64), ones_o)
+    assert (md_g.mask, md_g.bitval) == (md_o.mask, md_o.bitval)
+
+
+# ---------------------------------------------------------- codec (small) --
+
+def run_codec_case(ibp, x_u8: np.ndarray, mask: int, bitval: int, ids: np.ndarray):
+    md = gmd(ibp, mask, bitval)
+    xg = to_gpu(x_u8)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    torch.cuda.synchronize()
+    n_rows = x_u8.shape[0]
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x_u8)
+    assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    # decompress the GPU image and the oracle's image
+    back = ibp.ibp_decompress(md, slots, flags)
+    assert torch.equal(back, xg)
+    so = torch.from_numpy(slots_o).cuda()
+    fo = torch.from_numpy(flags_o.view(np.int64).copy() if flags_o.size else np.zeros(1, np.int64)).cuda()
+    assert torch.equal(ibp.ibp_decompress(md, so, fo), xg)
+    # gather
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress(md, slots, flags, idg)
+    torch.cuda.synchronize()
+    want = orc.gather_decompress(omd(md), slots_o, flags_o, ids)
+    assert np.array_equal(out.cpu().numpy(), want)
+    return flags_o
+
+
+def make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=0.85, raw_rows=()):
+    x = rng.integers(0, 2**32, (n_rows, row_bytes // 4), dtype=np.uint64).astype(np.uint32)
+    force = rng.random(x.shape) < match_p
+    x = np.where(force, (x & np.uint32(~mask & 0xFFFFFFFF)) | np.uint32(bitval), x)
+    for r in raw_rows:
+        x[r] = rng.integers(0, 2**32, row_bytes // 4, dtype=np.uint64).astype(np.uint32)
+    return x.astype(np.uint32).view(np.uint8)
+
+
+CODEC_CASES = [
+    # (n_rows, row_bytes, mask, bitval)            runs of ~mask
+    (130, 512, 0x7C000000, 0x3C000000),            # 2   fp32 exponent
+    (65, 2048, 0xFFFFFFFF, 0x00000000),            # 0   sparse
+    (64, 8192, 0x78007800, 0x38003800),            # 3   bf16 pairs, 2 segments
+    (33, 28672, 0x7C007C00, 0x3C003C00),           # 3   7 segments
+    (70, 4100, 0xF0000000, 0x30000000),            # 1   n = 1025: 2 segments, ragged
+    (67, 148, 0x7C000000, 0x3C000000),             # n = 37, row not 16-byte sized
+    (40, 12, 0xC0000000, 0x40000000),              # n = 3
+    (50, 260, 0x00F0F00F, 0x00A0A005),             # 4 runs
+    (45, 1024, 0x55555555, 0x11111111),            # 16 runs (generic path)
+    (20, 2048, 0x00000000, 0x00000000),            # p = 0: everything raw
+    (1, 4, 0xFFFFFFFE, 0x00000000),                # one block
+    (3, 98304, 0x7F800000, 0x3F800000),            # largest compressible row
+]
+
+
+@pytest.mark.parametrize("case", CODEC_CASES, ids=lambda c: f"{c[0]}x{c[1]}_{c[2]:08x}")
+def test_codec_parity(ibp, case):
+    n_rows, row_bytes, mask, bitval = case
+    rng = np.random.default_rng(n_rows * 7919 + row_bytes)
+    say(f"codec rows={n_rows} row_bytes={row_bytes} mask={mask:08x}")
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, raw_rows=(0, n_rows // 2))
+    ids = rng.integers(0, n_rows, 3 * n_rows + 5).astype(np.int64)
+    ids[:3] = [n_rows - 1, 0, n_rows - 1]
+    flags_o = run_codec_case(ibp, x, mask, bitval, ids)
+    if bin(mask).count("1") >= 2 and n_rows > 2 and row_bytes >= 16:
+        assert flags_o.any()  # compressed rows are exercised
+
+
+def test_tiny_dense_round_trip_and_image(ibp):
+    """4096 x 128 fp32 N(0, 0.1^2): metadata, image, decompress, gather."""
+    x = syn.tiny_dense()
+    md, _ = ibp.ibp_build_metadata(to_gpu(x.reshape(-1)[None]))
+    assert (md.mask, md.bitval) == (0x7C000000, 0x3C000000)
+    ids = np.random.default_rng(1).integers(0, 4096, 1000).astype(np.int64)
+    flags_o = run_codec_case(ibp, x.view(np.uint8), md.mask, md.bitval, ids)
+    assert flags_o.all()
+
+
+def test_gather_edge_cases(ibp):
+    rng = np.random.default_rng(3)
+    x = make_rows(rng, 10, 256, 0x7C000000, 0x3C000000)
+    md = gmd(ibp, 0x7C000000, 0x3C000000)
+    xg = to_gpu(x)
+    slots, flags, _ = ibp.ibp_compress(md, xg)
+    # no ids: nothing is written
+    out = torch.full((4, 256), 7, dtype=torch.uint8, device="cuda")
+    ibp.ibp_gather_decompress(md, slots, flags, torch.empty(0, dtype=torch.int64, device="cuda"),
+                              out=out)
+    torch.cuda.synchronize()
+    assert (out == 7).all()
+    # ids outside the table give zero rows; valid ones are restored
+    ids = torch.tensor([3, 10, -1, 9, 1 << 40, 3], dtype=torch.int64, device="cuda")
+    out = ibp.ibp_gather_decompress(md, slots, flags, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], xg[3]) and torch.equal(out[3], xg[9]) and torch.equal(out[5], xg[3])
+    assert (out[1] == 0).all() and (out[2] == 0).all() and (out[4] == 0).all()
+
+
+def test_deterministic_and_stream_ordered(ibp):
+    """Two compressions on a side stream give the same image bytes."""
+    rng = np.random.default_rng(9)
+    x = make_rows(rng, 300, 1024, 0x7C000000, 0x3C000000, raw_rows=(5,))
+    md = gmd(ibp, 0x7C000000, 0x3C000000)
+    xg = to_gpu(x)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        a = ibp.ibp_compress(md, xg)
+        b = ibp.ibp_compress(md, xg)
+        back = ibp.ibp_decompress(md, b[0], b[1])
+    s.synchronize()
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2])
+    assert torch.equal(back, xg)
+    fl = flags_np(a[1], 300)
+    rb = a[2].cpu().numpy()
+    sa, sb = a[0].cpu().numpy(), b[0].cpu().numpy()
+    for r in range(300):
+        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        nb = orc.stored_bytes(1024, int(rb[r]), f)
+        assert np.array_equal(sa[r, :nb], sb[r, :nb])
+
+
+def test_pinned_host_image_gather(ibp):
+    """Zero-copy: the image lives in pinned host memory and the kernels read
+    it across the host link; output equals the device-image gather."""
+    x = syn.llm_kv_batch(0, seq=512).reshape(-1, 2048)       # 1024 pages of 4 KiB
+    md, _ = ibp.ibp_build_metadata(to_gpu(x.reshape(-1)[None]))
+    xg = to_gpu(x)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    host_slots = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host_slots.copy_(slots)
+    ids = torch.from_numpy(np.random.default_rng(4).permutation(1024)[:700].astype(np.int64)).cuda()
+    a = ibp.ibp_gather_decompress(md, slots, flags, ids)
+    b = ibp.ibp_gather_decompress(md, host_slots, flags, ids)
+    full = ibp.ibp_decompress(md, host_slots, flags)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(a, xg[ids])
+    assert torch.equal(full, xg)
+    # compress straight into pinned host slots
+    hs2 = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    _, f2, _ = ibp.ibp_compress(md, xg, slots=hs2)
+    torch.cuda.synchronize()
+    assert torch.equal(f2, flags)
+    assert torch.equal(ibp.ibp_decompress(md, hs2, f2), xg)
+
+
+# ----------------------------------------------------- full-size workloads --
+
+def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
+    """Metadata over the first min(N, 2^24) blocks, compress the whole table,
+    closed-form sizes for every row, sampled image rows against the oracle,
+    every gather batch against the source rows, sampled outputs against the
+    oracle's gather."""
+    n_rows, S = x_np.shape[0], x_np.nbytes // x_np.shape[0]
+    n = S // 4
+    say(f"{name}: table {n_rows} x {S} B")
+    xg = to_gpu(x_np)
+    sample_blocks = min(n_rows * n, 1 << 24)
+    md, ones = ibp.ibp_build_metadata(xg, n_blocks=sample_blocks)
+    md_o, ones_o = orc.build_metadata(x_np.reshape(-1).view(np.uint8)[:sample_blocks * 4], 32)
+    assert (md.mask, md.bitval) == (md_o.mask, md_o.bitval)
+    assert np.array_equal(np.array(ones, np.uint64), ones_o)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    # closed form: C = n + 32n - p*m for every row, m counted with torch
+    words = xg.view(torch.int32).view(n_rows, n)
+    mask_i = int(np.array(md.mask, np.uint32).view(np.int32))
+    bitval_i = int(np.array(md.bitval, np.uint32).view(np.int32))
+    m = ((words & mask_i) == bitval_i).sum(1, dtype=torch.int64)
+    c = n + 32 * n - md.invariant_bits * m
+    assert torch.equal(rb[:n_rows].to(torch.int64), c)
+    fl = flags_np(flags, n_rows)
+    cc = c.cpu().numpy()
+    bits = np.zeros(((n_rows + 63) // 64) * 64, np.uint8)
+    bits[:n_rows] = cc < 32 * n
+    want_flags = np.packbits(bits, bitorder="little").view(np.uint64)
+    assert np.array_equal(fl, want_flags)
+    # sampled rows of the image against the oracle
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([[0, n_rows - 1], rng.integers(0, n_rows, sample_rows)]))
+    sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
+    for j, r in enumerate(rows):
+        s_o, c_o, f_o = orc.compress_row(omd(md), x_np[r])
+        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        assert (c_o, f_o) == (int(cc[r]), f)
+        nb = orc.stored_bytes(S, c_o, f_o)
+        assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
+    # every gather batch against the source rows; sampled outputs vs oracle
+    out = torch.empty((ids_batches.shape[1], S), dtype=torch.uint8, device="cuda")
+    for bi, ids in enumerate(ids_batches):
+        idg = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+        ibp.ibp_gather_decompress(md, slots, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"batch {bi}"
+    pick = rng.integers(0, ids_batches.shape[1], 64)
+    last = ids_batches[-1][pick]
+    got = out[torch.from_numpy(pick).cuda()].cpu().numpy()
+    for j, r in enumerate(last):
+        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        row = orc.decompress_row(omd(md), slots[int(r)].cpu().numpy(), f)
+        assert np.array_equal(got[j], row)
+    stored = sum(orc.stored_bytes(S, int(cc[r]), int(cc[r] < 32 * n)) for r in range(n_rows)) \
+        if n_rows <= 8192 else None
+    say(f"{name}: ok" + (f", ratio {n_rows * S / stored:.3f}" if stored else ""))
+    return md, slots, flags
+
+
+def test_full_sparse_gnn(ibp):
+    x = syn.sparse_gnn_rows()
+    ids = syn.uniform_ids(syn.SPARSE_GNN_ROWS, 8, 65536)
+    md, _, _ = check_full_table(ibp, "sparse_gnn", x, ids)
+    assert (md.mask, md.bitval) == (0xFFFFFFFF, 0)
+
+
+def test_full_dense_gnn(ibp):
+    x = syn.dense_gnn_rows()
+    ids = syn.zipf_ids(syn.DENSE_GNN_ROWS, 8, 65536)
+    md, _, _ = check_full_table(ibp, "dense_gnn", x, ids)
+    assert (md.mask, md.bitval) == (0x7C000000, 0x3C000000)
+
+
+def test_full_dlrm_emb(ibp):
+    x = syn.dlrm_emb_rows()
+    ids = syn.zipf_ids(syn.DLRM_EMB_ROWS, 8, 65536, seed=2)
+    md, _, _ = check_full_table(ibp, "dlrm_emb", x, ids)
+    assert (md.mask, md.bitval) == (0x78000000, 0x38000000)
+
+
+def test_full_llm_kv(ibp):
+    x = syn.llm_kv_pages()
+    ids = syn.kv_page_ids()
+    md, slots, flags = check_full_table(ibp, "llm_kv", x, ids, sample_rows=96)
+    assert (md.mask, md.bitval) == (0x7C007C00, 0x3C003C00)
+    # the same gather from a pinned host copy of the image
+    host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(slots)
+    idg = torch.from_numpy(ids[3]).cuda()
+    a = ibp.ibp_gather_decompress(md, host, flags, idg)
+    assert torch.equal(a, to_gpu(x)[idg])
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_full_llm_weights_layer(ibp, layer):
+    """Every matrix of one layer at full size: compress, full decompress,
+    sampled rows against the oracle.  Metadata of the whole model is the one
+    of layer 0's first matrix sample (same distribution everywhere)."""
+    w0 = syn.llm_weight(0, 0)
+    md, _ = ibp.ibp_build_metadata(to_gpu(w0), n_blocks=min(w0.size // 2, 1 << 24))
+    assert (md.mask, md.bitval) == (0x78007800, 0x38003800)
+    rng = np.random.default_rng(layer)
+    for j in range(syn.LLM_MATRICES):
+        w = syn.llm_weight(layer, j)
+        say(f"layer {layer} matrix {j} shape {w.shape}")
+        wg = to_gpu(w)
+        slots, flags, rb = ibp.ibp_compress(md, wg)
+        back = ibp.ibp_decompress(md, slots, flags)
+        assert torch.equal(back, wg)
+        fl = flags_np(flags, w.shape[0])
+        rbn = rb.cpu().numpy()
+        for r in np.concatenate([[0, w.shape[0] - 1], rng.integers(0, w.shape[0], 24)]):
+            s_o, c_o, f_o = orc.compress_row(omd(md), w[r])
+            assert int(rbn[r]) == c_o
+            assert int((int(fl[r >> 6]) >> (r & 63)) & 1) == f_o
+            nb = orc.stored_bytes(w.shape[1] * 2, c_o, f_o)
+            assert np.array_equal(slots[int(r), :nb].cpu().numpy(), s_o[:nb])
