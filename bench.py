@@ -171,6 +171,9 @@ def main():
                     choices=["sparse_gnn", "dense_gnn", "dlrm_emb", "llm_weights", "llm_kv"])
     ap.add_argument("--source", default="device", choices=["device", "host"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the timed loop "
+                         "(calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -262,6 +265,14 @@ def main():
             ibp.ibp_decompress(md, slots, flags, out=out)
         else:
             ibp.ibp_gather_decompress(md, slots, flags, idg, out=out)
+
+    if args.pmc_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
 
     for k in range(args.warmup):
         launch(k)

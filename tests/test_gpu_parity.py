@@ -46,6 +46,11 @@ def gmd(ibp, mask, bitval, t_ppm=900000):
     return md
 
 
+def flag_of(fl: np.ndarray, r) -> int:
+    r = int(r)
+    return (int(fl[r >> 6]) >> (r & 63)) & 1
+
+
 def flags_np(flags: torch.Tensor, n_rows: int) -> np.ndarray:
     return flags.cpu().numpy().view(np.uint64)[:(n_rows + 63) // 64]
 
@@ -57,7 +62,7 @@ def assert_image_equal(slots_g, flags_g, rb_g, slots_o, flags_o, rb_o, rows=None
     assert np.array_equal(rb_g.astype(np.uint64), rb_o)
     rows = range(n_rows) if rows is None else rows
     for r in rows:
-        f = int((int(flags_o[r >> 6]) >> (r & 63)) & 1)
+        f = flag_of(flags_o, r)
         nb = orc.stored_bytes(S, int(rb_o[r]), f)
         if not np.array_equal(slots_g[r, :nb], slots_o[r, :nb]):
             diff = np.nonzero(slots_g[r, :nb] != slots_o[r, :nb])[0]
@@ -212,7 +217,7 @@ def test_deterministic_and_stream_ordered(ibp):
     rb = a[2].cpu().numpy()
     sa, sb = a[0].cpu().numpy(), b[0].cpu().numpy()
     for r in range(300):
-        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        f = flag_of(fl, r)
         nb = orc.stored_bytes(1024, int(rb[r]), f)
         assert np.array_equal(sa[r, :nb], sb[r, :nb])
 
@@ -278,7 +283,7 @@ def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
     for j, r in enumerate(rows):
         s_o, c_o, f_o = orc.compress_row(omd(md), x_np[r])
-        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        f = flag_of(fl, r)
         assert (c_o, f_o) == (int(cc[r]), f)
         nb = orc.stored_bytes(S, c_o, f_o)
         assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
@@ -292,7 +297,7 @@ def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     last = ids_batches[-1][pick]
     got = out[torch.from_numpy(pick).cuda()].cpu().numpy()
     for j, r in enumerate(last):
-        f = int((int(fl[r >> 6]) >> (r & 63)) & 1)
+        f = flag_of(fl, r)
         row = orc.decompress_row(omd(md), slots[int(r)].cpu().numpy(), f)
         assert np.array_equal(got[j], row)
     stored = sum(orc.stored_bytes(S, int(cc[r]), int(cc[r] < 32 * n)) for r in range(n_rows)) \
@@ -356,6 +361,6 @@ def test_full_llm_weights_layer(ibp, layer):
         for r in np.concatenate([[0, w.shape[0] - 1], rng.integers(0, w.shape[0], 24)]):
             s_o, c_o, f_o = orc.compress_row(omd(md), w[r])
             assert int(rbn[r]) == c_o
-            assert int((int(fl[r >> 6]) >> (r & 63)) & 1) == f_o
+            assert flag_of(fl, r) == f_o
             nb = orc.stored_bytes(w.shape[1] * 2, c_o, f_o)
             assert np.array_equal(slots[int(r), :nb].cpu().numpy(), s_o[:nb])
