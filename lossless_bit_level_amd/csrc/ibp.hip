@@ -28,6 +28,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "ibp.h"
 
 namespace {
@@ -40,6 +42,7 @@ constexpr uint32_t kSegLdsWords = kSegBlocks + 8;
 constexpr uint64_t kMaxRowBytes = 1ull << 26;  // bit offsets fit 32 bits, counts 24
 constexpr int kMaxRuns = 16;                   // runs of ~Mask for W = 32
 constexpr uint32_t kMaxGrid = 1u << 24;
+constexpr uint32_t kSpecWords = 32;            // first slot words fetched with the header
 
 // Run decomposition of the kept (non-invariant) bit positions ~Mask.  Run j
 // is a maximal stretch of kept block bits; `place[j]` is its mask in the
@@ -103,10 +106,16 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint32_t lo, uint32_t hi) {
   return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
 }
 
+// Sum over the 64 lanes with DPP row shifts and row broadcasts (an inclusive
+// scan; lane 63 ends up with the total), result in a scalar register.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-  return v;
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, uint32_t lane) {
@@ -138,14 +147,16 @@ __device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t g) {
 // One block per lane: pull the payload at bit `rel` of the LDS window out of
 // two words with a funnel shift; a stripped block (its bit set in the 64-bit
 // chunk header, used directly as a lane mask) gets its invariant bits back.
+__device__ __forceinline__ uint32_t lds_bits(const uint32_t* lds, uint32_t rel) {
+  const uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
+  return __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], rel & 31u);
+}
+
 template <int NR>
 __device__ __forceinline__ uint32_t decode_block(const uint32_t* lds, uint32_t rel,
                                                  uint32_t h_lo, uint32_t h_hi,
                                                  const Codec& cd) {
-  const uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
-  const uint32_t w0 = lds[wi];
-  const uint32_t w1 = lds[wi + 1];
-  const uint32_t v = __builtin_amdgcn_alignbit(w1, w0, rel & 31u);
+  const uint32_t v = lds_bits(lds, rel);
   const uint32_t dep = deposit_kept<NR>(v, cd.runs, cd.bitval);
   const bool stripped =
       __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
 //      -> two LDS words -> funnel shift -> deposit + Bitval -> store.
 // A raw row is a straight copy.
 template <bool GATHER, int NR>
-__global__ __launch_bounds__(kBlockThreads) void decode_kernel(
+__global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     Codec cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t* __restrict__ dst, int vec) {
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
     if (lo) {
       uint32_t acc = 0;
       for (uint32_t t = lane; t < lo / 32; t += kWave) acc += __popc(src[t]);
-      carry = uniform(wave_sum(acc));
+      carry = wave_sum(acc);
     }
     // the segment's header words, one per lane; bits at or past n belong to
     // the payloads and are cleared
@@ -349,7 +360,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
       uint32_t valid_bits = min(32u, hi - 32u * t);
       if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
     }
-    const uint32_t m_seg = uniform(wave_sum(__popc(hw)));
+    const uint32_t m_seg = wave_sum(__popc(hw));
 
     // stream bit range of the segment's payloads, and its LDS window
     // (for an image that ibp_compress wrote, wb <= ceil(C/32) <= n; the
@@ -397,6 +408,165 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(
       if (valid) out[k0 + lane] = x;
     }
     wave_lds_sync();
+  }
+}
+
+// [IBP] Decompression of short rows (n <= kSegBlocks blocks: one task per
+// row), software pipelined across the rows a wave handles.  The first
+// kSpecWords words of a slot hold the whole participation header (n/32 <= 32
+// words) and, for well compressed rows, often the whole stream; so while the
+// wave decodes row j it already has in flight the id of row j+2 and the flag
+// word and first slot words of row j+1 (kept in one VGPR).
+//
+// One hardware counter tracks a wave's loads and stores together, so a wait
+// for the prefetched window can only spare the stores issued after it if
+// their number is known when the kernel is compiled.  With NCH > 0 (rows of
+// exactly 64*NCH blocks) every row path issues exactly NCH stores after the
+// prefetch, the decode is fully unrolled, and the first window is waited for
+// before the loop: the wait at the top of the loop then leaves the previous
+// row's stores in flight.  NCH == 0 handles any n.  n_out < 2^31 (the host
+// splits larger gathers).
+template <bool GATHER, int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
+    Codec cd, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint32_t n_out, uint32_t* __restrict__ dst, int vec) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint32_t n = NCH > 0 ? (uint32_t)NCH * kWave : cd.n;
+  const uint32_t spec = min(n, kSpecWords);
+  const uint32_t hw_n = (n + 31) / 32;
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  const uint32_t keep_bits = 32u - cd.p;
+  const uint32_t lane_keep = lane * keep_bits;
+  const uint32_t full = n & ~(uint32_t)(kWave - 1);
+
+  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (i >= n_out) return;
+
+  auto row_id = [&](uint32_t r) -> uint64_t { return GATHER ? (uint64_t)ids[r] : r; };
+  auto in_table = [&](uint64_t id) -> bool { return !GATHER || id < n_rows; };
+
+  uint64_t id = row_id(i);
+  unsigned long long fw = in_table(id) ? flags[id >> 6] : 0ull;
+  uint32_t win = (in_table(id) && lane < spec) ? slots[id * n + lane] : 0u;
+  uint64_t id_next = (i + stride < n_out) ? row_id(i + stride) : 0;
+  asm volatile("" ::"v"(win));  // the first window is waited for here, not in the loop
+
+  while (true) {
+    const uint32_t i_next = i + stride;
+    const bool have_next = i_next < n_out;
+    const uint64_t id_after = (have_next && i_next + stride < n_out) ? row_id(i_next + stride) : 0;
+    uint32_t* out = dst + (uint64_t)i * n;
+    const uint32_t* src = slots + id * n;
+    const bool valid_id = in_table(id);
+    const bool flag = valid_id && ((fw >> (id & 63)) & 1ull);
+
+    // with NCH > 0 a raw row is staged in LDS like a stream, so that its
+    // copy out issues no loads after the prefetch below
+    if (flag || (NCH > 0 && valid_id)) {
+      uint32_t wb = n;
+      if (flag) {
+        // header words are lanes [0, hw_n) of the window; bits at or past n
+        // belong to the payloads
+        uint32_t hw = lane < hw_n ? win : 0u;
+        if (lane == hw_n - 1 && (n & 31u)) hw &= (1u << (n & 31u)) - 1u;
+        const uint32_t m = wave_sum(__popc(hw));
+        wb = min((n + 32u * n - cd.p * m + 31u) >> 5, n);
+      }
+      if (lane < spec) lds[lane] = win;
+      if (wb > spec) {  // the rest of the stream
+        if (vec) {
+          const uint4* g4 = reinterpret_cast<const uint4*>(src);
+          uint4* l4 = reinterpret_cast<uint4*>(lds);
+          for (uint32_t j = spec / 4 + lane; j < (wb + 3u) / 4u; j += kWave) l4[j] = g4[j];
+        } else {
+          for (uint32_t j = spec + lane; j < wb; j += kWave) lds[j] = src[j];
+        }
+      }
+      wave_lds_sync();
+    }
+
+    // next row's flag word and window: in flight while this row is decoded
+    unsigned long long fw_next = 0;
+    uint32_t win_next = 0;
+    if (have_next && in_table(id_next)) {
+      fw_next = flags[id_next >> 6];
+      win_next = lane < spec ? slots[id_next * n + lane] : 0u;
+    }
+
+    if constexpr (NCH > 0) {
+      // exactly NCH stores on every path
+      uint32_t x[NCH];
+      if (!flag) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = valid_id ? lds[c * kWave + lane] : 0u;
+      } else {
+        uint32_t u = n;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+          const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+          const uint32_t rel = u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi));
+          x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+          u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) out[c * kWave + lane] = x[c];
+      // keep the stores ahead of the hand-over of the next window, so that
+      // waiting for it can leave them in flight
+      __builtin_amdgcn_sched_barrier(0);
+      wave_lds_sync();
+    } else if (!valid_id) {
+      for (uint32_t j = lane; j < n; j += kWave) out[j] = 0u;
+    } else if (!flag) {
+      if (vec) {
+        const uint4* a = reinterpret_cast<const uint4*>(src);
+        uint4* o = reinterpret_cast<uint4*>(out);
+        for (uint32_t j = lane; j < n / 4; j += kWave) o[j] = a[j];
+      } else {
+        for (uint32_t j = lane; j < n; j += kWave) out[j] = src[j];
+      }
+    } else {
+      // u: stream bit offset of the payload of the current chunk's first
+      // block.  Lane l's payload starts l*(32-p) + p*(unstripped blocks of the
+      // chunk below l) further on.
+      uint32_t u = n;
+      uint32_t k0 = 0;
+      for (; k0 < full; k0 += kWave) {
+        const uint32_t q = k0 / 32;
+        const uint32_t h_lo = __builtin_amdgcn_readlane(win, q);
+        const uint32_t h_hi = __builtin_amdgcn_readlane(win, q + 1);
+        const uint32_t rel = u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi));
+        uint32_t* o = out + k0;
+        o[lane] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+        u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+      }
+      if (k0 < n) {  // ragged end of the row (n not a multiple of 64)
+        const uint32_t q = k0 / 32;
+        const uint32_t bits0 = n - k0;  // 1..63 header bits left
+        uint32_t h_lo = __builtin_amdgcn_readlane(win, q);
+        uint32_t h_hi = q + 1 < hw_n ? __builtin_amdgcn_readlane(win, q + 1) : 0u;
+        if (bits0 < 32) { h_lo &= (1u << bits0) - 1u; h_hi = 0; }
+        else h_hi &= (bits0 == 32) ? 0u : ((1u << (bits0 - 32)) - 1u);
+        const bool valid = lane < bits0;
+        const uint32_t rel =
+            valid ? u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi)) : 0u;
+        const uint32_t x = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+        if (valid) out[k0 + lane] = x;
+      }
+      wave_lds_sync();
+    }
+
+    if (!have_next) break;
+    i = i_next;
+    id = id_next;
+    id_next = id_after;
+    fw = fw_next;
+    win = win_next;
   }
 }
 
@@ -483,14 +653,59 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
                                                           row_bits, vec, st);
 }
 
+int g_cu_count = 0;
+
+uint32_t resident_workgroups() {
+  if (!g_cu_count) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus > 0)
+      g_cu_count = cus;
+    else
+      g_cu_count = 256;
+  }
+  // 8 workgroups of 4 waves fill a CU's 32 wave slots
+  return 8u * (uint32_t)g_cu_count;
+}
+
 template <bool GATHER, int NR>
 void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
                      const int64_t* ids, uint64_t n_rows, uint64_t n_out, void* dst, int vec,
                      hipStream_t st) {
+  if (cd.n <= kSegBlocks) {
+    const uint64_t piece = 1ull << 30;
+    for (uint64_t off = 0; off < n_out; off += piece) {
+      const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, n_out - off);
+      const uint64_t wgs = (cnt + kWavesPerBlock - 1) / kWavesPerBlock;
+      const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, resident_workgroups());
+      // a full decompress is the identity gather: row `off + r` of the table
+      const uint32_t* sl = (const uint32_t*)slots;
+      const unsigned long long* fl = (const unsigned long long*)flags;
+      if (!GATHER) {  // shift the table window; flags stay word aligned (piece % 64 == 0)
+        sl += off * cd.n;
+        fl += off / 64;
+      }
+      const int64_t* id_p = GATHER ? ids + off : ids;
+      uint32_t* out_p = (uint32_t*)dst + off * cd.n;
+#define IBP_ROWS(NCH)                                                                     \
+  hipLaunchKernelGGL((decode_rows_kernel<GATHER, NR, NCH>), dim3(grid), dim3(kBlockThreads), \
+                     0, st, cd, sl, fl, id_p, n_rows, cnt, out_p, vec)
+      switch (cd.n) {
+        case 128: IBP_ROWS(2); break;
+        case 256: IBP_ROWS(4); break;
+        case 512: IBP_ROWS(8); break;
+        case 1024: IBP_ROWS(16); break;
+        default: IBP_ROWS(0); break;
+      }
+#undef IBP_ROWS
+    }
+    return;
+  }
   const uint32_t nseg = (cd.n + kSegBlocks - 1) / kSegBlocks;
   const uint64_t n_tasks = n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((decode_kernel<GATHER, NR>), dim3(grid_for(wgs)),
+  hipLaunchKernelGGL((decode_segments_kernel<GATHER, NR>), dim3(grid_for(wgs)),
                      dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
                      (const unsigned long long*)flags, ids, n_rows, n_tasks, nseg,
                      (uint32_t*)dst, vec);

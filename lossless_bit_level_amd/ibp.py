@@ -201,3 +201,40 @@ def ibp_gather_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Te
                                        flags.data_ptr(), row_ids.data_ptr(), n_ids,
                                        out.data_ptr(), _stream(stream)))
     return out
+
+
+def ibp_gather_decompress_launcher(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                                   row_ids: torch.Tensor, out: torch.Tensor, stream=None):
+    """ibp_gather_decompress with every argument converted once: returns a
+    no-argument callable that enqueues the same call again (for loops that
+    launch the same gather many times).  The tensors must stay alive."""
+    n_rows, row_bytes = _rows(slots)
+    if row_ids.dtype != torch.int64 or not row_ids.is_cuda:
+        raise ValueError("row_ids must be an int64 GPU tensor")
+    fn = lib().ibp_gather_decompress
+    args = (ctypes.byref(md), ctypes.c_uint64(n_rows), ctypes.c_uint64(row_bytes),
+            ctypes.c_void_p(_dptr(slots)), ctypes.c_void_p(flags.data_ptr()),
+            ctypes.c_void_p(row_ids.data_ptr()), ctypes.c_uint64(row_ids.numel()),
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_gather_decompress", rc)
+    return launch
+
+
+def ibp_decompress_launcher(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                            out: torch.Tensor, stream=None):
+    """ibp_decompress with its arguments converted once (see above)."""
+    n_rows, row_bytes = _rows(slots)
+    fn = lib().ibp_decompress
+    args = (ctypes.byref(md), ctypes.c_uint64(n_rows), ctypes.c_uint64(row_bytes),
+            ctypes.c_void_p(_dptr(slots)), ctypes.c_void_p(flags.data_ptr()),
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_decompress", rc)
+    return launch

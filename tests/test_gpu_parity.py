@@ -153,15 +153,23 @@ CODEC_CASES = [
     (20, 2048, 0x00000000, 0x00000000),            # p = 0: everything raw
     (1, 4, 0xFFFFFFFE, 0x00000000),                # one block
     (3, 98304, 0x7F800000, 0x3F800000),            # largest compressible row
+    # nearly every block stripped: whole chunks of stripped blocks
+    (64, 4096, 0xFFFFFFFF, 0x3F800000, 0.998),     # p = 32, n = 1024
+    (96, 2048, 0xFFFFFFFF, 0x00000000, 0.995),     # p = 32, n = 512
+    (50, 1024, 0x7C000000, 0x3C000000, 0.999),     # 2 runs
+    (40, 8192, 0x78007800, 0x38003800, 0.999),     # segmented rows
 ]
 
 
-@pytest.mark.parametrize("case", CODEC_CASES, ids=lambda c: f"{c[0]}x{c[1]}_{c[2]:08x}")
+@pytest.mark.parametrize("case", CODEC_CASES,
+                         ids=lambda c: f"{c[0]}x{c[1]}_{c[2]:08x}" + (f"_m{c[4]}" if len(c) > 4 else ""))
 def test_codec_parity(ibp, case):
-    n_rows, row_bytes, mask, bitval = case
+    n_rows, row_bytes, mask, bitval = case[:4]
+    match_p = case[4] if len(case) > 4 else 0.85
     rng = np.random.default_rng(n_rows * 7919 + row_bytes)
-    say(f"codec rows={n_rows} row_bytes={row_bytes} mask={mask:08x}")
-    x = make_rows(rng, n_rows, row_bytes, mask, bitval, raw_rows=(0, n_rows // 2))
+    say(f"codec rows={n_rows} row_bytes={row_bytes} mask={mask:08x} match={match_p}")
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=match_p,
+                  raw_rows=(0, n_rows // 2))
     ids = rng.integers(0, n_rows, 3 * n_rows + 5).astype(np.int64)
     ids[:3] = [n_rows - 1, 0, n_rows - 1]
     flags_o = run_codec_case(ibp, x, mask, bitval, ids)
