@@ -106,6 +106,11 @@ __device__ __forceinline__ uint32_t bits_below_lane(uint32_t lo, uint32_t hi) {
   return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
 }
 
+// The same plus acc (v_mbcnt accumulates into its second operand).
+__device__ __forceinline__ uint32_t bits_below_lane_acc(uint32_t lo, uint32_t hi, uint32_t acc) {
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, acc));
+}
+
 // Sum over the 64 lanes with DPP row shifts and row broadcasts (an inclusive
 // scan; lane 63 ends up with the total), result in a scalar register.
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
@@ -503,6 +508,21 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
       if (!flag) {
 #pragma unroll
         for (int c = 0; c < NCH; ++c) x[c] = valid_id ? lds[c * kWave + lane] : 0u;
+      } else if constexpr (NR == 0) {
+        // p = 32: a stripped block is Bitval and every other payload is one
+        // whole stream word (n is a multiple of 64, so payloads stay word
+        // aligned): word index = header words + unstripped blocks before it
+        uint32_t uw = n / 32;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+          const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+          const uint32_t v = lds[bits_below_lane_acc(~h_lo, ~h_hi, uw)];
+          const bool stripped =
+              __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+          x[c] = stripped ? cd.bitval : v;
+          uw += __popc(~h_lo) + __popc(~h_hi);
+        }
       } else {
         uint32_t u = n;
 #pragma unroll
@@ -514,8 +534,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
           u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
         }
       }
+      // the restored rows are streamed out: non-temporal stores
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) out[c * kWave + lane] = x[c];
+      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
       // keep the stores ahead of the hand-over of the next window, so that
       // waiting for it can leave them in flight
       __builtin_amdgcn_sched_barrier(0);
