@@ -399,8 +399,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
       const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
       const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
       const uint32_t rel = u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi));
-      uint32_t* o = out + k0;
-      o[lane] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+      __builtin_nontemporal_store(decode_block<NR>(lds, rel, h_lo, h_hi, cd), out + k0 + lane);
       u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
     }
     if (k0 < hi) {  // ragged end of the row (n not a multiple of 64)
@@ -676,7 +675,8 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
 
 int g_cu_count = 0;
 
-uint32_t resident_workgroups() {
+// Workgroups for a launch: mult per CU (8 workgroups of 4 waves fill a CU).
+uint32_t workgroups_per_device(uint32_t mult) {
   if (!g_cu_count) {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
@@ -686,8 +686,7 @@ uint32_t resident_workgroups() {
     else
       g_cu_count = 256;
   }
-  // 8 workgroups of 4 waves fill a CU's 32 wave slots
-  return 8u * (uint32_t)g_cu_count;
+  return mult * (uint32_t)g_cu_count;
 }
 
 template <bool GATHER, int NR>
@@ -699,7 +698,13 @@ void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
     for (uint64_t off = 0; off < n_out; off += piece) {
       const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, n_out - off);
       const uint64_t wgs = (cnt + kWavesPerBlock - 1) / kWavesPerBlock;
-      const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, resident_workgroups());
+      // Grid size (measured on MI355X): with Mask = all ones (p = 32) the
+      // streams of sparse rows fit the prefetched window and one row per wave
+      // with many workgroups in flight is fastest; rows of 1024 blocks do best
+      // with 16 workgroups per CU; shorter dense rows, which need a second
+      // load per row, profit most from the pipeline of a resident grid.
+      const uint32_t mult = cd.p == 32 ? 64u : (cd.n >= 1024 ? 16u : 8u);
+      const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(mult));
       // a full decompress is the identity gather: row `off + r` of the table
       const uint32_t* sl = (const uint32_t*)slots;
       const unsigned long long* fl = (const unsigned long long*)flags;
