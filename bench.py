@@ -223,11 +223,11 @@ def main():
         torch.cuda.synchronize()
         comp_ms += e0.elapsed_time(e1)
         rbn = rb.cpu().numpy()[:tg.shape[0]]
-        sb = stored_bytes_per_row(rbn, S)
+        sb = stored_bytes_per_row(rbn, tg.shape[1])
         images.append((slots, flags, sb))
         raw_bytes += tg.numel()
         stored += int(sb.sum())
-        bits_total += int(np.minimum(rbn.astype(np.int64), 8 * S).sum())
+        bits_total += int(np.minimum(rbn.astype(np.int64), 8 * tg.shape[1]).sum())
     comp_GBps = raw_bytes / (comp_ms / 1e3) / 1e9
     log(f"metadata {md} in {meta_ms:.1f} ms; compress {comp_ms:.2f} ms ({comp_GBps:.0f} GB/s); "
         f"ratio {raw_bytes / stored:.4f}")
@@ -257,7 +257,7 @@ def main():
         if ids is None:
             n = wl.tables[ti].shape[0]
             return int(sb.sum()) + wl.tables[ti].nbytes + 8 * ((n + 63) // 64)
-        return int(sb[ids].sum()) + len(ids) * S + 8 * len(ids) + \
+        return int(sb[ids].sum()) + len(ids) * wl.tables[ti].nbytes // wl.tables[ti].shape[0] + 8 * len(ids) + \
             8 * len(np.unique(ids >> 6))
 
     plan_bytes = [algo_bytes(ti, ids) for ti, _, _, ids in plan]

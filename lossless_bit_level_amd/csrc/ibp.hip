@@ -176,29 +176,67 @@ __global__ void fill_u64_kernel(unsigned long long* p, uint64_t n, unsigned long
     p[i] = v;
 }
 
-// [IBP] Preprocessing, device half: per-bit one counts over the sample.  Each
-// wave ballots bit b of its 64 blocks and accumulates the popcount in a
-// scalar register; one atomic per bit and wave at the end.
+// [IBP] Preprocessing, device half: per-bit one counts over the sample.
+// Each wave ballots bit b of its blocks and accumulates the popcount in a
+// scalar register; the 4 waves of a workgroup add theirs in LDS and the
+// workgroup writes one row of 32 partial counts (no atomics: contended
+// atomics on 32 counters serialise); reduce_counts_kernel sums the rows.
+// Blocks are read 4 per lane (16-byte loads) where the sample allows it.
 __global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
     const uint32_t* __restrict__ sample, uint64_t n_blocks,
-    unsigned long long* __restrict__ counts) {
+    unsigned long long* __restrict__ partials) {
+  __shared__ unsigned long long part[kWavesPerBlock][32];
   const uint32_t lane = lane_id();
-  const uint64_t gwave = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint64_t gwave = (uint64_t)blockIdx.x * kWavesPerBlock + wave;
   const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
   uint64_t acc[32];
 #pragma unroll
   for (int b = 0; b < 32; ++b) acc[b] = 0;
-  for (uint64_t base = gwave * kWave; base < n_blocks; base += nwaves * kWave) {
-    uint64_t k = base + lane;
-    uint32_t x = k < n_blocks ? sample[k] : 0u;
+  const bool vec = ((uintptr_t)sample % 16) == 0;
+  const uint64_t n4 = vec ? n_blocks / (4 * kWave) : 0;  // whole 256-block groups
+  for (uint64_t g = gwave; g < n4; g += nwaves) {
+    const uint4 x4 = reinterpret_cast<const uint4*>(sample)[g * kWave + lane];
+    const uint32_t xs[4] = {x4.x, x4.y, x4.z, x4.w};
 #pragma unroll
-    for (int b = 0; b < 32; ++b)
-      acc[b] += __popcll(__ballot((x >> b) & 1u));
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int b = 0; b < 32; ++b) acc[b] += __popcll(__ballot((xs[j] >> b) & 1u));
+    }
+  }
+  for (uint64_t base = n4 * 4 * kWave + gwave * kWave; base < n_blocks; base += nwaves * kWave) {
+    const uint64_t k = base + lane;
+    const uint32_t x = k < n_blocks ? sample[k] : 0u;
+#pragma unroll
+    for (int b = 0; b < 32; ++b) acc[b] += __popcll(__ballot((x >> b) & 1u));
   }
   if (lane == 0) {
 #pragma unroll
-    for (int b = 0; b < 32; ++b)
-      if (acc[b]) atomicAdd(&counts[b], (unsigned long long)acc[b]);
+    for (int b = 0; b < 32; ++b) part[wave][b] = acc[b];
+  }
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    unsigned long long t = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) t += part[w][threadIdx.x];
+    partials[(uint64_t)blockIdx.x * 32 + threadIdx.x] = t;
+  }
+}
+
+// counts[b] = sum over the n_parts rows of partials[.][b]; one workgroup.
+__global__ __launch_bounds__(kBlockThreads) void reduce_counts_kernel(
+    const unsigned long long* __restrict__ partials, uint32_t n_parts,
+    unsigned long long* __restrict__ counts) {
+  __shared__ unsigned long long red[kBlockThreads];
+  const uint32_t b = threadIdx.x & 31u, r0 = threadIdx.x >> 5;  // 8 row lanes per bit
+  unsigned long long t = 0;
+  for (uint32_t r = r0; r < n_parts; r += kBlockThreads / 32) t += partials[(uint64_t)r * 32 + b];
+  red[threadIdx.x] = t;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    unsigned long long s = 0;
+    for (uint32_t k = 0; k < kBlockThreads / 32; ++k) s += red[k * 32 + threadIdx.x];
+    counts[threadIdx.x] = s;
   }
 }
 
@@ -806,20 +844,24 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
   if (n_blocks == 0) return IBP_ERR_EMPTY;
   if (!aligned(sample, 4)) return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
-  unsigned long long* d_counts = nullptr;
-  hipError_t e = hipMalloc((void**)&d_counts, 32 * sizeof(unsigned long long));
+  const uint64_t waves = (n_blocks + 4 * kWave - 1) / (4 * kWave);
+  const uint32_t grid = (uint32_t)std::max<uint64_t>(
+      1, std::min<uint64_t>((waves + kWavesPerBlock - 1) / kWavesPerBlock,
+                            workgroups_per_device(4)));
+  // partial counts (grid rows of 32) followed by the 32 totals
+  unsigned long long* d_buf = nullptr;
+  hipError_t e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * 32 * sizeof(unsigned long long));
   if (e != hipSuccess) return hip_fail(e);
+  unsigned long long* d_counts = d_buf + (size_t)grid * 32;
   uint64_t ones[32];
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(1), dim3(64), 0, st, d_counts, 32ull, 0ull);
-  const uint64_t waves = (n_blocks + kWave - 1) / kWave;
-  uint64_t wgs = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (wgs > 2048) wgs = 2048;
-  hipLaunchKernelGGL(count_ones_kernel, dim3((uint32_t)wgs), dim3(kBlockThreads), 0, st,
-                     (const uint32_t*)sample, n_blocks, d_counts);
+  hipLaunchKernelGGL(count_ones_kernel, dim3(grid), dim3(kBlockThreads), 0, st,
+                     (const uint32_t*)sample, n_blocks, d_buf);
+  hipLaunchKernelGGL(reduce_counts_kernel, dim3(1), dim3(kBlockThreads), 0, st,
+                     (const unsigned long long*)d_buf, grid, d_counts);
   e = hipGetLastError();
   if (e == hipSuccess) e = hipMemcpyAsync(ones, d_counts, sizeof(ones), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  hipError_t ef = hipFree(d_counts);
+  hipError_t ef = hipFree(d_buf);
   if (e == hipSuccess) e = ef;
   if (e != hipSuccess) return hip_fail(e);
   if (out_ones)

@@ -207,6 +207,38 @@ def test_gather_edge_cases(ibp):
     assert (out[1] == 0).all() and (out[2] == 0).all() and (out[4] == 0).all()
 
 
+@pytest.mark.parametrize("n_ids,row_bytes,mask,bitval,match_p", [
+    (300_000, 2048, 0xFFFFFFFF, 0x00000000, 0.99),   # p = 32 path, several rows per wave
+    (40_000, 512, 0x7C000000, 0x3C000000, 0.95),     # pipelined dense path, several rows per wave
+    (30_000, 148, 0x7C000000, 0x3C000000, 0.95),     # n = 37: generic path, several rows per wave
+    (20_000, 4096, 0x7C007C00, 0x3C003C00, 0.90),    # rows of 1024 blocks
+])
+def test_gather_more_rows_than_waves(ibp, n_ids, row_bytes, mask, bitval, match_p):
+    """Gathers longer than one row per wave exercise the cross-row prefetch
+    pipeline (and its raw and out-of-table rows); checked against the source
+    rows on the GPU and sampled rows against the oracle."""
+    rng = np.random.default_rng(n_ids + row_bytes)
+    n_rows = 3000
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=match_p, raw_rows=(7, 1500))
+    md = gmd(ibp, mask, bitval)
+    xg = to_gpu(x)
+    slots, flags, _ = ibp.ibp_compress(md, xg)
+    ids = rng.integers(0, n_rows, n_ids).astype(np.int64)
+    ids[::997] = n_rows + 5          # outside the table: zero rows
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress(md, slots, flags, idg)
+    torch.cuda.synchronize()
+    bad = torch.from_numpy(ids >= n_rows).cuda()
+    ref = xg[idg.clamp(max=n_rows - 1)]
+    ref[bad] = 0
+    assert torch.equal(out, ref)
+    slots_o, flags_o, _ = orc.compress(omd(md), x)
+    pick = rng.integers(0, n_ids, 64)
+    pick = pick[ids[pick] < n_rows]
+    want = orc.gather_decompress(omd(md), slots_o, flags_o, ids[pick])
+    assert np.array_equal(out[torch.from_numpy(pick).cuda()].cpu().numpy(), want)
+
+
 def test_deterministic_and_stream_ordered(ibp):
     """Two compressions on a side stream give the same image bytes."""
     rng = np.random.default_rng(9)
