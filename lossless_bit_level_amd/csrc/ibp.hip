@@ -338,6 +338,78 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
   }
 }
 
+// [IBP] Compression of rows of exactly 64*NCH blocks, one wave per row: the
+// row is read once into registers (NCH blocks per lane), each chunk's match
+// ballot is its 64-bit header word, the chunk prefixes are a scalar running
+// sum, and the payloads are ORed into a wave-private LDS stream buffer that
+// is then written out with coalesced stores.  No workgroup barriers.
+template <int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
+    Codec cd, uint64_t n_rows, const uint32_t* __restrict__ src, uint32_t* __restrict__ slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  __shared__ uint32_t lds_all[kWavesPerBlock][NCH * kWave + 4];
+  constexpr uint32_t n = (uint32_t)NCH * kWave;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds_all[wave];
+  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
+    const uint32_t* x_row = src + row * n;
+    uint32_t* s_row = slots + row * n;
+    uint32_t x[NCH];
+    unsigned long long h[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
+      m += (uint32_t)__popcll(h[c]);
+    }
+    const uint32_t c_bits = n + 32u * n - cd.p * m;
+    const bool flag = c_bits < 32u * n;
+    if (!flag) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s_row[c * kWave + lane] = x[c];
+    } else {
+      const uint32_t nw = (c_bits + 31u) >> 5;
+      for (uint32_t j = n / 32 + lane; j < nw + 1; j += kWave) buf[j] = 0u;
+      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (lane == 2u * c) w = (uint32_t)h[c];
+          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
+        }
+        buf[lane] = w;
+      }
+      wave_lds_sync();
+      uint32_t carry = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
+        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+        const uint32_t off = n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
+        const uint32_t len = match ? 32u - cd.p : 32u;
+        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+        if (len) {
+          const uint32_t sh = off & 31u, wi = off >> 5;
+          atomicOr(&buf[wi], pay << sh);
+          if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+        }
+        carry += (uint32_t)__popcll(h[c]);
+      }
+      wave_lds_sync();
+      for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+      wave_lds_sync();
+    }
+    if (lane == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+  }
+}
+
 // [IBP] Decompression.  One wave per task = (output row, segment of up to
 // kSegBlocks blocks).  For a compressed row the wave
 //   1. counts the stripped blocks before its segment (popcount of header
@@ -688,29 +760,6 @@ uint32_t grid_for(uint64_t work_groups) {
   return (uint32_t)(work_groups < kMaxGrid ? work_groups : kMaxGrid);
 }
 
-template <int NR, uint32_t MAXW>
-void launch_compress_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
-                       uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
-  hipLaunchKernelGGL((compress_kernel<NR, MAXW>), dim3(grid_for(n_rows)),
-                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,
-                     (uint32_t*)slots, (unsigned long long*)flags, row_bits, vec);
-}
-
-template <int NR>
-void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
-                        uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
-  // LDS window tiers: the whole row stream (<= n words) lives in LDS
-  if (cd.n <= 1024)
-    launch_compress_t<NR, 1024>(cd, n_rows, src, slots, flags, row_bits, vec, st);
-  else if (cd.n <= 4096)
-    launch_compress_t<NR, 4096>(cd, n_rows, src, slots, flags, row_bits, vec, st);
-  else if (cd.n <= 8192)
-    launch_compress_t<NR, 8192>(cd, n_rows, src, slots, flags, row_bits, vec, st);
-  else
-    launch_compress_t<NR, IBP_MAX_COMPRESS_ROW_BYTES / 4>(cd, n_rows, src, slots, flags,
-                                                          row_bits, vec, st);
-}
-
 int g_cu_count = 0;
 
 // Workgroups for a launch: mult per CU (8 workgroups of 4 waves fill a CU).
@@ -725,6 +774,46 @@ uint32_t workgroups_per_device(uint32_t mult) {
       g_cu_count = 256;
   }
   return mult * (uint32_t)g_cu_count;
+}
+
+template <int NR, uint32_t MAXW>
+void launch_compress_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
+                       uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
+  hipLaunchKernelGGL((compress_kernel<NR, MAXW>), dim3(grid_for(n_rows)),
+                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,
+                     (uint32_t*)slots, (unsigned long long*)flags, row_bits, vec);
+}
+
+template <int NR, int NCH>
+void launch_compress_rows_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
+                            uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
+  const uint64_t wgs = (n_rows + kWavesPerBlock - 1) / kWavesPerBlock;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(32));
+  hipLaunchKernelGGL((compress_rows_kernel<NR, NCH>), dim3(grid), dim3(kBlockThreads), 0, st,
+                     cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,
+                     (unsigned long long*)flags, row_bits);
+}
+
+template <int NR>
+void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
+                        uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
+  switch (cd.n) {  // rows of 64 * NCH blocks: one wave per row
+    case 128: return launch_compress_rows_t<NR, 2>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 256: return launch_compress_rows_t<NR, 4>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 512: return launch_compress_rows_t<NR, 8>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 1024: return launch_compress_rows_t<NR, 16>(cd, n_rows, src, slots, flags, row_bits, st);
+    default: break;
+  }
+  // LDS window tiers: the whole row stream (<= n words) lives in LDS
+  if (cd.n <= 1024)
+    launch_compress_t<NR, 1024>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else if (cd.n <= 4096)
+    launch_compress_t<NR, 4096>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else if (cd.n <= 8192)
+    launch_compress_t<NR, 8192>(cd, n_rows, src, slots, flags, row_bits, vec, st);
+  else
+    launch_compress_t<NR, IBP_MAX_COMPRESS_ROW_BYTES / 4>(cd, n_rows, src, slots, flags,
+                                                          row_bits, vec, st);
 }
 
 template <bool GATHER, int NR>
