@@ -410,8 +410,9 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
   }
 }
 
-// [IBP] Decompression.  One wave per task = (output row, segment of up to
-// kSegBlocks blocks).  For a compressed row the wave
+// [IBP] Decompression.  One wave per task = (output row, segment of `seg`
+// blocks, seg a multiple of 64 and at most kSegBlocks).  For a compressed row
+// the wave
 //   1. counts the stripped blocks before its segment (popcount of header
 //      words) and inside it,
 //   2. fetches the segment's stream words [a/32, ceil(b/32)) into its LDS
@@ -423,7 +424,8 @@ template <bool GATHER, int NR>
 __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     Codec cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
-    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t* __restrict__ dst, int vec) {
+    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, uint32_t* __restrict__ dst,
+    int vec) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
@@ -438,8 +440,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     const uint32_t s = (uint32_t)(task - i * nseg);
     const uint64_t id = GATHER ? (uint64_t)ids[i] : i;
     uint32_t* out = dst + i * n;
-    const uint32_t lo = s * kSegBlocks;
-    const uint32_t hi = min(n, lo + kSegBlocks);
+    const uint32_t lo = s * seg;
+    const uint32_t hi = min(n, lo + seg);
     if (GATHER && id >= n_rows) {  // an id outside the table gives a zero row
       for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = 0u;
       continue;
@@ -855,13 +857,16 @@ void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
     }
     return;
   }
-  const uint32_t nseg = (cd.n + kSegBlocks - 1) / kSegBlocks;
+  // segments of kSegBlocks blocks (measured: shorter segments add more
+  // header-prefix reads than they gain in parallelism, even for 8 KiB rows)
+  const uint64_t seg = kSegBlocks;
+  const uint32_t nseg = (uint32_t)((cd.n + seg - 1) / seg);
   const uint64_t n_tasks = n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL((decode_segments_kernel<GATHER, NR>), dim3(grid_for(wgs)),
                      dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
                      (const unsigned long long*)flags, ids, n_rows, n_tasks, nseg,
-                     (uint32_t*)dst, vec);
+                     (uint32_t)seg, (uint32_t*)dst, vec);
 }
 
 template <bool GATHER>
