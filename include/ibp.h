@@ -43,20 +43,23 @@
  * for the device (pass the pointer ibp_host_device_pointer returns), which
  * the kernels then read across the host link without a staging copy
  * ([IBP] Compression and Decompression use zero-copy access to host memory).
- * All buffers must be 16-byte aligned and row_bytes a multiple of 4.
+ * row_bytes must be a multiple of 4 and every buffer 4-byte aligned (flags and
+ * row ids 8-byte aligned); 16-byte aligned slots/src/dst with row_bytes a
+ * multiple of 16 enable 16-byte memory operations.
  * ibp_compress, ibp_decompress and ibp_gather_decompress only enqueue work on
  * `stream` (a hipStream_t, NULL = the null stream) and return at once; they
  * allocate nothing, copy nothing on the host and never synchronise.
  * ibp_build_metadata is synchronous.  The library keeps no state between
- * calls apart from the last HIP error code of the calling thread.
+ * calls apart from the last HIP error code of the calling thread and the
+ * compute-unit count of the device (read once, to size launches).
  *
  * Errors
  * ------
  * Every entry point validates its arguments on the host before it enqueues
  * anything; a negative status means nothing was enqueued.  IBP_ERR_HIP means
  * a HIP call or launch failed; ibp_last_hip_error() gives its hipError_t.
- * Row ids outside [0, n_rows) are a precondition violation: they are not
- * checked on the device.
+ * A row id outside [0, n_rows) (negative ids included) yields an all-zero
+ * output row; the kernels never read outside the image for it.
  */
 #ifndef IBP_H_
 #define IBP_H_
@@ -104,11 +107,12 @@ int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
 /*
  * [IBP] Preprocessing.  Counts the ones of every bit position over the
  * n_blocks 32-bit blocks at `sample` (device memory or mapped pinned host
- * memory, 16-byte aligned) on the GPU, then applies the threshold rule of
+ * memory, 4-byte aligned) on the GPU, then applies the threshold rule of
  * ibp_metadata_from_counts.  out: host struct.  out_ones: optional host
- * array of width_bits counters.  SYNCHRONOUS: waits for `stream`.  Uses a
- * 256-byte device buffer of its own for the counters for the duration of
- * the call.
+ * array of width_bits counters.  SYNCHRONOUS: waits for `stream`.  Allocates
+ * (hipMalloc) and frees a device buffer of partial counts, 256 bytes per
+ * workgroup of the count kernel (at most 4 per compute unit, plus one),
+ * for the duration of the call.
  */
 int ibp_build_metadata(const void *sample, uint64_t n_blocks,
                        uint32_t width_bits, uint32_t t_ppm, ibp_metadata *out,
@@ -136,7 +140,8 @@ int ibp_decompress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
 
 /*
  * Gather-decompress: dst row i = row row_ids[i] restored, for i < n_ids, in
- * id order; duplicate ids are allowed.  The fetch of a feature / embedding /
+ * id order; duplicate ids are allowed; an id outside [0, n_rows) gives a
+ * zero row.  The fetch of a feature / embedding /
  * KV page by index that the page's GNN, DLRM and LLM integrations perform
  * ([IBP] Decompression; System integration).  row_ids: device int64 array.
  * n_ids == 0 is a no-op.  Asynchronous on `stream`.
