@@ -119,11 +119,16 @@ int ibp_build_metadata(const void *sample, uint64_t n_blocks,
                        uint64_t *out_ones, void *stream);
 
 /*
- * [IBP] Compression, out of place.  src: n_rows x row_bytes device table.
- * Writes the image (slots, flags) described above and, when row_bits is not
- * NULL, row_bits[r] = C of row r (also for rows stored raw).  slots may be
- * device memory or mapped pinned host memory.  Asynchronous on `stream`.
- * row_bytes <= IBP_MAX_COMPRESS_ROW_BYTES.  Equal inputs give equal bytes.
+ * [IBP] Compression.  src: the n_rows x row_bytes table.  Writes the image
+ * (slots, flags) described above and, when row_bits is not NULL,
+ * row_bits[r] = C of row r (also for rows stored raw).  src and slots may be
+ * device memory or mapped pinned host memory (zero-copy).  src == slots
+ * compresses in place, each row into its own fixed-size buffer ([IBP] System
+ * integration: in-place compression of host tensors before transfer); the
+ * slot bytes past a compressed row's stream then keep raw bytes, which are
+ * not part of the image.  Any other overlap of src and slots is
+ * INVALID_ARGUMENT.  Asynchronous on `stream`.  row_bytes <=
+ * IBP_MAX_COMPRESS_ROW_BYTES.  Equal inputs give equal bytes.
  */
 int ibp_compress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
                  const void *src, void *slots, uint64_t *flags,

@@ -245,12 +245,13 @@ __global__ __launch_bounds__(kBlockThreads) void reduce_counts_kernel(
 // match counts, then every lane ORs its payload (<= 2 words) into place with
 // LDS atomics (OR commutes, so the bytes do not depend on timing), and the
 // finished words are written out with coalesced stores.  A row whose stream
-// would not be shorter than the raw row is copied raw.
+// would not be shorter than the raw row is copied raw.  In place (src ==
+// slots) is safe: every read of a row happens before the barrier that
+// precedes its first write.
 template <int NR, uint32_t MAXW>
 __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
-    Codec cd, uint64_t n_rows, const uint32_t* __restrict__ src,
-    uint32_t* __restrict__ slots, unsigned long long* __restrict__ flags,
-    uint32_t* __restrict__ row_bits, int vec) {
+    Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits, int vec) {
   __shared__ uint32_t buf[MAXW + 4];
   __shared__ uint32_t chunk_pre[MAXW / kWave + 1];
   __shared__ uint32_t total_m;
@@ -342,10 +343,12 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
 // row is read once into registers (NCH blocks per lane), each chunk's match
 // ballot is its 64-bit header word, the chunk prefixes are a scalar running
 // sum, and the payloads are ORed into a wave-private LDS stream buffer that
-// is then written out with coalesced stores.  No workgroup barriers.
+// is then written out with coalesced stores.  No workgroup barriers.  In
+// place (src == slots) is safe: the row decision needs every block, so all
+// of a row's loads complete before its first store.
 template <int NR, int NCH>
 __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
-    Codec cd, uint64_t n_rows, const uint32_t* __restrict__ src, uint32_t* __restrict__ slots,
+    Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
     unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
   __shared__ uint32_t lds_all[kWavesPerBlock][NCH * kWave + 4];
   constexpr uint32_t n = (uint32_t)NCH * kWave;
@@ -975,6 +978,10 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
   if (!aligned(src, 4) || !aligned(slots, 4) || !aligned(flags, 8) ||
       (row_bits && !aligned(row_bits, 4)))
     return IBP_ERR_LAYOUT;
+  {  // in place (src == slots) is allowed, any other overlap is not
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)slots, len = n_rows * row_bytes;
+    if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
+  }
   hipStream_t st = (hipStream_t)stream;
   const Codec cd = make_codec(md, row_bytes);
   const int vec = row_bytes % 16 == 0 && aligned(src, 16) && aligned(slots, 16);

@@ -102,6 +102,14 @@ def _dptr(t: torch.Tensor) -> int:
     raise ValueError("tensor must be on the GPU or in pinned host memory")
 
 
+def _need_cuda(t: torch.Tensor, name: str):
+    """Arguments the kernels write, or read as device memory, must be GPU
+    tensors (a CPU pointer there would fault the GPU)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    return t
+
+
 def _rows(t: torch.Tensor):
     """(n_rows, row_bytes) of a tensor whose first axis is the row axis."""
     if t.dim() == 0:
@@ -159,13 +167,16 @@ def ibp_compress(md: ibp_metadata, src: torch.Tensor, slots: torch.Tensor | None
     (slots uint8 [n_rows, row_bytes], flags int64 [flag words], row_bits
     int32 [n_rows] or None).  Asynchronous on the current stream."""
     n_rows, row_bytes = _rows(src)
-    dev = src.device
+    dev = src.device if src.is_cuda else torch.device("cuda")
     if slots is None:
         slots = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device=dev)
     if flags is None:
         flags = torch.empty(max(1, ibp_flag_words(n_rows)), dtype=torch.int64, device=dev)
     if row_bits is None and want_row_bits:
         row_bits = torch.empty(max(1, n_rows), dtype=torch.int32, device=dev)
+    _need_cuda(flags, "flags")
+    if row_bits is not None:
+        _need_cuda(row_bits, "row_bits")
     _check("ibp_compress",
            lib().ibp_compress(ctypes.byref(md), n_rows, row_bytes, _dptr(src), _dptr(slots),
                               flags.data_ptr(),
@@ -180,6 +191,8 @@ def ibp_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
     n_rows, row_bytes = _rows(slots)
     if out is None:
         out = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device="cuda")
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
     _check("ibp_decompress",
            lib().ibp_decompress(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
                                 flags.data_ptr(), out.data_ptr(), _stream(stream)))
@@ -196,6 +209,8 @@ def ibp_gather_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Te
     n_ids = row_ids.numel()
     if out is None:
         out = torch.empty((n_ids, row_bytes), dtype=torch.uint8, device="cuda")
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
     _check("ibp_gather_decompress",
            lib().ibp_gather_decompress(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
                                        flags.data_ptr(), row_ids.data_ptr(), n_ids,
@@ -211,6 +226,8 @@ def ibp_gather_decompress_launcher(md: ibp_metadata, slots: torch.Tensor, flags:
     n_rows, row_bytes = _rows(slots)
     if row_ids.dtype != torch.int64 or not row_ids.is_cuda:
         raise ValueError("row_ids must be an int64 GPU tensor")
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
     fn = lib().ibp_gather_decompress
     args = (ctypes.byref(md), ctypes.c_uint64(n_rows), ctypes.c_uint64(row_bytes),
             ctypes.c_void_p(_dptr(slots)), ctypes.c_void_p(flags.data_ptr()),
@@ -228,6 +245,8 @@ def ibp_decompress_launcher(md: ibp_metadata, slots: torch.Tensor, flags: torch.
                             out: torch.Tensor, stream=None):
     """ibp_decompress with its arguments converted once (see above)."""
     n_rows, row_bytes = _rows(slots)
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
     fn = lib().ibp_decompress
     args = (ctypes.byref(md), ctypes.c_uint64(n_rows), ctypes.c_uint64(row_bytes),
             ctypes.c_void_p(_dptr(slots)), ctypes.c_void_p(flags.data_ptr()),

@@ -79,6 +79,9 @@ def test_validation_before_enqueue(ibp):
     assert L.ibp_compress(byref(md), 4, ibp.IBP_MAX_COMPRESS_ROW_BYTES + 4, fake, fake, fake, None, None) == ibp.IBP_ERR_UNSUPPORTED
     assert L.ibp_compress(byref(md), 4, 16, None, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_compress(byref(md), 1 << 62, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    # src and slots may coincide (in place) but must not partly overlap
+    assert L.ibp_compress(byref(md), 4, 16, fake, fake + 16, fake + 1024, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(md), 4, 16, fake + 48, fake, fake + 1024, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     # empty work is a no-op that needs no pointers
     assert L.ibp_compress(byref(md), 0, 16, None, None, None, None, None) == ibp.IBP_OK
     assert L.ibp_gather_decompress(byref(md), 10, 16, fake, fake, fake, 0, fake, None) == ibp.IBP_OK

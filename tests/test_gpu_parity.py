@@ -287,6 +287,33 @@ def test_pinned_host_image_gather(ibp):
     assert torch.equal(ibp.ibp_decompress(md, hs2, f2), xg)
 
 
+@pytest.mark.parametrize("where", ["device", "pinned_host"])
+@pytest.mark.parametrize("row_bytes,mask,bitval", [(4096, 0x7C007C00, 0x3C003C00),
+                                                  (2048, 0xFFFFFFFF, 0x00000000),
+                                                  (8192, 0x78007800, 0x38003800)])
+def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
+    """In-place compression (each row into its own buffer, as for host tensors
+    compressed before transfer): same flags, sizes and image bytes as the
+    oracle; the image then decompresses (also zero-copy from pinned host)."""
+    rng = np.random.default_rng(row_bytes + (where == "device"))
+    n_rows = 700
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=0.93, raw_rows=(3, 400))
+    md = gmd(ibp, mask, bitval)
+    if where == "device":
+        buf = to_gpu(x)
+    else:
+        buf = torch.from_numpy(x.copy()).pin_memory()
+    slots, flags, rb = ibp.ibp_compress(md, buf, slots=buf)
+    torch.cuda.synchronize()
+    assert slots.data_ptr() == buf.data_ptr()
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    assert_image_equal(buf.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    back = ibp.ibp_decompress(md, buf, flags)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), x)
+
+
 # ----------------------------------------------------- full-size workloads --
 
 def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
