@@ -111,8 +111,8 @@ int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
  * ibp_metadata_from_counts.  out: host struct.  out_ones: optional host
  * array of width_bits counters.  SYNCHRONOUS: waits for `stream`.  Allocates
  * (hipMalloc) and frees a device buffer of partial counts, 256 bytes per
- * workgroup of the count kernel (at most 4 per compute unit, plus one),
- * for the duration of the call.
+ * workgroup of the count kernel (two per compute unit, plus one, for
+ * samples below 2^40 blocks), for the duration of the call.
  */
 int ibp_build_metadata(const void *sample, uint64_t n_blocks,
                        uint32_t width_bits, uint32_t t_ppm, ibp_metadata *out,

@@ -177,67 +177,147 @@ __global__ void fill_u64_kernel(unsigned long long* p, uint64_t n, unsigned long
 }
 
 // [IBP] Preprocessing, device half: per-bit one counts over the sample.
-// Each wave ballots bit b of its blocks and accumulates the popcount in a
-// scalar register; the 4 waves of a workgroup add theirs in LDS and the
-// workgroup writes one row of 32 partial counts (no atomics: contended
-// atomics on 32 counters serialise); reduce_counts_kernel sums the rows.
-// Blocks are read 4 per lane (16-byte loads) where the sample allows it.
+//
+// Bit-sliced counting.  A lane takes 32 blocks per step (eight 16-byte loads,
+// each coalesced over the wave) and adds them with a tree of ripple-carry
+// adders that works on all 32 bit positions at once: afterwards bit b of
+// plane j is bit j of the number of ones at position b among those blocks.
+// That 6-plane number is added into a P-plane accumulator the same way, and
+// only after the last step are the planes turned into 32 counters and summed
+// over the wave.  About 7 VALU per block and no scalar work in the loop; a
+// ballot per bit would cost 32 ballots plus their scalar popcounts per block,
+// on a scalar unit that the four SIMDs of a CU share.
+constexpr int kCountWords = 32;                              // blocks per lane per step
+constexpr uint32_t kCountGroup = kCountWords * kWave;        // blocks per wave step
+constexpr uint64_t kCountMaxSteps = (1u << 24) / kCountWords - 1;  // per wave, so P <= 24
+
+// out[0..B] = x[0..B) + y[0..B), bit-sliced.
+template <int B>
+__device__ __forceinline__ void sliced_add(const uint32_t* x, const uint32_t* y, uint32_t* out) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < B; ++j) {
+    const uint32_t t = x[j] ^ y[j];
+    out[j] = t ^ c;
+    c = (x[j] & y[j]) | (c & t);
+  }
+  out[B] = c;
+}
+
+// acc += s, bit-sliced; the caller keeps every position's total below 2^P.
+template <int P>
+__device__ __forceinline__ void sliced_accumulate(uint32_t (&acc)[P], const uint32_t (&s)[6]) {
+  uint32_t c = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const uint32_t a = acc[j];
+    if (j < 6) {
+      const uint32_t t = a ^ s[j];
+      acc[j] = t ^ c;
+      c = (a & s[j]) | (c & t);
+    } else {
+      acc[j] = a ^ c;
+      c = a & c;
+    }
+  }
+}
+
+// Ones per position among the 32 blocks w[], as 6 planes.
+__device__ __forceinline__ void sliced_count32(const uint32_t (&w)[kCountWords], uint32_t (&s)[6]) {
+  uint32_t l1[16][2], l2[8][3], l3[4][4], l4[2][5];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sliced_add<1>(&w[2 * i], &w[2 * i + 1], l1[i]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sliced_add<2>(l1[2 * i], l1[2 * i + 1], l2[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sliced_add<3>(l2[2 * i], l2[2 * i + 1], l3[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sliced_add<4>(l3[2 * i], l3[2 * i + 1], l4[i]);
+  sliced_add<5>(l4[0], l4[1], s);
+}
+
+// Step g of the sample covers blocks [g*2048, (g+1)*2048): lane L takes the
+// four blocks of 16-byte unit g*512 + j*64 + L for j < 8.  Blocks past the
+// end read as 0 (they add no ones).  Partial counts go out transposed,
+// partials[b * gridDim.x + workgroup], so the reduction reads each bit's
+// column contiguously.
+template <int P>
 __global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
     const uint32_t* __restrict__ sample, uint64_t n_blocks,
     unsigned long long* __restrict__ partials) {
-  __shared__ unsigned long long part[kWavesPerBlock][32];
+  __shared__ uint32_t part[kWavesPerBlock][32];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint64_t gwave = (uint64_t)blockIdx.x * kWavesPerBlock + wave;
   const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
-  uint64_t acc[32];
+  const uint64_t n_steps = (n_blocks + kCountGroup - 1) / kCountGroup;
+  const uint64_t n_vec = ((uintptr_t)sample % 16) == 0 ? n_blocks / kCountGroup : 0;
+  uint32_t acc[P];
 #pragma unroll
-  for (int b = 0; b < 32; ++b) acc[b] = 0;
-  const bool vec = ((uintptr_t)sample % 16) == 0;
-  const uint64_t n4 = vec ? n_blocks / (4 * kWave) : 0;  // whole 256-block groups
-  for (uint64_t g = gwave; g < n4; g += nwaves) {
-    const uint4 x4 = reinterpret_cast<const uint4*>(sample)[g * kWave + lane];
-    const uint32_t xs[4] = {x4.x, x4.y, x4.z, x4.w};
+  for (int j = 0; j < P; ++j) acc[j] = 0;
+  for (uint64_t g = gwave; g < n_steps; g += nwaves) {
+    uint32_t w[kCountWords];
+    if (g < n_vec) {
+      const uint4* q = reinterpret_cast<const uint4*>(sample) + g * (kCountGroup / 4) + lane;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kCountWords / 4; ++j) {
+        const uint4 v = q[j * kWave];
+        w[4 * j] = v.x; w[4 * j + 1] = v.y; w[4 * j + 2] = v.z; w[4 * j + 3] = v.w;
+      }
+    } else {
+      const uint64_t base = g * kCountGroup + 4ull * lane;
 #pragma unroll
-      for (int b = 0; b < 32; ++b) acc[b] += __popcll(__ballot((xs[j] >> b) & 1u));
+      for (int j = 0; j < kCountWords / 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint64_t k = base + 4ull * kWave * j + c;
+          w[4 * j + c] = k < n_blocks ? sample[k] : 0u;
+        }
     }
+    uint32_t s[6];
+    sliced_count32(w, s);
+    sliced_accumulate<P>(acc, s);
   }
-  for (uint64_t base = n4 * 4 * kWave + gwave * kWave; base < n_blocks; base += nwaves * kWave) {
-    const uint64_t k = base + lane;
-    const uint32_t x = k < n_blocks ? sample[k] : 0u;
+  // each lane's count is below 2^24 (at most kCountMaxSteps steps per wave),
+  // so a wave's sum fits 32 bits
 #pragma unroll
-    for (int b = 0; b < 32; ++b) acc[b] += __popcll(__ballot((x >> b) & 1u));
-  }
-  if (lane == 0) {
+  for (int b = 0; b < 32; ++b) {
+    uint32_t c = 0;
 #pragma unroll
-    for (int b = 0; b < 32; ++b) part[wave][b] = acc[b];
+    for (int j = 0; j < P; ++j) c += __builtin_amdgcn_ubfe(acc[j], b, 1) << j;
+    const uint32_t t = wave_sum(c);
+    if (lane == 0) part[wave][b] = t;
   }
   __syncthreads();
   if (threadIdx.x < 32) {
     unsigned long long t = 0;
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; ++w) t += part[w][threadIdx.x];
-    partials[(uint64_t)blockIdx.x * 32 + threadIdx.x] = t;
+    partials[(uint64_t)threadIdx.x * gridDim.x + blockIdx.x] = t;
   }
 }
 
-// counts[b] = sum over the n_parts rows of partials[.][b]; one workgroup.
+// counts[b] = sum of column b of the transposed partials; one wave per bit
+// (launched as 8 workgroups of 4 waves).
 __global__ __launch_bounds__(kBlockThreads) void reduce_counts_kernel(
     const unsigned long long* __restrict__ partials, uint32_t n_parts,
     unsigned long long* __restrict__ counts) {
-  __shared__ unsigned long long red[kBlockThreads];
-  const uint32_t b = threadIdx.x & 31u, r0 = threadIdx.x >> 5;  // 8 row lanes per bit
-  unsigned long long t = 0;
-  for (uint32_t r = r0; r < n_parts; r += kBlockThreads / 32) t += partials[(uint64_t)r * 32 + b];
-  red[threadIdx.x] = t;
-  __syncthreads();
-  if (threadIdx.x < 32) {
-    unsigned long long s = 0;
-    for (uint32_t k = 0; k < kBlockThreads / 32; ++k) s += red[k * 32 + threadIdx.x];
-    counts[threadIdx.x] = s;
+  const uint32_t lane = lane_id();
+  const uint32_t b = uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  const unsigned long long* col = partials + (uint64_t)b * n_parts;
+  unsigned long long t0 = 0, t1 = 0, t2 = 0, t3 = 0;
+  uint32_t i = lane;
+  for (; i + 3 * kWave < n_parts; i += 4 * kWave) {
+    t0 += col[i];
+    t1 += col[i + kWave];
+    t2 += col[i + 2 * kWave];
+    t3 += col[i + 3 * kWave];
   }
+  for (; i < n_parts; i += kWave) t0 += col[i];
+  unsigned long long t = (t0 + t1) + (t2 + t3);
+#pragma unroll
+  for (int d = kWave / 2; d > 0; d >>= 1) t += __shfl_xor(t, d, kWave);
+  if (lane == 0) counts[b] = t;
 }
 
 // [IBP] Compression, one workgroup per row.  The row's stream is assembled
@@ -941,19 +1021,32 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
   if (n_blocks == 0) return IBP_ERR_EMPTY;
   if (!aligned(sample, 4)) return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
-  const uint64_t waves = (n_blocks + 4 * kWave - 1) / (4 * kWave);
-  const uint32_t grid = (uint32_t)std::max<uint64_t>(
-      1, std::min<uint64_t>((waves + kWavesPerBlock - 1) / kWavesPerBlock,
-                            workgroups_per_device(4)));
-  // partial counts (grid rows of 32) followed by the 32 totals
+  // about two workgroups per CU; more only when a wave would otherwise take
+  // more than kCountMaxSteps steps (its lanes' counts must stay below 2^24)
+  const uint64_t steps = (n_blocks + kCountGroup - 1) / kCountGroup;
+  uint64_t wgs = std::min<uint64_t>((steps + kWavesPerBlock - 1) / kWavesPerBlock,
+                                    workgroups_per_device(2));
+  const uint64_t per_wg = kCountMaxSteps * kWavesPerBlock;
+  wgs = std::max<uint64_t>({wgs, (steps + per_wg - 1) / per_wg, 1});
+  if (wgs > kMaxGrid) return IBP_ERR_INVALID_ARGUMENT;
+  const uint32_t grid = (uint32_t)wgs;
+  const uint64_t lane_max = (steps + wgs * kWavesPerBlock - 1) / (wgs * kWavesPerBlock) * kCountWords;
+  // partial counts (32 columns of grid) followed by the 32 totals
   unsigned long long* d_buf = nullptr;
   hipError_t e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * 32 * sizeof(unsigned long long));
   if (e != hipSuccess) return hip_fail(e);
   unsigned long long* d_counts = d_buf + (size_t)grid * 32;
   uint64_t ones[32];
-  hipLaunchKernelGGL(count_ones_kernel, dim3(grid), dim3(kBlockThreads), 0, st,
-                     (const uint32_t*)sample, n_blocks, d_buf);
-  hipLaunchKernelGGL(reduce_counts_kernel, dim3(1), dim3(kBlockThreads), 0, st,
+  const uint32_t* smp = (const uint32_t*)sample;
+  if (lane_max < (1u << 8))
+    hipLaunchKernelGGL(count_ones_kernel<8>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
+  else if (lane_max < (1u << 12))
+    hipLaunchKernelGGL(count_ones_kernel<12>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
+  else if (lane_max < (1u << 16))
+    hipLaunchKernelGGL(count_ones_kernel<16>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
+  else
+    hipLaunchKernelGGL(count_ones_kernel<24>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
+  hipLaunchKernelGGL(reduce_counts_kernel, dim3(32 / kWavesPerBlock), dim3(kBlockThreads), 0, st,
                      (const unsigned long long*)d_buf, grid, d_counts);
   e = hipGetLastError();
   if (e == hipSuccess) e = hipMemcpyAsync(ones, d_counts, sizeof(ones), hipMemcpyDeviceToHost, st);

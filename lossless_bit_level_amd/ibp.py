@@ -149,8 +149,13 @@ def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 3
 
     Returns (ibp_metadata, ones) with ones a list of the per-bit counts.
     Synchronous."""
+    avail = sample.numel() * sample.element_size() * 8 // width_bits
     if n_blocks is None:
-        n_blocks = sample.numel() * sample.element_size() * 8 // width_bits
+        n_blocks = avail
+    if not 0 <= n_blocks <= avail:
+        raise ValueError(f"n_blocks={n_blocks} but the sample holds {avail} blocks")
+    if not sample.is_contiguous():
+        raise ValueError("sample must be contiguous")
     ppm = int(round(t * 1_000_000)) if t_ppm is None else int(t_ppm)
     md = ibp_metadata()
     ones = (ctypes.c_uint64 * width_bits)()

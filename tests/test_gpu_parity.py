@@ -95,6 +95,25 @@ def test_metadata_parity(ibp, name):
         assert md_g.invariant_bits == md_o.invariant_bits
 
 
+@pytest.mark.parametrize("offset", [0, 4, 8])
+def test_metadata_ragged_sizes_and_alignment(ibp, offset):
+    """Sizes around the count kernel's 2048-block step (and below one wave),
+    with samples 16-byte aligned (vector loads) or only 4-byte aligned."""
+    rng = np.random.default_rng(11 + offset)
+    # every bit position gets its own density, so no count is trivially 0 or N
+    dens = np.linspace(0.02, 0.98, 32)
+    for n in (1, 63, 64, 65, 2047, 2048, 2049, 3 * 2048 + 5, 262144 + 77):
+        bits = rng.random((n, 32)) < dens
+        x = (bits.astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(1).astype(np.uint32)
+        say(f"metadata ragged n={n} offset={offset}")
+        buf = torch.zeros(n * 4 + 16, dtype=torch.uint8, device="cuda")
+        buf[offset:offset + n * 4] = torch.from_numpy(x.view(np.uint8).copy()).cuda()
+        md_g, ones_g = ibp.ibp_build_metadata(buf[offset:offset + n * 4], n_blocks=n)
+        md_o, ones_o = orc.build_metadata(x, 32)
+        assert np.array_equal(np.array(ones_g, np.uint64), ones_o), n
+        assert (md_g.mask, md_g.bitval) == (md_o.mask, md_o.bitval)
+
+
 def test_metadata_pinned_host_sample(ibp):
     x = syn.tiny_dense()
     host = torch.from_numpy(x.reshape(-1).view(np.uint8).copy()).pin_memory()
