@@ -156,6 +156,74 @@ int ibp_gather_decompress(const ibp_metadata *md, uint64_t n_rows,
                           const uint64_t *flags, const int64_t *row_ids,
                           uint64_t n_ids, void *dst, void *stream);
 
+/*
+ * Compressed row cache in GPU memory ([IBP] System integration: tensors kept
+ * in a GPU software cache are stored compressed, so the same memory holds
+ * more of them).
+ *
+ * Packed arena: a device buffer holding the stored form of selected rows of
+ * an image back to back, each entry starting at a 16-byte boundary: entry e
+ * is the first `words` 32-bit words of the row's slot (the stream of a
+ * compressed row, the S raw bytes of a raw row), zero padded to a multiple
+ * of 4 words.
+ *
+ * Locator (uint64): where a table row lives in the arena.
+ *   bit 63       IBP_LOC_RESIDENT: the row is in the arena (0: it is not; a
+ *                locator of 0 means "not cached")
+ *   bit 62       IBP_LOC_COMPRESSED: the entry is a compressed stream (the
+ *                row's flag in the image)
+ *   bits 36..61  words: 32-bit words stored (ceil(C/32), or S/4 when raw)
+ *   bits 0..35   offset of the entry in the arena, in 16-byte units
+ */
+#define IBP_LOC_RESIDENT (1ull << 63)
+#define IBP_LOC_COMPRESSED (1ull << 62)
+#define IBP_LOC_WORDS_SHIFT 36
+#define IBP_LOC_WORDS_MASK ((1ull << 26) - 1)
+#define IBP_LOC_OFFSET_MASK ((1ull << 36) - 1)
+
+/*
+ * Plans a packed arena for the rows row_ids[0..n_ids) of an image (slots,
+ * flags as ibp_compress wrote them; slots may be mapped pinned host memory).
+ * entry_loc (device, n_ids uint64): the locator of entry e = row row_ids[e],
+ * entries laid out in id order; an id outside [0, n_rows) gets locator 0 and
+ * no space.  *arena_bytes (host): bytes the arena needs.  SYNCHRONOUS: waits
+ * for `stream`.  Allocates (hipMalloc) and frees a scratch buffer of 8 bytes
+ * per 4096 ids, plus 8, for the duration of the call.  Errors as for
+ * ibp_gather_decompress; UNSUPPORTED when the arena would exceed 2^40 bytes.
+ */
+int ibp_cache_plan(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
+                   const void *slots, const uint64_t *flags, const int64_t *row_ids,
+                   uint64_t n_ids, uint64_t *entry_loc, uint64_t *arena_bytes,
+                   void *stream);
+
+/*
+ * Fills the arena planned by ibp_cache_plan (same row_ids and entry_loc) and
+ * the table's locators: cache_loc (device, n_rows uint64) is cleared to 0,
+ * then cache_loc[row_ids[e]] = entry_loc[e] for every resident entry.  A row
+ * listed twice gets two entries, and cache_loc points at one of them.
+ * arena: device, 16-byte aligned, arena_bytes long; an entry that would end
+ * past arena_bytes is skipped (its row stays uncached).  Asynchronous on
+ * `stream`.
+ */
+int ibp_cache_fill(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
+                   const void *slots, const uint64_t *flags, const int64_t *row_ids,
+                   uint64_t n_ids, const uint64_t *entry_loc, void *arena,
+                   uint64_t arena_bytes, uint64_t *cache_loc, void *stream);
+
+/*
+ * Gather-decompress through the cache: dst row i = row row_ids[i] restored,
+ * decoded from the arena when cache_loc[row_ids[i]] is resident (a hit),
+ * else from the image (slots, flags) (a miss; with slots in mapped pinned
+ * host memory that is the zero-copy fetch over the host link).  Same id rules
+ * and output as ibp_gather_decompress.  arena, cache_loc: as ibp_cache_fill
+ * left them (device).  Asynchronous on `stream`.
+ */
+int ibp_gather_decompress_cached(const ibp_metadata *md, uint64_t n_rows,
+                                 uint64_t row_bytes, const void *arena,
+                                 const uint64_t *cache_loc, const void *slots,
+                                 const uint64_t *flags, const int64_t *row_ids,
+                                 uint64_t n_ids, void *dst, void *stream);
+
 /* (n_rows + 63) / 64: the number of uint64 words of a flag bitmap. */
 uint64_t ibp_flag_words(uint64_t n_rows);
 

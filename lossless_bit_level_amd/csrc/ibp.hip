@@ -170,6 +170,41 @@ __device__ __forceinline__ uint32_t decode_block(const uint32_t* lds, uint32_t r
 
 // ------------------------------------------------------------ kernels --
 
+// Where a decode task finds its row.
+constexpr int kModeTable = 0;   // row i of the image (full decompress)
+constexpr int kModeGather = 1;  // row ids[i] of the image
+constexpr int kModeCached = 2;  // row ids[i]: the packed cache entry when resident, else the image
+
+// First word of a row: its cache entry (locator resident), else its slot.
+template <int MODE>
+__device__ __forceinline__ const uint32_t* row_source(const uint32_t* slots,
+                                                      const uint32_t* arena, uint64_t id,
+                                                      uint32_t n, unsigned long long loc) {
+  if constexpr (MODE == kModeCached)
+    if (loc & IBP_LOC_RESIDENT) return arena + (loc & IBP_LOC_OFFSET_MASK) * 4;
+  return slots + id * n;
+}
+
+// Words that may be read from there: the entry's stored words, or the slot.
+template <int MODE>
+__device__ __forceinline__ uint32_t row_words(uint32_t n, unsigned long long loc) {
+  if constexpr (MODE == kModeCached)
+    if (loc & IBP_LOC_RESIDENT) return (uint32_t)((loc >> IBP_LOC_WORDS_SHIFT) & IBP_LOC_WORDS_MASK);
+  return n;
+}
+
+// Stored compressed?  From the locator of a cached row, else the image's
+// flag word fw (the word holding bit id & 63).
+template <int MODE>
+__device__ __forceinline__ bool row_flag(unsigned long long fw, uint64_t id,
+                                         unsigned long long loc) {
+  if constexpr (MODE == kModeCached)
+    if (loc & IBP_LOC_RESIDENT) return (loc & IBP_LOC_COMPRESSED) != 0;
+  return (fw >> (id & 63)) & 1ull;
+}
+
+
+
 __global__ void fill_u64_kernel(unsigned long long* p, uint64_t n, unsigned long long v) {
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (uint64_t)gridDim.x * blockDim.x)
@@ -503,10 +538,11 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
 //   3. per 64-block chunk: header word -> per-lane bit offset (mbcnt + carry)
 //      -> two LDS words -> funnel shift -> deposit + Bitval -> store.
 // A raw row is a straight copy.
-template <bool GATHER, int NR>
+template <int MODE, int NR>
 __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     Codec cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
     uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, uint32_t* __restrict__ dst,
     int vec) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
@@ -521,16 +557,19 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     if (task >= n_tasks) break;
     const uint64_t i = task / nseg;
     const uint32_t s = (uint32_t)(task - i * nseg);
-    const uint64_t id = GATHER ? (uint64_t)ids[i] : i;
+    const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
     uint32_t* out = dst + i * n;
     const uint32_t lo = s * seg;
     const uint32_t hi = min(n, lo + seg);
-    if (GATHER && id >= n_rows) {  // an id outside the table gives a zero row
+    if (MODE != kModeTable && id >= n_rows) {  // an id outside the table gives a zero row
       for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = 0u;
       continue;
     }
-    const uint32_t* src = slots + id * n;
-    const bool flag = (flags[id >> 6] >> (id & 63)) & 1ull;
+    const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
+    const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
+    const uint32_t* src = row_source<MODE>(slots, arena, id, n, loc);
+    const uint32_t lim = row_words<MODE>(n, loc);
+    const bool flag = row_flag<MODE>(fw, id, loc);
 
     if (!flag) {
       if (vec) {
@@ -564,10 +603,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
 
     // stream bit range of the segment's payloads, and its LDS window
     // (for an image that ibp_compress wrote, wb <= ceil(C/32) <= n; the
-    // clamps only keep a corrupt header from reading past the slot)
+    // clamps only keep a corrupt header from reading past the slot or entry)
     const uint32_t a = n + 32u * lo - cd.p * carry;
     const uint32_t b = n + 32u * hi - cd.p * (carry + m_seg);
-    const uint32_t wb = min((b + 31u) >> 5, n);
+    const uint32_t wb = min((b + 31u) >> 5, lim);
     const uint32_t wa = min(a >> 5, wb);
     uint32_t base;
     if (vec) {
@@ -625,10 +664,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
 // before the loop: the wait at the top of the loop then leaves the previous
 // row's stores in flight.  NCH == 0 handles any n.  n_out < 2^31 (the host
 // splits larger gathers).
-template <bool GATHER, int NR, int NCH>
+template <int MODE, int NR, int NCH>
 __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
     Codec cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
     uint64_t n_rows, uint32_t n_out, uint32_t* __restrict__ dst, int vec) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
@@ -645,12 +685,17 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
   uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
   if (i >= n_out) return;
 
-  auto row_id = [&](uint32_t r) -> uint64_t { return GATHER ? (uint64_t)ids[r] : r; };
-  auto in_table = [&](uint64_t id) -> bool { return !GATHER || id < n_rows; };
+  auto row_id = [&](uint32_t r) -> uint64_t { return MODE != kModeTable ? (uint64_t)ids[r] : r; };
+  auto in_table = [&](uint64_t id) -> bool { return MODE == kModeTable || id < n_rows; };
 
+  // With the cache a row's window depends on its locator, one load further
+  // down the chain: the locator of row j+1 is requested at the top of the
+  // iteration for row j, before this row's stream is staged.
   uint64_t id = row_id(i);
+  unsigned long long loc = (MODE == kModeCached && in_table(id)) ? cache_loc[id] : 0ull;
   unsigned long long fw = in_table(id) ? flags[id >> 6] : 0ull;
-  uint32_t win = (in_table(id) && lane < spec) ? slots[id * n + lane] : 0u;
+  uint32_t win = (in_table(id) && lane < min(spec, row_words<MODE>(n, loc)))
+                     ? row_source<MODE>(slots, arena, id, n, loc)[lane] : 0u;
   uint64_t id_next = (i + stride < n_out) ? row_id(i + stride) : 0;
   asm volatile("" ::"v"(win));  // the first window is waited for here, not in the loop
 
@@ -658,22 +703,26 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
     const uint32_t i_next = i + stride;
     const bool have_next = i_next < n_out;
     const uint64_t id_after = (have_next && i_next + stride < n_out) ? row_id(i_next + stride) : 0;
+    unsigned long long loc_next = 0;
+    if constexpr (MODE == kModeCached)
+      if (have_next && in_table(id_next)) loc_next = cache_loc[id_next];
     uint32_t* out = dst + (uint64_t)i * n;
-    const uint32_t* src = slots + id * n;
+    const uint32_t* src = row_source<MODE>(slots, arena, id, n, loc);
+    const uint32_t lim = row_words<MODE>(n, loc);
     const bool valid_id = in_table(id);
-    const bool flag = valid_id && ((fw >> (id & 63)) & 1ull);
+    const bool flag = valid_id && row_flag<MODE>(fw, id, loc);
 
     // with NCH > 0 a raw row is staged in LDS like a stream, so that its
     // copy out issues no loads after the prefetch below
     if (flag || (NCH > 0 && valid_id)) {
-      uint32_t wb = n;
+      uint32_t wb = lim;
       if (flag) {
         // header words are lanes [0, hw_n) of the window; bits at or past n
         // belong to the payloads
         uint32_t hw = lane < hw_n ? win : 0u;
         if (lane == hw_n - 1 && (n & 31u)) hw &= (1u << (n & 31u)) - 1u;
         const uint32_t m = wave_sum(__popc(hw));
-        wb = min((n + 32u * n - cd.p * m + 31u) >> 5, n);
+        wb = min((n + 32u * n - cd.p * m + 31u) >> 5, lim);
       }
       if (lane < spec) lds[lane] = win;
       if (wb > spec) {  // the rest of the stream
@@ -693,7 +742,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
     uint32_t win_next = 0;
     if (have_next && in_table(id_next)) {
       fw_next = flags[id_next >> 6];
-      win_next = lane < spec ? slots[id_next * n + lane] : 0u;
+      win_next = lane < min(spec, row_words<MODE>(n, loc_next))
+                     ? row_source<MODE>(slots, arena, id_next, n, loc_next)[lane] : 0u;
     }
 
     if constexpr (NCH > 0) {
@@ -781,7 +831,152 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
     id = id_next;
     id_next = id_after;
     fw = fw_next;
+    loc = loc_next;
     win = win_next;
+  }
+}
+
+// ------------------------------------------------------ packed cache ----
+//
+// [IBP] System integration, cache compression: rows kept in a GPU software
+// cache are stored compressed.  The arena holds each cached row's stored
+// words back to back at 16-byte boundaries; a 64-bit locator per entry (and,
+// after filling, per table row) gives offset, word count and flag.  Planning
+// is sizes -> tile sums -> scan of the tile sums -> offsets.
+
+constexpr uint32_t kScanTile = 4096;                          // entries per scan workgroup
+constexpr uint32_t kScanPerThread = kScanTile / kBlockThreads;  // 16
+
+// 16-byte units an entry takes in the arena (0 when the row is not packed).
+__device__ __forceinline__ unsigned long long loc_units(unsigned long long loc) {
+  if (!(loc & IBP_LOC_RESIDENT)) return 0;
+  return (((loc >> IBP_LOC_WORDS_SHIFT) & IBP_LOC_WORDS_MASK) + 3) / 4;
+}
+
+// Inclusive scan over the workgroup's threads (buf: kBlockThreads slots).
+__device__ unsigned long long block_inclusive_scan(unsigned long long v, unsigned long long* buf) {
+  buf[threadIdx.x] = v;
+  __syncthreads();
+  for (uint32_t d = 1; d < kBlockThreads; d <<= 1) {
+    const unsigned long long t = threadIdx.x >= d ? buf[threadIdx.x - d] : 0ull;
+    __syncthreads();
+    buf[threadIdx.x] += t;
+    __syncthreads();
+  }
+  return buf[threadIdx.x];
+}
+
+// One wave per entry: loc[e] = resident | compressed | words of row ids[e]
+// (its offset comes later); 0 for an id outside the table.  The words of a
+// compressed row follow from its header: ceil((n + 32n - p*m) / 32).
+__global__ __launch_bounds__(kBlockThreads) void cache_sizes_kernel(
+    Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint64_t n_ids,
+    unsigned long long* __restrict__ loc) {
+  const uint32_t lane = lane_id();
+  const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
+  const uint32_t n = cd.n, hw_n = (n + 31) / 32;
+  for (uint64_t e = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+       e < n_ids; e += nwaves) {
+    const uint64_t id = (uint64_t)ids[e];
+    unsigned long long out = 0;
+    if (id < n_rows) {
+      const bool flag = (flags[id >> 6] >> (id & 63)) & 1ull;
+      uint32_t words = n;
+      if (flag) {
+        const uint32_t* src = slots + id * n;
+        uint32_t acc = 0;
+        for (uint32_t t = lane; t < hw_n; t += kWave) {
+          uint32_t h = src[t];
+          if (t == hw_n - 1 && (n & 31u)) h &= (1u << (n & 31u)) - 1u;
+          acc += __popc(h);
+        }
+        const uint64_t m = wave_sum(acc);
+        words = (uint32_t)std::min<uint64_t>((33ull * n - (uint64_t)cd.p * m + 31) >> 5, n);
+      }
+      out = IBP_LOC_RESIDENT | (flag ? IBP_LOC_COMPRESSED : 0ull) |
+            ((unsigned long long)words << IBP_LOC_WORDS_SHIFT);
+    }
+    if (lane == 0) loc[e] = out;
+  }
+}
+
+// sums[t] = 16-byte units of the entries of scan tile t.
+__global__ __launch_bounds__(kBlockThreads) void cache_tile_sums_kernel(
+    const unsigned long long* __restrict__ loc, uint64_t n_ids,
+    unsigned long long* __restrict__ sums) {
+  __shared__ unsigned long long buf[kBlockThreads];
+  const uint64_t base = (uint64_t)blockIdx.x * kScanTile;
+  unsigned long long t = 0;
+  for (uint32_t j = threadIdx.x; j < kScanTile; j += kBlockThreads)
+    if (base + j < n_ids) t += loc_units(loc[base + j]);
+  const unsigned long long incl = block_inclusive_scan(t, buf);
+  if (threadIdx.x == kBlockThreads - 1) sums[blockIdx.x] = incl;
+}
+
+// Exclusive scan of sums[0, nt) in place, total in sums[nt]; one workgroup.
+__global__ __launch_bounds__(kBlockThreads) void cache_scan_sums_kernel(
+    unsigned long long* __restrict__ sums, uint32_t nt) {
+  __shared__ unsigned long long buf[kBlockThreads];
+  unsigned long long carry = 0;
+  for (uint32_t t0 = 0; t0 < nt; t0 += kBlockThreads) {
+    const uint32_t j = t0 + threadIdx.x;
+    const unsigned long long v = j < nt ? sums[j] : 0ull;
+    const unsigned long long incl = block_inclusive_scan(v, buf);
+    if (j < nt) sums[j] = carry + incl - v;
+    carry += buf[kBlockThreads - 1];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sums[nt] = carry;
+}
+
+// Adds each entry's arena offset (16-byte units) to its locator.
+__global__ __launch_bounds__(kBlockThreads) void cache_offsets_kernel(
+    unsigned long long* __restrict__ loc, uint64_t n_ids,
+    const unsigned long long* __restrict__ sums) {
+  __shared__ unsigned long long buf[kBlockThreads];
+  const uint64_t base = (uint64_t)blockIdx.x * kScanTile + (uint64_t)threadIdx.x * kScanPerThread;
+  unsigned long long lv[kScanPerThread];
+  unsigned long long t = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < kScanPerThread; ++k) {
+    lv[k] = base + k < n_ids ? loc[base + k] : 0ull;
+    t += loc_units(lv[k]);
+  }
+  const unsigned long long incl = block_inclusive_scan(t, buf);
+  unsigned long long off = sums[blockIdx.x] + incl - t;
+#pragma unroll
+  for (uint32_t k = 0; k < kScanPerThread; ++k) {
+    if (lv[k] & IBP_LOC_RESIDENT) {
+      loc[base + k] = lv[k] | (off & IBP_LOC_OFFSET_MASK);
+      off += loc_units(lv[k]);
+    }
+  }
+}
+
+// One wave per entry: copy the row's stored words into its arena entry (zero
+// padded to 16 bytes) and point the row's table locator at it.  Entries
+// that would end past the arena, or whose id left the table, are skipped.
+__global__ __launch_bounds__(kBlockThreads) void cache_fill_kernel(
+    uint32_t n, const uint32_t* __restrict__ slots, const int64_t* __restrict__ ids,
+    const unsigned long long* __restrict__ entry_loc, uint64_t n_ids, uint64_t n_rows,
+    uint32_t* __restrict__ arena, uint64_t arena_units,
+    unsigned long long* __restrict__ cache_loc) {
+  const uint32_t lane = lane_id();
+  const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t e = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+       e < n_ids; e += nwaves) {
+    const unsigned long long l = entry_loc[e];
+    const uint64_t id = (uint64_t)ids[e];
+    if (!(l & IBP_LOC_RESIDENT) || id >= n_rows) continue;
+    const uint32_t words = (uint32_t)((l >> IBP_LOC_WORDS_SHIFT) & IBP_LOC_WORDS_MASK);
+    const uint64_t off = l & IBP_LOC_OFFSET_MASK;
+    if (words > n || off + loc_units(l) > arena_units) continue;
+    const uint32_t* src = slots + id * n;
+    uint32_t* out = arena + off * 4;
+    const uint32_t padded = (words + 3u) & ~3u;
+    for (uint32_t j = lane; j < padded; j += kWave) out[j] = j < words ? src[j] : 0u;
+    if (lane == 0) cache_loc[id] = l;
   }
 }
 
@@ -901,14 +1096,27 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
                                                           row_bits, vec, st);
 }
 
-template <bool GATHER, int NR>
-void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
-                     const int64_t* ids, uint64_t n_rows, uint64_t n_out, void* dst, int vec,
-                     hipStream_t st) {
+// Pointers of a decode launch; arena and cache_loc only for kModeCached.
+struct DecodeArgs {
+  const void* slots;
+  const uint64_t* flags;
+  const int64_t* ids;
+  const void* arena;
+  const uint64_t* cache_loc;
+  uint64_t n_rows;
+  uint64_t n_out;
+  void* dst;
+  int vec;
+};
+
+template <int MODE, int NR>
+void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
+  const uint32_t* arena = (const uint32_t*)a.arena;
+  const unsigned long long* cloc = (const unsigned long long*)a.cache_loc;
   if (cd.n <= kSegBlocks) {
     const uint64_t piece = 1ull << 30;
-    for (uint64_t off = 0; off < n_out; off += piece) {
-      const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, n_out - off);
+    for (uint64_t off = 0; off < a.n_out; off += piece) {
+      const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, a.n_out - off);
       const uint64_t wgs = (cnt + kWavesPerBlock - 1) / kWavesPerBlock;
       // Grid size (measured on MI355X): with Mask = all ones (p = 32) the
       // streams of sparse rows fit the prefetched window and one row per wave
@@ -918,17 +1126,17 @@ void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
       const uint32_t mult = cd.p == 32 ? 64u : (cd.n >= 1024 ? 16u : 8u);
       const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(mult));
       // a full decompress is the identity gather: row `off + r` of the table
-      const uint32_t* sl = (const uint32_t*)slots;
-      const unsigned long long* fl = (const unsigned long long*)flags;
-      if (!GATHER) {  // shift the table window; flags stay word aligned (piece % 64 == 0)
+      const uint32_t* sl = (const uint32_t*)a.slots;
+      const unsigned long long* fl = (const unsigned long long*)a.flags;
+      if (MODE == kModeTable) {  // shift the table window; flags stay word aligned (piece % 64 == 0)
         sl += off * cd.n;
         fl += off / 64;
       }
-      const int64_t* id_p = GATHER ? ids + off : ids;
-      uint32_t* out_p = (uint32_t*)dst + off * cd.n;
+      const int64_t* id_p = MODE != kModeTable ? a.ids + off : a.ids;
+      uint32_t* out_p = (uint32_t*)a.dst + off * cd.n;
 #define IBP_ROWS(NCH)                                                                     \
-  hipLaunchKernelGGL((decode_rows_kernel<GATHER, NR, NCH>), dim3(grid), dim3(kBlockThreads), \
-                     0, st, cd, sl, fl, id_p, n_rows, cnt, out_p, vec)
+  hipLaunchKernelGGL((decode_rows_kernel<MODE, NR, NCH>), dim3(grid), dim3(kBlockThreads), \
+                     0, st, cd, sl, fl, id_p, arena, cloc, a.n_rows, cnt, out_p, a.vec)
       switch (cd.n) {
         case 128: IBP_ROWS(2); break;
         case 256: IBP_ROWS(4); break;
@@ -944,25 +1152,23 @@ void launch_decode_t(const Codec& cd, const void* slots, const uint64_t* flags,
   // header-prefix reads than they gain in parallelism, even for 8 KiB rows)
   const uint64_t seg = kSegBlocks;
   const uint32_t nseg = (uint32_t)((cd.n + seg - 1) / seg);
-  const uint64_t n_tasks = n_out * nseg;
+  const uint64_t n_tasks = a.n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((decode_segments_kernel<GATHER, NR>), dim3(grid_for(wgs)),
-                     dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
-                     (const unsigned long long*)flags, ids, n_rows, n_tasks, nseg,
-                     (uint32_t)seg, (uint32_t*)dst, vec);
+  hipLaunchKernelGGL((decode_segments_kernel<MODE, NR>), dim3(grid_for(wgs)),
+                     dim3(kBlockThreads), 0, st, cd, (const uint32_t*)a.slots,
+                     (const unsigned long long*)a.flags, a.ids, arena, cloc, a.n_rows, n_tasks,
+                     nseg, (uint32_t)seg, (uint32_t*)a.dst, a.vec);
 }
 
-template <bool GATHER>
-void launch_decode(const Codec& cd, const void* slots, const uint64_t* flags,
-                   const int64_t* ids, uint64_t n_rows, uint64_t n_out, void* dst, int vec,
-                   hipStream_t st) {
+template <int MODE>
+void launch_decode(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   switch (cd.runs.n) {
-    case 0: launch_decode_t<GATHER, 0>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
-    case 1: launch_decode_t<GATHER, 1>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
-    case 2: launch_decode_t<GATHER, 2>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
-    case 3: launch_decode_t<GATHER, 3>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
-    case 4: launch_decode_t<GATHER, 4>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
-    default: launch_decode_t<GATHER, -1>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st); break;
+    case 0: launch_decode_t<MODE, 0>(cd, a, st); break;
+    case 1: launch_decode_t<MODE, 1>(cd, a, st); break;
+    case 2: launch_decode_t<MODE, 2>(cd, a, st); break;
+    case 3: launch_decode_t<MODE, 3>(cd, a, st); break;
+    case 4: launch_decode_t<MODE, 4>(cd, a, st); break;
+    default: launch_decode_t<MODE, -1>(cd, a, st); break;
   }
 }
 
@@ -1095,25 +1301,34 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
 
 static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
                          const void* slots, const uint64_t* flags, const int64_t* ids,
-                         uint64_t n_out, void* dst, void* stream, bool gather) {
+                         uint64_t n_out, void* dst, void* stream, int mode,
+                         const void* arena = nullptr, const uint64_t* cache_loc = nullptr) {
   int rc = check_metadata(md);
   if (rc) return rc;
   rc = check_rows(n_rows, row_bytes);
   if (rc) return rc;
   if (n_out > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
   if (n_out == 0) return IBP_OK;
+  const bool gather = mode != kModeTable;
   if (n_rows == 0 || !slots || !flags || !dst || (gather && !ids))
     return IBP_ERR_INVALID_ARGUMENT;
+  if (mode == kModeCached && (!arena || !cache_loc)) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(slots, 4) || !aligned(dst, 4) || !aligned(flags, 8) ||
       (gather && !aligned(ids, 8)))
     return IBP_ERR_LAYOUT;
+  if (mode == kModeCached && (!aligned(arena, 16) || !aligned(cache_loc, 8)))
+    return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
   const Codec cd = make_codec(md, row_bytes);
+  // cache entries start at 16-byte boundaries of the (16-byte aligned) arena
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
-  if (gather)
-    launch_decode<true>(cd, slots, flags, ids, n_rows, n_out, dst, vec, st);
+  const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec};
+  if (mode == kModeCached)
+    launch_decode<kModeCached>(cd, a, st);
+  else if (gather)
+    launch_decode<kModeGather>(cd, a, st);
   else
-    launch_decode<false>(cd, slots, flags, nullptr, n_rows, n_out, dst, vec, st);
+    launch_decode<kModeTable>(cd, a, st);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? IBP_OK : hip_fail(e);
 }
@@ -1121,14 +1336,107 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
 int ibp_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
                    const void* slots, const uint64_t* flags, void* dst, void* stream) {
   return decode_common(md, n_rows, row_bytes, slots, flags, nullptr, n_rows, dst, stream,
-                       false);
+                       kModeTable);
 }
 
 int ibp_gather_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
                           const void* slots, const uint64_t* flags, const int64_t* row_ids,
                           uint64_t n_ids, void* dst, void* stream) {
   return decode_common(md, n_rows, row_bytes, slots, flags, row_ids, n_ids, dst, stream,
-                       true);
+                       kModeGather);
+}
+
+static int check_cache_image(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                             const void* slots, const uint64_t* flags, const int64_t* row_ids,
+                             uint64_t n_ids) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  rc = check_rows(n_rows, row_bytes);
+  if (rc) return rc;
+  if (n_ids > (1ull << 36)) return IBP_ERR_INVALID_ARGUMENT;  // scan tiles fit one grid
+  if (n_ids == 0) return IBP_OK;
+  if (n_rows == 0 || !slots || !flags || !row_ids) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(slots, 4) || !aligned(flags, 8) || !aligned(row_ids, 8)) return IBP_ERR_LAYOUT;
+  return IBP_OK;
+}
+
+int ibp_cache_plan(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                   const void* slots, const uint64_t* flags, const int64_t* row_ids,
+                   uint64_t n_ids, uint64_t* entry_loc, uint64_t* arena_bytes, void* stream) {
+  int rc = check_cache_image(md, n_rows, row_bytes, slots, flags, row_ids, n_ids);
+  if (rc) return rc;
+  if (!arena_bytes) return IBP_ERR_INVALID_ARGUMENT;
+  if (n_ids == 0) {
+    *arena_bytes = 0;
+    return IBP_OK;
+  }
+  if (!entry_loc) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(entry_loc, 8)) return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  const Codec cd = make_codec(md, row_bytes);
+  const uint64_t n_tiles = (n_ids + kScanTile - 1) / kScanTile;  // <= 2^28
+  unsigned long long* d_sums = nullptr;
+  hipError_t e = hipMalloc((void**)&d_sums, (n_tiles + 1) * sizeof(unsigned long long));
+  if (e != hipSuccess) return hip_fail(e);
+  unsigned long long* loc = (unsigned long long*)entry_loc;
+  const uint64_t size_wgs = (n_ids + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL(cache_sizes_kernel,
+                     dim3((uint32_t)std::min<uint64_t>(size_wgs, workgroups_per_device(16))),
+                     dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
+                     (const unsigned long long*)flags, row_ids, n_rows, n_ids, loc);
+  hipLaunchKernelGGL(cache_tile_sums_kernel, dim3((uint32_t)n_tiles), dim3(kBlockThreads), 0, st,
+                     (const unsigned long long*)loc, n_ids, d_sums);
+  hipLaunchKernelGGL(cache_scan_sums_kernel, dim3(1), dim3(kBlockThreads), 0, st, d_sums,
+                     (uint32_t)n_tiles);
+  hipLaunchKernelGGL(cache_offsets_kernel, dim3((uint32_t)n_tiles), dim3(kBlockThreads), 0, st,
+                     loc, n_ids, (const unsigned long long*)d_sums);
+  unsigned long long units = 0;
+  e = hipGetLastError();
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(&units, d_sums + n_tiles, sizeof(units), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  hipError_t ef = hipFree(d_sums);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  if (units > IBP_LOC_OFFSET_MASK) return IBP_ERR_UNSUPPORTED;
+  *arena_bytes = units * 16;
+  return IBP_OK;
+}
+
+int ibp_cache_fill(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                   const void* slots, const uint64_t* flags, const int64_t* row_ids,
+                   uint64_t n_ids, const uint64_t* entry_loc, void* arena,
+                   uint64_t arena_bytes, uint64_t* cache_loc, void* stream) {
+  int rc = check_cache_image(md, n_rows, row_bytes, slots, flags, row_ids, n_ids);
+  if (rc) return rc;
+  if (!cache_loc || (n_ids && (!entry_loc || (!arena && arena_bytes))))
+    return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(cache_loc, 8) || (entry_loc && !aligned(entry_loc, 8)) ||
+      (arena && !aligned(arena, 16)))
+    return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((n_rows + 255) / 256)), dim3(256), 0, st,
+                     (unsigned long long*)cache_loc, n_rows, 0ull);
+  if (n_ids && arena_bytes >= 16) {
+    const uint64_t wgs = (n_ids + kWavesPerBlock - 1) / kWavesPerBlock;
+    hipLaunchKernelGGL(cache_fill_kernel,
+                       dim3((uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(16))),
+                       dim3(kBlockThreads), 0, st, (uint32_t)(row_bytes / 4),
+                       (const uint32_t*)slots, row_ids, (const unsigned long long*)entry_loc,
+                       n_ids, n_rows, (uint32_t*)arena, arena_bytes / 16,
+                       (unsigned long long*)cache_loc);
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+int ibp_gather_decompress_cached(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                                 const void* arena, const uint64_t* cache_loc,
+                                 const void* slots, const uint64_t* flags,
+                                 const int64_t* row_ids, uint64_t n_ids, void* dst,
+                                 void* stream) {
+  return decode_common(md, n_rows, row_bytes, slots, flags, row_ids, n_ids, dst, stream,
+                       kModeCached, arena, cache_loc);
 }
 
 int ibp_host_device_pointer(const void* host_ptr, void** device_ptr) {

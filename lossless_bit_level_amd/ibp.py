@@ -21,6 +21,11 @@ IBP_ERR_LAYOUT = -3
 IBP_ERR_EMPTY = -4
 IBP_ERR_HIP = -5
 IBP_MAX_COMPRESS_ROW_BYTES = 98304
+IBP_LOC_RESIDENT = 1 << 63
+IBP_LOC_COMPRESSED = 1 << 62
+IBP_LOC_WORDS_SHIFT = 36
+IBP_LOC_WORDS_MASK = (1 << 26) - 1
+IBP_LOC_OFFSET_MASK = (1 << 36) - 1
 
 
 class ibp_metadata(ctypes.Structure):
@@ -65,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.ibp_compress.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp]
         L.ibp_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, vp]
         L.ibp_gather_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp]
+        L.ibp_cache_plan.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, ctypes.POINTER(u64), vp]
+        L.ibp_cache_fill.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp, u64, vp, vp]
+        L.ibp_gather_decompress_cached.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp, u64, vp, vp]
         L.ibp_flag_words.argtypes = [u64]
         L.ibp_flag_words.restype = u64
         L.ibp_host_device_pointer.argtypes = [vp, ctypes.POINTER(vp)]
@@ -73,7 +81,8 @@ def lib() -> ctypes.CDLL:
         L.ibp_last_hip_error.argtypes = []
         for f in ("ibp_metadata_from_counts", "ibp_build_metadata", "ibp_compress",
                   "ibp_decompress", "ibp_gather_decompress", "ibp_host_device_pointer",
-                  "ibp_last_hip_error"):
+                  "ibp_last_hip_error", "ibp_cache_plan", "ibp_cache_fill",
+                  "ibp_gather_decompress_cached"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -261,4 +270,112 @@ def ibp_decompress_launcher(md: ibp_metadata, slots: torch.Tensor, flags: torch.
         rc = fn(*args)
         if rc:
             raise IBPError("ibp_decompress", rc)
+    return launch
+
+
+def _ids(row_ids: torch.Tensor) -> torch.Tensor:
+    if row_ids.dtype != torch.int64 or not row_ids.is_cuda or not row_ids.is_contiguous():
+        raise ValueError("row_ids must be a contiguous int64 GPU tensor")
+    return row_ids
+
+
+def _need_size(t: torch.Tensor, nbytes: int, name: str):
+    if t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous and hold at least {nbytes} bytes")
+
+
+def ibp_cache_plan(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                   row_ids: torch.Tensor, entry_loc: torch.Tensor | None = None,
+                   stream=None):
+    """Plan a packed cache of rows row_ids of the image (slots, flags).
+    Returns (entry_loc int64 [n_ids] on the GPU, arena_bytes).  Synchronous."""
+    n_rows, row_bytes = _rows(slots)
+    _ids(row_ids)
+    _need_cuda(flags, "flags")
+    _need_size(flags, 8 * ibp_flag_words(n_rows), "flags")
+    n_ids = row_ids.numel()
+    if entry_loc is None:
+        entry_loc = torch.empty(max(1, n_ids), dtype=torch.int64, device=row_ids.device)
+    _need_cuda(entry_loc, "entry_loc")
+    _need_size(entry_loc, 8 * n_ids, "entry_loc")
+    total = ctypes.c_uint64()
+    _check("ibp_cache_plan",
+           lib().ibp_cache_plan(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
+                                flags.data_ptr(), row_ids.data_ptr(), n_ids,
+                                entry_loc.data_ptr(), ctypes.byref(total), _stream(stream)))
+    return entry_loc, int(total.value)
+
+
+def ibp_cache_fill(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
+                   row_ids: torch.Tensor, entry_loc: torch.Tensor, arena_bytes: int,
+                   arena: torch.Tensor | None = None, cache_loc: torch.Tensor | None = None,
+                   stream=None):
+    """Fill the planned arena and the table's locators.  Returns
+    (arena uint8 [arena_bytes] on the GPU, cache_loc int64 [n_rows])."""
+    n_rows, row_bytes = _rows(slots)
+    _ids(row_ids)
+    _need_cuda(flags, "flags")
+    _need_size(flags, 8 * ibp_flag_words(n_rows), "flags")
+    n_ids = row_ids.numel()
+    _need_cuda(entry_loc, "entry_loc")
+    _need_size(entry_loc, 8 * n_ids, "entry_loc")
+    if arena is None:
+        arena = torch.empty(max(16, arena_bytes), dtype=torch.uint8, device=row_ids.device)
+    if cache_loc is None:
+        cache_loc = torch.empty(max(1, n_rows), dtype=torch.int64, device=row_ids.device)
+    _need_cuda(arena, "arena")
+    _need_size(arena, arena_bytes, "arena")
+    _need_cuda(cache_loc, "cache_loc")
+    _need_size(cache_loc, 8 * n_rows, "cache_loc")
+    _check("ibp_cache_fill",
+           lib().ibp_cache_fill(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
+                                flags.data_ptr(), row_ids.data_ptr(), n_ids,
+                                entry_loc.data_ptr(), arena.data_ptr(), arena_bytes,
+                                cache_loc.data_ptr(), _stream(stream)))
+    return arena, cache_loc
+
+
+def ibp_gather_decompress_cached(md: ibp_metadata, arena: torch.Tensor,
+                                 cache_loc: torch.Tensor, slots: torch.Tensor,
+                                 flags: torch.Tensor, row_ids: torch.Tensor,
+                                 out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out[i] = restored row row_ids[i], from the arena for cached rows, else
+    from the image (slots on the GPU or pinned host)."""
+    return ibp_gather_decompress_cached_launcher(md, arena, cache_loc, slots, flags, row_ids,
+                                                 out, stream, _run=True)
+
+
+def ibp_gather_decompress_cached_launcher(md: ibp_metadata, arena: torch.Tensor,
+                                          cache_loc: torch.Tensor, slots: torch.Tensor,
+                                          flags: torch.Tensor, row_ids: torch.Tensor,
+                                          out: torch.Tensor | None = None, stream=None,
+                                          _run: bool = False):
+    """ibp_gather_decompress_cached with its arguments converted once: returns
+    a no-argument callable that enqueues the call (or, internally, the output
+    after one call)."""
+    n_rows, row_bytes = _rows(slots)
+    _ids(row_ids)
+    for t, name in ((flags, "flags"), (arena, "arena"), (cache_loc, "cache_loc")):
+        _need_cuda(t, name)
+    _need_size(flags, 8 * ibp_flag_words(n_rows), "flags")
+    _need_size(cache_loc, 8 * n_rows, "cache_loc")
+    n_ids = row_ids.numel()
+    if out is None:
+        out = torch.empty((n_ids, row_bytes), dtype=torch.uint8, device=row_ids.device)
+    _need_cuda(out, "out")
+    _need_size(out, n_ids * row_bytes, "out")
+    fn = lib().ibp_gather_decompress_cached
+    args = (ctypes.byref(md), ctypes.c_uint64(n_rows), ctypes.c_uint64(row_bytes),
+            ctypes.c_void_p(arena.data_ptr()), ctypes.c_void_p(cache_loc.data_ptr()),
+            ctypes.c_void_p(_dptr(slots)), ctypes.c_void_p(flags.data_ptr()),
+            ctypes.c_void_p(row_ids.data_ptr()), ctypes.c_uint64(n_ids),
+            ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_gather_decompress_cached", rc)
+    if _run:
+        launch()
+        return out
     return launch

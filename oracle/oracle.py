@@ -225,3 +225,69 @@ def image_bytes_equal(slots_a: np.ndarray, slots_b: np.ndarray,
         nb = stored_bytes(row_bytes, int(row_bits[r]), f)
         ok[r] = np.array_equal(a[r, :nb], b[r, :nb])
     return ok
+
+
+# ----------------------------------------------------------- packed cache --
+# Cache compression ([IBP] System integration): rows held in a GPU software
+# cache are kept in their stored form.  The page fixes no layout for it; this
+# is the library's, written out from its definition:
+#   * entry e holds the stored words of row ids[e] (ceil(C/32) words of a
+#     compressed row, all S/4 words of a raw row), zero padded to a multiple
+#     of 16 bytes; entries follow each other in id order from offset 0;
+#   * its locator is resident (bit 63) | compressed (bit 62) | words << 36 |
+#     offset in 16-byte units (bits 0..35); an id outside the table gets
+#     locator 0 and no space.
+LOC_RESIDENT = 1 << 63
+LOC_COMPRESSED = 1 << 62
+LOC_WORDS_SHIFT = 36
+LOC_WORDS_MASK = (1 << 26) - 1
+LOC_OFFSET_MASK = (1 << 36) - 1
+
+
+def cache_pack(slots: np.ndarray, flags: np.ndarray, row_bits: np.ndarray,
+               ids: np.ndarray):
+    """(entry locators uint64 [n_ids], arena uint8) for rows ids of an image."""
+    s = _bytes2d(slots)
+    n_rows, row_bytes = s.shape
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    locs = np.zeros(ids.size, np.uint64)
+    parts = []
+    off = 0
+    for e, r in enumerate(ids):
+        r = int(r)
+        if not 0 <= r < n_rows:
+            continue
+        f = (int(flags[r >> 6]) >> (r & 63)) & 1
+        nb = stored_bytes(row_bytes, int(row_bits[r]), f)
+        padded = (nb + 15) // 16 * 16
+        entry = np.zeros(padded, np.uint8)
+        entry[:nb] = s[r, :nb]
+        parts.append(entry)
+        locs[e] = LOC_RESIDENT | (f * LOC_COMPRESSED) | ((nb // 4) << LOC_WORDS_SHIFT) | off
+        off += padded // 16
+    arena = np.concatenate(parts) if parts else np.zeros(0, np.uint8)
+    return locs, arena
+
+
+def cache_gather(md: Metadata, arena: np.ndarray, cache_loc: np.ndarray,
+                 slots: np.ndarray, flags: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """out[i] = row ids[i] restored from its arena entry when cache_loc marks
+    it resident, else from the image; zero for an id outside the table."""
+    s = _bytes2d(slots)
+    n_rows, row_bytes = s.shape
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.zeros((ids.size, row_bytes), np.uint8)
+    for i, r in enumerate(ids):
+        r = int(r)
+        if not 0 <= r < n_rows:
+            continue
+        loc = int(cache_loc[r])
+        if loc & LOC_RESIDENT:
+            words = (loc >> LOC_WORDS_SHIFT) & LOC_WORDS_MASK
+            at = (loc & LOC_OFFSET_MASK) * 16
+            slot = np.zeros(row_bytes, np.uint8)
+            slot[:words * 4] = arena[at:at + words * 4]
+            out[i] = decompress_row(md, slot, int(bool(loc & LOC_COMPRESSED)))
+        else:
+            out[i] = decompress_row(md, s[r], (int(flags[r >> 6]) >> (r & 63)) & 1)
+    return out

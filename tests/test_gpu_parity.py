@@ -335,6 +335,78 @@ def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
 
 # ----------------------------------------------------- full-size workloads --
 
+# ------------------------------------------------------------ packed cache --
+
+CACHE_CASES = [
+    # (n_rows, row_bytes, mask, bitval, match_p)      decode path for gathers
+    (300, 512, 0x7C000000, 0x3C000000, 0.85),         # rows kernel, 2 chunks
+    (200, 2048, 0xFFFFFFFF, 0x00000000, 0.99),        # p = 32 word path
+    (150, 1024, 0x7C000000, 0x3C000000, 0.9),         # 4 chunks
+    (100, 4096, 0x7C007C00, 0x3C003C00, 0.9),         # 16 chunks
+    (90, 148, 0x7C000000, 0x3C000000, 0.85),          # n = 37, any-n path
+    (40, 8192, 0x78007800, 0x38003800, 0.9),          # segments kernel
+    (30, 28672, 0x7C007C00, 0x3C003C00, 0.9),         # 7 segments
+    (64, 2048, 0x00000000, 0x00000000, 0.0),          # p = 0: raw entries only
+]
+
+
+def check_cache_fill(ibp, md, slots_img, flags, rb_o, slots_o, flags_o, ids_c):
+    n_rows = slots_o.shape[0]
+    idc = torch.from_numpy(ids_c).cuda()
+    entry_loc, nbytes = ibp.ibp_cache_plan(md, slots_img, flags, idc)
+    locs_o, arena_o = orc.cache_pack(slots_o, flags_o, rb_o, ids_c)
+    assert np.array_equal(entry_loc.cpu().numpy().view(np.uint64)[:ids_c.size], locs_o)
+    assert nbytes == arena_o.size
+    arena, cache_loc = ibp.ibp_cache_fill(md, slots_img, flags, idc, entry_loc, nbytes)
+    torch.cuda.synchronize()
+    assert np.array_equal(arena.cpu().numpy()[:nbytes], arena_o)
+    cl = cache_loc.cpu().numpy().view(np.uint64)[:n_rows]
+    for r in range(n_rows):
+        allowed = {int(locs_o[e]) for e in np.nonzero(ids_c == r)[0]}
+        assert (int(cl[r]) in allowed) if allowed else cl[r] == 0, r
+    return arena, cache_loc
+
+
+@pytest.mark.parametrize("where", ["device", "pinned_host"])
+@pytest.mark.parametrize("case", CACHE_CASES, ids=lambda c: f"{c[0]}x{c[1]}_{c[2]:08x}")
+def test_cache_parity(ibp, case, where):
+    n_rows, S, mask, bitval, match_p = case
+    rng = np.random.default_rng(n_rows * 31 + S)
+    say(f"cache rows={n_rows} row_bytes={S} mask={mask:08x} image={where}")
+    x = make_rows(rng, n_rows, S, mask, bitval, match_p=match_p, raw_rows=(1,))
+    md = gmd(ibp, mask, bitval)
+    xg = to_gpu(x)
+    slots, flags, _ = ibp.ibp_compress(md, xg)
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    if where == "device":
+        img = slots
+    else:
+        img = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+        img.copy_(slots)
+    torch.cuda.synchronize()
+    q = rng.integers(0, n_rows, 4 * n_rows + 7).astype(np.int64)
+    q[:6] = [-1, n_rows, 1, 1, n_rows - 1, -(2**40)]
+    qg = torch.from_numpy(q).cuda()
+    # the oracle gathers the ids inside the table; the library gives zero rows
+    # for the others
+    inside = (q >= 0) & (q < n_rows)
+    want = np.zeros((q.size, S), np.uint8)
+    want[inside] = orc.gather_decompress(omd(md), slots_o, flags_o, q[inside])
+    # a third of the rows cached, one of them twice, plus ids outside the table
+    part = rng.choice(n_rows, max(1, n_rows // 3), replace=False).astype(np.int64)
+    caches = {
+        "part": np.concatenate([part, [part[0], -1, n_rows]]).astype(np.int64),
+        "none": np.zeros(0, np.int64),
+        "all": np.arange(n_rows, dtype=np.int64),
+    }
+    for name, ids_c in caches.items():
+        say(f"  cache {name}: {ids_c.size} entries")
+        arena, cache_loc = check_cache_fill(ibp, md, img, flags, rb_o, slots_o, flags_o, ids_c)
+        out = ibp.ibp_gather_decompress_cached(md, arena, cache_loc, img, flags, qg)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want), name
+
+
 def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     """Metadata over the first min(N, 2^24) blocks, compress the whole table,
     closed-form sizes for every row, sampled image rows against the oracle,
@@ -450,3 +522,59 @@ def test_full_llm_weights_layer(ibp, layer):
             assert flag_of(fl, r) == f_o
             nb = orc.stored_bytes(w.shape[1] * 2, c_o, f_o)
             assert np.array_equal(slots[int(r), :nb].cpu().numpy(), s_o[:nb])
+
+
+def test_full_sparse_gnn_cache_of_whole_table(ibp):
+    """The sparse feature table cached whole in GPU memory (its packed arena
+    is ~1/24 of the raw table) and the image in pinned host memory: every
+    gather batch is served from the arena."""
+    x = syn.sparse_gnn_rows()
+    n_rows = x.shape[0]
+    xg = to_gpu(x)
+    md, _ = ibp.ibp_build_metadata(xg, n_blocks=min(x.size, 1 << 24))
+    slots, flags, _ = ibp.ibp_compress(md, xg)
+    host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(slots)
+    all_ids = torch.arange(n_rows, dtype=torch.int64, device="cuda")
+    entry_loc, nbytes = ibp.ibp_cache_plan(md, host, flags, all_ids)
+    arena, cache_loc = ibp.ibp_cache_fill(md, host, flags, all_ids, entry_loc, nbytes)
+    say(f"sparse_gnn arena {nbytes / 2**20:.1f} MiB for a {x.nbytes / 2**30:.1f} GiB table")
+    assert nbytes * 16 < x.nbytes
+    assert bool((cache_loc < 0).all())  # every row resident (bit 63 set)
+    ids = syn.uniform_ids(syn.SPARSE_GNN_ROWS, 8, 65536)
+    out = torch.empty((ids.shape[1], x.shape[1] * 4), dtype=torch.uint8, device="cuda")
+    for bi, b in enumerate(ids):
+        idg = torch.from_numpy(np.ascontiguousarray(b)).cuda()
+        ibp.ibp_gather_decompress_cached(md, arena, cache_loc, host, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"batch {bi}"
+    del host
+
+
+def test_full_dense_gnn_partial_cache(ibp):
+    """Dense features with Zipf ids: the hottest rows (by id frequency) that
+    fit 256 MiB of packed arena, the rest fetched from pinned host memory."""
+    x = syn.dense_gnn_rows()
+    n_rows, S = x.shape[0], x.nbytes // x.shape[0]
+    xg = to_gpu(x)
+    md, _ = ibp.ibp_build_metadata(xg, n_blocks=1 << 24)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(slots)
+    ids = syn.zipf_ids(syn.DENSE_GNN_ROWS, 8, 65536)
+    counts = np.bincount(ids.reshape(-1), minlength=n_rows)
+    hot = np.argsort(-counts, kind="stable")
+    stored = ((rb.to(torch.int64) + 31) // 32 * 4).cpu().numpy()[:n_rows]
+    padded = (stored[hot] + 15) // 16 * 16
+    k = int(np.searchsorted(np.cumsum(padded), 256 << 20, side="right"))
+    cached = torch.from_numpy(hot[:k].astype(np.int64)).cuda()
+    entry_loc, nbytes = ibp.ibp_cache_plan(md, host, flags, cached)
+    assert nbytes <= 256 << 20
+    arena, cache_loc = ibp.ibp_cache_fill(md, host, flags, cached, entry_loc, nbytes)
+    hits = np.isin(ids, hot[:k]).mean()
+    say(f"dense_gnn: {k} rows cached ({k / n_rows:.1%}), hit rate {hits:.3f}")
+    out = torch.empty((ids.shape[1], S), dtype=torch.uint8, device="cuda")
+    for bi, b in enumerate(ids):
+        idg = torch.from_numpy(np.ascontiguousarray(b)).cuda()
+        ibp.ibp_gather_decompress_cached(md, arena, cache_loc, host, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"batch {bi}"
+    del host

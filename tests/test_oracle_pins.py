@@ -432,3 +432,69 @@ def test_gather_order_duplicates_and_empty():
     assert orc.gather_decompress(md, slots, flags, ids[:0]).shape == (0, 512)
     with pytest.raises(ValueError):
         orc.gather_decompress(md, slots, flags, np.array([300]))
+
+
+# ------------------------------------------------------------ packed cache --
+
+def test_cache_pack_round_trip_and_layout():
+    """The packed cache (cache compression of the page's System integration):
+    each entry, put back in a slot, decodes to its source row with the page's
+    decoder; entries tile the arena in id order at 16-byte boundaries with
+    zero padding; the stored words follow the closed form C = n + nW - p*m
+    with m counted by numpy; out-of-table ids get nothing."""
+    rng = np.random.default_rng(21)
+    mask, bitval = 0x7C000000, 0x3C000000
+    md = orc.Metadata(32, mask, bitval, 900000)
+    for S in (512, 148, 8):
+        n = S // 4
+        x = rng.standard_normal((40, n)).astype(np.float32).view(np.uint32)
+        x[3] = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)  # raw row
+        slots, flags, rb = orc.compress(md, x)
+        ids = np.array([5, 3, 39, -1, 5, 40, 0, 17, 2**40], np.int64)
+        locs, arena = orc.cache_pack(slots, flags, rb, ids)
+        m = ((x & np.uint32(mask)) == np.uint32(bitval)).sum(1)
+        c = n + 32 * n - 5 * m
+        end = 0
+        for e, r in enumerate(ids):
+            loc = int(locs[e])
+            if not 0 <= r < 40:
+                assert loc == 0
+                continue
+            comp = bool(loc & orc.LOC_COMPRESSED)
+            words = (loc >> orc.LOC_WORDS_SHIFT) & orc.LOC_WORDS_MASK
+            at = (loc & orc.LOC_OFFSET_MASK) * 16
+            assert loc & orc.LOC_RESIDENT and at == end
+            assert comp == (c[r] < 32 * n)
+            assert words == ((c[r] + 31) // 32 if comp else n)
+            end = at + (words * 4 + 15) // 16 * 16
+            assert not arena[at + words * 4:end].any()
+            slot = np.zeros(S, np.uint8)
+            slot[:words * 4] = arena[at:at + words * 4]
+            assert np.array_equal(orc.decompress_row(md, slot, int(comp)),
+                                  x[r].view(np.uint8)), (S, r)
+        assert end == arena.size
+        # the table's locators (one entry per row) and the gather through them
+        cache_loc = np.zeros(40, np.uint64)
+        for e, r in enumerate(ids):
+            if 0 <= r < 40:
+                cache_loc[r] = locs[e]
+        q = np.array([5, 6, 3, -7, 39, 0, 40, 17, 17, 1], np.int64)
+        want = np.zeros((q.size, S), np.uint8)
+        for i, r in enumerate(q):
+            if 0 <= r < 40:
+                want[i] = x[r].view(np.uint8)
+        assert np.array_equal(orc.cache_gather(md, arena, cache_loc, slots, flags, q), want)
+
+
+def test_cache_locator_constants_match_header():
+    """The oracle's locator layout is the one include/ibp.h declares."""
+    import re
+    text = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                             "include", "ibp.h")).read()
+    vals = {k: eval(v.replace("ull", ""), {}) for k, v in
+            re.findall(r"#define (IBP_LOC_[A-Z_]+) (.+)", text)}
+    assert vals == {"IBP_LOC_RESIDENT": orc.LOC_RESIDENT,
+                    "IBP_LOC_COMPRESSED": orc.LOC_COMPRESSED,
+                    "IBP_LOC_WORDS_SHIFT": orc.LOC_WORDS_SHIFT,
+                    "IBP_LOC_WORDS_MASK": orc.LOC_WORDS_MASK,
+                    "IBP_LOC_OFFSET_MASK": orc.LOC_OFFSET_MASK}
