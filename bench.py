@@ -46,10 +46,11 @@ class Workload:
     """tables: list of numpy arrays (rows on axis 0); steps: list of
     (table index, ids or None); sample_for_metadata: numpy array."""
 
-    def __init__(self, name, desc, tables, steps, sample, n_out_bytes):
+    def __init__(self, name, desc, tables, steps, sample, n_out_bytes, hot=None):
         self.name, self.desc, self.tables, self.steps = name, desc, tables, steps
         self.sample = sample
         self.n_out_bytes = n_out_bytes
+        self.hot = hot  # row ids by static popularity (cache fill order)
 
 
 def make_workload(name: str) -> Workload:
@@ -58,7 +59,8 @@ def make_workload(name: str) -> Workload:
         x = syn.sparse_gnn_rows()
         ids = syn.uniform_ids(syn.SPARSE_GNN_ROWS, 8, 65536)
         return Workload(name, "sparse GNN features 1048576 x 512 fp32, gather 8 x 65536 "
-                        "uniform ids", [x], [(0, b) for b in ids], x, 65536 * 2048)
+                        "uniform ids", [x], [(0, b) for b in ids], x, 65536 * 2048,
+                        hot=np.arange(x.shape[0], dtype=np.int64))
     if name in ("dense_gnn", "dlrm_emb"):
         if name == "dense_gnn":
             x = syn.dense_gnn_rows()
@@ -69,12 +71,14 @@ def make_workload(name: str) -> Workload:
             ids = syn.zipf_ids(syn.DLRM_EMB_ROWS, 8, 65536, seed=2)
             desc = "DLRM embedding 4194304 x 128 fp32 U(-0.05,0.05)"
         return Workload(name, desc + ", gather 8 x 65536 Zipf(1.05) ids", [x],
-                        [(0, b) for b in ids], x, 65536 * x.shape[1] * 4)
+                        [(0, b) for b in ids], x, 65536 * x.shape[1] * 4,
+                        hot=syn.zipf_hot_order(x.shape[0]))
     if name == "llm_kv":
         x = syn.llm_kv_pages()
         ids = syn.kv_page_ids()
         return Workload(name, "LLM KV cache [16,32,4096,128] bf16, 4 KiB pages, gather "
-                        "8 x 16384 page ids", [x], [(0, b) for b in ids], x, 16384 * 4096)
+                        "8 x 16384 page ids", [x], [(0, b) for b in ids], x, 16384 * 4096,
+                        hot=np.arange(x.shape[0], dtype=np.int64))
     if name == "llm_weights":
         tables = [syn.llm_weight(layer, j) for layer in (0, 1) for j in range(7)]
         steps = [(t, None) for t in range(len(tables))]
@@ -175,6 +179,10 @@ def main():
     ap.add_argument("--workload", default="sparse_gnn",
                     choices=["sparse_gnn", "dense_gnn", "dlrm_emb", "llm_weights", "llm_kv"])
     ap.add_argument("--source", default="device", choices=["device", "host"])
+    ap.add_argument("--cache-mib", type=int, default=0,
+                    help="keep the most popular rows that fit this many MiB in a packed, "
+                         "compressed GPU cache; the other rows come from the image "
+                         "(--source host: pinned host memory)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the timed loop "
@@ -262,6 +270,45 @@ def main():
         images = host_images
     del tables_g
 
+    # [IBP] System integration, cache compression: the most popular rows that
+    # fit the budget, in their stored form, packed into a GPU arena
+    cache = None
+    resident = None
+    if args.cache_mib:
+        if len(wl.tables) != 1 or wl.hot is None or any(ids is None for _, ids in wl.steps):
+            raise SystemExit("--cache-mib needs a gather workload over one table")
+        slots, flags, sb = images[0]
+        n_rows = wl.tables[0].shape[0]
+        budget = args.cache_mib << 20
+        k = int(np.searchsorted(np.cumsum((sb[wl.hot] + 15) // 16 * 16), budget, side="right"))
+        cached = torch.from_numpy(wl.hot[:k].copy()).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        entry_loc, arena_bytes = ibp.ibp_cache_plan(md, slots, flags, cached)
+        plan_ms = (time.perf_counter() - t0) * 1e3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        arena = torch.empty(max(16, arena_bytes), dtype=torch.uint8, device=dev)
+        cache_loc = torch.empty(n_rows, dtype=torch.int64, device=dev)
+        e0.record(stream)
+        ibp.ibp_cache_fill(md, slots, flags, cached, entry_loc, arena_bytes, arena=arena,
+                           cache_loc=cache_loc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del entry_loc
+        resident = np.zeros(n_rows, bool)
+        resident[wl.hot[:k]] = True
+        all_ids = np.concatenate([ids for _, ids in wl.steps])
+        counts = np.bincount(all_ids, minlength=n_rows)
+        raw_rows = min(n_rows, budget // S)
+        cache = {"budget_mib": args.cache_mib, "rows": k, "rows_fraction": round(k / n_rows, 4),
+                 "arena_mib": round(arena_bytes / 2**20, 2),
+                 "hit_rate": round(float(resident[all_ids].mean()), 4),
+                 "raw_cache_rows": int(raw_rows),
+                 "raw_cache_hit_rate": round(float(counts[wl.hot[:raw_rows]].sum() /
+                                                   counts.sum()), 4),
+                 "plan_ms": round(plan_ms, 3), "fill_ms": round(e0.elapsed_time(e1), 3)}
+        log(f"cache: {cache}")
+
     # per-step launch plan: (image index, ids tensor or None, output buffer)
     plan = []
     outs = []
@@ -274,14 +321,33 @@ def main():
         plan.append((ti, idg, outs[-1], ids))
 
     def algo_bytes(ti, ids):
+        """(bytes the launch must move, duplicates counted; bytes of it read
+        from the image; bytes of distinct image rows, which is what must cross
+        the host link when the image is in host memory: a repeated row is
+        served from the GPU's caches)."""
         slots, flags, sb = images[ti]
         if ids is None:
             n = wl.tables[ti].shape[0]
-            return int(sb.sum()) + wl.tables[ti].nbytes + 8 * ((n + 63) // 64)
-        return int(sb[ids].sum()) + len(ids) * wl.tables[ti].nbytes // wl.tables[ti].shape[0] + 8 * len(ids) + \
-            8 * len(np.unique(ids >> 6))
+            img = int(sb.sum())
+            return img + wl.tables[ti].nbytes + 8 * ((n + 63) // 64), img, img
+        row_out = wl.tables[ti].nbytes // wl.tables[ti].shape[0]
+        if resident is None:
+            img = int(sb[ids].sum())
+            return (img + len(ids) * row_out + 8 * len(ids) + 8 * len(np.unique(ids >> 6)), img,
+                    int(sb[np.unique(ids)].sum()))
+        hit = resident[ids]
+        miss_ids = ids[~hit]
+        img = int(sb[miss_ids].sum())
+        # hits: the arena entry (16-byte padded) and the locator; misses: the
+        # locator, the flag word and the stored row from the image
+        return (img + int(((sb[ids[hit]] + 15) // 16 * 16).sum()) + len(ids) * row_out +
+                16 * len(ids) + 8 * len(np.unique(miss_ids >> 6))), img, \
+            int(sb[np.unique(miss_ids)].sum())
 
-    plan_bytes = [algo_bytes(ti, ids) for ti, _, _, ids in plan]
+    plan_split = [algo_bytes(ti, ids) for ti, _, _, ids in plan]
+    plan_bytes = [b for b, _, _ in plan_split]
+    plan_img = [i for _, i, _ in plan_split]
+    plan_link = [u for _, _, u in plan_split]
     plan_out = [o.numel() for _, _, o, _ in plan]
 
     launchers = []
@@ -289,6 +355,9 @@ def main():
         slots, flags, _ = images[ti]
         if idg is None:
             launchers.append(ibp.ibp_decompress_launcher(md, slots, flags, out))
+        elif cache is not None:
+            launchers.append(ibp.ibp_gather_decompress_cached_launcher(
+                md, arena, cache_loc, slots, flags, idg, out))
         else:
             launchers.append(ibp.ibp_gather_decompress_launcher(md, slots, flags, idg, out))
 
@@ -360,13 +429,22 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         link = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
-        link_read = a_bytes - np.mean(plan_out)   # bytes that cross the link per launch
-        roof = {"bound": "host_link", "achieved": round(link_read / mean_launch_s / 1e9, 2),
-                "peak": round(link, 2), "unit": "GB/s",
-                "frac": round(link_read / mean_launch_s / 1e9 / link, 4), "traffic": None,
-                "peak_note": "measured pinned host->device hipMemcpy ceiling, 1 GiB"}
+        del h, d
+        link_read = sum(plan_link[k % len(plan)] for k in range(K)) / K  # crosses the link
+        hbm_bytes = a_bytes - sum(plan_img[k % len(plan)] for k in range(K)) / K
+        if link_read / link >= hbm_bytes / HBM_PEAK_GBPS:
+            roof = {"bound": "host_link", "achieved": round(link_read / mean_launch_s / 1e9, 2),
+                    "peak": round(link, 2), "unit": "GB/s",
+                    "frac": round(link_read / mean_launch_s / 1e9 / link, 4), "traffic": None,
+                    "peak_note": "measured pinned host->device hipMemcpy ceiling, 1 GiB"}
+        else:  # cache hits dominate: the HBM side bounds the launch
+            roof = {"bound": "hbm", "achieved": round(hbm_bytes / mean_launch_s / 1e9, 2),
+                    "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(hbm_bytes / mean_launch_s / 1e9 / HBM_PEAK_GBPS, 4),
+                    "traffic": None, "link_GB_per_s": round(link_read / mean_launch_s / 1e9, 2),
+                    "link_peak": round(link, 2)}
     else:
-        traffic = traffic_from_profiles(decode_kernel_name(S), wl.name)
+        traffic = None if cache else traffic_from_profiles(decode_kernel_name(S), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}
@@ -385,7 +463,7 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": wl.name, "desc": wl.desc, "source": args.source,
-                   "row_bytes": S, "parallelism": "none (1 GPU)"},
+                   "row_bytes": S, "cache_mib": args.cache_mib, "parallelism": "none (1 GPU)"},
         "compression_ratio": round(raw_bytes / stored, 4),
         "compression_ratio_bits": round(raw_bytes * 8 / bits_total, 4),
         "metadata": {"mask": f"0x{md.mask:08X}", "bitval": f"0x{md.bitval:08X}",
@@ -399,6 +477,8 @@ def main():
                    "source_sha256_16": kernel_source_hash()},
         "roofline": roof,
     }
+    if cache is not None:
+        res["cache"] = cache
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, md)

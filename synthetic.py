@@ -130,6 +130,12 @@ def zipf_ids(n_rows: int, batches: int, per_batch: int, a: float = 1.05,
     return perm[rank].astype(np.int64)
 
 
+def zipf_hot_order(n_rows: int, perm_seed: int = 3) -> np.ndarray:
+    """Row ids from most to least popular under zipf_ids (rank order): the
+    static popularity a feature cache is filled by (like node degree)."""
+    return np.random.default_rng(perm_seed).permutation(n_rows).astype(np.int64)
+
+
 LLM_LAYERS = 32
 LLM_HIDDEN, LLM_FFN = 4096, 14336
 LLM_MATRICES = 7  # q, k, v, o as [4096, 4096]; three MLP matrices [4096, 14336]
