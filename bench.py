@@ -94,8 +94,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def decode_kernel_name(row_bytes: int) -> str:
+def decode_kernel_name(row_bytes: int, width: int = 32) -> str:
     """The decode kernel libibp launches for rows of this size."""
+    if width != 32:
+        return "decode_wide_kernel"
     return "decode_rows_kernel" if row_bytes <= 4096 else "decode_segments_kernel"
 
 
@@ -128,7 +130,7 @@ def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
     from concurrent.futures import ThreadPoolExecutor
     from oracle import oracle as orc
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    md_o = orc.Metadata(32, int(md.mask), int(md.bitval), int(md.t_ppm))
+    md_o = orc.Metadata(int(md.width_bits), int(md.mask), int(md.bitval), int(md.t_ppm))
     t_idx, ids0 = wl.steps[0]
     table = wl.tables[t_idx]
     S = table.nbytes // table.shape[0]
@@ -179,6 +181,8 @@ def main():
     ap.add_argument("--workload", default="sparse_gnn",
                     choices=["sparse_gnn", "dense_gnn", "dlrm_emb", "llm_weights", "llm_kv"])
     ap.add_argument("--source", default="device", choices=["device", "host"])
+    ap.add_argument("--width", type=int, default=32, choices=[16, 32, 64],
+                    help="block width W in bits (32: the tuned kernels)")
     ap.add_argument("--cache-mib", type=int, default=0,
                     help="keep the most popular rows that fit this many MiB in a packed, "
                          "compressed GPU cache; the other rows come from the image "
@@ -211,10 +215,10 @@ def main():
 
     # metadata (first min(N, 2^24) blocks) and compression, timed apart
     samp = torch.from_numpy(wl.sample.reshape(-1).view(np.uint8)).to(dev)
-    n_blocks = min(samp.numel() // 4, 1 << 24)
+    n_blocks = min(samp.numel() * 8 // args.width, 1 << 24)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks)
+    md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks, width_bits=args.width)
     meta_ms = (time.perf_counter() - t0) * 1e3
     del samp
     images = []
@@ -444,7 +448,8 @@ def main():
                     "traffic": None, "link_GB_per_s": round(link_read / mean_launch_s / 1e9, 2),
                     "link_peak": round(link, 2)}
     else:
-        traffic = None if cache else traffic_from_profiles(decode_kernel_name(S), wl.name)
+        traffic = None if cache or args.width != 32 else \
+            traffic_from_profiles(decode_kernel_name(S), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}
@@ -463,14 +468,17 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": wl.name, "desc": wl.desc, "source": args.source,
-                   "row_bytes": S, "cache_mib": args.cache_mib, "parallelism": "none (1 GPU)"},
+                   "row_bytes": S, "block_bits": args.width, "cache_mib": args.cache_mib,
+                   "parallelism": "none (1 GPU)"},
         "compression_ratio": round(raw_bytes / stored, 4),
         "compression_ratio_bits": round(raw_bytes * 8 / bits_total, 4),
-        "metadata": {"mask": f"0x{md.mask:08X}", "bitval": f"0x{md.bitval:08X}",
+        "metadata": {"mask": f"0x{md.mask:0{args.width // 4}X}",
+                     "bitval": f"0x{md.bitval:0{args.width // 4}X}",
                      "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
-        "kernel": {"name": decode_kernel_name(S), "mean_launch_us": round(mean_launch_s * 1e6, 3),
+        "kernel": {"name": decode_kernel_name(S, args.width),
+                   "mean_launch_us": round(mean_launch_s * 1e6, 3),
                    "event_pair_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
                    "event_pair_min_us": round(float(launch_ms.min()) * 1e3, 3),
                    "algorithmic_bytes_per_launch": int(a_bytes),

@@ -11,10 +11,11 @@
  * Data model
  * ----------
  * A table is n_rows rows of row_bytes (= S) bytes, row r at byte r*S.  The
- * unit the page calls a tensor is a row here.  A row is cut into n = S/4
- * blocks of W = 32 bits (block k = little-endian 32-bit word k; a bf16 row
- * packs two elements per block).  One ibp_metadata (Mask/Bitval) covers the
- * whole table.
+ * unit the page calls a tensor is a row here.  A row is cut into n = 8S/W
+ * blocks of W bits, W = 16, 32 or 64 (block k = little-endian W-bit word k:
+ * with W = 32 a bf16 row packs two elements per block, with W = 16 one, with
+ * W = 64 four, or one fp64).  S is a multiple of 4, and of 8 when W = 64.
+ * One ibp_metadata (Mask/Bitval) covers the whole table.
  *
  * Compressed image
  * ----------------
@@ -44,8 +45,9 @@
  * the kernels then read across the host link without a staging copy
  * ([IBP] Compression and Decompression use zero-copy access to host memory).
  * row_bytes must be a multiple of 4 and every buffer 4-byte aligned (flags and
- * row ids 8-byte aligned); 16-byte aligned slots/src/dst with row_bytes a
- * multiple of 16 enable 16-byte memory operations.
+ * row ids 8-byte aligned; with W = 64 src, slots and dst 8-byte aligned too);
+ * 16-byte aligned slots/src/dst with row_bytes a multiple of 16 enable
+ * 16-byte memory operations (W = 32).
  * ibp_compress, ibp_decompress and ibp_gather_decompress only enqueue work on
  * `stream` (a hipStream_t, NULL = the null stream) and return at once; they
  * allocate nothing, copy nothing on the host and never synchronise.
@@ -72,7 +74,7 @@ extern "C" {
 
 #define IBP_OK 0
 #define IBP_ERR_INVALID_ARGUMENT (-1) /* null pointer, overflow, t_ppm > 1e6, bad metadata */
-#define IBP_ERR_UNSUPPORTED (-2)      /* block width other than 32, row too long */
+#define IBP_ERR_UNSUPPORTED (-2)      /* block width not 16, 32 or 64; row too long */
 #define IBP_ERR_LAYOUT (-3)           /* row_bytes not a multiple of 4, misaligned pointer */
 #define IBP_ERR_EMPTY (-4)            /* empty sample */
 #define IBP_ERR_HIP (-5)              /* HIP API or launch failure */
@@ -83,7 +85,7 @@ extern "C" {
 /* The fixed-size global metadata of [IBP] Preprocessing: one Mask/Bitval
  * pair for every block of the data set, 32 bytes, built once and reused. */
 typedef struct ibp_metadata {
-    uint32_t width_bits;     /* W; this library: 32 */
+    uint32_t width_bits;     /* W: 16, 32 or 64 */
     uint32_t invariant_bits; /* p = popcount(mask) */
     uint64_t mask;           /* bit b set <=> block bit b is invariant; bits >= W are 0 */
     uint64_t bitval;         /* values of the invariant bits; (bitval & ~mask) == 0 */
@@ -98,7 +100,7 @@ typedef struct ibp_metadata {
  * exact integers.  ones: width_bits host counters.  Pure host code; lets
  * counts from several devices or passes be summed before thresholding.
  * Errors: INVALID_ARGUMENT (null, ones[b] > n_blocks, t_ppm > 1e6),
- * UNSUPPORTED (width not 32), EMPTY (n_blocks == 0).
+ * UNSUPPORTED (width not 16, 32 or 64), EMPTY (n_blocks == 0).
  */
 int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
                              uint32_t width_bits, uint32_t t_ppm,
@@ -106,7 +108,7 @@ int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
 
 /*
  * [IBP] Preprocessing.  Counts the ones of every bit position over the
- * n_blocks 32-bit blocks at `sample` (device memory or mapped pinned host
+ * n_blocks W-bit blocks at `sample` (device memory or mapped pinned host
  * memory, 4-byte aligned) on the GPU, then applies the threshold rule of
  * ibp_metadata_from_counts.  out: host struct.  out_ones: optional host
  * array of width_bits counters.  SYNCHRONOUS: waits for `stream`.  Allocates

@@ -223,7 +223,7 @@ __global__ void fill_u64_kernel(unsigned long long* p, uint64_t n, unsigned long
 // ballot per bit would cost 32 ballots plus their scalar popcounts per block,
 // on a scalar unit that the four SIMDs of a CU share.
 constexpr int kCountWords = 32;                              // blocks per lane per step
-constexpr uint32_t kCountGroup = kCountWords * kWave;        // blocks per wave step
+constexpr uint32_t kCountGroup = kCountWords * kWave;        // words per wave step
 constexpr uint64_t kCountMaxSteps = (1u << 24) / kCountWords - 1;  // per wave, so P <= 24
 
 // out[0..B] = x[0..B) + y[0..B), bit-sliced.
@@ -240,13 +240,13 @@ __device__ __forceinline__ void sliced_add(const uint32_t* x, const uint32_t* y,
 }
 
 // acc += s, bit-sliced; the caller keeps every position's total below 2^P.
-template <int P>
-__device__ __forceinline__ void sliced_accumulate(uint32_t (&acc)[P], const uint32_t (&s)[6]) {
+template <int P, int S>
+__device__ __forceinline__ void sliced_accumulate(uint32_t (&acc)[P], const uint32_t (&s)[S]) {
   uint32_t c = 0;
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const uint32_t a = acc[j];
-    if (j < 6) {
+    if (j < S) {
       const uint32_t t = a ^ s[j];
       acc[j] = t ^ c;
       c = (a & s[j]) | (c & t);
@@ -271,25 +271,43 @@ __device__ __forceinline__ void sliced_count32(const uint32_t (&w)[kCountWords],
   sliced_add<5>(l4[0], l4[1], s);
 }
 
-// Step g of the sample covers blocks [g*2048, (g+1)*2048): lane L takes the
-// four blocks of 16-byte unit g*512 + j*64 + L for j < 8.  Blocks past the
-// end read as 0 (they add no ones).  Partial counts go out transposed,
-// partials[b * gridDim.x + workgroup], so the reduction reads each bit's
-// column contiguously.
-template <int P>
+// The same for 16 blocks, as 5 planes.
+__device__ __forceinline__ void sliced_count16(const uint32_t (&w)[16], uint32_t (&s)[5]) {
+  uint32_t l1[8][2], l2[4][3], l3[2][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sliced_add<1>(&w[2 * i], &w[2 * i + 1], l1[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sliced_add<2>(l1[2 * i], l1[2 * i + 1], l2[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) sliced_add<3>(l2[2 * i], l2[2 * i + 1], l3[i]);
+  sliced_add<4>(l3[0], l3[1], s);
+}
+
+// Step g of the sample covers words [g*2048, (g+1)*2048): lane L takes the
+// four words of 16-byte unit g*512 + j*64 + L for j < 8.  Words past the
+// end read as 0 (they add no ones).  NPOS = 32 counts the 32 bit positions
+// of every word; NPOS = 64 counts even and odd words apart (the low and high
+// halves of 64-bit blocks: a word's parity is that of its component in the
+// unit).  Partial counts go out transposed, partials[b * gridDim.x +
+// workgroup], so the reduction reads each position's column contiguously.
+template <int P, int NPOS>
 __global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
     const uint32_t* __restrict__ sample, uint64_t n_blocks,
     unsigned long long* __restrict__ partials) {
-  __shared__ uint32_t part[kWavesPerBlock][32];
+  static_assert(NPOS == 32 || NPOS == 64, "32 or 64 positions");
+  constexpr int NACC = NPOS / 32;
+  __shared__ uint32_t part[kWavesPerBlock][NPOS];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint64_t gwave = (uint64_t)blockIdx.x * kWavesPerBlock + wave;
   const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
   const uint64_t n_steps = (n_blocks + kCountGroup - 1) / kCountGroup;
   const uint64_t n_vec = ((uintptr_t)sample % 16) == 0 ? n_blocks / kCountGroup : 0;
-  uint32_t acc[P];
+  uint32_t acc[NACC][P];
 #pragma unroll
-  for (int j = 0; j < P; ++j) acc[j] = 0;
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int j = 0; j < P; ++j) acc[a][j] = 0;
   for (uint64_t g = gwave; g < n_steps; g += nwaves) {
     uint32_t w[kCountWords];
     if (g < n_vec) {
@@ -309,22 +327,37 @@ __global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
           w[4 * j + c] = k < n_blocks ? sample[k] : 0u;
         }
     }
-    uint32_t s[6];
-    sliced_count32(w, s);
-    sliced_accumulate<P>(acc, s);
+    if constexpr (NPOS == 32) {
+      uint32_t s[6];
+      sliced_count32(w, s);
+      sliced_accumulate<P, 6>(acc[0], s);
+    } else {
+      uint32_t we[16], wo[16], se[5], so[5];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        we[2 * j] = w[4 * j];
+        we[2 * j + 1] = w[4 * j + 2];
+        wo[2 * j] = w[4 * j + 1];
+        wo[2 * j + 1] = w[4 * j + 3];
+      }
+      sliced_count16(we, se);
+      sliced_count16(wo, so);
+      sliced_accumulate<P, 5>(acc[0], se);
+      sliced_accumulate<P, 5>(acc[NACC - 1], so);
+    }
   }
   // each lane's count is below 2^24 (at most kCountMaxSteps steps per wave),
   // so a wave's sum fits 32 bits
 #pragma unroll
-  for (int b = 0; b < 32; ++b) {
+  for (int b = 0; b < NPOS; ++b) {
     uint32_t c = 0;
 #pragma unroll
-    for (int j = 0; j < P; ++j) c += __builtin_amdgcn_ubfe(acc[j], b, 1) << j;
+    for (int j = 0; j < P; ++j) c += __builtin_amdgcn_ubfe(acc[b / 32][j], b % 32, 1) << j;
     const uint32_t t = wave_sum(c);
     if (lane == 0) part[wave][b] = t;
   }
   __syncthreads();
-  if (threadIdx.x < 32) {
+  if (threadIdx.x < NPOS) {
     unsigned long long t = 0;
 #pragma unroll
     for (int w = 0; w < kWavesPerBlock; ++w) t += part[w][threadIdx.x];
@@ -332,8 +365,8 @@ __global__ __launch_bounds__(kBlockThreads) void count_ones_kernel(
   }
 }
 
-// counts[b] = sum of column b of the transposed partials; one wave per bit
-// (launched as 8 workgroups of 4 waves).
+// counts[b] = sum of column b of the transposed partials; one wave per
+// position (launched as NPOS / 4 workgroups of 4 waves).
 __global__ __launch_bounds__(kBlockThreads) void reduce_counts_kernel(
     const unsigned long long* __restrict__ partials, uint32_t n_parts,
     unsigned long long* __restrict__ counts) {
@@ -836,6 +869,217 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
   }
 }
 
+// ---------------------------------------------------- other block widths --
+//
+// Blocks of 16 or 64 bits ([IBP] Compression cuts a tensor into blocks and
+// leaves their size open: 16 bits is one fp16/bf16 element, 64 bits one fp64
+// element or four half elements).  The scheme is the one above: one block
+// per lane, a 64-block chunk per wave step whose 64 participation bits are
+// one header word, payload offsets n + W*k - p*(stripped blocks before k) by
+// v_mbcnt.  A payload has W - p or W bits; a 64-bit one is read from three
+// LDS words with two funnel shifts.  Rows are whole 32-bit words (W = 16:
+// an even number of blocks; W = 64: rows and buffers 8-byte aligned).
+
+template <typename T>
+struct WideCodec {
+  static constexpr uint32_t W = 8 * sizeof(T);
+  T mask;
+  T bitval;
+  uint32_t p;      // invariant bits
+  uint32_t n;      // blocks per row
+  uint32_t nw;     // 32-bit words per row
+  uint32_t nruns;  // runs of ~mask
+  uint32_t shift[W / 2];
+  T place[W / 2];
+};
+
+template <typename T>
+__device__ __forceinline__ T extract_wide(T x, const WideCodec<T>& cd) {
+  T v = 0;
+  for (uint32_t j = 0; j < cd.nruns; ++j) v |= (T)((x & cd.place[j]) >> cd.shift[j]);
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T deposit_wide(T v, const WideCodec<T>& cd) {
+  T x = cd.bitval;
+  for (uint32_t j = 0; j < cd.nruns; ++j) x |= (T)((T)(v << cd.shift[j]) & cd.place[j]);
+  return x;
+}
+
+// The W bits of the stream at bit `rel` of the LDS window (bits past the
+// payload's length come from the next payload and are never used).
+template <typename T>
+__device__ __forceinline__ T lds_payload(const uint32_t* lds, uint32_t rel) {
+  const uint32_t wi = rel >> 5, s = rel & 31u;
+  const uint32_t lo = __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], s);
+  if constexpr (sizeof(T) == 8) {
+    const uint32_t hi = __builtin_amdgcn_alignbit(lds[wi + 2], lds[wi + 1], s);
+    return ((uint64_t)hi << 32) | lo;
+  } else {
+    return (T)lo;
+  }
+}
+
+// [IBP] Compression for W = 16 / 64, one workgroup per row (the stream is
+// assembled in LDS as in compress_kernel; in place is safe the same way).
+template <typename T, uint32_t MAXW>
+__global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
+    WideCodec<T> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t W = WideCodec<T>::W;
+  __shared__ uint32_t buf[MAXW + 4];
+  __shared__ uint32_t chunk_pre[(MAXW * 32 / W + kWave - 1) / kWave];
+  __shared__ uint32_t total_m;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t n = cd.n, nw = cd.nw;
+  const uint32_t nchunks = (n + kWave - 1) / kWave;
+
+  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const T* x_row = reinterpret_cast<const T*>(src + row * nw);
+    uint32_t* s_row = slots + row * nw;
+    for (uint32_t j = threadIdx.x; j < nw + 4; j += kBlockThreads) buf[j] = 0;
+    __syncthreads();
+    for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {
+      const uint32_t k = c * kWave + lane;
+      const bool valid = k < n;
+      const T x = valid ? x_row[k] : (T)0;
+      const unsigned long long h = __ballot(valid && (T)(x & cd.mask) == cd.bitval);
+      if (lane == 0) {
+        chunk_pre[c] = (uint32_t)__popcll(h);
+        buf[2 * c] = (uint32_t)h;
+        if (2 * c + 1 < (n + 31) / 32) buf[2 * c + 1] = (uint32_t)(h >> 32);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t carry = 0;
+      for (uint32_t b0 = 0; b0 < nchunks; b0 += kWave) {
+        const uint32_t c = b0 + lane;
+        const uint32_t v = c < nchunks ? chunk_pre[c] : 0u;
+        const uint32_t inc = wave_inclusive_scan(v, lane);
+        if (c < nchunks) chunk_pre[c] = carry + inc - v;
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
+      if (lane == 0) total_m = carry;
+    }
+    __syncthreads();
+    const uint32_t m = total_m;
+    const uint32_t c_bits = n + W * n - cd.p * m;
+    const bool flag = c_bits < W * n;
+    if (!flag) {
+      const uint32_t* xr = src + row * nw;
+      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = xr[j];
+    } else {
+      for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {
+        const uint32_t k = c * kWave + lane;
+        const bool valid = k < n;
+        const T x = valid ? x_row[k] : (T)0;
+        const bool match = valid && (T)(x & cd.mask) == cd.bitval;
+        const unsigned long long h = __ballot(match);
+        const uint32_t pre = chunk_pre[c] + bits_below_lane((uint32_t)h, (uint32_t)(h >> 32));
+        if (valid) {
+          const uint32_t off = n + W * k - cd.p * pre;
+          const uint32_t len = match ? W - cd.p : W;
+          const uint64_t pay = match ? (uint64_t)extract_wide<T>(x, cd) : (uint64_t)x;
+          if (len) {
+            const uint32_t sh = off & 31u, wi = off >> 5;
+            const uint64_t lo = pay << sh;  // bits [0, 64) of the placed payload
+            atomicOr(&buf[wi], (uint32_t)lo);
+            if (sh + len > 32u) atomicOr(&buf[wi + 1], (uint32_t)(lo >> 32));
+            if (sh + len > 64u) atomicOr(&buf[wi + 2], (uint32_t)(pay >> (64u - sh)));
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t words = (c_bits + 31u) >> 5;
+      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+    __syncthreads();
+  }
+}
+
+// [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
+// blocks), in the three row-source modes of the 32-bit kernels.
+template <typename T, int MODE>
+__global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
+    WideCodec<T> cd, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
+    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, T* __restrict__ dst) {
+  constexpr uint32_t W = WideCodec<T>::W;
+  __shared__ uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint32_t n = cd.n, nw = cd.nw;
+  const uint32_t g = gridDim.x;
+  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+    const uint64_t task = wg * kWavesPerBlock + wave;
+    if (task >= n_tasks) break;
+    const uint64_t i = task / nseg;
+    const uint32_t s = (uint32_t)(task - i * nseg);
+    const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
+    T* out = dst + i * n;
+    const uint32_t lo = s * seg;
+    const uint32_t hi = min(n, lo + seg);
+    if (MODE != kModeTable && id >= n_rows) {
+      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = (T)0;
+      continue;
+    }
+    const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
+    const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
+    const uint32_t* src = row_source<MODE>(slots, arena, id, nw, loc);
+    const uint32_t lim = row_words<MODE>(nw, loc);
+    if (!row_flag<MODE>(fw, id, loc)) {
+      const T* a = reinterpret_cast<const T*>(src);
+      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = a[j];
+      continue;
+    }
+    uint32_t carry = 0;  // stripped blocks before the segment (lo is a multiple of 64)
+    if (lo) {
+      uint32_t acc = 0;
+      for (uint32_t t = lane; t < lo / 32; t += kWave) acc += __popc(src[t]);
+      carry = wave_sum(acc);
+    }
+    const uint32_t hw_n = (hi - lo + 31) / 32;
+    uint32_t hw = 0;
+    if (lane < hw_n) {
+      const uint32_t t = lo / 32 + lane;
+      hw = src[t];
+      const uint32_t valid_bits = min(32u, hi - 32u * t);
+      if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
+    }
+    const uint32_t m_seg = wave_sum(__popc(hw));
+    const uint32_t a = n + W * lo - cd.p * carry;
+    const uint32_t b = n + W * hi - cd.p * (carry + m_seg);
+    const uint32_t wb = min((b + 31u) >> 5, lim);
+    const uint32_t wa = min(a >> 5, wb);
+    for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+    wave_lds_sync();
+    uint32_t u = a - 32u * wa;
+    for (uint32_t k0 = lo; k0 < hi; k0 += kWave) {
+      const uint32_t q = (k0 - lo) / 32;
+      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+      const bool valid = k0 + lane < hi;
+      const uint32_t rel = valid ? u + W * lane - __umul24(cd.p, bits_below_lane(h_lo, h_hi)) : 0u;
+      const T v = lds_payload<T>(lds, rel);
+      const bool stripped =
+          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+      const T x = stripped ? deposit_wide<T>(v, cd) : v;
+      if (valid) out[k0 + lane] = x;
+      u += W * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+    }
+    wave_lds_sync();
+  }
+}
+
 // ------------------------------------------------------ packed cache ----
 //
 // [IBP] System integration, cache compression: rows kept in a GPU software
@@ -868,23 +1112,23 @@ __device__ unsigned long long block_inclusive_scan(unsigned long long v, unsigne
 
 // One wave per entry: loc[e] = resident | compressed | words of row ids[e]
 // (its offset comes later); 0 for an id outside the table.  The words of a
-// compressed row follow from its header: ceil((n + 32n - p*m) / 32).
+// compressed row of n blocks follow from its header: ceil((n + W*n - p*m) / 32).
 __global__ __launch_bounds__(kBlockThreads) void cache_sizes_kernel(
-    Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
-    const int64_t* __restrict__ ids, uint64_t n_rows, uint64_t n_ids,
-    unsigned long long* __restrict__ loc) {
+    uint32_t n, uint32_t nw, uint32_t w_bits, uint32_t p, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint64_t n_ids, unsigned long long* __restrict__ loc) {
   const uint32_t lane = lane_id();
   const uint64_t nwaves = (uint64_t)gridDim.x * kWavesPerBlock;
-  const uint32_t n = cd.n, hw_n = (n + 31) / 32;
+  const uint32_t hw_n = (n + 31) / 32;
   for (uint64_t e = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
        e < n_ids; e += nwaves) {
     const uint64_t id = (uint64_t)ids[e];
     unsigned long long out = 0;
     if (id < n_rows) {
       const bool flag = (flags[id >> 6] >> (id & 63)) & 1ull;
-      uint32_t words = n;
+      uint32_t words = nw;
       if (flag) {
-        const uint32_t* src = slots + id * n;
+        const uint32_t* src = slots + id * nw;
         uint32_t acc = 0;
         for (uint32_t t = lane; t < hw_n; t += kWave) {
           uint32_t h = src[t];
@@ -892,7 +1136,8 @@ __global__ __launch_bounds__(kBlockThreads) void cache_sizes_kernel(
           acc += __popc(h);
         }
         const uint64_t m = wave_sum(acc);
-        words = (uint32_t)std::min<uint64_t>((33ull * n - (uint64_t)cd.p * m + 31) >> 5, n);
+        words = (uint32_t)std::min<uint64_t>(
+            ((uint64_t)n * (1 + w_bits) - (uint64_t)p * m + 31) >> 5, nw);
       }
       out = IBP_LOC_RESIDENT | (flag ? IBP_LOC_COMPRESSED : 0ull) |
             ((unsigned long long)words << IBP_LOC_WORDS_SHIFT);
@@ -997,17 +1242,22 @@ int popcount32(uint64_t x) {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+bool width_supported(uint32_t w) { return w == 16 || w == 32 || w == 64; }
+
 int check_metadata(const ibp_metadata* md) {
   if (!md) return IBP_ERR_INVALID_ARGUMENT;
-  if (md->width_bits != 32) return IBP_ERR_UNSUPPORTED;
-  if ((md->mask >> 32) != 0 || (md->bitval & ~md->mask) != 0 ||
+  if (!width_supported(md->width_bits)) return IBP_ERR_UNSUPPORTED;
+  if ((md->width_bits < 64 && (md->mask >> md->width_bits) != 0) ||
+      (md->bitval & ~md->mask) != 0 ||
       (int)md->invariant_bits != popcount32(md->mask) || md->t_ppm > 1000000u)
     return IBP_ERR_INVALID_ARGUMENT;
   return IBP_OK;
 }
 
-int check_rows(uint64_t n_rows, uint64_t row_bytes) {
-  if (row_bytes == 0 || row_bytes % 4 != 0) return IBP_ERR_LAYOUT;
+// Rows are whole 32-bit words, and whole blocks for 64-bit blocks.
+int check_rows(uint64_t n_rows, uint64_t row_bytes, uint32_t w_bits = 32) {
+  if (row_bytes == 0 || row_bytes % 4 != 0 || row_bytes % (w_bits / 8) != 0)
+    return IBP_ERR_LAYOUT;
   if (row_bytes > kMaxRowBytes) return IBP_ERR_UNSUPPORTED;
   if (n_rows > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
   return IBP_OK;
@@ -1033,6 +1283,32 @@ Codec make_codec(const ibp_metadata* md, uint64_t row_bytes) {
     b = e;
   }
   cd.runs.n = nr;
+  return cd;
+}
+
+template <typename T>
+WideCodec<T> make_wide_codec(const ibp_metadata* md, uint64_t row_bytes) {
+  constexpr uint32_t W = WideCodec<T>::W;
+  WideCodec<T> cd{};
+  cd.mask = (T)md->mask;
+  cd.bitval = (T)md->bitval;
+  cd.p = md->invariant_bits;
+  cd.n = (uint32_t)(row_bytes * 8 / W);
+  cd.nw = (uint32_t)(row_bytes / 4);
+  const uint64_t keep = ~md->mask & (W == 64 ? ~0ull : ((1ull << W) - 1));
+  uint32_t at = 0, nr = 0;
+  for (uint32_t b = 0; b < W;) {
+    if (!((keep >> b) & 1u)) { ++b; continue; }
+    uint32_t e = b;
+    while (e < W && ((keep >> e) & 1u)) ++e;
+    const uint32_t len = e - b;
+    cd.shift[nr] = b - at;
+    cd.place[nr] = (T)((len == 64 ? ~0ull : ((1ull << len) - 1)) << b);
+    ++nr;
+    at += len;
+    b = e;
+  }
+  cd.nruns = nr;
   return cd;
 }
 
@@ -1172,6 +1448,48 @@ void launch_decode(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   }
 }
 
+template <typename T>
+void launch_compress_wide(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                          const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
+                          hipStream_t st) {
+  const WideCodec<T> cd = make_wide_codec<T>(md, row_bytes);
+#define IBP_WIDE(MAXW)                                                                    \
+  hipLaunchKernelGGL((compress_wide_kernel<T, MAXW>), dim3(grid_for(n_rows)),             \
+                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,         \
+                     (uint32_t*)slots, (unsigned long long*)flags, row_bits)
+  if (cd.nw <= 1024) IBP_WIDE(1024);
+  else if (cd.nw <= 4096) IBP_WIDE(4096);
+  else if (cd.nw <= 8192) IBP_WIDE(8192);
+  else IBP_WIDE(IBP_MAX_COMPRESS_ROW_BYTES / 4);
+#undef IBP_WIDE
+}
+
+template <typename T, int MODE>
+void launch_decode_wide(const ibp_metadata* md, uint64_t row_bytes, const DecodeArgs& a,
+                        hipStream_t st) {
+  const WideCodec<T> cd = make_wide_codec<T>(md, row_bytes);
+  // a segment's stream stays within the LDS window: <= seg * W / 32 + 3 words
+  const uint32_t seg = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+  const uint32_t nseg = (cd.n + seg - 1) / seg;
+  const uint64_t n_tasks = a.n_out * nseg;
+  const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+  hipLaunchKernelGGL((decode_wide_kernel<T, MODE>), dim3(grid_for(wgs)), dim3(kBlockThreads), 0,
+                     st, cd, (const uint32_t*)a.slots, (const unsigned long long*)a.flags, a.ids,
+                     (const uint32_t*)a.arena, (const unsigned long long*)a.cache_loc, a.n_rows,
+                     n_tasks, nseg, seg, (T*)a.dst);
+}
+
+template <typename T>
+void launch_decode_wide_mode(const ibp_metadata* md, uint64_t row_bytes, const DecodeArgs& a,
+                             int mode, hipStream_t st) {
+  if (mode == kModeCached)
+    launch_decode_wide<T, kModeCached>(md, row_bytes, a, st);
+  else if (mode == kModeGather)
+    launch_decode_wide<T, kModeGather>(md, row_bytes, a, st);
+  else
+    launch_decode_wide<T, kModeTable>(md, row_bytes, a, st);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI ----
@@ -1197,7 +1515,7 @@ const char* ibp_status_string(int status) {
 int ibp_metadata_from_counts(const uint64_t* ones, uint64_t n_blocks, uint32_t width_bits,
                              uint32_t t_ppm, ibp_metadata* out) {
   if (!ones || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
-  if (width_bits != 32) return IBP_ERR_UNSUPPORTED;
+  if (!width_supported(width_bits)) return IBP_ERR_UNSUPPORTED;
   if (n_blocks == 0) return IBP_ERR_EMPTY;
   uint64_t mask = 0, bitval = 0;
   for (uint32_t b = 0; b < width_bits; ++b) {
@@ -1223,45 +1541,72 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
                        uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
                        void* stream) {
   if (!sample || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
-  if (width_bits != 32) return IBP_ERR_UNSUPPORTED;
+  if (!width_supported(width_bits)) return IBP_ERR_UNSUPPORTED;
   if (n_blocks == 0) return IBP_ERR_EMPTY;
+  if (n_blocks > (1ull << 56)) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(sample, 4)) return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
-  // about two workgroups per CU; more only when a wave would otherwise take
-  // more than kCountMaxSteps steps (its lanes' counts must stay below 2^24)
-  const uint64_t steps = (n_blocks + kCountGroup - 1) / kCountGroup;
-  uint64_t wgs = std::min<uint64_t>((steps + kWavesPerBlock - 1) / kWavesPerBlock,
-                                    workgroups_per_device(2));
-  const uint64_t per_wg = kCountMaxSteps * kWavesPerBlock;
-  wgs = std::max<uint64_t>({wgs, (steps + per_wg - 1) / per_wg, 1});
-  if (wgs > kMaxGrid) return IBP_ERR_INVALID_ARGUMENT;
-  const uint32_t grid = (uint32_t)wgs;
-  const uint64_t lane_max = (steps + wgs * kWavesPerBlock - 1) / (wgs * kWavesPerBlock) * kCountWords;
-  // partial counts (32 columns of grid) followed by the 32 totals
+  // The kernel counts 32-bit words: W = 16 adds the two halves of every word
+  // (and a last odd block on the host), W = 64 counts even and odd words.
+  const uint64_t words = width_bits == 16 ? n_blocks / 2
+                         : width_bits == 32 ? n_blocks : 2 * n_blocks;
+  const int npos = width_bits == 64 ? 64 : 32;
+  uint64_t counts[64] = {0};
+  uint16_t odd_block = 0;
+  hipError_t e = hipSuccess;
   unsigned long long* d_buf = nullptr;
-  hipError_t e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * 32 * sizeof(unsigned long long));
-  if (e != hipSuccess) return hip_fail(e);
-  unsigned long long* d_counts = d_buf + (size_t)grid * 32;
-  uint64_t ones[32];
-  const uint32_t* smp = (const uint32_t*)sample;
-  if (lane_max < (1u << 8))
-    hipLaunchKernelGGL(count_ones_kernel<8>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
-  else if (lane_max < (1u << 12))
-    hipLaunchKernelGGL(count_ones_kernel<12>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
-  else if (lane_max < (1u << 16))
-    hipLaunchKernelGGL(count_ones_kernel<16>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
-  else
-    hipLaunchKernelGGL(count_ones_kernel<24>, dim3(grid), dim3(kBlockThreads), 0, st, smp, n_blocks, d_buf);
-  hipLaunchKernelGGL(reduce_counts_kernel, dim3(32 / kWavesPerBlock), dim3(kBlockThreads), 0, st,
-                     (const unsigned long long*)d_buf, grid, d_counts);
-  e = hipGetLastError();
-  if (e == hipSuccess) e = hipMemcpyAsync(ones, d_counts, sizeof(ones), hipMemcpyDeviceToHost, st);
+  if (words) {
+    // about two workgroups per CU; more only when a wave would otherwise take
+    // more than kCountMaxSteps steps (its lanes' counts must stay below 2^24)
+    const uint64_t steps = (words + kCountGroup - 1) / kCountGroup;
+    uint64_t wgs = std::min<uint64_t>((steps + kWavesPerBlock - 1) / kWavesPerBlock,
+                                      workgroups_per_device(2));
+    const uint64_t per_wg = kCountMaxSteps * kWavesPerBlock;
+    wgs = std::max<uint64_t>({wgs, (steps + per_wg - 1) / per_wg, 1});
+    if (wgs > kMaxGrid) return IBP_ERR_INVALID_ARGUMENT;
+    const uint32_t grid = (uint32_t)wgs;
+    const uint64_t lane_max =
+        (steps + wgs * kWavesPerBlock - 1) / (wgs * kWavesPerBlock) * kCountWords;
+    // partial counts (npos columns of grid) followed by the npos totals
+    e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * npos * sizeof(unsigned long long));
+    if (e != hipSuccess) return hip_fail(e);
+    unsigned long long* d_counts = d_buf + (size_t)grid * npos;
+    const uint32_t* smp = (const uint32_t*)sample;
+#define IBP_COUNT(P, NPOS)                                                              \
+  hipLaunchKernelGGL((count_ones_kernel<P, NPOS>), dim3(grid), dim3(kBlockThreads), 0, st, \
+                     smp, words, d_buf)
+#define IBP_COUNT_NPOS(NPOS)                     \
+  if (lane_max < (1u << 8)) IBP_COUNT(8, NPOS);  \
+  else if (lane_max < (1u << 12)) IBP_COUNT(12, NPOS); \
+  else if (lane_max < (1u << 16)) IBP_COUNT(16, NPOS); \
+  else IBP_COUNT(24, NPOS);
+    if (npos == 64) {
+      IBP_COUNT_NPOS(64)
+    } else {
+      IBP_COUNT_NPOS(32)
+    }
+#undef IBP_COUNT_NPOS
+#undef IBP_COUNT
+    hipLaunchKernelGGL(reduce_counts_kernel, dim3(npos / kWavesPerBlock), dim3(kBlockThreads), 0,
+                       st, (const unsigned long long*)d_buf, grid, d_counts);
+    e = hipGetLastError();
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(counts, d_counts, npos * sizeof(uint64_t), hipMemcpyDeviceToHost, st);
+  }
+  if (e == hipSuccess && width_bits == 16 && (n_blocks & 1))
+    e = hipMemcpyAsync(&odd_block, (const uint16_t*)sample + (n_blocks - 1), 2,
+                       hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  hipError_t ef = hipFree(d_buf);
-  if (e == hipSuccess) e = ef;
+  if (d_buf) {
+    hipError_t ef = hipFree(d_buf);
+    if (e == hipSuccess) e = ef;
+  }
   if (e != hipSuccess) return hip_fail(e);
+  uint64_t ones[64];
+  for (uint32_t b = 0; b < width_bits; ++b)
+    ones[b] = width_bits == 16 ? counts[b] + counts[b + 16] + ((odd_block >> b) & 1u) : counts[b];
   if (out_ones)
-    for (int b = 0; b < 32; ++b) out_ones[b] = ones[b];
+    for (uint32_t b = 0; b < width_bits; ++b) out_ones[b] = ones[b];
   return ibp_metadata_from_counts(ones, n_blocks, width_bits, t_ppm, out);
 }
 
@@ -1269,12 +1614,13 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
                  void* slots, uint64_t* flags, uint32_t* row_bits, void* stream) {
   int rc = check_metadata(md);
   if (rc) return rc;
-  rc = check_rows(n_rows, row_bytes);
+  rc = check_rows(n_rows, row_bytes, md->width_bits);
   if (rc) return rc;
   if (row_bytes > IBP_MAX_COMPRESS_ROW_BYTES) return IBP_ERR_UNSUPPORTED;
   if (n_rows == 0) return IBP_OK;
   if (!src || !slots || !flags) return IBP_ERR_INVALID_ARGUMENT;
-  if (!aligned(src, 4) || !aligned(slots, 4) || !aligned(flags, 8) ||
+  const uintptr_t al = md->width_bits == 64 ? 8 : 4;
+  if (!aligned(src, al) || !aligned(slots, al) || !aligned(flags, 8) ||
       (row_bits && !aligned(row_bits, 4)))
     return IBP_ERR_LAYOUT;
   {  // in place (src == slots) is allowed, any other overlap is not
@@ -1282,11 +1628,19 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
     if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
   }
   hipStream_t st = (hipStream_t)stream;
-  const Codec cd = make_codec(md, row_bytes);
-  const int vec = row_bytes % 16 == 0 && aligned(src, 16) && aligned(slots, 16);
   const uint64_t fw = ibp_flag_words(n_rows);
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
                      (unsigned long long*)flags, fw, 0ull);
+  if (md->width_bits != 32) {
+    if (md->width_bits == 16)
+      launch_compress_wide<uint16_t>(md, n_rows, row_bytes, src, slots, flags, row_bits, st);
+    else
+      launch_compress_wide<uint64_t>(md, n_rows, row_bytes, src, slots, flags, row_bits, st);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? IBP_OK : hip_fail(e);
+  }
+  const Codec cd = make_codec(md, row_bytes);
+  const int vec = row_bytes % 16 == 0 && aligned(src, 16) && aligned(slots, 16);
   switch (cd.runs.n) {
     case 0: launch_compress_nr<0>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
     case 1: launch_compress_nr<1>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
@@ -1305,7 +1659,7 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
                          const void* arena = nullptr, const uint64_t* cache_loc = nullptr) {
   int rc = check_metadata(md);
   if (rc) return rc;
-  rc = check_rows(n_rows, row_bytes);
+  rc = check_rows(n_rows, row_bytes, md->width_bits);
   if (rc) return rc;
   if (n_out > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
   if (n_out == 0) return IBP_OK;
@@ -1319,6 +1673,16 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
   if (mode == kModeCached && (!aligned(arena, 16) || !aligned(cache_loc, 8)))
     return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
+  if (md->width_bits != 32) {
+    if (md->width_bits == 64 && (!aligned(slots, 8) || !aligned(dst, 8))) return IBP_ERR_LAYOUT;
+    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, 0};
+    if (md->width_bits == 16)
+      launch_decode_wide_mode<uint16_t>(md, row_bytes, a, mode, st);
+    else
+      launch_decode_wide_mode<uint64_t>(md, row_bytes, a, mode, st);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? IBP_OK : hip_fail(e);
+  }
   const Codec cd = make_codec(md, row_bytes);
   // cache entries start at 16-byte boundaries of the (16-byte aligned) arena
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
@@ -1351,7 +1715,7 @@ static int check_cache_image(const ibp_metadata* md, uint64_t n_rows, uint64_t r
                              uint64_t n_ids) {
   int rc = check_metadata(md);
   if (rc) return rc;
-  rc = check_rows(n_rows, row_bytes);
+  rc = check_rows(n_rows, row_bytes, md->width_bits);
   if (rc) return rc;
   if (n_ids > (1ull << 36)) return IBP_ERR_INVALID_ARGUMENT;  // scan tiles fit one grid
   if (n_ids == 0) return IBP_OK;
@@ -1373,8 +1737,7 @@ int ibp_cache_plan(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
   if (!entry_loc) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(entry_loc, 8)) return IBP_ERR_LAYOUT;
   hipStream_t st = (hipStream_t)stream;
-  const Codec cd = make_codec(md, row_bytes);
-  const uint64_t n_tiles = (n_ids + kScanTile - 1) / kScanTile;  // <= 2^28
+  const uint64_t n_tiles = (n_ids + kScanTile - 1) / kScanTile;  // <= 2^24
   unsigned long long* d_sums = nullptr;
   hipError_t e = hipMalloc((void**)&d_sums, (n_tiles + 1) * sizeof(unsigned long long));
   if (e != hipSuccess) return hip_fail(e);
@@ -1382,8 +1745,10 @@ int ibp_cache_plan(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
   const uint64_t size_wgs = (n_ids + kWavesPerBlock - 1) / kWavesPerBlock;
   hipLaunchKernelGGL(cache_sizes_kernel,
                      dim3((uint32_t)std::min<uint64_t>(size_wgs, workgroups_per_device(16))),
-                     dim3(kBlockThreads), 0, st, cd, (const uint32_t*)slots,
-                     (const unsigned long long*)flags, row_ids, n_rows, n_ids, loc);
+                     dim3(kBlockThreads), 0, st, (uint32_t)(row_bytes * 8 / md->width_bits),
+                     (uint32_t)(row_bytes / 4), md->width_bits, md->invariant_bits,
+                     (const uint32_t*)slots, (const unsigned long long*)flags, row_ids, n_rows,
+                     n_ids, loc);
   hipLaunchKernelGGL(cache_tile_sums_kernel, dim3((uint32_t)n_tiles), dim3(kBlockThreads), 0, st,
                      (const unsigned long long*)loc, n_ids, d_sums);
   hipLaunchKernelGGL(cache_scan_sums_kernel, dim3(1), dim3(kBlockThreads), 0, st, d_sums,

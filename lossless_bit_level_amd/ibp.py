@@ -154,7 +154,8 @@ def ibp_metadata_from_counts(ones, n_blocks: int, t_ppm: int = 900000,
 def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 32,
                        n_blocks: int | None = None, t_ppm: int | None = None,
                        stream=None):
-    """Mask/Bitval over the 32-bit blocks of `sample` (GPU or pinned host).
+    """Mask/Bitval over the width_bits-bit blocks of `sample` (GPU or pinned
+    host memory).
 
     Returns (ibp_metadata, ones) with ones a list of the per-bit counts.
     Synchronous."""

@@ -67,7 +67,13 @@ def test_validation_before_enqueue(ibp):
     fake = 0x10000  # never dereferenced: every call below fails validation
     # null metadata / bad metadata
     assert L.ibp_compress(None, 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
-    assert L.ibp_compress(byref(_md(ibp, w=16)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_compress(byref(_md(ibp, w=8)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_UNSUPPORTED
+    # a 16-bit mask must fit 16 bits; 64-bit blocks need 8-byte rows and buffers
+    assert L.ibp_compress(byref(_md(ibp, w=16)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress(byref(_md(ibp, 0x7C00, 0x3C00, w=16)), 0, 16, None, None, None, None, None) == ibp.IBP_OK
+    assert L.ibp_compress(byref(_md(ibp, w=64)), 4, 12, fake, fake, fake, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_compress(byref(_md(ibp, w=64)), 4, 16, fake + 4, fake + 4096, fake, None, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_decompress(byref(_md(ibp, w=64)), 4, 16, fake, fake, fake + 4, None) == ibp.IBP_ERR_LAYOUT
     assert L.ibp_compress(byref(_md(ibp, bitval=0x1)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_compress(byref(_md(ibp, p=3)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_compress(byref(_md(ibp, mask=1 << 40, bitval=0)), 4, 16, fake, fake, fake, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
@@ -96,7 +102,7 @@ def test_validation_before_enqueue(ibp):
     # metadata build
     out = ibp.ibp_metadata()
     assert L.ibp_build_metadata(fake, 0, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_EMPTY
-    assert L.ibp_build_metadata(fake, 10, 16, 900000, byref(out), None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_build_metadata(fake, 10, 8, 900000, byref(out), None, None) == ibp.IBP_ERR_UNSUPPORTED
     assert L.ibp_build_metadata(fake, 10, 32, 1000001, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_build_metadata(None, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_build_metadata(fake + 1, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_LAYOUT
@@ -123,5 +129,19 @@ def test_metadata_from_counts_rejects(ibp):
     out = ibp.ibp_metadata()
     assert L.ibp_metadata_from_counts(ones, 4, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_metadata_from_counts(ones, 0, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_EMPTY
-    assert L.ibp_metadata_from_counts(ones, 8, 64, 900000, ctypes.byref(out)) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_metadata_from_counts(ones, 8, 8, 900000, ctypes.byref(out)) == ibp.IBP_ERR_UNSUPPORTED
     assert L.ibp_metadata_from_counts(None, 8, 32, 900000, ctypes.byref(out)) == ibp.IBP_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("w", [16, 64])
+def test_metadata_from_counts_other_widths(ibp, w):
+    rng = np.random.default_rng(w)
+    dt = {16: np.uint16, 64: np.uint64}[w]
+    x = rng.standard_normal(3000).astype(np.float32).view(np.uint32)
+    samples = [x.view(dt), rng.integers(0, 2**63, 1000, dtype=np.int64).view(dt)]
+    for t_ppm in (500000, 900000, 1000000):
+        for smp in samples:
+            md_o, ones = orc.build_metadata(smp, w, t_ppm=t_ppm)
+            md = ibp.ibp_metadata_from_counts(ones, smp.size, t_ppm=t_ppm, width_bits=w)
+            assert (md.mask, md.bitval, md.invariant_bits, md.width_bits) == \
+                (md_o.mask, md_o.bitval, md_o.invariant_bits, w)

@@ -36,12 +36,12 @@ def to_gpu(x: np.ndarray) -> torch.Tensor:
 
 
 def omd(md) -> orc.Metadata:
-    return orc.Metadata(32, int(md.mask), int(md.bitval), int(md.t_ppm))
+    return orc.Metadata(int(md.width_bits), int(md.mask), int(md.bitval), int(md.t_ppm))
 
 
-def gmd(ibp, mask, bitval, t_ppm=900000):
+def gmd(ibp, mask, bitval, t_ppm=900000, w=32):
     md = ibp.ibp_metadata()
-    md.width_bits, md.mask, md.bitval, md.t_ppm = 32, mask, bitval, t_ppm
+    md.width_bits, md.mask, md.bitval, md.t_ppm = w, mask, bitval, t_ppm
     md.invariant_bits = bin(mask).count("1")
     return md
 
@@ -334,6 +334,130 @@ def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
 
 
 # ----------------------------------------------------- full-size workloads --
+
+# ------------------------------------------------------ other block widths --
+
+_DT = {16: np.uint16, 64: np.uint64}
+
+
+@pytest.mark.parametrize("w", [16, 64])
+def test_metadata_parity_other_widths(ibp, w):
+    """Per-bit counts of 16- and 64-bit blocks (W = 16 with an odd block count
+    and a sample only 4-byte aligned; W = 64 over bf16 quads and fp64)."""
+    rng = np.random.default_rng(40 + w)
+    if w == 16:
+        kv = syn.llm_kv_batch(0, seq=64).reshape(-1)
+        samples = {"kv_bf16": kv[:kv.size - 1], "small_odd": kv[:2049]}
+    else:
+        samples = {"bf16_quads": syn.llm_weight(0, 0, rows=slice(0, 64)).reshape(-1).view(np.uint64),
+                   "fp64": (rng.standard_normal(300_001) * 0.3).view(np.uint64)}
+    for name, x in samples.items():
+        for offset in (0, 4) if w == 16 else (0,):
+            say(f"metadata W={w} {name} blocks={x.size} offset={offset}")
+            buf = torch.zeros(x.nbytes + 16, dtype=torch.uint8, device="cuda")
+            buf[offset:offset + x.nbytes] = torch.from_numpy(x.view(np.uint8).copy()).cuda()
+            for t_ppm in (900000, 500000):
+                md_o, ones_o = orc.build_metadata(x, w, t_ppm=t_ppm)
+                md_g, ones_g = ibp.ibp_build_metadata(buf[offset:offset + x.nbytes], width_bits=w,
+                                                      n_blocks=x.size, t_ppm=t_ppm)
+                assert np.array_equal(np.array(ones_g, np.uint64), ones_o), (name, t_ppm)
+                assert (md_g.mask, md_g.bitval, md_g.width_bits) == (md_o.mask, md_o.bitval, w)
+
+
+def make_rows_w(rng, w, n_rows, row_bytes, mask, bitval, match_p=0.85, raw_rows=()):
+    dt = _DT[w]
+    x = rng.integers(0, 256, (n_rows, row_bytes), dtype=np.uint8).view(dt)
+    force = rng.random(x.shape) < match_p
+    keep = dt(~mask & ((1 << w) - 1))
+    x = np.where(force, (x & keep) | dt(bitval), x).astype(dt)
+    for r in raw_rows:
+        x[r] = rng.integers(0, 256, row_bytes, dtype=np.uint8).view(dt)
+    return np.ascontiguousarray(x).view(np.uint8).reshape(n_rows, row_bytes)
+
+
+WIDE_CASES = [
+    # (W, n_rows, row_bytes, mask, bitval, match_p)
+    (16, 130, 512, 0x7C00, 0x3C00, 0.85),                 # bf16 exponent bits
+    (16, 67, 148, 0x7C00, 0x3C00, 0.85),                  # n = 74: ragged chunk
+    (16, 33, 28672, 0x7800, 0x3800, 0.9),                 # 14 segments
+    (16, 40, 2048, 0xFFFF, 0x0000, 0.99),                 # p = 16
+    (16, 20, 1024, 0x0000, 0x0000, 0.0),                  # p = 0: all raw
+    (16, 50, 260, 0x5555, 0x1111, 0.9),                   # 8 runs
+    (16, 3, 98304, 0x7C00, 0x3C00, 0.9),                  # largest row
+    (64, 130, 1024, 0x7FF0000000000000, 0x3FF0000000000000, 0.85),  # fp64 exponent
+    (64, 70, 8200, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 1025 blocks, 3 segments
+    (64, 40, 24, 0xFFFF0000FFFF0000, 0x1234000056780000, 0.9),      # n = 3
+    (64, 20, 2048, 0xFFFFFFFFFFFFFFFF, 0x0, 0.99),                  # p = 64
+    (64, 30, 512, 0x5555555555555555, 0x1111111111111111, 0.9),     # 32 runs
+    (64, 3, 98304, 0x7FF0000000000000, 0x3FF0000000000000, 0.9),    # largest row
+]
+
+
+@pytest.mark.parametrize("case", WIDE_CASES, ids=lambda c: f"W{c[0]}_{c[1]}x{c[2]}_{c[3]:x}")
+def test_codec_parity_other_widths(ibp, case):
+    w, n_rows, S, mask, bitval, match_p = case
+    rng = np.random.default_rng(n_rows * 131 + S + w)
+    say(f"codec W={w} rows={n_rows} row_bytes={S} mask={mask:x} match={match_p}")
+    x = make_rows_w(rng, w, n_rows, S, mask, bitval, match_p, raw_rows=(0, n_rows // 2))
+    md = gmd(ibp, mask, bitval, w=w)
+    xg = to_gpu(x)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    torch.cuda.synchronize()
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    assert torch.equal(ibp.ibp_decompress(md, slots, flags), xg)
+    ids = rng.integers(0, n_rows, 3 * n_rows + 5).astype(np.int64)
+    ids[:4] = [n_rows - 1, 0, -1, n_rows]
+    inside = (ids >= 0) & (ids < n_rows)
+    want = np.zeros((ids.size, S), np.uint8)
+    want[inside] = orc.gather_decompress(omd(md), slots_o, flags_o, ids[inside])
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress(md, slots, flags, idg)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want)
+    # through a cache of every other row, the image in pinned host memory
+    host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host.copy_(slots)
+    torch.cuda.synchronize()
+    ids_c = np.arange(0, n_rows, 2, dtype=np.int64)
+    arena, cache_loc = check_cache_fill(ibp, md, host, flags, rb_o, slots_o, flags_o, ids_c)
+    out = ibp.ibp_gather_decompress_cached(md, arena, cache_loc, host, flags, idg)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want)
+    if bin(mask).count("1") >= 2 and match_p > 0.5:
+        assert flags_o.any()
+
+
+def test_full_llm_kv_width16(ibp):
+    """The KV pages with one bf16 element per block: metadata over 2^24
+    blocks, compress, every page-gather batch against the source pages."""
+    x = syn.llm_kv_pages()
+    n_rows, S = x.shape[0], x.nbytes // x.shape[0]
+    xg = to_gpu(x)
+    md, ones = ibp.ibp_build_metadata(xg, width_bits=16, n_blocks=1 << 24)
+    md_o, ones_o = orc.build_metadata(x.reshape(-1)[:1 << 24], 16)
+    assert np.array_equal(np.array(ones, np.uint64), ones_o)
+    assert (md.mask, md.bitval) == (md_o.mask, md_o.bitval)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    rng = np.random.default_rng(9)
+    fl = flags_np(flags, n_rows)
+    rows = rng.integers(0, n_rows, 48)
+    sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
+    rbn = rb.cpu().numpy()
+    for j, r in enumerate(rows):
+        s_o, c_o, f_o = orc.compress_row(omd(md), x[r])
+        assert (c_o, f_o) == (int(rbn[r]), flag_of(fl, r))
+        nb = orc.stored_bytes(S, c_o, f_o)
+        assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
+    ids = syn.kv_page_ids()
+    out = torch.empty((ids.shape[1], S), dtype=torch.uint8, device="cuda")
+    for bi, b in enumerate(ids):
+        idg = torch.from_numpy(np.ascontiguousarray(b)).cuda()
+        ibp.ibp_gather_decompress(md, slots, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"batch {bi}"
+    say(f"llm_kv W=16: mask {md.mask:04x} bitval {md.bitval:04x}")
+
 
 # ------------------------------------------------------------ packed cache --
 
