@@ -893,17 +893,29 @@ struct WideCodec {
   T place[W / 2];
 };
 
-template <typename T>
+// Extract / deposit by the runs of ~mask; NR >= 0 is the run count known at
+// compile time (unrolled, run tables in scalar registers), NR < 0 any count.
+template <typename T, int NR>
 __device__ __forceinline__ T extract_wide(T x, const WideCodec<T>& cd) {
   T v = 0;
-  for (uint32_t j = 0; j < cd.nruns; ++j) v |= (T)((x & cd.place[j]) >> cd.shift[j]);
+  if constexpr (NR >= 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) v |= (T)((x & cd.place[j]) >> cd.shift[j]);
+  } else {
+    for (uint32_t j = 0; j < cd.nruns; ++j) v |= (T)((x & cd.place[j]) >> cd.shift[j]);
+  }
   return v;
 }
 
-template <typename T>
+template <typename T, int NR>
 __device__ __forceinline__ T deposit_wide(T v, const WideCodec<T>& cd) {
   T x = cd.bitval;
-  for (uint32_t j = 0; j < cd.nruns; ++j) x |= (T)((T)(v << cd.shift[j]) & cd.place[j]);
+  if constexpr (NR >= 0) {
+#pragma unroll
+    for (int j = 0; j < NR; ++j) x |= (T)((T)(v << cd.shift[j]) & cd.place[j]);
+  } else {
+    for (uint32_t j = 0; j < cd.nruns; ++j) x |= (T)((T)(v << cd.shift[j]) & cd.place[j]);
+  }
   return x;
 }
 
@@ -923,7 +935,7 @@ __device__ __forceinline__ T lds_payload(const uint32_t* lds, uint32_t rel) {
 
 // [IBP] Compression for W = 16 / 64, one workgroup per row (the stream is
 // assembled in LDS as in compress_kernel; in place is safe the same way).
-template <typename T, uint32_t MAXW>
+template <typename T, int NR, uint32_t MAXW>
 __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
     WideCodec<T> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
     unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
@@ -982,7 +994,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
         if (valid) {
           const uint32_t off = n + W * k - cd.p * pre;
           const uint32_t len = match ? W - cd.p : W;
-          const uint64_t pay = match ? (uint64_t)extract_wide<T>(x, cd) : (uint64_t)x;
+          const uint64_t pay = match ? (uint64_t)extract_wide<T, NR>(x, cd) : (uint64_t)x;
           if (len) {
             const uint32_t sh = off & 31u, wi = off >> 5;
             const uint64_t lo = pay << sh;  // bits [0, 64) of the placed payload
@@ -1006,14 +1018,15 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
 
 // [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
 // blocks), in the three row-source modes of the 32-bit kernels.
-template <typename T, int MODE>
+template <typename T, int MODE, int NR>
 __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     WideCodec<T> cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
-    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, T* __restrict__ dst) {
+    uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, T* __restrict__ dst,
+    int vec) {
   constexpr uint32_t W = WideCodec<T>::W;
-  __shared__ uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
@@ -1037,8 +1050,15 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     const uint32_t* src = row_source<MODE>(slots, arena, id, nw, loc);
     const uint32_t lim = row_words<MODE>(nw, loc);
     if (!row_flag<MODE>(fw, id, loc)) {
-      const T* a = reinterpret_cast<const T*>(src);
-      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = a[j];
+      if (vec) {  // 16-byte units of the segment (lo and hi are multiples of 16 bytes)
+        const uint4* a = reinterpret_cast<const uint4*>(src);
+        uint4* o = reinterpret_cast<uint4*>(out);
+        constexpr uint32_t per = 16 / sizeof(T);
+        for (uint32_t j = lo / per + lane; j < hi / per; j += kWave) o[j] = a[j];
+      } else {
+        const T* a = reinterpret_cast<const T*>(src);
+        for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = a[j];
+      }
       continue;
     }
     uint32_t carry = 0;  // stripped blocks before the segment (lo is a multiple of 64)
@@ -1060,9 +1080,17 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     const uint32_t b = n + W * hi - cd.p * (carry + m_seg);
     const uint32_t wb = min((b + 31u) >> 5, lim);
     const uint32_t wa = min(a >> 5, wb);
-    for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+    uint32_t base = wa;
+    if (vec) {  // 16-byte loads from the 16-byte unit holding word wa
+      base = wa & ~3u;
+      const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
+      uint4* l4 = reinterpret_cast<uint4*>(lds);
+      for (uint32_t j = lane; j < (wb - base + 3u) / 4u; j += kWave) l4[j] = g4[j];
+    } else {
+      for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+    }
     wave_lds_sync();
-    uint32_t u = a - 32u * wa;
+    uint32_t u = a - 32u * base;
     for (uint32_t k0 = lo; k0 < hi; k0 += kWave) {
       const uint32_t q = (k0 - lo) / 32;
       const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
@@ -1072,8 +1100,18 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
       const T v = lds_payload<T>(lds, rel);
       const bool stripped =
           __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-      const T x = stripped ? deposit_wide<T>(v, cd) : v;
-      if (valid) out[k0 + lane] = x;
+      const T x = stripped ? deposit_wide<T, NR>(v, cd) : v;
+      if constexpr (sizeof(T) == 2) {
+        // an even lane takes its odd neighbour's block (DPP quad_perm 1,0,3,2)
+        // and stores the pair as one word; rows and segments hold an even
+        // number of blocks, so both blocks of a pair are valid or neither
+        const uint32_t nb = __builtin_amdgcn_mov_dpp((uint32_t)x, 0xB1, 0xF, 0xF, false);
+        if (valid && !(lane & 1u))
+          __builtin_nontemporal_store((uint32_t)x | (nb << 16),
+                                      reinterpret_cast<uint32_t*>(out) + (k0 + lane) / 2);
+      } else {
+        if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
+      }
       u += W * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
     }
     wave_lds_sync();
@@ -1448,13 +1486,11 @@ void launch_decode(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   }
 }
 
-template <typename T>
-void launch_compress_wide(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
-                          const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
-                          hipStream_t st) {
-  const WideCodec<T> cd = make_wide_codec<T>(md, row_bytes);
+template <typename T, int NR>
+void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void* src,
+                             void* slots, uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
 #define IBP_WIDE(MAXW)                                                                    \
-  hipLaunchKernelGGL((compress_wide_kernel<T, MAXW>), dim3(grid_for(n_rows)),             \
+  hipLaunchKernelGGL((compress_wide_kernel<T, NR, MAXW>), dim3(grid_for(n_rows)),         \
                      dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,         \
                      (uint32_t*)slots, (unsigned long long*)flags, row_bits)
   if (cd.nw <= 1024) IBP_WIDE(1024);
@@ -1464,19 +1500,48 @@ void launch_compress_wide(const ibp_metadata* md, uint64_t n_rows, uint64_t row_
 #undef IBP_WIDE
 }
 
-template <typename T, int MODE>
-void launch_decode_wide(const ibp_metadata* md, uint64_t row_bytes, const DecodeArgs& a,
-                        hipStream_t st) {
+template <typename T>
+void launch_compress_wide(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                          const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
+                          hipStream_t st) {
   const WideCodec<T> cd = make_wide_codec<T>(md, row_bytes);
+  switch (cd.nruns) {
+    case 0: return launch_compress_wide_nr<T, 0>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 1: return launch_compress_wide_nr<T, 1>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 2: return launch_compress_wide_nr<T, 2>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 3: return launch_compress_wide_nr<T, 3>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 4: return launch_compress_wide_nr<T, 4>(cd, n_rows, src, slots, flags, row_bits, st);
+    case 5: return launch_compress_wide_nr<T, 5>(cd, n_rows, src, slots, flags, row_bits, st);
+    default: return launch_compress_wide_nr<T, -1>(cd, n_rows, src, slots, flags, row_bits, st);
+  }
+}
+
+template <typename T, int MODE, int NR>
+void launch_decode_wide_nr(const WideCodec<T>& cd, const DecodeArgs& a, hipStream_t st) {
   // a segment's stream stays within the LDS window: <= seg * W / 32 + 3 words
   const uint32_t seg = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
   const uint32_t nseg = (cd.n + seg - 1) / seg;
   const uint64_t n_tasks = a.n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
-  hipLaunchKernelGGL((decode_wide_kernel<T, MODE>), dim3(grid_for(wgs)), dim3(kBlockThreads), 0,
-                     st, cd, (const uint32_t*)a.slots, (const unsigned long long*)a.flags, a.ids,
-                     (const uint32_t*)a.arena, (const unsigned long long*)a.cache_loc, a.n_rows,
-                     n_tasks, nseg, seg, (T*)a.dst);
+  hipLaunchKernelGGL((decode_wide_kernel<T, MODE, NR>), dim3(grid_for(wgs)), dim3(kBlockThreads),
+                     0, st, cd, (const uint32_t*)a.slots, (const unsigned long long*)a.flags,
+                     a.ids, (const uint32_t*)a.arena, (const unsigned long long*)a.cache_loc,
+                     a.n_rows, n_tasks, nseg, seg, (T*)a.dst, a.vec);
+}
+
+template <typename T, int MODE>
+void launch_decode_wide(const ibp_metadata* md, uint64_t row_bytes, const DecodeArgs& a,
+                        hipStream_t st) {
+  const WideCodec<T> cd = make_wide_codec<T>(md, row_bytes);
+  switch (cd.nruns) {
+    case 0: return launch_decode_wide_nr<T, MODE, 0>(cd, a, st);
+    case 1: return launch_decode_wide_nr<T, MODE, 1>(cd, a, st);
+    case 2: return launch_decode_wide_nr<T, MODE, 2>(cd, a, st);
+    case 3: return launch_decode_wide_nr<T, MODE, 3>(cd, a, st);
+    case 4: return launch_decode_wide_nr<T, MODE, 4>(cd, a, st);
+    case 5: return launch_decode_wide_nr<T, MODE, 5>(cd, a, st);
+    default: return launch_decode_wide_nr<T, MODE, -1>(cd, a, st);
+  }
 }
 
 template <typename T>
@@ -1675,7 +1740,10 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
   hipStream_t st = (hipStream_t)stream;
   if (md->width_bits != 32) {
     if (md->width_bits == 64 && (!aligned(slots, 8) || !aligned(dst, 8))) return IBP_ERR_LAYOUT;
-    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, 0};
+    // 16-byte staging and raw copies need 16-byte rows (segments are
+    // multiples of 64 blocks, so their bounds are 16-byte aligned too)
+    const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
+    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec};
     if (md->width_bits == 16)
       launch_decode_wide_mode<uint16_t>(md, row_bytes, a, mode, st);
     else
