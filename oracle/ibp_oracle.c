@@ -36,6 +36,7 @@
  */
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -361,6 +362,182 @@ int orc_gather_decompress(const uint8_t *slots, const uint64_t *flags,
         int f = (int)((flags[(uint64_t)id >> 6] >> ((uint64_t)id & 63)) & 1u);
         rc = orc_decompress_row(slots + (uint64_t)id * row_bytes, row_bytes, w,
                                 mask, bitval, f, out + i * row_bytes);
+        if (rc)
+            return rc;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------ per-position metadata -- */
+/*
+ * The kilobyte-sized reading of [IBP] Preprocessing ("fixed-size" metadata
+ * of a few kilobytes): one Mask/Bitval pair per block position k of a row
+ * (k < n), each obtained by the rule of orc_build_metadata from the k-th
+ * blocks of the sample rows.  Compression and decompression are the ones
+ * above with Mask, Bitval and p taken at each block's own position.
+ */
+int orc_build_metadata_positional(const uint8_t *sample, uint64_t n_sample_rows,
+                                  uint64_t row_bytes, unsigned w, uint32_t t_ppm,
+                                  uint64_t *mask_out, uint64_t *bitval_out)
+{
+    if (!width_ok(w))
+        return ORC_EWIDTH;
+    if (row_bytes == 0 || (row_bytes * 8) % w != 0)
+        return ORC_ELAYOUT;
+    if (!sample || !mask_out || !bitval_out)
+        return ORC_EINVAL;
+    if (n_sample_rows == 0)
+        return ORC_EEMPTY;
+    const uint64_t n = row_bytes * 8 / w;
+    uint8_t *column = (uint8_t *)calloc(n_sample_rows * w / 8 + 8, 1);
+    if (!column)
+        return ORC_EINVAL;
+    int rc = ORC_OK;
+    for (uint64_t k = 0; k < n && rc == ORC_OK; ++k) {
+        memset(column, 0, n_sample_rows * w / 8 + 8);
+        for (uint64_t r = 0; r < n_sample_rows; ++r)
+            write_bits(column, r * w, w, read_bits(sample + r * row_bytes, k * w, w));
+        rc = orc_build_metadata(column, n_sample_rows, w, t_ppm, NULL, &mask_out[k],
+                                &bitval_out[k]);
+    }
+    free(column);
+    return rc;
+}
+
+static int positional_args_ok(uint64_t row_bytes, unsigned w, const uint64_t *mask,
+                              const uint64_t *bitval)
+{
+    if (!width_ok(w))
+        return ORC_EWIDTH;
+    if (row_bytes == 0 || (row_bytes * 8) % w != 0)
+        return ORC_ELAYOUT;
+    if (!mask || !bitval)
+        return ORC_EINVAL;
+    for (uint64_t k = 0; k < row_bytes * 8 / w; ++k)
+        if ((mask[k] & ~width_mask(w)) != 0 || (bitval[k] & ~mask[k]) != 0)
+            return ORC_EINVAL;
+    return ORC_OK;
+}
+
+/* Compression of one row with per-position metadata: block k matches when
+ * its bits under mask[k] equal bitval[k]; a match keeps W - popcount(mask[k])
+ * bits (extract by ~mask[k]); header, order, fallback as in orc_compress_row. */
+int orc_compress_row_positional(const uint8_t *row, uint64_t row_bytes, unsigned w,
+                                const uint64_t *mask, const uint64_t *bitval,
+                                uint8_t *slot, uint64_t *c_bits, int *flag)
+{
+    int rc = positional_args_ok(row_bytes, w, mask, bitval);
+    if (rc)
+        return rc;
+    if (!row || !slot || !c_bits || !flag)
+        return ORC_EINVAL;
+    const uint64_t n = row_bytes * 8 / w;
+
+    uint64_t c = n;
+    for (uint64_t k = 0; k < n; ++k) {
+        uint64_t x = read_bits(row, k * w, w);
+        int match = (x & mask[k]) == bitval[k];
+        c += match ? (uint64_t)(w - popcount64(mask[k])) : (uint64_t)w;
+    }
+    int shorter = c < row_bytes * 8;
+    *c_bits = c;
+    *flag = shorter;
+    if (!shorter) {
+        memcpy(slot, row, row_bytes);
+        return ORC_OK;
+    }
+    memset(slot, 0, row_bytes);
+    uint64_t cursor = 0;
+    for (uint64_t k = 0; k < n; ++k) {
+        uint64_t x = read_bits(row, k * w, w);
+        put_bit(slot, cursor++, (x & mask[k]) == bitval[k]);
+    }
+    for (uint64_t k = 0; k < n; ++k) {
+        uint64_t x = read_bits(row, k * w, w);
+        if ((x & mask[k]) == bitval[k]) {
+            unsigned len = w - popcount64(mask[k]);
+            write_bits(slot, cursor, len, orc_pext(x, ~mask[k] & width_mask(w)));
+            cursor += len;
+        } else {
+            write_bits(slot, cursor, w, x);
+            cursor += w;
+        }
+    }
+    return cursor == c ? ORC_OK : ORC_EINVAL;
+}
+
+int orc_decompress_row_positional(const uint8_t *slot, uint64_t row_bytes, unsigned w,
+                                  const uint64_t *mask, const uint64_t *bitval, int flag,
+                                  uint8_t *row)
+{
+    int rc = positional_args_ok(row_bytes, w, mask, bitval);
+    if (rc)
+        return rc;
+    if (!slot || !row)
+        return ORC_EINVAL;
+    if (!flag) {
+        memcpy(row, slot, row_bytes);
+        return ORC_OK;
+    }
+    const uint64_t n = row_bytes * 8 / w;
+    const uint64_t limit = row_bytes * 8;
+    uint64_t cursor = n;
+    for (uint64_t k = 0; k < n; ++k) {
+        int stripped = (int)get_bit(slot, k);
+        unsigned len = stripped ? w - popcount64(mask[k]) : w;
+        if (cursor + len > limit)
+            return ORC_ELAYOUT;
+        uint64_t v = read_bits(slot, cursor, len);
+        cursor += len;
+        uint64_t x = stripped ? (orc_pdep(v, ~mask[k] & width_mask(w)) | bitval[k]) : v;
+        write_bits(row, k * w, w, x);
+    }
+    return ORC_OK;
+}
+
+int orc_compress_table_positional(const uint8_t *src, uint64_t n_rows, uint64_t row_bytes,
+                                  unsigned w, const uint64_t *mask, const uint64_t *bitval,
+                                  uint8_t *slots, uint64_t *flags, uint64_t *row_bits)
+{
+    int rc = positional_args_ok(row_bytes, w, mask, bitval);
+    if (rc)
+        return rc;
+    if ((n_rows && (!src || !slots)) || !flags)
+        return ORC_EINVAL;
+    for (uint64_t i = 0; i < (n_rows + 63) / 64; ++i)
+        flags[i] = 0;
+    for (uint64_t r = 0; r < n_rows; ++r) {
+        uint64_t c;
+        int compressed;
+        rc = orc_compress_row_positional(src + r * row_bytes, row_bytes, w, mask, bitval,
+                                         slots + r * row_bytes, &c, &compressed);
+        if (rc)
+            return rc;
+        if (compressed)
+            flags[r >> 6] |= (uint64_t)1 << (r & 63);
+        if (row_bits)
+            row_bits[r] = c;
+    }
+    return ORC_OK;
+}
+
+int orc_gather_decompress_positional(const uint8_t *slots, const uint64_t *flags,
+                                     uint64_t n_rows, uint64_t row_bytes, unsigned w,
+                                     const uint64_t *mask, const uint64_t *bitval,
+                                     const int64_t *ids, uint64_t n_ids, uint8_t *out)
+{
+    int rc = positional_args_ok(row_bytes, w, mask, bitval);
+    if (rc)
+        return rc;
+    if (n_ids && (!slots || !flags || !ids || !out))
+        return ORC_EINVAL;
+    for (uint64_t i = 0; i < n_ids; ++i) {
+        int64_t id = ids[i];
+        if (id < 0 || (uint64_t)id >= n_rows)
+            return ORC_EINVAL;
+        int compressed = (int)((flags[(uint64_t)id >> 6] >> ((uint64_t)id & 63)) & 1u);
+        rc = orc_decompress_row_positional(slots + (uint64_t)id * row_bytes, row_bytes, w,
+                                           mask, bitval, compressed, out + i * row_bytes);
         if (rc)
             return rc;
     }

@@ -68,6 +68,19 @@ def lib() -> ctypes.CDLL:
         L.orc_gather_decompress.restype = c_int
         L.orc_gather_decompress.argtypes = [u8p, u64p, u64, u64, c_uint, u64,
                                             u64, i64p, u64, u8p]
+        L.orc_build_metadata_positional.restype = c_int
+        L.orc_build_metadata_positional.argtypes = [u8p, u64, u64, c_uint, u32, u64p, u64p]
+        L.orc_compress_row_positional.restype = c_int
+        L.orc_compress_row_positional.argtypes = [u8p, u64, c_uint, u64p, u64p, u8p, u64p,
+                                                  ctypes.POINTER(c_int)]
+        L.orc_decompress_row_positional.restype = c_int
+        L.orc_decompress_row_positional.argtypes = [u8p, u64, c_uint, u64p, u64p, c_int, u8p]
+        L.orc_compress_table_positional.restype = c_int
+        L.orc_compress_table_positional.argtypes = [u8p, u64, u64, c_uint, u64p, u64p, u8p,
+                                                    u64p, u64p]
+        L.orc_gather_decompress_positional.restype = c_int
+        L.orc_gather_decompress_positional.argtypes = [u8p, u64p, u64, u64, c_uint, u64p,
+                                                       u64p, i64p, u64, u8p]
         _lib = L
     return _lib
 
@@ -291,3 +304,101 @@ def cache_gather(md: Metadata, arena: np.ndarray, cache_loc: np.ndarray,
         else:
             out[i] = decompress_row(md, s[r], (int(flags[r >> 6]) >> (r & 63)) & 1)
     return out
+
+
+
+# ---------------------------------------------------- per-position metadata --
+# One Mask/Bitval per block position k of a row (the kilobyte-sized reading
+# of the page's fixed-size metadata); arithmetic in ibp_oracle.c.
+
+@dataclass
+class PositionalMetadata:
+    width_bits: int
+    mask: np.ndarray      # uint64 [n]
+    bitval: np.ndarray    # uint64 [n]
+    t_ppm: int = 900000
+
+    @property
+    def invariant_bits(self) -> np.ndarray:
+        return np.array([bin(int(m)).count("1") for m in self.mask], np.int64)
+
+
+def build_metadata_positional(sample_rows: np.ndarray, width_bits: int = 32,
+                              t: float = 0.9, t_ppm: int | None = None) -> PositionalMetadata:
+    """Per-position metadata from the rows of a sample (first axis = rows)."""
+    s = _bytes2d(sample_rows)
+    n_rows, row_bytes = s.shape
+    n = row_bytes * 8 // width_bits
+    ppm = t_to_ppm(t) if t_ppm is None else int(t_ppm)
+    mask = np.zeros(n, np.uint64)
+    bitval = np.zeros(n, np.uint64)
+    rc = lib().orc_build_metadata_positional(
+        _p(s, ctypes.c_uint8), n_rows, row_bytes, width_bits, ppm,
+        _p(mask, ctypes.c_uint64), _p(bitval, ctypes.c_uint64))
+    if rc:
+        raise ValueError(f"orc_build_metadata_positional failed: {rc}")
+    return PositionalMetadata(width_bits, mask, bitval, ppm)
+
+
+def _pm_arrays(pm: PositionalMetadata):
+    return (np.ascontiguousarray(pm.mask, dtype=np.uint64),
+            np.ascontiguousarray(pm.bitval, dtype=np.uint64))
+
+
+def compress_positional(pm: PositionalMetadata, x: np.ndarray):
+    """Like compress(), with per-position metadata."""
+    src = _bytes2d(x)
+    n_rows, row_bytes = src.shape
+    m, b = _pm_arrays(pm)
+    slots = np.zeros((n_rows, row_bytes), np.uint8)
+    flags = np.zeros(max(1, (n_rows + 63) // 64), np.uint64)
+    row_bits = np.zeros(max(1, n_rows), np.uint64)
+    rc = lib().orc_compress_table_positional(
+        _p(src, ctypes.c_uint8) if n_rows else None, n_rows, row_bytes, pm.width_bits,
+        _p(m, ctypes.c_uint64), _p(b, ctypes.c_uint64),
+        _p(slots, ctypes.c_uint8) if n_rows else None,
+        _p(flags, ctypes.c_uint64), _p(row_bits, ctypes.c_uint64))
+    if rc:
+        raise ValueError(f"orc_compress_table_positional failed: {rc}")
+    return slots, flags[:(n_rows + 63) // 64], row_bits[:n_rows]
+
+
+def compress_row_positional(pm: PositionalMetadata, row: np.ndarray):
+    r = np.ascontiguousarray(row).reshape(-1).view(np.uint8)
+    m, b = _pm_arrays(pm)
+    slot = np.zeros_like(r)
+    c = ctypes.c_uint64()
+    f = ctypes.c_int()
+    rc = lib().orc_compress_row_positional(
+        _p(r, ctypes.c_uint8), r.size, pm.width_bits, _p(m, ctypes.c_uint64),
+        _p(b, ctypes.c_uint64), _p(slot, ctypes.c_uint8), ctypes.byref(c), ctypes.byref(f))
+    if rc:
+        raise ValueError(f"orc_compress_row_positional failed: {rc}")
+    return slot, int(c.value), int(f.value)
+
+
+def gather_decompress_positional(pm: PositionalMetadata, slots: np.ndarray,
+                                 flags: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    s = _bytes2d(slots)
+    n_rows, row_bytes = s.shape
+    m, b = _pm_arrays(pm)
+    ids = np.ascontiguousarray(ids, dtype=np.int64).reshape(-1)
+    fl = np.ascontiguousarray(flags, dtype=np.uint64)
+    if fl.size == 0:
+        fl = np.zeros(1, np.uint64)
+    out = np.zeros((ids.size, row_bytes), np.uint8)
+    if ids.size == 0:
+        return out
+    rc = lib().orc_gather_decompress_positional(
+        _p(s, ctypes.c_uint8), _p(fl, ctypes.c_uint64), n_rows, row_bytes, pm.width_bits,
+        _p(m, ctypes.c_uint64), _p(b, ctypes.c_uint64), _p(ids, ctypes.c_int64), ids.size,
+        _p(out, ctypes.c_uint8))
+    if rc:
+        raise ValueError(f"orc_gather_decompress_positional failed: {rc}")
+    return out
+
+
+def decompress_positional(pm: PositionalMetadata, slots: np.ndarray,
+                          flags: np.ndarray) -> np.ndarray:
+    n_rows = _bytes2d(slots).shape[0]
+    return gather_decompress_positional(pm, slots, flags, np.arange(n_rows, dtype=np.int64))

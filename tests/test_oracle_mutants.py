@@ -39,6 +39,13 @@ MUTANTS = {
                         "int f = (int)((flags[(uint64_t)id >> 6] >> ((uint64_t)id & 31)) & 1u);"),
     "pad_to_byte": ("uint64_t b = ((c_bits + 31) / 32) * 4;",
                     "uint64_t b = (c_bits + 7) / 8;"),
+    # per-position metadata
+    "positional_first_mask": ("int match = (x & mask[k]) == bitval[k];",
+                              "int match = (x & mask[0]) == bitval[0];"),
+    "positional_len_neighbour": ("unsigned len = stripped ? w - popcount64(mask[k]) : w;",
+                                 "unsigned len = stripped ? w - popcount64(mask[k ? k - 1 : 0]) : w;"),
+    "positional_column_shift": ("write_bits(column, r * w, w, read_bits(sample + r * row_bytes, k * w, w));",
+                                "write_bits(column, r * w, w, read_bits(sample + r * row_bytes, (k ^ 1) * w, w));"),
 }
 
 

@@ -498,3 +498,117 @@ def test_cache_locator_constants_match_header():
                     "IBP_LOC_WORDS_SHIFT": orc.LOC_WORDS_SHIFT,
                     "IBP_LOC_WORDS_MASK": orc.LOC_WORDS_MASK,
                     "IBP_LOC_OFFSET_MASK": orc.LOC_OFFSET_MASK}
+
+
+# ------------------------------------------------- per-position metadata --
+
+def test_positional_worked_example_width8():
+    """Two 8-bit blocks with their own masks, stream derived by hand:
+    block 0 = 0x55 under Mask 0xF0 / Bitval 0x50 keeps its low nibble 0x5,
+    block 1 = 0xF0 under Mask 0x0F / Bitval 0x00 keeps its high nibble 0xF.
+    Header bits 1,1; payload 0101 (LSB first) at bits 2-5; 1111 at bits 6-9:
+    C = 10 bits, bytes 0xD7 0x03."""
+    pm = orc.PositionalMetadata(8, np.array([0xF0, 0x0F], np.uint64),
+                                np.array([0x50, 0x00], np.uint64))
+    row = np.array([0x55, 0xF0], np.uint8)
+    slot, c, f = orc.compress_row_positional(pm, row)
+    assert (c, f) == (10, 1) and list(slot) == [0xD7, 0x03]
+    slots, flags, _ = orc.compress_positional(pm, row[None])
+    assert np.array_equal(orc.decompress_positional(pm, slots, flags)[0], row)
+
+
+@pytest.mark.parametrize("w", [8, 16, 32, 64])
+def test_positional_with_equal_masks_is_the_global_image(w):
+    """The same Mask/Bitval at every position gives the global image byte for
+    byte (the global codec is pinned above)."""
+    rng = np.random.default_rng(w)
+    for _ in range(6):
+        mask = int(rng.integers(0, 2**63)) & ((1 << w) - 1) if w < 64 else int(rng.integers(0, 2**63)) << 1
+        bitval = mask & int(rng.integers(0, 2**63))
+        S = w // 8 * int(rng.integers(1, 40))
+        x = rng.integers(0, 256, (30, S), dtype=np.uint8)
+        blocks = x.view({8: np.uint8, 16: np.uint16, 32: np.uint32, 64: np.uint64}[w])
+        force = rng.random(blocks.shape) < 0.8
+        blocks[force] = (blocks[force] & blocks.dtype.type(~mask & ((1 << w) - 1))) | \
+            blocks.dtype.type(bitval)
+        n = S * 8 // w
+        pm = orc.PositionalMetadata(w, np.full(n, mask, np.uint64), np.full(n, bitval, np.uint64))
+        g = orc.compress(orc.Metadata(w, mask, bitval, 900000), x)
+        q = orc.compress_positional(pm, x)
+        for a, b in zip(g, q):
+            assert np.array_equal(a, b)
+
+
+def test_positional_metadata_is_the_rule_per_column():
+    """Per-position metadata against numpy column counts and the threshold
+    rule in exact fractions (majority, ties to 0, count/N >= T)."""
+    rng = np.random.default_rng(3)
+    n_rows, n = 157, 24
+    dens = rng.random((1, n, 32)) ** 3            # per position and bit
+    dens[0, 5] = 0.5                              # exact ties at one position
+    bits = rng.random((n_rows, n, 32)) < dens
+    bits[:, 7] = False                            # a constant-zero column
+    x = (bits.astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(2).astype(np.uint32)
+    if n_rows % 2 == 0:
+        x[0, 5] ^= 1
+    ones = bits.sum(0)                            # [n, 32]
+    for t_ppm in (500000, 900000, 1000000):
+        pm = orc.build_metadata_positional(x, 32, t_ppm=t_ppm)
+        T = Fraction(t_ppm, 1000000)
+        for k in range(n):
+            m = bv = 0
+            for b in range(32):
+                o = int(ones[k, b])
+                z = n_rows - o
+                maj = 1 if o > z else 0
+                if Fraction(max(o, z), n_rows) >= T:
+                    m |= 1 << b
+                    bv |= maj << b
+            assert (int(pm.mask[k]), int(pm.bitval[k])) == (m, bv), (t_ppm, k)
+
+
+@pytest.mark.parametrize("w", [8, 32, 64])
+def test_positional_sizes_closed_form_and_round_trip(w):
+    """Masks that differ per position, including none (p = 0) and all (p = W):
+    C = n + sum over blocks of (W - p_k if matched else W), with matches
+    counted by numpy; every row decodes back; raw rows stay raw."""
+    rng = np.random.default_rng(100 + w)
+    dt = {8: np.uint8, 32: np.uint32, 64: np.uint64}[w]
+    n = 37
+    full = (1 << w) - 1
+    masks = [int(rng.integers(0, 2**63)) & full for _ in range(n)]
+    masks[0], masks[1] = 0, full
+    bitvals = [m & int(rng.integers(0, 2**63)) for m in masks]
+    x = rng.integers(0, 256, (60, n * w // 8), dtype=np.uint8).view(dt)
+    force = rng.random(x.shape) < 0.9
+    for k in range(n):
+        col = x[:, k]
+        col[force[:, k]] = (col[force[:, k]] & dt(~masks[k] & full)) | dt(bitvals[k])
+    x[3] = rng.integers(0, 256, n * w // 8, dtype=np.uint8).view(dt)   # likely raw
+    pm = orc.PositionalMetadata(w, np.array(masks, np.uint64), np.array(bitvals, np.uint64))
+    slots, flags, rb = orc.compress_positional(pm, x)
+    p = np.array([bin(m).count("1") for m in masks])
+    match = (x & np.array(masks, np.uint64).astype(dt)) == np.array(bitvals, np.uint64).astype(dt)
+    c = n + np.where(match, w - p, w).sum(1)
+    assert np.array_equal(rb, c.astype(np.uint64))
+    fl = [(int(flags[r >> 6]) >> (r & 63)) & 1 for r in range(60)]
+    assert fl == [int(v < n * w) for v in c]
+    assert np.array_equal(orc.decompress_positional(pm, slots, flags), x.view(np.uint8))
+
+
+def test_positional_bruteforce_width4():
+    """W = 4, rows of two blocks: random per-position (Mask, Bitval) pairs,
+    every one of the 256 rows, round trip and C against direct counting."""
+    rng = np.random.default_rng(4)
+    rows = np.arange(256, dtype=np.uint8)[:, None]
+    for _ in range(300):
+        m = [int(v) for v in rng.integers(0, 16, 2)]
+        b = [m[i] & int(rng.integers(0, 16)) for i in range(2)]
+        pm = orc.PositionalMetadata(4, np.array(m, np.uint64), np.array(b, np.uint64))
+        slots, flags, rb = orc.compress_positional(pm, rows)
+        assert np.array_equal(orc.decompress_positional(pm, slots, flags), rows)
+        for v in range(256):
+            blk = [v & 15, v >> 4]
+            c = 2 + sum(4 - bin(m[k]).count("1") if (blk[k] & m[k]) == b[k] else 4
+                        for k in range(2))
+            assert int(rb[v]) == c
