@@ -226,6 +226,64 @@ int ibp_gather_decompress_cached(const ibp_metadata *md, uint64_t n_rows,
                                  const uint64_t *flags, const int64_t *row_ids,
                                  uint64_t n_ids, void *dst, void *stream);
 
+/*
+ * Per-position metadata: the reading of [IBP] Preprocessing in which the
+ * fixed-size metadata of a few kilobytes holds one Mask/Bitval pair per block
+ * position k of a row (k < n = S/4), each chosen by the threshold rule from
+ * the k-th blocks of the sample rows.  The stream format is the one above
+ * with Mask, Bitval and p taken at each block's own position: payload k has
+ * 32 - p_k bits when stripped, so C = n + sum over k of (stripped ? 32 - p_k
+ * : 32), and payload k starts at bit n + 32k - (sum of p_j over stripped
+ * j < k).  W = 32 only.
+ *
+ * Position table (device memory, 16-byte aligned,
+ * ibp_positional_table_bytes(n) bytes): for each position k a 32-byte entry
+ * {Mask_k, Bitval_k, p_k, five 32-bit masks derived from ~Mask_k that drive
+ * the bit extract and deposit (the parallel suffix method of Hacker's
+ * Delight)}, then for each 64-position chunk c six 64-bit planes of the p
+ * values (bit L of plane t = bit t of p at position 64c + L) and two zero
+ * words.  Built by ibp_positional_table or ibp_build_metadata_positional;
+ * the other calls take it as it is and assume it was built for n = S/4.
+ */
+uint64_t ibp_positional_table_bytes(uint64_t n_positions);
+
+/* Host: fills `table` (host memory, ibp_positional_table_bytes(n) bytes)
+ * from the n pairs mask[k], bitval[k].  INVALID_ARGUMENT when a bitval has
+ * bits outside its mask, or on null pointers with n > 0. */
+int ibp_positional_table(const uint32_t *mask, const uint32_t *bitval,
+                         uint64_t n_positions, void *table);
+
+/*
+ * Per-position [IBP] Preprocessing on the GPU: counts the ones of every bit
+ * at every position over the n_sample_rows rows of S bytes at `sample`
+ * (device or mapped pinned host memory, 4-byte aligned), applies the rule of
+ * ibp_metadata_from_counts position by position, and writes the table to
+ * `table` (device).  mask_out / bitval_out: optional host arrays of n.
+ * SYNCHRONOUS.  Allocates (hipMalloc) and frees 128 bytes of counters per
+ * position for the duration of the call.
+ */
+int ibp_build_metadata_positional(const void *sample, uint64_t n_sample_rows,
+                                  uint64_t row_bytes, uint32_t t_ppm, void *table,
+                                  uint32_t *mask_out, uint32_t *bitval_out,
+                                  void *stream);
+
+/* ibp_compress with per-position metadata (same image layout, flags and
+ * row_bits; in place allowed).  row_bytes <= IBP_MAX_COMPRESS_ROW_BYTES. */
+int ibp_compress_positional(const void *table, uint64_t n_rows, uint64_t row_bytes,
+                            const void *src, void *slots, uint64_t *flags,
+                            uint32_t *row_bits, void *stream);
+
+/* ibp_decompress with per-position metadata. */
+int ibp_decompress_positional(const void *table, uint64_t n_rows, uint64_t row_bytes,
+                              const void *slots, const uint64_t *flags, void *dst,
+                              void *stream);
+
+/* ibp_gather_decompress with per-position metadata (same id rules). */
+int ibp_gather_decompress_positional(const void *table, uint64_t n_rows,
+                                     uint64_t row_bytes, const void *slots,
+                                     const uint64_t *flags, const int64_t *row_ids,
+                                     uint64_t n_ids, void *dst, void *stream);
+
 /* (n_rows + 63) / 64: the number of uint64 words of a flag bitmap. */
 uint64_t ibp_flag_words(uint64_t n_rows);
 

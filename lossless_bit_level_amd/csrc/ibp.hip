@@ -29,6 +29,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "ibp.h"
 
@@ -1118,6 +1119,284 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
   }
 }
 
+// ---------------------------------------------------- per-position metadata --
+//
+// One Mask/Bitval per block position of a row (W = 32).  Lengths now differ
+// per position, so the offset of a lane's payload is a real prefix sum: the
+// DPP wave scan of (stripped ? p_k : 0) over the chunk.  The kept bits come
+// out and go back with five shift-and-select steps whose masks depend only
+// on ~Mask_k (parallel suffix method, Hacker's Delight sections 7-4 and 7-5)
+// and are precomputed in the position table.  A row's stripped bits are
+// summed from the header words and six bit planes of p per chunk on the
+// scalar unit, so its stream length is known before the stream is fetched.
+
+struct PosEntry {
+  uint32_t mask, bitval, p;
+  uint32_t sfx[5];
+};
+static_assert(sizeof(PosEntry) == 32, "position table entries are 32 bytes");
+constexpr uint32_t kPlaneWords = 8;  // u64 per chunk: 6 planes of p, 2 zero
+
+__device__ __forceinline__ PosEntry load_entry(const PosEntry* t, uint32_t k) {
+  const uint4* q = reinterpret_cast<const uint4*>(t + k);
+  const uint4 a = q[0], b = q[1];
+  return PosEntry{a.x, a.y, a.z, {a.w, b.x, b.y, b.z, b.w}};
+}
+
+// Kept bits of x (under ~mask) packed to the bottom, and the inverse.
+__device__ __forceinline__ uint32_t extract_pos(uint32_t x, const PosEntry& e) {
+  x &= ~e.mask;
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t t = x & e.sfx[i];
+    x = (x ^ t) | (t >> (1u << i));
+  }
+  return x;
+}
+
+__device__ __forceinline__ uint32_t deposit_pos(uint32_t v, const PosEntry& e) {
+#pragma unroll
+  for (int i = 4; i >= 0; --i)
+    v = ((v << (1u << i)) & e.sfx[i]) | (v & ~e.sfx[i]);
+  return (v & ~e.mask) | e.bitval;
+}
+
+// Inclusive prefix sum over the 64 lanes (DPP row shifts, then row
+// broadcasts across the four rows of 16 lanes).
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Sum of p over the stripped blocks of one chunk, from its 64-bit header and
+// the chunk's planes of p (scalar).
+__device__ __forceinline__ uint32_t chunk_stripped_bits(unsigned long long h,
+                                                        const unsigned long long* planes) {
+  uint32_t s = 0;
+#pragma unroll
+  for (int t = 0; t < 6; ++t) s += (uint32_t)__popcll(h & planes[t]) << t;
+  return s;
+}
+
+// Per-position ones counts: one wave per (64 positions, range of rows);
+// lane = position, rows summed bit-sliced 32 at a time, then added to
+// counts[k * 32 + b] with one atomic per set count.
+__global__ __launch_bounds__(kBlockThreads) void count_positions_kernel(
+    const uint32_t* __restrict__ sample, uint64_t n_srows, uint32_t n, uint32_t n_chunks,
+    uint32_t rows_per_task, uint64_t n_tasks, uint32_t* __restrict__ counts) {
+  const uint32_t lane = lane_id();
+  const uint64_t task = (uint64_t)blockIdx.x * kWavesPerBlock + uniform(threadIdx.x / kWave);
+  if (task >= n_tasks) return;
+  const uint32_t c = (uint32_t)(task % n_chunks);
+  const uint64_t r0 = (task / n_chunks) * rows_per_task;
+  const uint64_t r1 = std::min<uint64_t>(n_srows, r0 + rows_per_task);
+  const uint32_t k = c * kWave + lane;
+  const bool valid = k < n;
+  uint32_t acc[12];  // rows_per_task < 2^12
+#pragma unroll
+  for (int j = 0; j < 12; ++j) acc[j] = 0;
+  for (uint64_t r = r0; r < r1; r += kCountWords) {
+    uint32_t w[kCountWords];
+#pragma unroll
+    for (int j = 0; j < kCountWords; ++j)
+      w[j] = (valid && r + j < r1) ? sample[(r + j) * n + k] : 0u;
+    uint32_t s[6];
+    sliced_count32(w, s);
+    sliced_accumulate<12, 6>(acc, s);
+  }
+  if (!valid) return;
+#pragma unroll
+  for (int b = 0; b < 32; ++b) {
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < 12; ++j) cnt += __builtin_amdgcn_ubfe(acc[j], b, 1) << j;
+    if (cnt) atomicAdd(&counts[(uint64_t)k * 32 + b], cnt);
+  }
+}
+
+// [IBP] Compression with per-position metadata, one workgroup per row (the
+// stream is assembled in LDS as in compress_kernel).
+template <uint32_t MAXW>
+__global__ __launch_bounds__(kBlockThreads) void compress_positional_kernel(
+    const PosEntry* __restrict__ table, uint32_t n, uint64_t n_rows, const uint32_t* src,
+    uint32_t* slots, unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  __shared__ uint32_t buf[MAXW + 4];
+  __shared__ uint32_t chunk_pre[MAXW / kWave + 1];
+  __shared__ uint32_t total_s;
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t nchunks = (n + kWave - 1) / kWave;
+  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const uint32_t* x_row = src + row * n;
+    uint32_t* s_row = slots + row * n;
+    for (uint32_t j = threadIdx.x; j < n + 4; j += kBlockThreads) buf[j] = 0;
+    __syncthreads();
+    for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {  // header, chunk sums
+      const uint32_t k = c * kWave + lane;
+      const bool valid = k < n;
+      uint32_t x = 0, mask = 0, bitval = 0, p = 0;
+      if (valid) {
+        x = x_row[k];
+        mask = table[k].mask;
+        bitval = table[k].bitval;
+        p = table[k].p;
+      }
+      const bool match = valid && (x & mask) == bitval;
+      const unsigned long long h = __ballot(match);
+      const uint32_t s = wave_sum(match ? p : 0u);
+      if (lane == 0) {
+        chunk_pre[c] = s;
+        buf[2 * c] = (uint32_t)h;
+        buf[2 * c + 1] = (uint32_t)(h >> 32);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      uint32_t carry = 0;
+      for (uint32_t b0 = 0; b0 < nchunks; b0 += kWave) {
+        const uint32_t c = b0 + lane;
+        const uint32_t v = c < nchunks ? chunk_pre[c] : 0u;
+        const uint32_t inc = wave_inclusive_scan(v, lane);
+        if (c < nchunks) chunk_pre[c] = carry + inc - v;
+        carry += __shfl(inc, kWave - 1, kWave);
+      }
+      if (lane == 0) total_s = carry;
+    }
+    __syncthreads();
+    const uint32_t c_bits = n + 32u * n - total_s;
+    const bool flag = c_bits < 32u * n;
+    if (!flag) {
+      for (uint32_t j = threadIdx.x; j < n; j += kBlockThreads) s_row[j] = x_row[j];
+    } else {
+      for (uint32_t c = wave; c < nchunks; c += kWavesPerBlock) {
+        const uint32_t k = c * kWave + lane;
+        const bool valid = k < n;
+        const PosEntry e = load_entry(table, valid ? k : 0u);
+        const uint32_t x = valid ? x_row[k] : 0u;
+        const bool match = valid && (x & e.mask) == e.bitval;
+        const uint32_t v = match ? e.p : 0u;
+        const uint32_t incl = wave_scan_incl(v);
+        if (valid) {
+          const uint32_t off = n + 32u * k - (chunk_pre[c] + incl - v);
+          const uint32_t len = 32u - v;
+          const uint32_t pay = match ? extract_pos(x, e) : x;
+          if (len) {
+            const uint32_t sh = off & 31u, wi = off >> 5;
+            atomicOr(&buf[wi], pay << sh);
+            if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t words = (c_bits + 31u) >> 5;
+      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+    __syncthreads();
+  }
+}
+
+// [IBP] Decompression with per-position metadata: one wave per output row,
+// its segments of kSegBlocks blocks in order (a running count of stripped
+// bits carries the stream offset from one segment to the next).
+template <bool GATHER>
+__global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
+    const PosEntry* __restrict__ table, uint32_t n, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint64_t n_out, uint32_t* __restrict__ dst, int vec) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const unsigned long long* planes =
+      reinterpret_cast<const unsigned long long*>(table + n);  // after the n entries
+  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t i = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+       i < n_out; i += stride) {
+    const uint64_t id = GATHER ? (uint64_t)ids[i] : i;
+    uint32_t* out = dst + i * n;
+    if (GATHER && id >= n_rows) {
+      for (uint32_t j = lane; j < n; j += kWave) out[j] = 0u;
+      continue;
+    }
+    const uint32_t* src = slots + id * n;
+    if (!((flags[id >> 6] >> (id & 63)) & 1ull)) {
+      if (vec) {
+        const uint4* a = reinterpret_cast<const uint4*>(src);
+        uint4* o = reinterpret_cast<uint4*>(out);
+        for (uint32_t j = lane; j < n / 4; j += kWave) o[j] = a[j];
+      } else {
+        for (uint32_t j = lane; j < n; j += kWave) out[j] = src[j];
+      }
+      continue;
+    }
+    uint32_t carry = 0;  // sum of p over the stripped blocks before the segment
+    for (uint32_t lo = 0; lo < n; lo += kSegBlocks) {
+      const uint32_t hi = min(n, lo + kSegBlocks);
+      const uint32_t hw_n = (hi - lo + 31) / 32;
+      uint32_t hw = 0;
+      if (lane < hw_n) {
+        const uint32_t t = lo / 32 + lane;
+        hw = src[t];
+        const uint32_t valid_bits = min(32u, hi - 32u * t);
+        if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
+      }
+      uint32_t s_seg = 0;
+      for (uint32_t k0 = lo; k0 < hi; k0 += kWave) {
+        const uint32_t q = (k0 - lo) / 32;
+        // readlane yields an int: narrow to 32 bits before widening, or bit 31
+        // of the low word would be sign-extended into the high word
+        const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+        const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+        const unsigned long long h = ((unsigned long long)h_hi << 32) | h_lo;
+        s_seg += chunk_stripped_bits(h, planes + (uint64_t)(k0 / kWave) * kPlaneWords);
+      }
+      const uint32_t a = n + 32u * lo - carry;
+      const uint32_t b = n + 32u * hi - (carry + s_seg);
+      const uint32_t wb = min((b + 31u) >> 5, n);
+      const uint32_t wa = min(a >> 5, wb);
+      uint32_t base = wa;
+      if (vec) {
+        base = wa & ~3u;
+        const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
+        uint4* l4 = reinterpret_cast<uint4*>(lds);
+        for (uint32_t j = lane; j < (wb - base + 3u) / 4u; j += kWave) l4[j] = g4[j];
+      } else {
+        for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+      }
+      wave_lds_sync();
+      uint32_t u = a - 32u * base;
+      for (uint32_t k0 = lo; k0 < hi; k0 += kWave) {
+        const uint32_t q = (k0 - lo) / 32;
+        const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+        const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+        const bool valid = k0 + lane < hi;
+        const PosEntry e = load_entry(table, valid ? k0 + lane : 0u);
+        const bool stripped =
+            __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+        const uint32_t v = stripped ? e.p : 0u;
+        const uint32_t incl = wave_scan_incl(v);
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        const uint32_t rel = valid ? u + 32u * lane - (incl - v) : 0u;
+        const uint32_t w = lds_bits(lds, rel);
+        const uint32_t x = stripped ? deposit_pos(w, e) : w;
+        if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
+        u += 32u * kWave - total;
+      }
+      carry += s_seg;
+      wave_lds_sync();
+    }
+  }
+}
+
 // ------------------------------------------------------ packed cache ----
 //
 // [IBP] System integration, cache compression: rows kept in a GPU software
@@ -1555,6 +1834,34 @@ void launch_decode_wide_mode(const ibp_metadata* md, uint64_t row_bytes, const D
     launch_decode_wide<T, kModeTable>(md, row_bytes, a, st);
 }
 
+// Shift masks for extracting / depositing the bits of `keep` (parallel
+// suffix method, Hacker's Delight sections 7-4 and 7-5): step i moves by 2^i
+// the kept bits whose count of dropped bits below them has bit i set.
+void suffix_masks(uint32_t keep, uint32_t sfx[5]) {
+  uint32_t below = ~keep << 1;  // dropped positions, shifted to count "below"
+  for (int i = 0; i < 5; ++i) {
+    uint32_t par = below ^ (below << 1);  // prefix parity from bit 0 upward
+    par ^= par << 2;
+    par ^= par << 4;
+    par ^= par << 8;
+    par ^= par << 16;
+    const uint32_t move = par & keep;
+    sfx[i] = move;
+    keep = (keep ^ move) | (move >> (1u << i));
+    below &= ~par;
+  }
+}
+
+template <uint32_t MAXW>
+void launch_compress_positional_t(const void* table, uint32_t n, uint64_t n_rows,
+                                  const void* src, void* slots, uint64_t* flags,
+                                  uint32_t* row_bits, hipStream_t st) {
+  hipLaunchKernelGGL((compress_positional_kernel<MAXW>), dim3(grid_for(n_rows)),
+                     dim3(kBlockThreads), 0, st, (const PosEntry*)table, n, n_rows,
+                     (const uint32_t*)src, (uint32_t*)slots, (unsigned long long*)flags,
+                     row_bits);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI ----
@@ -1870,6 +2177,170 @@ int ibp_gather_decompress_cached(const ibp_metadata* md, uint64_t n_rows, uint64
                                  void* stream) {
   return decode_common(md, n_rows, row_bytes, slots, flags, row_ids, n_ids, dst, stream,
                        kModeCached, arena, cache_loc);
+}
+
+uint64_t ibp_positional_table_bytes(uint64_t n_positions) {
+  return n_positions * sizeof(PosEntry) + (n_positions + 63) / 64 * kPlaneWords * 8;
+}
+
+int ibp_positional_table(const uint32_t* mask, const uint32_t* bitval, uint64_t n_positions,
+                         void* table) {
+  if (n_positions && (!mask || !bitval || !table)) return IBP_ERR_INVALID_ARGUMENT;
+  if (n_positions > (1ull << 24)) return IBP_ERR_INVALID_ARGUMENT;
+  for (uint64_t k = 0; k < n_positions; ++k)
+    if (bitval[k] & ~mask[k]) return IBP_ERR_INVALID_ARGUMENT;
+  PosEntry* e = (PosEntry*)table;
+  unsigned long long* planes = (unsigned long long*)(e + n_positions);
+  const uint64_t n_chunks = (n_positions + 63) / 64;
+  for (uint64_t i = 0; i < n_chunks * kPlaneWords; ++i) planes[i] = 0;
+  for (uint64_t k = 0; k < n_positions; ++k) {
+    e[k].mask = mask[k];
+    e[k].bitval = bitval[k];
+    e[k].p = (uint32_t)popcount32(mask[k]);
+    suffix_masks(~mask[k], e[k].sfx);
+    for (int t = 0; t < 6; ++t)
+      if ((e[k].p >> t) & 1u) planes[(k / 64) * kPlaneWords + t] |= 1ull << (k % 64);
+  }
+  return IBP_OK;
+}
+
+int ibp_build_metadata_positional(const void* sample, uint64_t n_sample_rows,
+                                  uint64_t row_bytes, uint32_t t_ppm, void* table,
+                                  uint32_t* mask_out, uint32_t* bitval_out, void* stream) {
+  if (!sample || !table || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
+  int rc = check_rows(n_sample_rows, row_bytes);
+  if (rc) return rc;
+  if (n_sample_rows == 0) return IBP_ERR_EMPTY;
+  if (n_sample_rows >= (1ull << 32) || row_bytes / 4 > (1u << 24)) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(sample, 4) || !aligned(table, 16)) return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  const uint32_t n = (uint32_t)(row_bytes / 4);
+  const uint32_t n_chunks = (n + kWave - 1) / kWave;
+  // rows per wave task: a multiple of 32 below 2^12, enough tasks to fill the GPU
+  uint64_t rows_per_task =
+      (n_sample_rows * n_chunks + (uint64_t)workgroups_per_device(8) * kWavesPerBlock - 1) /
+      ((uint64_t)workgroups_per_device(8) * kWavesPerBlock);
+  rows_per_task = std::min<uint64_t>(2048, std::max<uint64_t>(32, (rows_per_task + 31) / 32 * 32));
+  const uint64_t n_ranges = (n_sample_rows + rows_per_task - 1) / rows_per_task;
+  const uint64_t n_tasks = n_ranges * n_chunks;
+  const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (wgs > kMaxGrid) return IBP_ERR_INVALID_ARGUMENT;
+  uint32_t* d_counts = nullptr;
+  hipError_t e = hipMalloc((void**)&d_counts, (size_t)n * 32 * sizeof(uint32_t));
+  if (e != hipSuccess) return hip_fail(e);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for(((uint64_t)n * 16 + 255) / 256)), dim3(256),
+                     0, st, (unsigned long long*)d_counts, (uint64_t)n * 16, 0ull);
+  hipLaunchKernelGGL(count_positions_kernel, dim3((uint32_t)wgs), dim3(kBlockThreads), 0, st,
+                     (const uint32_t*)sample, n_sample_rows, n, n_chunks,
+                     (uint32_t)rows_per_task, n_tasks, d_counts);
+  std::vector<uint32_t> counts((size_t)n * 32);
+  e = hipGetLastError();
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(counts.data(), d_counts, counts.size() * sizeof(uint32_t),
+                       hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  hipError_t ef = hipFree(d_counts);
+  if (e == hipSuccess) e = ef;
+  if (e != hipSuccess) return hip_fail(e);
+  std::vector<uint32_t> mask(n), bitval(n);
+  for (uint32_t k = 0; k < n; ++k) {
+    uint64_t ones[32];
+    for (int b = 0; b < 32; ++b) ones[b] = counts[(size_t)k * 32 + b];
+    ibp_metadata md;
+    rc = ibp_metadata_from_counts(ones, n_sample_rows, 32, t_ppm, &md);
+    if (rc) return rc;
+    mask[k] = (uint32_t)md.mask;
+    bitval[k] = (uint32_t)md.bitval;
+  }
+  std::vector<unsigned char> host(ibp_positional_table_bytes(n));
+  rc = ibp_positional_table(mask.data(), bitval.data(), n, host.data());
+  if (rc) return rc;
+  e = hipMemcpyAsync(table, host.data(), host.size(), hipMemcpyHostToDevice, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_fail(e);
+  if (mask_out)
+    for (uint32_t k = 0; k < n; ++k) mask_out[k] = mask[k];
+  if (bitval_out)
+    for (uint32_t k = 0; k < n; ++k) bitval_out[k] = bitval[k];
+  return IBP_OK;
+}
+
+int ibp_compress_positional(const void* table, uint64_t n_rows, uint64_t row_bytes,
+                            const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
+                            void* stream) {
+  if (!table) return IBP_ERR_INVALID_ARGUMENT;
+  int rc = check_rows(n_rows, row_bytes);
+  if (rc) return rc;
+  if (row_bytes > IBP_MAX_COMPRESS_ROW_BYTES) return IBP_ERR_UNSUPPORTED;
+  if (n_rows == 0) return IBP_OK;
+  if (!src || !slots || !flags) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(table, 16) || !aligned(src, 4) || !aligned(slots, 4) || !aligned(flags, 8) ||
+      (row_bits && !aligned(row_bits, 4)))
+    return IBP_ERR_LAYOUT;
+  {  // in place (src == slots) is allowed, any other overlap is not
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)slots, len = n_rows * row_bytes;
+    if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const uint64_t fw = ibp_flag_words(n_rows);
+  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
+                     (unsigned long long*)flags, fw, 0ull);
+  const uint32_t n = (uint32_t)(row_bytes / 4);
+  if (n <= 1024)
+    launch_compress_positional_t<1024>(table, n, n_rows, src, slots, flags, row_bits, st);
+  else if (n <= 4096)
+    launch_compress_positional_t<4096>(table, n, n_rows, src, slots, flags, row_bits, st);
+  else if (n <= 8192)
+    launch_compress_positional_t<8192>(table, n, n_rows, src, slots, flags, row_bits, st);
+  else
+    launch_compress_positional_t<IBP_MAX_COMPRESS_ROW_BYTES / 4>(table, n, n_rows, src, slots,
+                                                                 flags, row_bits, st);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_bytes,
+                             const void* slots, const uint64_t* flags, const int64_t* ids,
+                             uint64_t n_out, void* dst, void* stream, bool gather) {
+  if (!table) return IBP_ERR_INVALID_ARGUMENT;
+  int rc = check_rows(n_rows, row_bytes);
+  if (rc) return rc;
+  if (n_out > UINT64_MAX / row_bytes) return IBP_ERR_INVALID_ARGUMENT;
+  if (n_out == 0) return IBP_OK;
+  if (n_rows == 0 || !slots || !flags || !dst || (gather && !ids)) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(table, 16) || !aligned(slots, 4) || !aligned(dst, 4) || !aligned(flags, 8) ||
+      (gather && !aligned(ids, 8)))
+    return IBP_ERR_LAYOUT;
+  hipStream_t st = (hipStream_t)stream;
+  const uint32_t n = (uint32_t)(row_bytes / 4);
+  const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
+  const uint64_t wgs = (n_out + kWavesPerBlock - 1) / kWavesPerBlock;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(8));
+  if (gather)
+    hipLaunchKernelGGL(decode_positional_kernel<true>, dim3(grid), dim3(kBlockThreads), 0, st,
+                       (const PosEntry*)table, n, (const uint32_t*)slots,
+                       (const unsigned long long*)flags, ids, n_rows, n_out, (uint32_t*)dst, vec);
+  else
+    hipLaunchKernelGGL(decode_positional_kernel<false>, dim3(grid), dim3(kBlockThreads), 0, st,
+                       (const PosEntry*)table, n, (const uint32_t*)slots,
+                       (const unsigned long long*)flags, nullptr, n_rows, n_out, (uint32_t*)dst,
+                       vec);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+int ibp_decompress_positional(const void* table, uint64_t n_rows, uint64_t row_bytes,
+                              const void* slots, const uint64_t* flags, void* dst, void* stream) {
+  return decode_positional(table, n_rows, row_bytes, slots, flags, nullptr, n_rows, dst, stream,
+                           false);
+}
+
+int ibp_gather_decompress_positional(const void* table, uint64_t n_rows, uint64_t row_bytes,
+                                     const void* slots, const uint64_t* flags,
+                                     const int64_t* row_ids, uint64_t n_ids, void* dst,
+                                     void* stream) {
+  return decode_positional(table, n_rows, row_bytes, slots, flags, row_ids, n_ids, dst, stream,
+                           true);
 }
 
 int ibp_host_device_pointer(const void* host_ptr, void** device_ptr) {

@@ -73,6 +73,13 @@ def lib() -> ctypes.CDLL:
         L.ibp_cache_plan.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, ctypes.POINTER(u64), vp]
         L.ibp_cache_fill.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp, u64, vp, vp]
         L.ibp_gather_decompress_cached.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp, u64, vp, vp]
+        L.ibp_positional_table_bytes.argtypes = [u64]
+        L.ibp_positional_table_bytes.restype = u64
+        L.ibp_positional_table.argtypes = [vp, vp, u64, vp]
+        L.ibp_build_metadata_positional.argtypes = [vp, u64, u64, u32, vp, vp, vp, vp]
+        L.ibp_compress_positional.argtypes = [vp, u64, u64, vp, vp, vp, vp, vp]
+        L.ibp_decompress_positional.argtypes = [vp, u64, u64, vp, vp, vp, vp]
+        L.ibp_gather_decompress_positional.argtypes = [vp, u64, u64, vp, vp, vp, u64, vp, vp]
         L.ibp_flag_words.argtypes = [u64]
         L.ibp_flag_words.restype = u64
         L.ibp_host_device_pointer.argtypes = [vp, ctypes.POINTER(vp)]
@@ -82,7 +89,9 @@ def lib() -> ctypes.CDLL:
         for f in ("ibp_metadata_from_counts", "ibp_build_metadata", "ibp_compress",
                   "ibp_decompress", "ibp_gather_decompress", "ibp_host_device_pointer",
                   "ibp_last_hip_error", "ibp_cache_plan", "ibp_cache_fill",
-                  "ibp_gather_decompress_cached"):
+                  "ibp_gather_decompress_cached", "ibp_positional_table",
+                  "ibp_build_metadata_positional", "ibp_compress_positional",
+                  "ibp_decompress_positional", "ibp_gather_decompress_positional"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -380,3 +389,135 @@ def ibp_gather_decompress_cached_launcher(md: ibp_metadata, arena: torch.Tensor,
         launch()
         return out
     return launch
+
+
+
+# ---------------------------------------------------- per-position metadata --
+
+def ibp_positional_table_bytes(n_positions: int) -> int:
+    return int(lib().ibp_positional_table_bytes(n_positions))
+
+
+def ibp_positional_table(mask, bitval) -> torch.Tensor:
+    """Position table (host uint8 tensor) from per-position mask/bitval
+    sequences of 32-bit values; move it to the GPU before use."""
+    import numpy as np
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint64).astype(np.uint32))
+    b = np.ascontiguousarray(np.asarray(bitval, dtype=np.uint64).astype(np.uint32))
+    if m.shape != b.shape or m.ndim != 1:
+        raise ValueError("mask and bitval must be 1-D of equal length")
+    out = torch.zeros(max(16, ibp_positional_table_bytes(m.size)), dtype=torch.uint8)
+    _check("ibp_positional_table",
+           lib().ibp_positional_table(m.ctypes.data, b.ctypes.data, m.size, out.data_ptr()))
+    return out
+
+
+def ibp_build_metadata_positional(sample: torch.Tensor, t: float = 0.9,
+                                  n_sample_rows: int | None = None,
+                                  t_ppm: int | None = None, stream=None):
+    """Per-position metadata over the rows of `sample` (first axis = rows; GPU
+    or pinned host).  Returns (table uint8 on the GPU, mask, bitval) with
+    mask/bitval numpy uint32 arrays.  Synchronous."""
+    import numpy as np
+    n_rows, row_bytes = _rows(sample)
+    if n_sample_rows is None:
+        n_sample_rows = n_rows
+    if not 0 <= n_sample_rows <= n_rows:
+        raise ValueError(f"n_sample_rows={n_sample_rows} but the sample holds {n_rows} rows")
+    n = row_bytes // 4
+    ppm = int(round(t * 1_000_000)) if t_ppm is None else int(t_ppm)
+    table = torch.empty(max(16, ibp_positional_table_bytes(n)), dtype=torch.uint8,
+                        device="cuda")
+    mask = np.zeros(n, np.uint32)
+    bitval = np.zeros(n, np.uint32)
+    _check("ibp_build_metadata_positional",
+           lib().ibp_build_metadata_positional(_dptr(sample), n_sample_rows, row_bytes, ppm,
+                                               table.data_ptr(), mask.ctypes.data,
+                                               bitval.ctypes.data, _stream(stream)))
+    return table, mask, bitval
+
+
+def _need_table(table: torch.Tensor, row_bytes: int):
+    _need_cuda(table, "table")
+    _need_size(table, ibp_positional_table_bytes(row_bytes // 4), "table")
+    if table.data_ptr() % 16:
+        raise ValueError("table must be 16-byte aligned")
+
+
+def ibp_compress_positional(table: torch.Tensor, src: torch.Tensor,
+                            slots: torch.Tensor | None = None,
+                            flags: torch.Tensor | None = None,
+                            row_bits: torch.Tensor | None = None,
+                            want_row_bits: bool = True, stream=None):
+    """ibp_compress with a position table.  Returns (slots, flags, row_bits)."""
+    n_rows, row_bytes = _rows(src)
+    _need_table(table, row_bytes)
+    dev = src.device if src.is_cuda else torch.device("cuda")
+    if slots is None:
+        slots = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device=dev)
+    if flags is None:
+        flags = torch.empty(max(1, ibp_flag_words(n_rows)), dtype=torch.int64, device=dev)
+    if row_bits is None and want_row_bits:
+        row_bits = torch.empty(max(1, n_rows), dtype=torch.int32, device=dev)
+    _need_cuda(flags, "flags")
+    _need_size(flags, 8 * ibp_flag_words(n_rows), "flags")
+    if row_bits is not None:
+        _need_cuda(row_bits, "row_bits")
+        _need_size(row_bits, 4 * n_rows, "row_bits")
+    _need_size(slots, n_rows * row_bytes, "slots")
+    _check("ibp_compress_positional",
+           lib().ibp_compress_positional(table.data_ptr(), n_rows, row_bytes, _dptr(src),
+                                         _dptr(slots), flags.data_ptr(),
+                                         row_bits.data_ptr() if row_bits is not None else None,
+                                         _stream(stream)))
+    return slots, flags, row_bits
+
+
+def ibp_decompress_positional(table: torch.Tensor, slots: torch.Tensor, flags: torch.Tensor,
+                              out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    n_rows, row_bytes = _rows(slots)
+    _need_table(table, row_bytes)
+    if out is None:
+        out = torch.empty((n_rows, row_bytes), dtype=torch.uint8, device="cuda")
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
+    _need_size(out, n_rows * row_bytes, "out")
+    _check("ibp_decompress_positional",
+           lib().ibp_decompress_positional(table.data_ptr(), n_rows, row_bytes, _dptr(slots),
+                                           flags.data_ptr(), out.data_ptr(), _stream(stream)))
+    return out
+
+
+def ibp_gather_decompress_positional_launcher(table: torch.Tensor, slots: torch.Tensor,
+                                              flags: torch.Tensor, row_ids: torch.Tensor,
+                                              out: torch.Tensor, stream=None):
+    """ibp_gather_decompress_positional with its arguments converted once."""
+    n_rows, row_bytes = _rows(slots)
+    _need_table(table, row_bytes)
+    _ids(row_ids)
+    _need_cuda(flags, "flags")
+    _need_cuda(out, "out")
+    _need_size(out, row_ids.numel() * row_bytes, "out")
+    fn = lib().ibp_gather_decompress_positional
+    args = (ctypes.c_void_p(table.data_ptr()), ctypes.c_uint64(n_rows),
+            ctypes.c_uint64(row_bytes), ctypes.c_void_p(_dptr(slots)),
+            ctypes.c_void_p(flags.data_ptr()), ctypes.c_void_p(row_ids.data_ptr()),
+            ctypes.c_uint64(row_ids.numel()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_gather_decompress_positional", rc)
+    return launch
+
+
+def ibp_gather_decompress_positional(table: torch.Tensor, slots: torch.Tensor,
+                                     flags: torch.Tensor, row_ids: torch.Tensor,
+                                     out: torch.Tensor | None = None,
+                                     stream=None) -> torch.Tensor:
+    n_rows, row_bytes = _rows(slots)
+    if out is None:
+        out = torch.empty((row_ids.numel(), row_bytes), dtype=torch.uint8, device="cuda")
+    ibp_gather_decompress_positional_launcher(table, slots, flags, row_ids, out, stream)()
+    return out

@@ -145,3 +145,38 @@ def test_metadata_from_counts_other_widths(ibp, w):
             md = ibp.ibp_metadata_from_counts(ones, smp.size, t_ppm=t_ppm, width_bits=w)
             assert (md.mask, md.bitval, md.invariant_bits, md.width_bits) == \
                 (md_o.mask, md_o.bitval, md_o.invariant_bits, w)
+
+
+def test_positional_table_drives_extract_and_deposit(ibp):
+    """The host-built position table: mask/bitval/p per entry, the planes of p
+    per 64-position chunk, and five shift masks with which the kernels'
+    extract and deposit steps (replayed here) equal bit-serial PEXT/PDEP."""
+    rng = np.random.default_rng(8)
+    n = 150
+    mask = rng.integers(0, 2**32, n, dtype=np.uint64)
+    mask[:6] = [0, 0xFFFFFFFF, 0x80000000, 1, 0x83FF83FF, 0x7C007C00]
+    bitval = mask & rng.integers(0, 2**32, n, dtype=np.uint64)
+    tab = ibp.ibp_positional_table(mask, bitval).numpy()
+    assert tab.size >= ibp.ibp_positional_table_bytes(n) == 32 * n + 64 * 3
+    ent = tab[:32 * n].view(np.uint32).reshape(n, 8)
+    planes = tab[32 * n:32 * n + 64 * 3].view(np.uint64).reshape(3, 8)
+    M = 0xFFFFFFFF
+    for k in range(n):
+        m, bv, p = int(ent[k, 0]), int(ent[k, 1]), int(ent[k, 2])
+        assert (m, bv, p) == (int(mask[k]), int(bitval[k]), bin(int(mask[k])).count("1"))
+        for t in range(8):
+            assert (int(planes[k // 64, t]) >> (k % 64)) & 1 == ((p >> t) & 1 if t < 6 else 0)
+        sfx = [int(v) for v in ent[k, 3:8]]
+        keep = ~m & M
+        for x in [int(v) for v in rng.integers(0, 2**32, 40)]:
+            y = x & keep
+            for i in range(5):
+                t = y & sfx[i]
+                y = ((y ^ t) | (t >> (1 << i))) & M
+            assert y == orc.pext(x, keep)
+            v = y
+            for i in range(4, -1, -1):
+                v = (((v << (1 << i)) & M) & sfx[i]) | (v & ~sfx[i] & M)
+            assert ((v & keep) | bv) == ((x & keep) | bv)
+    with pytest.raises(ibp.IBPError):
+        ibp.ibp_positional_table([0x0F], [0x10])

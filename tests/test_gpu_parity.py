@@ -459,6 +459,114 @@ def test_full_llm_kv_width16(ibp):
     say(f"llm_kv W=16: mask {md.mask:04x} bitval {md.bitval:04x}")
 
 
+# --------------------------------------------------- per-position metadata --
+
+def _pm_from_np(mask, bitval):
+    return orc.PositionalMetadata(32, np.asarray(mask, np.uint64), np.asarray(bitval, np.uint64))
+
+
+@pytest.mark.parametrize("n_rows,row_bytes,offset", [
+    (1, 4, 0), (31, 148, 0), (33, 512, 4), (2049, 256, 0), (5000, 4100, 0), (300, 28672, 8)])
+def test_positional_metadata_parity(ibp, n_rows, row_bytes, offset):
+    """Per-position counts and masks against the oracle: ragged positions and
+    rows, several row ranges per position, samples only 4-byte aligned."""
+    rng = np.random.default_rng(n_rows + row_bytes)
+    n = row_bytes // 4
+    dens = rng.random((1, n, 32)) ** 4
+    bits = rng.random((n_rows, n, 32)) < dens
+    x = (bits.astype(np.uint64) << np.arange(32, dtype=np.uint64)).sum(2).astype(np.uint32)
+    say(f"positional metadata rows={n_rows} row_bytes={row_bytes} offset={offset}")
+    buf = torch.zeros(x.nbytes + 16, dtype=torch.uint8, device="cuda")
+    buf[offset:offset + x.nbytes] = torch.from_numpy(x.view(np.uint8).reshape(-1).copy()).cuda()
+    view = buf[offset:offset + x.nbytes].view(n_rows, row_bytes)
+    for t_ppm in (900000, 600000):
+        table, m, b = ibp.ibp_build_metadata_positional(view, t_ppm=t_ppm)
+        pm = orc.build_metadata_positional(x, 32, t_ppm=t_ppm)
+        assert np.array_equal(m.astype(np.uint64), pm.mask), t_ppm
+        assert np.array_equal(b.astype(np.uint64), pm.bitval), t_ppm
+        want = ibp.ibp_positional_table(m, b)
+        assert torch.equal(table.cpu()[:want.numel()], want)
+
+
+POS_CASES = [
+    # (n_rows, row_bytes, match_p)
+    (130, 512, 0.85),       # 2 chunks
+    (67, 148, 0.85),        # n = 37: ragged chunk
+    (64, 4096, 0.95),       # 16 chunks, one segment
+    (40, 4100, 0.9),        # n = 1025: two segments, ragged
+    (20, 28672, 0.9),       # 7 segments
+    (30, 2048, 0.999),      # nearly all stripped
+    (3, 98304, 0.9),        # largest row
+    (25, 12, 0.5),          # n = 3
+]
+
+
+@pytest.mark.parametrize("case", POS_CASES, ids=lambda c: f"{c[0]}x{c[1]}")
+def test_positional_codec_parity(ibp, case):
+    n_rows, S, match_p = case
+    rng = np.random.default_rng(n_rows * 17 + S)
+    n = S // 4
+    mask = rng.integers(0, 2**32, n, dtype=np.uint64)
+    mask = np.where(rng.random(n) < 0.5, mask & np.uint64(0x7F807F80), mask)
+    mask[: min(n, 2)] = [0, 0xFFFFFFFF][: min(n, 2)]
+    bitval = mask & rng.integers(0, 2**32, n, dtype=np.uint64)
+    say(f"positional codec rows={n_rows} row_bytes={S}")
+    x = rng.integers(0, 2**32, (n_rows, n), dtype=np.uint64).astype(np.uint32)
+    force = rng.random(x.shape) < match_p
+    m32, b32 = mask.astype(np.uint32), bitval.astype(np.uint32)
+    x = np.where(force, (x & ~m32) | b32, x).astype(np.uint32)
+    x[0] = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+    pm = _pm_from_np(mask, bitval)
+    table = ibp.ibp_positional_table(mask, bitval).cuda()
+    xg = to_gpu(x)
+    slots, flags, rb = ibp.ibp_compress_positional(table, xg)
+    torch.cuda.synchronize()
+    slots_o, flags_o, rb_o = orc.compress_positional(pm, x)
+    assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    assert torch.equal(ibp.ibp_decompress_positional(table, slots, flags), xg)
+    ids = rng.integers(0, n_rows, 3 * n_rows + 5).astype(np.int64)
+    ids[:3] = [-1, n_rows, n_rows - 1]
+    inside = (ids >= 0) & (ids < n_rows)
+    want = np.zeros((ids.size, S), np.uint8)
+    want[inside] = orc.gather_decompress_positional(pm, slots_o, flags_o, ids[inside])
+    out = ibp.ibp_gather_decompress_positional(table, slots, flags, torch.from_numpy(ids).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), want)
+    if n > 2 and match_p > 0.8:
+        assert flags_o.any()
+
+
+def test_full_llm_kv_positional(ibp):
+    """KV pages with per-position metadata from the first 2^24 blocks:
+    masks against the oracle, sampled image rows, every gather batch."""
+    x = syn.llm_kv_pages()
+    n_rows, S = x.shape[0], x.nbytes // x.shape[0]
+    xg = to_gpu(x)
+    sample_rows = (1 << 24) // (S // 4)
+    table, m, b = ibp.ibp_build_metadata_positional(xg, n_sample_rows=sample_rows)
+    pm = orc.build_metadata_positional(x[:sample_rows], 32)
+    assert np.array_equal(m.astype(np.uint64), pm.mask)
+    assert np.array_equal(b.astype(np.uint64), pm.bitval)
+    slots, flags, rb = ibp.ibp_compress_positional(table, xg)
+    fl = flags_np(flags, n_rows)
+    rbn = rb.cpu().numpy()
+    rng = np.random.default_rng(5)
+    rows = rng.integers(0, n_rows, 40)
+    sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
+    for j, r in enumerate(rows):
+        s_o, c_o, f_o = orc.compress_row_positional(pm, x[r])
+        assert (c_o, f_o) == (int(rbn[r]), flag_of(fl, r))
+        nb = orc.stored_bytes(S, c_o, f_o)
+        assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
+    ids = syn.kv_page_ids()
+    out = torch.empty((ids.shape[1], S), dtype=torch.uint8, device="cuda")
+    for bi, bt in enumerate(ids):
+        idg = torch.from_numpy(np.ascontiguousarray(bt)).cuda()
+        ibp.ibp_gather_decompress_positional(table, slots, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"batch {bi}"
+
+
 # ------------------------------------------------------------ packed cache --
 
 CACHE_CASES = [
