@@ -94,8 +94,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def decode_kernel_name(row_bytes: int, width: int = 32) -> str:
+def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False) -> str:
     """The decode kernel libibp launches for rows of this size."""
+    if positional:
+        return "decode_positional_kernel"
     if width != 32:
         return "decode_wide_kernel"
     return "decode_rows_kernel" if row_bytes <= 4096 else "decode_segments_kernel"
@@ -122,7 +124,7 @@ def stored_bytes_per_row(row_bits: np.ndarray, row_bytes: int) -> np.ndarray:
     return np.where(comp, 4 * ((c + 31) // 32), row_bytes)
 
 
-def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
+def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0, pos_mask=None, pos_bitval=None):
     """Time the CPU oracle's gather-decompress on a bounded sample of the same
     workload: the rows the first ids of the gather batches reference are
     compressed by the oracle (untimed), then the oracle's gather over those
@@ -131,6 +133,14 @@ def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
     from oracle import oracle as orc
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     md_o = orc.Metadata(int(md.width_bits), int(md.mask), int(md.bitval), int(md.t_ppm))
+    if pos_mask is not None:   # per-position metadata: the oracle's positional codec
+        pm = orc.PositionalMetadata(32, np.asarray(pos_mask, np.uint64),
+                                    np.asarray(pos_bitval, np.uint64))
+        comp = lambda rows: orc.compress_positional(pm, rows)
+        gath = lambda sl, fl, ids: orc.gather_decompress_positional(pm, sl, fl, ids)
+    else:
+        comp = lambda rows: orc.compress(md_o, rows)
+        gath = lambda sl, fl, ids: orc.gather_decompress(md_o, sl, fl, ids)
     t_idx, ids0 = wl.steps[0]
     table = wl.tables[t_idx]
     S = table.nbytes // table.shape[0]
@@ -141,9 +151,9 @@ def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
     # calibrate on 64 rows, size the sample for ~target_core_s core-seconds
     probe = np.unique(ids0[:64])
     local = table[probe]
-    slots, flags, _ = orc.compress(md_o, local)
+    slots, flags, _ = comp(local)
     t0 = time.perf_counter()
-    orc.gather_decompress(md_o, slots, flags, np.arange(len(probe)))
+    gath(slots, flags, np.arange(len(probe)))
     per_row = (time.perf_counter() - t0) / len(probe)
     n_ids = int(min(len(ids0), max(threads * 64, target_core_s / max(per_row, 1e-9))))
     ids = ids0[:n_ids]
@@ -151,7 +161,7 @@ def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
     src = table[uniq]
     parts = np.array_split(np.arange(len(uniq)), threads)
     with ThreadPoolExecutor(threads) as ex:   # oracle compress of the sample rows
-        res = list(ex.map(lambda p: orc.compress(md_o, src[p]), parts))
+        res = list(ex.map(lambda p: comp(src[p]), parts))
     slots = np.concatenate([r[0] for r in res])
     flag_bits = np.concatenate([[(int(r[1][i >> 6]) >> (i & 63)) & 1 for i in range(len(p))]
                                 for r, p in zip(res, parts)]).astype(np.uint8)
@@ -161,7 +171,7 @@ def cpu_baseline(wl: Workload, md, target_core_s: float = 20.0):
     id_parts = np.array_split(inv.astype(np.int64), threads)
     t0 = time.perf_counter()
     with ThreadPoolExecutor(threads) as ex:
-        outs = list(ex.map(lambda p: orc.gather_decompress(md_o, slots, flags, p), id_parts))
+        outs = list(ex.map(lambda p: gath(slots, flags, p), id_parts))
     dt = time.perf_counter() - t0
     out = np.concatenate(outs)
     assert np.array_equal(out, table[ids].reshape(len(ids), -1).view(np.uint8))
@@ -183,6 +193,9 @@ def main():
     ap.add_argument("--source", default="device", choices=["device", "host"])
     ap.add_argument("--width", type=int, default=32, choices=[16, 32, 64],
                     help="block width W in bits (32: the tuned kernels)")
+    ap.add_argument("--positional", action="store_true",
+                    help="per-position Mask/Bitval (one pair per block position of a row) "
+                         "instead of one global pair; W = 32")
     ap.add_argument("--cache-mib", type=int, default=0,
                     help="keep the most popular rows that fit this many MiB in a packed, "
                          "compressed GPU cache; the other rows come from the image "
@@ -221,16 +234,35 @@ def main():
     md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks, width_bits=args.width)
     meta_ms = (time.perf_counter() - t0) * 1e3
     del samp
+    pos_table = pmask = pbitval = None
+    if args.positional:
+        if args.width != 32 or args.cache_mib:
+            raise SystemExit("--positional runs with W = 32 and without --cache-mib")
+        # the same 2^24-block budget, as whole sample rows of the first table
+        s_rows = max(1, min(wl.sample.shape[0], (1 << 24) // (wl.sample.nbytes // wl.sample.shape[0] // 4)))
+        samp = torch.from_numpy(wl.sample[:s_rows].reshape(s_rows, -1).view(np.uint8)).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pos_table, pmask, pbitval = ibp.ibp_build_metadata_positional(samp)
+        meta_ms = (time.perf_counter() - t0) * 1e3
+        del samp
+        log(f"positional metadata over {s_rows} rows in {meta_ms:.1f} ms; "
+            f"{len(set(pmask.tolist()))} distinct masks")
     images = []
     comp_ms = 0.0
     raw_bytes = stored = 0
     bits_total = 0
+    def compress(tg):
+        if pos_table is not None:
+            return ibp.ibp_compress_positional(pos_table, tg)
+        return ibp.ibp_compress(md, tg)
+
     for tg in tables_g:
-        ibp.ibp_compress(md, tg)              # warm
+        compress(tg)                          # warm
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        slots, flags, rb = ibp.ibp_compress(md, tg)
+        slots, flags, rb = compress(tg)
         e1.record(stream)
         torch.cuda.synchronize()
         comp_ms += e0.elapsed_time(e1)
@@ -252,12 +284,18 @@ def main():
         raw_ip = 0
         for t in wl.tables:
             h = torch.from_numpy(t.reshape(t.shape[0], -1).view(np.uint8)).pin_memory()
-            ibp.ibp_compress(md, h, slots=h, want_row_bits=False)
+
+            def in_place():
+                if pos_table is not None:
+                    ibp.ibp_compress_positional(pos_table, h, slots=h, want_row_bits=False)
+                else:
+                    ibp.ibp_compress(md, h, slots=h, want_row_bits=False)
+            in_place()
             torch.cuda.synchronize()
             h.copy_(torch.from_numpy(t.reshape(t.shape[0], -1).view(np.uint8)))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            ibp.ibp_compress(md, h, slots=h, want_row_bits=False)
+            in_place()
             e1.record(stream)
             torch.cuda.synchronize()
             t_ip += e0.elapsed_time(e1) / 1e3
@@ -357,7 +395,14 @@ def main():
     launchers = []
     for ti, idg, out, _ in plan:
         slots, flags, _ = images[ti]
-        if idg is None:
+        if pos_table is not None:
+            if idg is None:
+                launchers.append(lambda s=slots, f=flags, o=out:
+                                 ibp.ibp_decompress_positional(pos_table, s, f, out=o))
+            else:
+                launchers.append(ibp.ibp_gather_decompress_positional_launcher(
+                    pos_table, slots, flags, idg, out))
+        elif idg is None:
             launchers.append(ibp.ibp_decompress_launcher(md, slots, flags, out))
         elif cache is not None:
             launchers.append(ibp.ibp_gather_decompress_cached_launcher(
@@ -448,7 +493,7 @@ def main():
                     "traffic": None, "link_GB_per_s": round(link_read / mean_launch_s / 1e9, 2),
                     "link_peak": round(link, 2)}
     else:
-        traffic = None if cache or args.width != 32 else \
+        traffic = None if cache or args.width != 32 or args.positional else \
             traffic_from_profiles(decode_kernel_name(S), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
@@ -469,6 +514,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "desc": wl.desc, "source": args.source,
                    "row_bytes": S, "block_bits": args.width, "cache_mib": args.cache_mib,
+                   "metadata": "per_position" if args.positional else "global",
                    "parallelism": "none (1 GPU)"},
         "compression_ratio": round(raw_bytes / stored, 4),
         "compression_ratio_bits": round(raw_bytes * 8 / bits_total, 4),
@@ -477,7 +523,7 @@ def main():
                      "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
-        "kernel": {"name": decode_kernel_name(S, args.width),
+        "kernel": {"name": decode_kernel_name(S, args.width, args.positional),
                    "mean_launch_us": round(mean_launch_s * 1e6, 3),
                    "event_pair_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
                    "event_pair_min_us": round(float(launch_ms.min()) * 1e3, 3),
@@ -489,7 +535,8 @@ def main():
         res["cache"] = cache
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(wl, md)
+        res["cpu_baseline"] = cpu_baseline(wl, md, pos_mask=pmask if pos_table is not None else None,
+                                           pos_bitval=pbitval if pos_table is not None else None)
     print(json.dumps(res), flush=True)
 
 

@@ -1306,18 +1306,29 @@ __global__ __launch_bounds__(kBlockThreads) void compress_positional_kernel(
 
 // [IBP] Decompression with per-position metadata: one wave per output row,
 // its segments of kSegBlocks blocks in order (a running count of stripped
-// bits carries the stream offset from one segment to the next).
-template <bool GATHER>
+// bits carries the stream offset from one segment to the next).  With
+// TAB > 0 (rows of at most TAB blocks) the workgroup first copies the
+// position entries into LDS, so that the per-chunk entry reads are LDS reads;
+// the grid is then kept small and each wave decodes many rows.
+template <bool GATHER, uint32_t TAB>
 __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
     const PosEntry* __restrict__ table, uint32_t n, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     uint64_t n_rows, uint64_t n_out, uint32_t* __restrict__ dst, int vec) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  __shared__ __attribute__((aligned(16))) PosEntry tab_lds[TAB > 0 ? TAB : 1];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
   const unsigned long long* planes =
       reinterpret_cast<const unsigned long long*>(table + n);  // after the n entries
+  if constexpr (TAB > 0) {
+    const uint4* g = reinterpret_cast<const uint4*>(table);
+    uint4* l = reinterpret_cast<uint4*>(tab_lds);
+    for (uint32_t j = threadIdx.x; j < 2 * n; j += kBlockThreads) l[j] = g[j];
+    __syncthreads();
+  }
+  const PosEntry* entries = TAB > 0 ? tab_lds : table;
   const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
   for (uint64_t i = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
        i < n_out; i += stride) {
@@ -1379,7 +1390,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
         const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
         const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
         const bool valid = k0 + lane < hi;
-        const PosEntry e = load_entry(table, valid ? k0 + lane : 0u);
+        const PosEntry e = load_entry(entries, valid ? k0 + lane : 0u);
         const bool stripped =
             __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
         const uint32_t v = stripped ? e.p : 0u;
@@ -2315,16 +2326,22 @@ static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_by
   const uint32_t n = (uint32_t)(row_bytes / 4);
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
   const uint64_t wgs = (n_out + kWavesPerBlock - 1) / kWavesPerBlock;
-  const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(8));
-  if (gather)
-    hipLaunchKernelGGL(decode_positional_kernel<true>, dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const PosEntry*)table, n, (const uint32_t*)slots,
-                       (const unsigned long long*)flags, ids, n_rows, n_out, (uint32_t*)dst, vec);
-  else
-    hipLaunchKernelGGL(decode_positional_kernel<false>, dim3(grid), dim3(kBlockThreads), 0, st,
-                       (const PosEntry*)table, n, (const uint32_t*)slots,
-                       (const unsigned long long*)flags, nullptr, n_rows, n_out, (uint32_t*)dst,
-                       vec);
+  // with the table in LDS (48.5 KiB per workgroup): three workgroups per CU
+  // are resident, and the table copy is paid once per workgroup
+  const bool lds_table = n <= kSegBlocks;
+  const uint32_t grid =
+      (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(lds_table ? 3 : 8));
+#define IBP_POS(G, TAB)                                                                    \
+  hipLaunchKernelGGL((decode_positional_kernel<G, TAB>), dim3(grid), dim3(kBlockThreads), 0, \
+                     st, (const PosEntry*)table, n, (const uint32_t*)slots,                 \
+                     (const unsigned long long*)flags, G ? ids : nullptr, n_rows, n_out,   \
+                     (uint32_t*)dst, vec)
+  if (gather) {
+    if (lds_table) IBP_POS(true, kSegBlocks); else IBP_POS(true, 0);
+  } else {
+    if (lds_table) IBP_POS(false, kSegBlocks); else IBP_POS(false, 0);
+  }
+#undef IBP_POS
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? IBP_OK : hip_fail(e);
 }
