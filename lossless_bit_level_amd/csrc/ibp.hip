@@ -141,6 +141,33 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// 16 bytes as a native vector (kept in registers; HIP's uint4 struct is not
+// always promoted out of private memory when it is assigned conditionally).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Copy units [0, cnt) of g into the wave's LDS window l (16-byte units when
+// U is u32x4, words when U is uint32_t).  All loads of a batch of MAXV units
+// per lane are issued before the first LDS write, so that a window costs one
+// memory latency per batch, not one per 64 units (a plain strided loop waits
+// for each load before its LDS write).  cnt is wave-uniform.
+template <int MAXV, typename U>
+__device__ __forceinline__ void stage_window(const U* __restrict__ g, U* l, uint32_t cnt,
+                                             uint32_t lane) {
+  for (uint32_t j0 = 0; j0 < cnt; j0 += MAXV * kWave) {
+    U v[MAXV];
+#pragma unroll
+    for (int c = 0; c < MAXV; ++c) {
+      const uint32_t j = j0 + c * kWave + lane;
+      v[c] = j < cnt ? g[j] : U{};
+    }
+#pragma unroll
+    for (int c = 0; c < MAXV; ++c) {
+      const uint32_t j = j0 + c * kWave + lane;
+      if (j < cnt) l[j] = v[c];
+    }
+  }
+}
+
 // Workgroups are handed to the 8 XCDs round robin; renumber them so that
 // logical neighbours (segments of one row, rows of one batch) share an XCD
 // and its L2.  A bijection on [0, G).
@@ -605,6 +632,22 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     const uint32_t lim = row_words<MODE>(n, loc);
     const bool flag = row_flag<MODE>(fw, id, loc);
 
+    // The header words are requested together with the flag word (for a raw
+    // row they are row data inside the slot, read and then ignored): the
+    // segment's words one per lane, and the words before it, whose stripped
+    // count is the segment's carry, in batches of four per lane.
+    const uint32_t hw_n = (hi - lo + 31) / 32;
+    uint32_t hw = 0;
+    if (lane < hw_n) hw = src[lo / 32 + lane];
+    uint32_t acc = 0;
+    for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
+      uint32_t w[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
+    }
+
     if (!flag) {
       if (vec) {
         const uint4* a = reinterpret_cast<const uint4*>(src);
@@ -617,20 +660,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     }
 
     // stripped blocks before the segment: header words [0, lo/32) (all header)
-    uint32_t carry = 0;
-    if (lo) {
-      uint32_t acc = 0;
-      for (uint32_t t = lane; t < lo / 32; t += kWave) acc += __popc(src[t]);
-      carry = wave_sum(acc);
-    }
+    const uint32_t carry = lo ? wave_sum(acc) : 0u;
     // the segment's header words, one per lane; bits at or past n belong to
     // the payloads and are cleared
-    const uint32_t hw_n = (hi - lo + 31) / 32;
-    uint32_t hw = 0;
     if (lane < hw_n) {
-      uint32_t t = lo / 32 + lane;
-      hw = src[t];
-      uint32_t valid_bits = min(32u, hi - 32u * t);
+      const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
       if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
     }
     const uint32_t m_seg = wave_sum(__popc(hw));
@@ -645,13 +679,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     uint32_t base;
     if (vec) {
       base = wa & ~3u;
-      const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
-      uint4* l4 = reinterpret_cast<uint4*>(lds);
-      const uint32_t n4 = (wb - base + 3u) / 4u;
-      for (uint32_t j = lane; j < n4; j += kWave) l4[j] = g4[j];
+      stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
+                      (wb - base + 3u) / 4u, lane);
     } else {
       base = wa;
-      for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+      stage_window<4>(src + wa, lds, wb - wa, lane);
     }
     wave_lds_sync();
 
@@ -760,13 +792,14 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
       }
       if (lane < spec) lds[lane] = win;
       if (wb > spec) {  // the rest of the stream
-        if (vec) {
-          const uint4* g4 = reinterpret_cast<const uint4*>(src);
-          uint4* l4 = reinterpret_cast<uint4*>(lds);
-          for (uint32_t j = spec / 4 + lane; j < (wb + 3u) / 4u; j += kWave) l4[j] = g4[j];
-        } else {
-          for (uint32_t j = spec + lane; j < wb; j += kWave) lds[j] = src[j];
-        }
+        // one batch: n <= 64 * NCH words (<= 1024 for NCH == 0) past the window
+        constexpr int kV = NCH >= 8 ? NCH / 4 : (NCH > 0 ? 1 : 4);
+        if (vec)
+          stage_window<kV>(reinterpret_cast<const u32x4*>(src) + spec / 4,
+                           reinterpret_cast<u32x4*>(lds) + spec / 4, (wb + 3u) / 4u - spec / 4,
+                           lane);
+        else
+          stage_window<4>(src + spec, lds + spec, wb - spec, lane);
       }
       wave_lds_sync();
     }
@@ -1050,6 +1083,18 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
     const uint32_t* src = row_source<MODE>(slots, arena, id, nw, loc);
     const uint32_t lim = row_words<MODE>(nw, loc);
+    // header words requested with the flag word (see decode_segments_kernel)
+    const uint32_t hw_n = (hi - lo + 31) / 32;
+    uint32_t hw = 0;
+    if (lane < hw_n) hw = src[lo / 32 + lane];
+    uint32_t acc = 0;
+    for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
+      uint32_t w[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
+    }
     if (!row_flag<MODE>(fw, id, loc)) {
       if (vec) {  // 16-byte units of the segment (lo and hi are multiples of 16 bytes)
         const uint4* a = reinterpret_cast<const uint4*>(src);
@@ -1062,18 +1107,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
       }
       continue;
     }
-    uint32_t carry = 0;  // stripped blocks before the segment (lo is a multiple of 64)
-    if (lo) {
-      uint32_t acc = 0;
-      for (uint32_t t = lane; t < lo / 32; t += kWave) acc += __popc(src[t]);
-      carry = wave_sum(acc);
-    }
-    const uint32_t hw_n = (hi - lo + 31) / 32;
-    uint32_t hw = 0;
+    // stripped blocks before the segment (lo is a multiple of 64)
+    const uint32_t carry = lo ? wave_sum(acc) : 0u;
     if (lane < hw_n) {
-      const uint32_t t = lo / 32 + lane;
-      hw = src[t];
-      const uint32_t valid_bits = min(32u, hi - 32u * t);
+      const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
       if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
     }
     const uint32_t m_seg = wave_sum(__popc(hw));
@@ -1084,11 +1121,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     uint32_t base = wa;
     if (vec) {  // 16-byte loads from the 16-byte unit holding word wa
       base = wa & ~3u;
-      const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
-      uint4* l4 = reinterpret_cast<uint4*>(lds);
-      for (uint32_t j = lane; j < (wb - base + 3u) / 4u; j += kWave) l4[j] = g4[j];
+      stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
+                      (wb - base + 3u) / 4u, lane);
     } else {
-      for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+      stage_window<4>(src + wa, lds, wb - wa, lane);
     }
     wave_lds_sync();
     uint32_t u = a - 32u * base;
@@ -1377,11 +1413,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
       uint32_t base = wa;
       if (vec) {
         base = wa & ~3u;
-        const uint4* g4 = reinterpret_cast<const uint4*>(src + base);
-        uint4* l4 = reinterpret_cast<uint4*>(lds);
-        for (uint32_t j = lane; j < (wb - base + 3u) / 4u; j += kWave) l4[j] = g4[j];
+        stage_window<5>(reinterpret_cast<const u32x4*>(src + base),
+                        reinterpret_cast<u32x4*>(lds), (wb - base + 3u) / 4u, lane);
       } else {
-        for (uint32_t j = lane; j < wb - wa; j += kWave) lds[j] = src[wa + j];
+        stage_window<4>(src + wa, lds, wb - wa, lane);
       }
       wave_lds_sync();
       uint32_t u = a - 32u * base;
