@@ -94,12 +94,16 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False) -> str:
-    """The decode kernel libibp launches for rows of this size."""
+def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False,
+                       invariant_bits: int = 0, cached: bool = False) -> str:
+    """The decode kernel libibp launches for rows of this size (16-byte
+    aligned buffers)."""
     if positional:
         return "decode_positional_kernel"
     if width != 32:
         return "decode_wide_kernel"
+    if row_bytes in (512, 1024, 2048) and invariant_bits < 32 and not cached:
+        return "decode_pipe_kernel"
     return "decode_rows_kernel" if row_bytes <= 4096 else "decode_segments_kernel"
 
 
@@ -494,7 +498,7 @@ def main():
                     "link_peak": round(link, 2)}
     else:
         traffic = None if cache or args.width != 32 or args.positional else \
-            traffic_from_profiles(decode_kernel_name(S), wl.name)
+            traffic_from_profiles(decode_kernel_name(S, invariant_bits=md.invariant_bits), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}
@@ -523,7 +527,8 @@ def main():
                      "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
-        "kernel": {"name": decode_kernel_name(S, args.width, args.positional),
+        "kernel": {"name": decode_kernel_name(S, args.width, args.positional, md.invariant_bits,
+                                              bool(args.cache_mib)),
                    "mean_launch_us": round(mean_launch_s * 1e6, 3),
                    "event_pair_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
                    "event_pair_min_us": round(float(launch_ms.min()) * 1e3, 3),

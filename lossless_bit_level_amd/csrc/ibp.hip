@@ -903,6 +903,145 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
   }
 }
 
+// Buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data format).
+// A buffer load past `bytes` returns zeros and moves no data, so a load whose
+// lanes partly or wholly fall outside a row's stream needs no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// [IBP] Decompression of rows of exactly 64 * NCH blocks (NCH = 2, 4, 8, 16;
+// launched for 2-8) with 16-byte aligned slots and output, p < 32: a deeper
+// software pipeline than decode_rows_kernel.  While row j is decoded from
+// LDS, the rest of row j+1's stream (its length known from its header, which
+// arrived during row j-1) is already in flight into registers, together with
+// the window of row j+2; so each row's dependent fetch overlaps the previous
+// row's decode.  Every stream load is a buffer load whose range is the row's
+// stream, and every iteration issues the same number of vector memory
+// instructions (1 window load, RV stream loads, NCH stores), so the waits at
+// the top of an iteration leave the previous row's stores in flight.  Ids and
+// flag words are scalar loads.  A wave takes rows i, i + stride, ...; ids past
+// the table give zero rows.
+template <int MODE, int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
+    Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
+    uint32_t* __restrict__ dst) {
+  constexpr uint32_t n = NCH * kWave;   // blocks = words of a row
+  constexpr uint32_t kWin = 32;         // window words: the header (n/32 <= 32) and more
+  constexpr int RV = (int)((n / 4 - kWin / 4 + kWave - 1) / kWave);  // stream units per lane
+  // LDS window: every unit the loads can fill (>= n + 4 words, so a payload
+  // ending in the last stream word is read with a word after it), written
+  // unconditionally so that no branch separates the loads from their waits
+  constexpr uint32_t kLdsWords = kWin + RV * kWave * 4;
+  static_assert(kLdsWords >= n + 4, "window too small");
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  u32x4* l4 = reinterpret_cast<u32x4*>(lds);
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  const uint32_t lane_keep = lane * (32u - cd.p);
+
+  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (i >= n_out) return;
+
+  // row r of the launch: its id (r clamped into the launch, so the load is
+  // always in bounds), whether it is a row of the table
+  auto id_of = [&](uint32_t r) -> uint64_t {
+    return MODE == kModeGather ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
+  };
+  auto live = [&](uint32_t r, uint64_t id) -> bool { return r < n_out && id < n_rows; };
+  auto slot = [&](bool ok, uint64_t id) { return slots + (ok ? id : 0ull) * n; };
+  auto flag_word = [&](bool ok, uint64_t id) -> unsigned long long {
+    return flags[(ok ? id : 0ull) >> 6];
+  };
+  // words of the row's stored form: the stream for a compressed row, the
+  // whole slot for a raw one, nothing for a row outside the table
+  auto stored_words = [&](bool ok, unsigned long long fw, uint64_t id, uint32_t hwin) -> uint32_t {
+    if (!ok) return 0u;
+    if (!((fw >> (id & 63)) & 1ull)) return n;
+    const uint32_t m = wave_sum(__popc(lane < n / 32 ? hwin : 0u));
+    return min((n + 32u * n - cd.p * m + 31u) >> 5, n);
+  };
+  auto load_window = [&](bool ok, uint64_t id) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(slot(ok, id), ok ? kWin * 4 : 0u),
+                                                lane * 4, 0, 0);
+  };
+  auto load_rest = [&](bool ok, uint64_t id, uint32_t words, u32x4* r) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(slot(ok, id), ((words + 3u) & ~3u) * 4u);
+#pragma unroll
+    for (int c = 0; c < RV; ++c)
+      r[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
+  };
+
+  // prologue: windows of rows 0 and 1, the stream of row 0, the id of row 2
+  uint64_t id0 = id_of(i);
+  uint64_t id1 = id_of(i + stride);
+  bool ok0 = live(i, id0), ok1 = live(i + stride, id1);
+  unsigned long long fw0 = flag_word(ok0, id0), fw1 = flag_word(ok1, id1);
+  uint32_t win0 = load_window(ok0, id0);
+  uint32_t win1 = load_window(ok1, id1);
+  uint64_t id2 = id_of(i + 2 * stride);
+  u32x4 rest0[RV];
+  load_rest(ok0, id0, stored_words(ok0, fw0, id0, win0), rest0);
+  // wait for all of it here: at the loop top the compiler merges this state
+  // with the back edge's, where the previous row's stores are still pending
+  asm volatile("" ::"v"(win1));
+#pragma unroll
+  for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
+
+  while (true) {
+    // (1) row 0's stream has arrived: stage it in the wave's LDS window (the
+    //     window's lanes 32-63 are zeros that the stream units overwrite)
+    lds[lane] = win0;
+#pragma unroll
+    for (int c = 0; c < RV; ++c) l4[kWin / 4 + c * kWave + lane] = rest0[c];
+    wave_lds_sync();
+    // (2) row 1: its header gives its stream length; the rest of its stream
+    //     goes in flight now
+    const uint32_t words1 = stored_words(ok1, fw1, id1, win1);
+    u32x4 rest1[RV];
+    load_rest(ok1, id1, words1, rest1);
+    // (3) window and flag word of row 2, id of row 3
+    const bool ok2 = live(i + 2 * stride, id2);
+    const unsigned long long fw2 = flag_word(ok2, id2);
+    const uint32_t win2 = load_window(ok2, id2);
+    const uint64_t id3 = id_of(i + 3 * stride);
+    // (4) decode row 0: exactly NCH stores on every path
+    uint32_t x[NCH];
+    if (!ok0) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) x[c] = 0u;
+    } else if (!((fw0 >> (id0 & 63)) & 1ull)) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+    } else {
+      uint32_t u = n;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t h_lo = __builtin_amdgcn_readlane(win0, 2 * c);
+        const uint32_t h_hi = __builtin_amdgcn_readlane(win0, 2 * c + 1);
+        const uint32_t rel = u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi));
+        x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+        u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+      }
+    }
+    uint32_t* out = dst + (uint64_t)i * n;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+    __builtin_amdgcn_sched_barrier(0);
+    wave_lds_sync();
+    i += stride;
+    if (i >= n_out) break;
+    id0 = id1; ok0 = ok1; fw0 = fw1; win0 = win1;
+    for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
+    id1 = id2; ok1 = ok2; fw1 = fw2; win1 = win2;
+    id2 = id3;
+  }
+}
+
 // ---------------------------------------------------- other block widths --
 //
 // Blocks of 16 or 64 bits ([IBP] Compression cuts a tensor into blocks and
@@ -1776,6 +1915,27 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
 #define IBP_ROWS(NCH)                                                                     \
   hipLaunchKernelGGL((decode_rows_kernel<MODE, NR, NCH>), dim3(grid), dim3(kBlockThreads), \
                      0, st, cd, sl, fl, id_p, arena, cloc, a.n_rows, cnt, out_p, a.vec)
+#define IBP_PIPE(NCH)                                                                      \
+  hipLaunchKernelGGL((decode_pipe_kernel<MODE, NR, NCH>),                                   \
+                     dim3(pipe_grid), dim3(kBlockThreads), 0, st, cd, sl, fl, id_p, a.n_rows, \
+                     cnt, out_p)
+      // rows of 128-512 blocks with some invariant bits kept, 16-byte
+      // aligned, not through the cache: the pipelined kernel on a resident
+      // grid (measured: dense 1 KiB feature rows 21.1 -> 20.2 us per 65,536
+      // ids; for 4 KiB rows, of which a launch gives each wave about two,
+      // decode_rows_kernel on a larger grid is as fast or faster)
+      if constexpr (MODE != kModeCached && NR != 0) {
+        if (a.vec && (cd.n == 128 || cd.n == 256 || cd.n == 512)) {
+          const uint32_t pipe_grid =
+              (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(8));
+          switch (cd.n) {
+            case 128: IBP_PIPE(2); break;
+            case 256: IBP_PIPE(4); break;
+            default: IBP_PIPE(8); break;
+          }
+          continue;
+        }
+      }
       switch (cd.n) {
         case 128: IBP_ROWS(2); break;
         case 256: IBP_ROWS(4); break;
@@ -1784,6 +1944,7 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
         default: IBP_ROWS(0); break;
       }
 #undef IBP_ROWS
+#undef IBP_PIPE
     }
     return;
   }

@@ -229,6 +229,9 @@ def test_gather_edge_cases(ibp):
 @pytest.mark.parametrize("n_ids,row_bytes,mask,bitval,match_p", [
     (300_000, 2048, 0xFFFFFFFF, 0x00000000, 0.99),   # p = 32 path, several rows per wave
     (40_000, 512, 0x7C000000, 0x3C000000, 0.95),     # pipelined dense path, several rows per wave
+    (40_000, 1024, 0x7C000000, 0x3C000000, 0.95),    # pipelined, rows of 256 blocks
+    (30_000, 2048, 0x78007800, 0x38003800, 0.90),    # pipelined, rows of 512 blocks
+    (20_000, 1024, 0x55555555, 0x11111111, 0.90),    # pipelined, 16 runs (generic deposit)
     (30_000, 148, 0x7C000000, 0x3C000000, 0.95),     # n = 37: generic path, several rows per wave
     (20_000, 4096, 0x7C007C00, 0x3C003C00, 0.90),    # rows of 1024 blocks
 ])
