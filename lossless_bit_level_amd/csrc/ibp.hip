@@ -1582,6 +1582,156 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
   }
 }
 
+// [IBP] Decompression with per-position metadata for rows of exactly
+// 64 * NCH blocks (NCH = 2, 4, 8, 16), 16-byte aligned: the software
+// pipeline of decode_pipe_kernel (the rest of row j+1's stream and the
+// window of row j+2 in flight while row j is decoded).  The position
+// entries are copied once per workgroup of WPB waves into LDS, field by
+// field (Mask, Bitval, the five deposit masks: a wave reads one field of 64
+// consecutive positions, conflict free; a 32-byte entry per lane would put
+// lanes 4 apart on the same bank), and each lane's p values are packed as
+// bytes in registers.  A row's stripped-bit total, which gives its stream
+// length, is a per-lane sum over the chunks of p where the header bit is set
+// (the header word used as a lane mask) and one wave sum.
+template <bool GATHER, int NCH, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
+    const PosEntry* __restrict__ table, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint32_t n_out, uint32_t* __restrict__ dst) {
+  constexpr uint32_t n = NCH * kWave;
+  constexpr uint32_t kWin = 32;
+  constexpr int RV = (int)((n / 4 - kWin / 4 + kWave - 1) / kWave);
+  constexpr uint32_t kLdsWords = kWin + RV * kWave * 4;
+  constexpr int PW = (NCH + 3) / 4;  // registers of packed p bytes
+  __shared__ uint32_t tf[7][n];      // Mask, Bitval, sfx[0..4] by position
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[WPB][kLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  u32x4* l4 = reinterpret_cast<u32x4*>(lds);
+  {
+    const u32x4* g = reinterpret_cast<const u32x4*>(table);
+    for (uint32_t k = threadIdx.x; k < n; k += WPB * kWave) {
+      const u32x4 a = g[2 * k], b = g[2 * k + 1];  // {mask, bitval, p, sfx0}, {sfx1..4}
+      tf[0][k] = a.x;
+      tf[1][k] = a.y;
+      tf[2][k] = a.w;
+      tf[3][k] = b.x;
+      tf[4][k] = b.y;
+      tf[5][k] = b.z;
+      tf[6][k] = b.w;
+    }
+    __syncthreads();
+  }
+  uint32_t pp[PW];
+#pragma unroll
+  for (int w = 0; w < PW; ++w) pp[w] = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) pp[c / 4] |= (uint32_t)__popc(tf[0][c * kWave + lane]) << (8 * (c % 4));
+  auto entry = [&](uint32_t k) -> PosEntry {
+    return PosEntry{tf[0][k], tf[1][k], 0u, {tf[2][k], tf[3][k], tf[4][k], tf[5][k], tf[6][k]}};
+  };
+
+  const uint32_t stride = gridDim.x * WPB;
+  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * WPB + wave;
+  if (i >= n_out) return;
+
+  auto id_of = [&](uint32_t r) -> uint64_t {
+    return GATHER ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
+  };
+  auto live = [&](uint32_t r, uint64_t id) -> bool { return r < n_out && id < n_rows; };
+  auto slot = [&](bool ok, uint64_t id) { return slots + (ok ? id : 0ull) * n; };
+  auto flag_word = [&](bool ok, uint64_t id) -> unsigned long long {
+    return flags[(ok ? id : 0ull) >> 6];
+  };
+  auto stored_words = [&](bool ok, unsigned long long fw, uint64_t id, uint32_t hwin) -> uint32_t {
+    if (!ok) return 0u;
+    if (!((fw >> (id & 63)) & 1ull)) return n;
+    uint32_t s_lane = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t h_lo = __builtin_amdgcn_readlane(hwin, 2 * c);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(hwin, 2 * c + 1);
+      const bool stripped =
+          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+      s_lane += stripped ? __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8) : 0u;
+    }
+    const uint32_t s = wave_sum(s_lane);
+    return min((n + 32u * n - s + 31u) >> 5, n);
+  };
+  auto load_window = [&](bool ok, uint64_t id) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(slot(ok, id), ok ? kWin * 4 : 0u),
+                                                lane * 4, 0, 0);
+  };
+  auto load_rest = [&](bool ok, uint64_t id, uint32_t words, u32x4* r) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(slot(ok, id), ((words + 3u) & ~3u) * 4u);
+#pragma unroll
+    for (int c = 0; c < RV; ++c)
+      r[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
+  };
+
+  uint64_t id0 = id_of(i);
+  uint64_t id1 = id_of(i + stride);
+  bool ok0 = live(i, id0), ok1 = live(i + stride, id1);
+  unsigned long long fw0 = flag_word(ok0, id0), fw1 = flag_word(ok1, id1);
+  uint32_t win0 = load_window(ok0, id0);
+  uint32_t win1 = load_window(ok1, id1);
+  uint64_t id2 = id_of(i + 2 * stride);
+  u32x4 rest0[RV];
+  load_rest(ok0, id0, stored_words(ok0, fw0, id0, win0), rest0);
+  asm volatile("" ::"v"(win1));
+#pragma unroll
+  for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
+
+  while (true) {
+    lds[lane] = win0;
+#pragma unroll
+    for (int c = 0; c < RV; ++c) l4[kWin / 4 + c * kWave + lane] = rest0[c];
+    wave_lds_sync();
+    const uint32_t words1 = stored_words(ok1, fw1, id1, win1);
+    u32x4 rest1[RV];
+    load_rest(ok1, id1, words1, rest1);
+    const bool ok2 = live(i + 2 * stride, id2);
+    const unsigned long long fw2 = flag_word(ok2, id2);
+    const uint32_t win2 = load_window(ok2, id2);
+    const uint64_t id3 = id_of(i + 3 * stride);
+    uint32_t x[NCH];
+    if (!ok0) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) x[c] = 0u;
+    } else if (!((fw0 >> (id0 & 63)) & 1ull)) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+    } else {
+      uint32_t u = n;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t h_lo = __builtin_amdgcn_readlane(win0, 2 * c);
+        const uint32_t h_hi = __builtin_amdgcn_readlane(win0, 2 * c + 1);
+        const bool stripped =
+            __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+        const uint32_t v = stripped ? __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8) : 0u;
+        const uint32_t incl = wave_scan_incl(v);
+        const uint32_t rel = u + 32u * lane - (incl - v);
+        const uint32_t w = lds_bits(lds, rel);
+        x[c] = stripped ? deposit_pos(w, entry(c * kWave + lane)) : w;
+        u += 32u * kWave - __builtin_amdgcn_readlane(incl, kWave - 1);
+      }
+    }
+    uint32_t* out = dst + (uint64_t)i * n;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+    __builtin_amdgcn_sched_barrier(0);
+    wave_lds_sync();
+    i += stride;
+    if (i >= n_out) break;
+    id0 = id1; ok0 = ok1; fw0 = fw1; win0 = win1;
+    for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
+    id1 = id2; ok1 = ok2; fw1 = fw2; win1 = win2;
+    id2 = id3;
+  }
+}
+
 // ------------------------------------------------------ packed cache ----
 //
 // [IBP] System integration, cache compression: rows kept in a GPU software
@@ -2521,6 +2671,41 @@ static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_by
   hipStream_t st = (hipStream_t)stream;
   const uint32_t n = (uint32_t)(row_bytes / 4);
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
+  if (vec && (n == 128 || n == 256 || n == 512 || n == 1024)) {
+    // pipelined kernel, in launches of at most 2^30 rows (32-bit row indices)
+    const uint64_t piece = 1ull << 30;
+    for (uint64_t off = 0; off < n_out; off += piece) {
+      const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, n_out - off);
+      const uint32_t* sl = (const uint32_t*)slots;
+      const unsigned long long* fl = (const unsigned long long*)flags;
+      if (!gather) {  // rows off.. of the table; flags stay word aligned (piece % 64 == 0)
+        sl += off * n;
+        fl += off / 64;
+      }
+      const int64_t* id_p = gather ? ids + off : nullptr;
+      uint32_t* out_p = (uint32_t*)dst + off * n;
+      // workgroups of 4 waves (8 for 4 KiB rows, whose 32 KiB table is then
+      // shared by more waves); as many as stay resident
+#define IBP_PP(G, NCH, WPB, PER_CU)                                                             \
+  hipLaunchKernelGGL((decode_pos_pipe_kernel<G, NCH, WPB>),                                     \
+                     dim3((uint32_t)std::min<uint64_t>((cnt + WPB - 1) / WPB,                  \
+                                                       workgroups_per_device(PER_CU))),        \
+                     dim3(WPB * kWave), 0, st, (const PosEntry*)table, sl, fl, id_p,           \
+                     gather ? n_rows : (uint64_t)cnt, cnt, out_p)
+#define IBP_PP_N(G)                                         \
+  switch (n) {                                              \
+    case 128: IBP_PP(G, 2, 4, 8); break;                    \
+    case 256: IBP_PP(G, 4, 4, 8); break;                    \
+    case 512: IBP_PP(G, 8, 4, 5); break;                    \
+    default: IBP_PP(G, 16, 8, 2); break;                    \
+  }
+      if (gather) { IBP_PP_N(true); } else { IBP_PP_N(false); }
+#undef IBP_PP_N
+#undef IBP_PP
+    }
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? IBP_OK : hip_fail(e);
+  }
   const uint64_t wgs = (n_out + kWavesPerBlock - 1) / kWavesPerBlock;
   // with the table in LDS (48.5 KiB per workgroup): three workgroups per CU
   // are resident, and the table copy is paid once per workgroup

@@ -540,6 +540,46 @@ def test_positional_codec_parity(ibp, case):
         assert flags_o.any()
 
 
+@pytest.mark.parametrize("row_bytes,n_ids", [(512, 60_000), (1024, 60_000), (2048, 40_000),
+                                               (4096, 40_000)])
+def test_positional_gather_many_rows_per_wave(ibp, row_bytes, n_ids):
+    """Per-position decode with more rows than resident waves (the pipelined
+    kernel's cross-row prefetch), raw rows, ids outside the table, and a full
+    decompress of the table: against the source rows on the GPU, sampled rows
+    against the oracle."""
+    rng = np.random.default_rng(row_bytes + 11)
+    n = row_bytes // 4
+    n_rows = 3000
+    mask = np.where(rng.random(n) < 0.7, 0x7C007C00, rng.integers(0, 2**32, n, dtype=np.uint64)
+                    & np.uint64(0x7F807F80)).astype(np.uint64)
+    bitval = mask & rng.integers(0, 2**32, n, dtype=np.uint64)
+    m32, b32 = mask.astype(np.uint32), bitval.astype(np.uint32)
+    x = rng.integers(0, 2**32, (n_rows, n), dtype=np.uint64).astype(np.uint32)
+    x = np.where(rng.random(x.shape) < 0.93, (x & ~m32) | b32, x).astype(np.uint32)
+    x[[5, 1700]] = rng.integers(0, 2**32, (2, n), dtype=np.uint64).astype(np.uint32)  # raw rows
+    say(f"positional many rows: row_bytes={row_bytes} ids={n_ids}")
+    table = ibp.ibp_positional_table(mask, bitval).cuda()
+    xg = to_gpu(x)
+    slots, flags, _ = ibp.ibp_compress_positional(table, xg)
+    assert torch.equal(ibp.ibp_decompress_positional(table, slots, flags), xg)
+    ids = rng.integers(0, n_rows, n_ids).astype(np.int64)
+    ids[::991] = n_rows + 3
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress_positional(table, slots, flags, idg)
+    torch.cuda.synchronize()
+    bad = torch.from_numpy(ids >= n_rows).cuda()
+    ref = xg[idg.clamp(max=n_rows - 1)]
+    ref[bad] = 0
+    assert torch.equal(out, ref)
+    pm = _pm_from_np(mask, bitval)
+    slots_o, flags_o, _ = orc.compress_positional(pm, x)
+    assert np.array_equal(flags_np(flags, n_rows), flags_o)
+    pick = rng.integers(0, n_ids, 48)
+    pick = pick[ids[pick] < n_rows]
+    want = orc.gather_decompress_positional(pm, slots_o, flags_o, ids[pick])
+    assert np.array_equal(out[torch.from_numpy(pick).cuda()].cpu().numpy(), want)
+
+
 def test_full_llm_kv_positional(ibp):
     """KV pages with per-position metadata from the first 2^24 blocks:
     masks against the oracle, sampled image rows, every gather batch."""
