@@ -99,7 +99,8 @@ def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False
     """The decode kernel libibp launches for rows of this size (16-byte
     aligned buffers)."""
     if positional:
-        return "decode_positional_kernel"
+        return ("decode_pos_pipe_kernel" if row_bytes in (512, 1024, 2048, 4096)
+                else "decode_positional_kernel")
     if width != 32:
         return "decode_wide_kernel"
     if row_bytes in (512, 1024, 2048) and invariant_bits < 32 and not cached:
@@ -497,8 +498,9 @@ def main():
                     "traffic": None, "link_GB_per_s": round(link_read / mean_launch_s / 1e9, 2),
                     "link_peak": round(link, 2)}
     else:
-        traffic = None if cache or args.width != 32 or args.positional else \
-            traffic_from_profiles(decode_kernel_name(S, invariant_bits=md.invariant_bits), wl.name)
+        traffic = None if cache or args.width != 32 else \
+            traffic_from_profiles(decode_kernel_name(S, positional=args.positional,
+                                                     invariant_bits=md.invariant_bits), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}

@@ -1483,27 +1483,32 @@ __global__ __launch_bounds__(kBlockThreads) void compress_positional_kernel(
 // its segments of kSegBlocks blocks in order (a running count of stripped
 // bits carries the stream offset from one segment to the next).  With
 // TAB > 0 (rows of at most TAB blocks) the workgroup first copies the
-// position entries into LDS, so that the per-chunk entry reads are LDS reads;
-// the grid is then kept small and each wave decodes many rows.
+// position entries into LDS field by field (conflict-free reads of one field
+// of 64 consecutive positions), so that the per-chunk entry reads are LDS
+// reads; the grid is then kept small and each wave decodes many rows.
 template <bool GATHER, uint32_t TAB>
 __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
     const PosEntry* __restrict__ table, uint32_t n, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     uint64_t n_rows, uint64_t n_out, uint32_t* __restrict__ dst, int vec) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
-  __shared__ __attribute__((aligned(16))) PosEntry tab_lds[TAB > 0 ? TAB : 1];
+  __shared__ uint32_t tf[TAB > 0 ? 8 : 1][TAB > 0 ? TAB : 1];  // fields by position
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
   const unsigned long long* planes =
       reinterpret_cast<const unsigned long long*>(table + n);  // after the n entries
   if constexpr (TAB > 0) {
-    const uint4* g = reinterpret_cast<const uint4*>(table);
-    uint4* l = reinterpret_cast<uint4*>(tab_lds);
-    for (uint32_t j = threadIdx.x; j < 2 * n; j += kBlockThreads) l[j] = g[j];
+    const uint32_t* g = reinterpret_cast<const uint32_t*>(table);
+    for (uint32_t j = threadIdx.x; j < 8 * n; j += kBlockThreads) tf[j % 8][j / 8] = g[j];
     __syncthreads();
   }
-  const PosEntry* entries = TAB > 0 ? tab_lds : table;
+  auto entry = [&](uint32_t k) -> PosEntry {
+    if constexpr (TAB > 0)
+      return PosEntry{tf[0][k], tf[1][k], tf[2][k], {tf[3][k], tf[4][k], tf[5][k], tf[6][k], tf[7][k]}};
+    else
+      return load_entry(table, k);
+  };
   const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
   for (uint64_t i = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
        i < n_out; i += stride) {
@@ -1564,7 +1569,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
         const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
         const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
         const bool valid = k0 + lane < hi;
-        const PosEntry e = load_entry(entries, valid ? k0 + lane : 0u);
+        const PosEntry e = entry(valid ? k0 + lane : 0u);
         const bool stripped =
             __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
         const uint32_t v = stripped ? e.p : 0u;
