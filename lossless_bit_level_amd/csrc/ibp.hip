@@ -942,55 +942,61 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
   uint32_t* lds = lds_all[wave];
   u32x4* l4 = reinterpret_cast<u32x4*>(lds);
   const uint32_t stride = gridDim.x * kWavesPerBlock;
-  const uint32_t lane_keep = lane * (32u - cd.p);
 
   uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
   if (i >= n_out) return;
 
-  // row r of the launch: its id (r clamped into the launch, so the load is
-  // always in bounds), whether it is a row of the table
+  // A row in flight: where its slot is (slot 0 for a row outside the table,
+  // so that every address stays in bounds), whether it is a row of the table,
+  // and its flag word and id bits once they are known.
+  struct Row {
+    const uint32_t* src;
+    bool ok;
+    unsigned long long fw;
+    uint32_t bit;  // id & 63
+  };
+  const int negp = -(int)cd.p;
   auto id_of = [&](uint32_t r) -> uint64_t {
     return MODE == kModeGather ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
   };
-  auto live = [&](uint32_t r, uint64_t id) -> bool { return r < n_out && id < n_rows; };
-  auto slot = [&](bool ok, uint64_t id) { return slots + (ok ? id : 0ull) * n; };
-  auto flag_word = [&](bool ok, uint64_t id) -> unsigned long long {
-    return flags[(ok ? id : 0ull) >> 6];
+  // row r with id `id`: slot, flag word (scalar load) and window (buffer load)
+  auto open_row = [&](uint32_t r, uint64_t id, uint32_t& win) -> Row {
+    const bool ok = r < n_out && id < n_rows;
+    const uint64_t idc = ok ? id : 0ull;
+    Row w{slots + idc * n, ok, flags[idc >> 6], (uint32_t)idc & 63u};
+    win = __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(w.src, ok ? kWin * 4 : 0u), lane * 4,
+                                               0, 0);
+    return w;
   };
+  auto flagged = [&](const Row& w) { return w.ok && ((w.fw >> w.bit) & 1ull); };
   // words of the row's stored form: the stream for a compressed row, the
   // whole slot for a raw one, nothing for a row outside the table
-  auto stored_words = [&](bool ok, unsigned long long fw, uint64_t id, uint32_t hwin) -> uint32_t {
-    if (!ok) return 0u;
-    if (!((fw >> (id & 63)) & 1ull)) return n;
+  auto stored_words = [&](const Row& w, uint32_t hwin) -> uint32_t {
+    if (!w.ok) return 0u;
+    if (!flagged(w)) return n;
     const uint32_t m = wave_sum(__popc(lane < n / 32 ? hwin : 0u));
     return min((n + 32u * n - cd.p * m + 31u) >> 5, n);
   };
-  auto load_window = [&](bool ok, uint64_t id) -> uint32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(slot(ok, id), ok ? kWin * 4 : 0u),
-                                                lane * 4, 0, 0);
-  };
-  auto load_rest = [&](bool ok, uint64_t id, uint32_t words, u32x4* r) {
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(slot(ok, id), ((words + 3u) & ~3u) * 4u);
+  auto load_rest = [&](const Row& w, uint32_t words, u32x4* r) {
+    const __amdgpu_buffer_rsrc_t rs = row_rsrc(w.src, ((words + 3u) & ~3u) * 4u);
 #pragma unroll
     for (int c = 0; c < RV; ++c)
       r[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
   };
 
   // prologue: windows of rows 0 and 1, the stream of row 0, the id of row 2
-  uint64_t id0 = id_of(i);
-  uint64_t id1 = id_of(i + stride);
-  bool ok0 = live(i, id0), ok1 = live(i + stride, id1);
-  unsigned long long fw0 = flag_word(ok0, id0), fw1 = flag_word(ok1, id1);
-  uint32_t win0 = load_window(ok0, id0);
-  uint32_t win1 = load_window(ok1, id1);
+  uint32_t win0, win1;
+  Row w0 = open_row(i, id_of(i), win0);
+  Row w1 = open_row(i + stride, id_of(i + stride), win1);
   uint64_t id2 = id_of(i + 2 * stride);
   u32x4 rest0[RV];
-  load_rest(ok0, id0, stored_words(ok0, fw0, id0, win0), rest0);
+  load_rest(w0, stored_words(w0, win0), rest0);
   // wait for all of it here: at the loop top the compiler merges this state
   // with the back edge's, where the previous row's stores are still pending
   asm volatile("" ::"v"(win1));
 #pragma unroll
   for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
+  const uint32_t l32 = 32u * lane;
 
   while (true) {
     // (1) row 0's stream has arrived: stage it in the wave's LDS window (the
@@ -1001,29 +1007,30 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
     wave_lds_sync();
     // (2) row 1: its header gives its stream length; the rest of its stream
     //     goes in flight now
-    const uint32_t words1 = stored_words(ok1, fw1, id1, win1);
     u32x4 rest1[RV];
-    load_rest(ok1, id1, words1, rest1);
+    load_rest(w1, stored_words(w1, win1), rest1);
     // (3) window and flag word of row 2, id of row 3
-    const bool ok2 = live(i + 2 * stride, id2);
-    const unsigned long long fw2 = flag_word(ok2, id2);
-    const uint32_t win2 = load_window(ok2, id2);
+    uint32_t win2;
+    const Row w2 = open_row(i + 2 * stride, id2, win2);
     const uint64_t id3 = id_of(i + 3 * stride);
     // (4) decode row 0: exactly NCH stores on every path
     uint32_t x[NCH];
-    if (!ok0) {
+    if (!w0.ok) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) x[c] = 0u;
-    } else if (!((fw0 >> (id0 & 63)) & 1ull)) {
+    } else if (!flagged(w0)) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
     } else {
+      // bit offset of lane l's payload: u + 32 l - p * (stripped blocks of
+      // the chunk below l)
       uint32_t u = n;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const uint32_t h_lo = __builtin_amdgcn_readlane(win0, 2 * c);
         const uint32_t h_hi = __builtin_amdgcn_readlane(win0, 2 * c + 1);
-        const uint32_t rel = u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi));
+        const uint32_t rel =
+            (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
         x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
         u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
       }
@@ -1035,9 +1042,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
     wave_lds_sync();
     i += stride;
     if (i >= n_out) break;
-    id0 = id1; ok0 = ok1; fw0 = fw1; win0 = win1;
+    w0 = w1; win0 = win1;
     for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
-    id1 = id2; ok1 = ok2; fw1 = fw2; win1 = win2;
+    w1 = w2; win1 = win2;
     id2 = id3;
   }
 }
