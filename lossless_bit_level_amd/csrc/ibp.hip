@@ -911,53 +911,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
                                            0x00020000);
 }
 
-// [IBP] Decompression of rows of exactly 64 * NCH blocks (NCH = 2, 4, 8, 16;
-// launched for 2-8) with 16-byte aligned slots and output, p < 32: a deeper
-// software pipeline than decode_rows_kernel.  While row j is decoded from
-// LDS, the rest of row j+1's stream (its length known from its header, which
-// arrived during row j-1) is already in flight into registers, together with
-// the window of row j+2; so each row's dependent fetch overlaps the previous
-// row's decode.  Every stream load is a buffer load whose range is the row's
-// stream, and every iteration issues the same number of vector memory
-// instructions (1 window load, RV stream loads, NCH stores), so the waits at
-// the top of an iteration leave the previous row's stores in flight.  Ids and
-// flag words are scalar loads.  A wave takes rows i, i + stride, ...; ids past
-// the table give zero rows.
-template <int MODE, int NR, int NCH>
-__global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
-    Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
-    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
-    uint32_t* __restrict__ dst) {
-  constexpr uint32_t n = NCH * kWave;   // blocks = words of a row
-  constexpr uint32_t kWin = 32;         // window words: the header (n/32 <= 32) and more
-  constexpr int RV = (int)((n / 4 - kWin / 4 + kWave - 1) / kWave);  // stream units per lane
+// The row pipeline shared by decode_pipe_kernel and decode_pos_pipe_kernel,
+// for rows of exactly n = 64 * NCH blocks (NCH = 2, 4, 8, 16) with 16-byte
+// aligned slots and output.  While row j is decoded from the wave's LDS
+// window, the rest of row j+1's stream (its length known from its header,
+// which arrived during row j-1) is in flight into registers, together with
+// the window (first 32 words) of row j+2; so each row's dependent fetch
+// overlaps the previous row's decode.  Every stream load is a buffer load
+// whose range is the row's stream, and every iteration issues the same
+// vector memory instructions (one window load, RV stream loads, NCH stores),
+// so the waits at the top of an iteration leave the previous row's stores in
+// flight.  Ids and flag words are scalar loads, one clamped id per row (slot
+// 0 stands in for a row outside the table, so every address is in bounds).
+// A wave takes rows i, i + stride, ...; ids past the table give zero rows.
+//   stream_words(win): words of a compressed row's stream, from its window
+//   decode(win, x):    the row's n words from the LDS window, x[c] = word
+//                      c * 64 + lane (every lane of the wave calls it)
+template <int NCH>
+struct RowPipe {
+  static constexpr uint32_t n = NCH * kWave;  // blocks = words of a row
+  static constexpr uint32_t kWin = 32;        // window words: the header (n/32 <= 32) and more
+  static constexpr int RV = (int)((n / 4 - kWin / 4 + kWave - 1) / kWave);  // units per lane
   // LDS window: every unit the loads can fill (>= n + 4 words, so a payload
   // ending in the last stream word is read with a word after it), written
   // unconditionally so that no branch separates the loads from their waits
-  constexpr uint32_t kLdsWords = kWin + RV * kWave * 4;
+  static constexpr uint32_t kLdsWords = kWin + RV * kWave * 4;
   static_assert(kLdsWords >= n + 4, "window too small");
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kLdsWords];
+};
+
+template <int NCH, bool GATHER, typename StreamWords, typename Decode>
+__device__ __forceinline__ void run_row_pipeline(
+    const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
+    uint32_t* __restrict__ dst, uint32_t* lds, uint32_t i, uint32_t stride,
+    StreamWords stream_words, Decode decode) {
+  using P = RowPipe<NCH>;
+  constexpr uint32_t n = P::n, kWin = P::kWin;
+  constexpr int RV = P::RV;
   const uint32_t lane = lane_id();
-  const uint32_t wave = uniform(threadIdx.x / kWave);
-  uint32_t* lds = lds_all[wave];
   u32x4* l4 = reinterpret_cast<u32x4*>(lds);
-  const uint32_t stride = gridDim.x * kWavesPerBlock;
-
-  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
-  if (i >= n_out) return;
-
-  // A row in flight: where its slot is (slot 0 for a row outside the table,
-  // so that every address stays in bounds), whether it is a row of the table,
-  // and its flag word and id bits once they are known.
   struct Row {
     const uint32_t* src;
-    bool ok;
-    unsigned long long fw;
-    uint32_t bit;  // id & 63
+    bool ok;                // a row of the table
+    unsigned long long fw;  // its flag word
+    uint32_t bit;           // id & 63
   };
-  const int negp = -(int)cd.p;
   auto id_of = [&](uint32_t r) -> uint64_t {
-    return MODE == kModeGather ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
+    return GATHER ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
   };
   // row r with id `id`: slot, flag word (scalar load) and window (buffer load)
   auto open_row = [&](uint32_t r, uint64_t id, uint32_t& win) -> Row {
@@ -971,11 +971,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
   auto flagged = [&](const Row& w) { return w.ok && ((w.fw >> w.bit) & 1ull); };
   // words of the row's stored form: the stream for a compressed row, the
   // whole slot for a raw one, nothing for a row outside the table
-  auto stored_words = [&](const Row& w, uint32_t hwin) -> uint32_t {
+  auto stored = [&](const Row& w, uint32_t win) -> uint32_t {
     if (!w.ok) return 0u;
     if (!flagged(w)) return n;
-    const uint32_t m = wave_sum(__popc(lane < n / 32 ? hwin : 0u));
-    return min((n + 32u * n - cd.p * m + 31u) >> 5, n);
+    return min(stream_words(win), n);
   };
   auto load_rest = [&](const Row& w, uint32_t words, u32x4* r) {
     const __amdgpu_buffer_rsrc_t rs = row_rsrc(w.src, ((words + 3u) & ~3u) * 4u);
@@ -990,13 +989,12 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
   Row w1 = open_row(i + stride, id_of(i + stride), win1);
   uint64_t id2 = id_of(i + 2 * stride);
   u32x4 rest0[RV];
-  load_rest(w0, stored_words(w0, win0), rest0);
+  load_rest(w0, stored(w0, win0), rest0);
   // wait for all of it here: at the loop top the compiler merges this state
   // with the back edge's, where the previous row's stores are still pending
   asm volatile("" ::"v"(win1));
 #pragma unroll
   for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
-  const uint32_t l32 = 32u * lane;
 
   while (true) {
     // (1) row 0's stream has arrived: stage it in the wave's LDS window (the
@@ -1008,7 +1006,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
     // (2) row 1: its header gives its stream length; the rest of its stream
     //     goes in flight now
     u32x4 rest1[RV];
-    load_rest(w1, stored_words(w1, win1), rest1);
+    load_rest(w1, stored(w1, win1), rest1);
     // (3) window and flag word of row 2, id of row 3
     uint32_t win2;
     const Row w2 = open_row(i + 2 * stride, id2, win2);
@@ -1022,18 +1020,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
     } else {
-      // bit offset of lane l's payload: u + 32 l - p * (stripped blocks of
-      // the chunk below l)
-      uint32_t u = n;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint32_t h_lo = __builtin_amdgcn_readlane(win0, 2 * c);
-        const uint32_t h_hi = __builtin_amdgcn_readlane(win0, 2 * c + 1);
-        const uint32_t rel =
-            (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
-        x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
-        u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
-      }
+      decode(win0, x);
     }
     uint32_t* out = dst + (uint64_t)i * n;
 #pragma unroll
@@ -1047,6 +1034,45 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
     w1 = w2; win1 = win2;
     id2 = id3;
   }
+}
+
+// [IBP] Decompression of rows of 64 * NCH blocks with one global Mask/Bitval
+// (p < 32): the row pipeline above.  A compressed row's stream length is
+// n + 32 n - p m bits (m = its header popcount); a payload's bit offset is
+// u + 32 lane - p * (stripped blocks of the chunk below the lane).
+template <int MODE, int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
+    Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
+    uint32_t* __restrict__ dst) {
+  using P = RowPipe<NCH>;
+  constexpr uint32_t n = P::n;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][P::kLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  const uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  if (i >= n_out) return;
+  const int negp = -(int)cd.p;
+  const uint32_t l32 = 32u * lane;
+  auto stream_words = [&](uint32_t win) -> uint32_t {
+    const uint32_t m = wave_sum(__popc(lane < n / 32 ? win : 0u));
+    return (n + 32u * n - cd.p * m + 31u) >> 5;
+  };
+  auto decode = [&](uint32_t win, uint32_t* x) {
+    uint32_t u = n;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+      const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
+      x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+      u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+    }
+  };
+  run_row_pipeline<NCH, MODE == kModeGather>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                             stride, stream_words, decode);
 }
 
 // ---------------------------------------------------- other block widths --
@@ -1595,32 +1621,29 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
 }
 
 // [IBP] Decompression with per-position metadata for rows of exactly
-// 64 * NCH blocks (NCH = 2, 4, 8, 16), 16-byte aligned: the software
-// pipeline of decode_pipe_kernel (the rest of row j+1's stream and the
-// window of row j+2 in flight while row j is decoded).  The position
-// entries are copied once per workgroup of WPB waves into LDS, field by
-// field (Mask, Bitval, the five deposit masks: a wave reads one field of 64
-// consecutive positions, conflict free; a 32-byte entry per lane would put
-// lanes 4 apart on the same bank), and each lane's p values are packed as
-// bytes in registers.  A row's stripped-bit total, which gives its stream
-// length, is a per-lane sum over the chunks of p where the header bit is set
-// (the header word used as a lane mask) and one wave sum.
+// 64 * NCH blocks (NCH = 2, 4, 8, 16), 16-byte aligned: the row pipeline of
+// run_row_pipeline.  The position entries are copied once per workgroup of
+// WPB waves into LDS, field by field (Mask, Bitval, the five deposit masks: a
+// wave reads one field of 64 consecutive positions, conflict free; a 32-byte
+// entry per lane would put lanes 4 apart on the same bank), and each lane's
+// p values are packed as bytes in registers.  A row's stripped-bit total,
+// which gives its stream length, is a per-lane sum over the chunks of p where
+// the header bit is set (the header word used as a lane mask) and one wave
+// sum; a payload's offset within a chunk is a DPP wave scan of the stripped
+// p values.
 template <bool GATHER, int NCH, int WPB>
 __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
     const PosEntry* __restrict__ table, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     uint64_t n_rows, uint32_t n_out, uint32_t* __restrict__ dst) {
-  constexpr uint32_t n = NCH * kWave;
-  constexpr uint32_t kWin = 32;
-  constexpr int RV = (int)((n / 4 - kWin / 4 + kWave - 1) / kWave);
-  constexpr uint32_t kLdsWords = kWin + RV * kWave * 4;
+  using P = RowPipe<NCH>;
+  constexpr uint32_t n = P::n;
   constexpr int PW = (NCH + 3) / 4;  // registers of packed p bytes
   __shared__ uint32_t tf[7][n];      // Mask, Bitval, sfx[0..4] by position
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[WPB][kLdsWords];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[WPB][P::kLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
-  u32x4* l4 = reinterpret_cast<u32x4*>(lds);
   {
     const u32x4* g = reinterpret_cast<const u32x4*>(table);
     for (uint32_t k = threadIdx.x; k < n; k += WPB * kWave) {
@@ -1639,109 +1662,46 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
 #pragma unroll
   for (int w = 0; w < PW; ++w) pp[w] = 0;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) pp[c / 4] |= (uint32_t)__popc(tf[0][c * kWave + lane]) << (8 * (c % 4));
+  for (int c = 0; c < NCH; ++c)
+    pp[c / 4] |= (uint32_t)__popc(tf[0][c * kWave + lane]) << (8 * (c % 4));
+  auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
   auto entry = [&](uint32_t k) -> PosEntry {
     return PosEntry{tf[0][k], tf[1][k], 0u, {tf[2][k], tf[3][k], tf[4][k], tf[5][k], tf[6][k]}};
   };
-
   const uint32_t stride = gridDim.x * WPB;
-  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * WPB + wave;
+  const uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * WPB + wave;
   if (i >= n_out) return;
-
-  auto id_of = [&](uint32_t r) -> uint64_t {
-    return GATHER ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
-  };
-  auto live = [&](uint32_t r, uint64_t id) -> bool { return r < n_out && id < n_rows; };
-  auto slot = [&](bool ok, uint64_t id) { return slots + (ok ? id : 0ull) * n; };
-  auto flag_word = [&](bool ok, uint64_t id) -> unsigned long long {
-    return flags[(ok ? id : 0ull) >> 6];
-  };
-  auto stored_words = [&](bool ok, unsigned long long fw, uint64_t id, uint32_t hwin) -> uint32_t {
-    if (!ok) return 0u;
-    if (!((fw >> (id & 63)) & 1ull)) return n;
+  const uint32_t l32 = 32u * lane;
+  auto stream_words = [&](uint32_t win) -> uint32_t {
     uint32_t s_lane = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const uint32_t h_lo = __builtin_amdgcn_readlane(hwin, 2 * c);
-      const uint32_t h_hi = __builtin_amdgcn_readlane(hwin, 2 * c + 1);
+      const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
       const bool stripped =
           __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-      s_lane += stripped ? __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8) : 0u;
+      s_lane += stripped ? p_of(c) : 0u;
     }
-    const uint32_t s = wave_sum(s_lane);
-    return min((n + 32u * n - s + 31u) >> 5, n);
+    return (n + 32u * n - wave_sum(s_lane) + 31u) >> 5;
   };
-  auto load_window = [&](bool ok, uint64_t id) -> uint32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(slot(ok, id), ok ? kWin * 4 : 0u),
-                                                lane * 4, 0, 0);
-  };
-  auto load_rest = [&](bool ok, uint64_t id, uint32_t words, u32x4* r) {
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(slot(ok, id), ((words + 3u) & ~3u) * 4u);
+  auto decode = [&](uint32_t win, uint32_t* x) {
+    uint32_t u = n;
 #pragma unroll
-    for (int c = 0; c < RV; ++c)
-      r[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
-  };
-
-  uint64_t id0 = id_of(i);
-  uint64_t id1 = id_of(i + stride);
-  bool ok0 = live(i, id0), ok1 = live(i + stride, id1);
-  unsigned long long fw0 = flag_word(ok0, id0), fw1 = flag_word(ok1, id1);
-  uint32_t win0 = load_window(ok0, id0);
-  uint32_t win1 = load_window(ok1, id1);
-  uint64_t id2 = id_of(i + 2 * stride);
-  u32x4 rest0[RV];
-  load_rest(ok0, id0, stored_words(ok0, fw0, id0, win0), rest0);
-  asm volatile("" ::"v"(win1));
-#pragma unroll
-  for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
-
-  while (true) {
-    lds[lane] = win0;
-#pragma unroll
-    for (int c = 0; c < RV; ++c) l4[kWin / 4 + c * kWave + lane] = rest0[c];
-    wave_lds_sync();
-    const uint32_t words1 = stored_words(ok1, fw1, id1, win1);
-    u32x4 rest1[RV];
-    load_rest(ok1, id1, words1, rest1);
-    const bool ok2 = live(i + 2 * stride, id2);
-    const unsigned long long fw2 = flag_word(ok2, id2);
-    const uint32_t win2 = load_window(ok2, id2);
-    const uint64_t id3 = id_of(i + 3 * stride);
-    uint32_t x[NCH];
-    if (!ok0) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) x[c] = 0u;
-    } else if (!((fw0 >> (id0 & 63)) & 1ull)) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
-    } else {
-      uint32_t u = n;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint32_t h_lo = __builtin_amdgcn_readlane(win0, 2 * c);
-        const uint32_t h_hi = __builtin_amdgcn_readlane(win0, 2 * c + 1);
-        const bool stripped =
-            __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-        const uint32_t v = stripped ? __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8) : 0u;
-        const uint32_t incl = wave_scan_incl(v);
-        const uint32_t rel = u + 32u * lane - (incl - v);
-        const uint32_t w = lds_bits(lds, rel);
-        x[c] = stripped ? deposit_pos(w, entry(c * kWave + lane)) : w;
-        u += 32u * kWave - __builtin_amdgcn_readlane(incl, kWave - 1);
-      }
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+      const bool stripped =
+          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+      const uint32_t v = stripped ? p_of(c) : 0u;
+      const uint32_t incl = wave_scan_incl(v);
+      const uint32_t rel = (u + l32) - (incl - v);
+      const uint32_t w = lds_bits(lds, rel);
+      x[c] = stripped ? deposit_pos(w, entry(c * kWave + lane)) : w;
+      u += 32u * kWave - __builtin_amdgcn_readlane(incl, kWave - 1);
     }
-    uint32_t* out = dst + (uint64_t)i * n;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
-    __builtin_amdgcn_sched_barrier(0);
-    wave_lds_sync();
-    i += stride;
-    if (i >= n_out) break;
-    id0 = id1; ok0 = ok1; fw0 = fw1; win0 = win1;
-    for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
-    id1 = id2; ok1 = ok2; fw1 = fw2; win1 = win2;
-    id2 = id3;
-  }
+  };
+  run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                stream_words, decode);
 }
 
 // ------------------------------------------------------ packed cache ----
