@@ -746,6 +746,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
   const uint32_t stride = gridDim.x * kWavesPerBlock;
   const uint32_t keep_bits = 32u - cd.p;
   const uint32_t lane_keep = lane * keep_bits;
+  const int negp = -(int)cd.p;
+  const uint32_t l32 = 32u * lane;
   const uint32_t full = n & ~(uint32_t)(kWave - 1);
 
   uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
@@ -828,11 +830,12 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
         for (int c = 0; c < NCH; ++c) {
           const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
           const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
-          const uint32_t v = lds[bits_below_lane_acc(~h_lo, ~h_hi, uw)];
-          const bool stripped =
-              __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-          x[c] = stripped ? cd.bitval : v;
-          uw += __popc(~h_lo) + __popc(~h_hi);
+          // 64-bit scalar ops on the header word (one s_not_b64, one s_bcnt1_b64)
+          const unsigned long long h = ((unsigned long long)h_hi << 32) | h_lo;
+          const unsigned long long kept = ~h;
+          const uint32_t v = lds[bits_below_lane_acc((uint32_t)kept, (uint32_t)(kept >> 32), uw)];
+          x[c] = __builtin_amdgcn_inverse_ballot_w64(h) ? cd.bitval : v;
+          uw += (uint32_t)__popcll(kept);
         }
       } else {
         uint32_t u = n;
@@ -840,9 +843,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
         for (int c = 0; c < NCH; ++c) {
           const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
           const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
-          const uint32_t rel = u + lane_keep + __umul24(cd.p, bits_below_lane(~h_lo, ~h_hi));
+          const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
           x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
-          u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+          u += 32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
         }
       }
       // the restored rows are streamed out: non-temporal stores
@@ -1068,7 +1071,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
       const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
       const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
       x[c] = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
-      u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+      u += 32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
     }
   };
   run_row_pipeline<NCH, MODE == kModeGather>(slots, flags, ids, n_rows, n_out, dst, lds, i,
