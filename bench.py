@@ -257,6 +257,7 @@ def main():
     comp_ms = 0.0
     raw_bytes = stored = 0
     bits_total = 0
+    side_bytes = 0   # flag words of every table
     def compress(tg):
         if pos_table is not None:
             return ibp.ibp_compress_positional(pos_table, tg)
@@ -276,6 +277,7 @@ def main():
         images.append((slots, flags, sb))
         raw_bytes += tg.numel()
         stored += int(sb.sum())
+        side_bytes += 8 * ((tg.shape[0] + 63) // 64)
         bits_total += int(np.minimum(rbn.astype(np.int64), 8 * tg.shape[1]).sum())
     comp_GBps = raw_bytes / (comp_ms / 1e3) / 1e9
     log(f"metadata {md} in {meta_ms:.1f} ms; compress {comp_ms:.2f} ms ({comp_GBps:.0f} GB/s); "
@@ -524,6 +526,9 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "compression_ratio": round(raw_bytes / stored, 4),
         "compression_ratio_bits": round(raw_bytes * 8 / bits_total, 4),
+        # with the flag words and the metadata (32 bytes, or the position table)
+        "compression_ratio_with_side_data": round(raw_bytes / (stored + side_bytes + (
+            pos_table.numel() if pos_table is not None else 32)), 4),
         "metadata": {"mask": f"0x{md.mask:0{args.width // 4}X}",
                      "bitval": f"0x{md.bitval:0{args.width // 4}X}",
                      "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
