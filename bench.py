@@ -95,7 +95,8 @@ def kernel_source_hash() -> str:
 
 
 def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False,
-                       invariant_bits: int = 0, cached: bool = False) -> str:
+                       invariant_bits: int = 0, cached: bool = False,
+                       host_image: bool = False) -> str:
     """The decode kernel libibp launches for rows of this size (16-byte
     aligned buffers)."""
     if positional:
@@ -103,6 +104,8 @@ def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False
                 else "decode_positional_kernel")
     if width != 32:
         return "decode_wide_kernel"
+    if host_image and invariant_bits < 32 and row_bytes >= 4096 and not cached:
+        return "decode_segments_kernel"   # 256-block tasks for an image in host memory
     if row_bytes in (512, 1024, 2048) and invariant_bits < 32 and not cached:
         return "decode_pipe_kernel"
     return "decode_rows_kernel" if row_bytes <= 4096 else "decode_segments_kernel"
@@ -535,7 +538,7 @@ def main():
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
         "kernel": {"name": decode_kernel_name(S, args.width, args.positional, md.invariant_bits,
-                                              bool(args.cache_mib)),
+                                              bool(args.cache_mib), args.source == "host"),
                    "mean_launch_us": round(mean_launch_s * 1e6, 3),
                    "event_pair_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
                    "event_pair_min_us": round(float(launch_ms.min()) * 1e3, 3),

@@ -2010,13 +2010,31 @@ struct DecodeArgs {
   uint64_t n_out;
   void* dst;
   int vec;
+  bool host_image;  // slots in pinned host memory (read across the host link)
 };
+
+// Is p host memory (pinned, mapped for the device)?  A decode from such an
+// image is bound by the host link's latency and request count rather than by
+// HBM, and prefers more, smaller tasks.
+bool is_host_memory(const void* p) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // unregistered memory: clear the error, treat as device
+    return false;
+  }
+  return at.type == hipMemoryTypeHost;
+}
 
 template <int MODE, int NR>
 void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   const uint32_t* arena = (const uint32_t*)a.arena;
   const unsigned long long* cloc = (const unsigned long long*)a.cache_loc;
-  if (cd.n <= kSegBlocks) {
+  // an image in host memory, rows of >= 1024 blocks with kept bits: tasks of
+  // 256 blocks, so that more and smaller reads cross the host link at once
+  // (measured: KV page gather 1004 -> 933 us, 28 KiB weight rows 1020 ->
+  // 981 us; the link ceiling then bounds both at 0.96-0.97)
+  const bool small_tasks = a.host_image && NR != 0 && MODE != kModeCached && cd.n >= 1024;
+  if (cd.n <= kSegBlocks && !small_tasks) {
     const uint64_t piece = 1ull << 30;
     for (uint64_t off = 0; off < a.n_out; off += piece) {
       const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, a.n_out - off);
@@ -2075,7 +2093,7 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   }
   // segments of kSegBlocks blocks (measured: shorter segments add more
   // header-prefix reads than they gain in parallelism, even for 8 KiB rows)
-  const uint64_t seg = kSegBlocks;
+  const uint64_t seg = small_tasks ? 256 : kSegBlocks;
   const uint32_t nseg = (uint32_t)((cd.n + seg - 1) / seg);
   const uint64_t n_tasks = a.n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -2382,7 +2400,7 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
     // 16-byte staging and raw copies need 16-byte rows (segments are
     // multiples of 64 blocks, so their bounds are 16-byte aligned too)
     const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
-    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec};
+    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec, false};
     if (md->width_bits == 16)
       launch_decode_wide_mode<uint16_t>(md, row_bytes, a, mode, st);
     else
@@ -2393,7 +2411,8 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
   const Codec cd = make_codec(md, row_bytes);
   // cache entries start at 16-byte boundaries of the (16-byte aligned) arena
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
-  const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec};
+  const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec,
+                     is_host_memory(slots)};
   if (mode == kModeCached)
     launch_decode<kModeCached>(cd, a, st);
   else if (gather)
