@@ -1623,6 +1623,128 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
   }
 }
 
+// The position entries of rows of n blocks staged into LDS field by field
+// (tf[0] Mask, tf[1] Bitval, tf[2..6] the five parallel-suffix masks), so
+// that a wave reads one field of 64 consecutive positions without bank
+// conflicts; a 32-byte entry per lane would put lanes 4 apart on one bank.
+// Every thread of the workgroup takes part (ends with a barrier).
+template <uint32_t n>
+__device__ __forceinline__ void stage_pos_table(const PosEntry* __restrict__ table,
+                                                uint32_t (*tf)[n]) {
+  const u32x4* g = reinterpret_cast<const u32x4*>(table);
+  for (uint32_t k = threadIdx.x; k < n; k += blockDim.x) {
+    const u32x4 a = g[2 * k], b = g[2 * k + 1];  // {mask, bitval, p, sfx0}, {sfx1..4}
+    tf[0][k] = a.x;
+    tf[1][k] = a.y;
+    tf[2][k] = a.w;
+    tf[3][k] = b.x;
+    tf[4][k] = b.y;
+    tf[5][k] = b.z;
+    tf[6][k] = b.w;
+  }
+  __syncthreads();
+}
+
+template <uint32_t n>
+__device__ __forceinline__ PosEntry pos_entry(const uint32_t (*tf)[n], uint32_t k) {
+  return PosEntry{tf[0][k], tf[1][k], 0u, {tf[2][k], tf[3][k], tf[4][k], tf[5][k], tf[6][k]}};
+}
+
+// p of the lane's position in each chunk c, as byte c % 4 of pp[c / 4].
+template <int NCH>
+__device__ __forceinline__ void pack_pos_p(const uint32_t (*tf)[NCH * kWave], uint32_t lane,
+                                           uint32_t* pp) {
+#pragma unroll
+  for (int w = 0; w < (NCH + 3) / 4; ++w) pp[w] = 0;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+    pp[c / 4] |= (uint32_t)__popc(tf[0][c * kWave + lane]) << (8 * (c % 4));
+}
+
+// [IBP] Compression with per-position metadata of rows of exactly 64 * NCH
+// blocks, one wave per row (the scheme of compress_rows_kernel): the row is
+// read once into registers, each chunk's match ballot is its header word,
+// the bit offset of a block's payload is n + 32 k minus the stripped p of
+// the blocks before it (a scalar carry across chunks plus a DPP wave scan
+// within one), and the payloads are ORed into a wave-private LDS stream that
+// is then written with coalesced stores.  In place is safe: every load of a
+// row completes before its first store.
+template <int NCH, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
+    const PosEntry* __restrict__ table, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t n = NCH * kWave;
+  __shared__ uint32_t tf[7][n];
+  __shared__ uint32_t lds_all[WPB][n + 4];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds_all[wave];
+  stage_pos_table<n>(table, tf);
+  uint32_t pp[(NCH + 3) / 4];
+  pack_pos_p<NCH>(tf, lane, pp);
+  auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
+  const uint64_t stride = (uint64_t)gridDim.x * WPB;
+  for (uint64_t row = (uint64_t)blockIdx.x * WPB + wave; row < n_rows; row += stride) {
+    const uint32_t* x_row = src + row * n;
+    uint32_t* s_row = slots + row * n;
+    uint32_t x[NCH];
+    unsigned long long h[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+    uint32_t s_lane = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t k = c * kWave + lane;
+      const bool match = (x[c] & tf[0][k]) == tf[1][k];
+      h[c] = __ballot(match);
+      s_lane += match ? p_of(c) : 0u;
+    }
+    const uint32_t c_bits = n + 32u * n - wave_sum(s_lane);
+    const bool flag = c_bits < 32u * n;
+    if (!flag) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s_row[c * kWave + lane] = x[c];
+    } else {
+      const uint32_t nw = (c_bits + 31u) >> 5;
+      for (uint32_t j = n / 32 + lane; j < nw + 1; j += kWave) buf[j] = 0u;
+      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (lane == 2u * c) w = (uint32_t)h[c];
+          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
+        }
+        buf[lane] = w;
+      }
+      wave_lds_sync();
+      uint32_t carry = 0;  // stripped p of the chunks before this one
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t k = c * kWave + lane;
+        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+        const uint32_t v = match ? p_of(c) : 0u;
+        const uint32_t incl = wave_scan_incl(v);
+        const uint32_t off = n + 32u * k - (carry + incl - v);
+        const uint32_t len = 32u - v;
+        const uint32_t pay = match ? extract_pos(x[c], pos_entry<n>(tf, k)) : x[c];
+        if (len) {
+          const uint32_t sh = off & 31u, wi = off >> 5;
+          atomicOr(&buf[wi], pay << sh);
+          if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+        }
+        carry += __builtin_amdgcn_readlane(incl, kWave - 1);
+      }
+      wave_lds_sync();
+      for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+      wave_lds_sync();
+    }
+    if (lane == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+  }
+}
+
 // [IBP] Decompression with per-position metadata for rows of exactly
 // 64 * NCH blocks (NCH = 2, 4, 8, 16), 16-byte aligned: the row pipeline of
 // run_row_pipeline.  The position entries are copied once per workgroup of
@@ -1647,30 +1769,11 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
-  {
-    const u32x4* g = reinterpret_cast<const u32x4*>(table);
-    for (uint32_t k = threadIdx.x; k < n; k += WPB * kWave) {
-      const u32x4 a = g[2 * k], b = g[2 * k + 1];  // {mask, bitval, p, sfx0}, {sfx1..4}
-      tf[0][k] = a.x;
-      tf[1][k] = a.y;
-      tf[2][k] = a.w;
-      tf[3][k] = b.x;
-      tf[4][k] = b.y;
-      tf[5][k] = b.z;
-      tf[6][k] = b.w;
-    }
-    __syncthreads();
-  }
+  stage_pos_table<n>(table, tf);
   uint32_t pp[PW];
-#pragma unroll
-  for (int w = 0; w < PW; ++w) pp[w] = 0;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c)
-    pp[c / 4] |= (uint32_t)__popc(tf[0][c * kWave + lane]) << (8 * (c % 4));
+  pack_pos_p<NCH>(tf, lane, pp);
   auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
-  auto entry = [&](uint32_t k) -> PosEntry {
-    return PosEntry{tf[0][k], tf[1][k], 0u, {tf[2][k], tf[3][k], tf[4][k], tf[5][k], tf[6][k]}};
-  };
+  auto entry = [&](uint32_t k) { return pos_entry<n>(tf, k); };
   const uint32_t stride = gridDim.x * WPB;
   const uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * WPB + wave;
   if (i >= n_out) return;
@@ -2637,7 +2740,23 @@ int ibp_compress_positional(const void* table, uint64_t n_rows, uint64_t row_byt
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
                      (unsigned long long*)flags, fw, 0ull);
   const uint32_t n = (uint32_t)(row_bytes / 4);
-  if (n <= 1024)
+  if (n == 128 || n == 256 || n == 512 || n == 1024) {
+    // one wave per row on a resident grid, the table in LDS per workgroup
+#define IBP_CPR(NCH, WPB, PER_CU)                                                              \
+  hipLaunchKernelGGL((compress_pos_rows_kernel<NCH, WPB>),                                     \
+                     dim3((uint32_t)std::min<uint64_t>((n_rows + WPB - 1) / WPB,               \
+                                                       workgroups_per_device(PER_CU))),        \
+                     dim3(WPB * kWave), 0, st, (const PosEntry*)table, n_rows,                 \
+                     (const uint32_t*)src, (uint32_t*)slots, (unsigned long long*)flags,       \
+                     row_bits)
+    switch (n) {
+      case 128: IBP_CPR(2, 4, 8); break;
+      case 256: IBP_CPR(4, 4, 8); break;
+      case 512: IBP_CPR(8, 4, 5); break;
+      default: IBP_CPR(16, 8, 2); break;
+    }
+#undef IBP_CPR
+  } else if (n <= 1024)
     launch_compress_positional_t<1024>(table, n, n_rows, src, slots, flags, row_bits, st);
   else if (n <= 4096)
     launch_compress_positional_t<4096>(table, n, n_rows, src, slots, flags, row_bits, st);

@@ -309,6 +309,41 @@ def test_pinned_host_image_gather(ibp):
     assert torch.equal(ibp.ibp_decompress(md, hs2, f2), xg)
 
 
+@pytest.mark.parametrize("row_bytes,mask,bitval", [(4096, 0x7C007C00, 0x3C003C00),
+                                                  (8192, 0x78007800, 0x38003800),
+                                                  (28672, 0x7C007C00, 0x3C003C00),
+                                                  (4096, 0x55555555, 0x11111111)])
+def test_pinned_host_image_small_tasks(ibp, row_bytes, mask, bitval):
+    """An image in pinned host memory with rows of 1024+ blocks is decoded in
+    256-block tasks: gather (raw rows, repeated ids, ids outside the table)
+    and full decompress against the source rows, sampled rows against the
+    oracle."""
+    rng = np.random.default_rng(row_bytes + mask % 97)
+    n_rows = 300
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=0.9, raw_rows=(3, 150))
+    md = gmd(ibp, mask, bitval)
+    xg = to_gpu(x)
+    slots, flags, _ = ibp.ibp_compress(md, xg)
+    host_slots = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+    host_slots.copy_(slots)
+    ids = rng.integers(0, n_rows, 900).astype(np.int64)
+    ids[::37] = n_rows + 1
+    ids[:2] = [3, 150]
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress(md, host_slots, flags, idg)
+    full = ibp.ibp_decompress(md, host_slots, flags)
+    torch.cuda.synchronize()
+    bad = torch.from_numpy(ids >= n_rows).cuda()
+    ref = xg[idg.clamp(max=n_rows - 1)]
+    ref[bad] = 0
+    assert torch.equal(out, ref)
+    assert torch.equal(full, xg)
+    slots_o, flags_o, _ = orc.compress(omd(md), x)
+    pick = np.nonzero(ids < n_rows)[0][:24]
+    want = orc.gather_decompress(omd(md), slots_o, flags_o, ids[pick])
+    assert np.array_equal(out[torch.from_numpy(pick).cuda()].cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("where", ["device", "pinned_host"])
 @pytest.mark.parametrize("row_bytes,mask,bitval", [(4096, 0x7C007C00, 0x3C003C00),
                                                   (2048, 0xFFFFFFFF, 0x00000000),
@@ -560,8 +595,14 @@ def test_positional_gather_many_rows_per_wave(ibp, row_bytes, n_ids):
     say(f"positional many rows: row_bytes={row_bytes} ids={n_ids}")
     table = ibp.ibp_positional_table(mask, bitval).cuda()
     xg = to_gpu(x)
-    slots, flags, _ = ibp.ibp_compress_positional(table, xg)
+    slots, flags, rb = ibp.ibp_compress_positional(table, xg)
     assert torch.equal(ibp.ibp_decompress_positional(table, slots, flags), xg)
+    # in place: the same image (stream words, flags, sizes) as out of place
+    inplace = xg.clone()
+    _, f2, rb2 = ibp.ibp_compress_positional(table, inplace, slots=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(f2, flags) and torch.equal(rb2, rb)
+    assert torch.equal(ibp.ibp_decompress_positional(table, inplace, f2), xg)
     ids = rng.integers(0, n_rows, n_ids).astype(np.int64)
     ids[::991] = n_rows + 3
     idg = torch.from_numpy(ids).cuda()
