@@ -46,11 +46,12 @@ class Workload:
     """tables: list of numpy arrays (rows on axis 0); steps: list of
     (table index, ids or None); sample_for_metadata: numpy array."""
 
-    def __init__(self, name, desc, tables, steps, sample, n_out_bytes, hot=None):
+    def __init__(self, name, desc, tables, steps, sample, n_out_bytes, hot=None, layer_size=1):
         self.name, self.desc, self.tables, self.steps = name, desc, tables, steps
         self.sample = sample
         self.n_out_bytes = n_out_bytes
         self.hot = hot  # row ids by static popularity (cache fill order)
+        self.layer_size = layer_size  # consecutive steps that one batched launch may take
 
 
 def make_workload(name: str) -> Workload:
@@ -83,8 +84,9 @@ def make_workload(name: str) -> Workload:
         tables = [syn.llm_weight(layer, j) for layer in (0, 1) for j in range(7)]
         steps = [(t, None) for t in range(len(tables))]
         return Workload(name, "LLM weights bf16, 4 x [4096,4096] + 3 x [4096,14336] per "
-                        "layer, full decompress per matrix (2 resident layers)", tables,
-                        steps, tables[0], None)
+                        "layer, full decompress layer by layer (the 7 matrices of a layer in "
+                        "one batched call; 2 resident layers)", tables,
+                        steps, tables[0], None, layer_size=7)
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -96,7 +98,7 @@ def kernel_source_hash() -> str:
 
 def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False,
                        invariant_bits: int = 0, cached: bool = False,
-                       host_image: bool = False) -> str:
+                       host_image: bool = False, batched: bool = False) -> str:
     """The decode kernel libibp launches for rows of this size (16-byte
     aligned buffers)."""
     if positional:
@@ -104,6 +106,8 @@ def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False
                 else "decode_positional_kernel")
     if width != 32:
         return "decode_wide_kernel"
+    if batched:
+        return "decode_batch_kernel"
     if host_image and invariant_bits < 32 and row_bytes >= 4096 and not cached:
         return "decode_segments_kernel"   # 256-block tasks for an image in host memory
     if row_bytes in (512, 1024, 2048) and invariant_bits < 32 and not cached:
@@ -208,6 +212,9 @@ def main():
                     help="keep the most popular rows that fit this many MiB in a packed, "
                          "compressed GPU cache; the other rows come from the image "
                          "(--source host: pinned host memory)")
+    ap.add_argument("--per-tensor", action="store_true",
+                    help="llm_weights: one launch per matrix instead of one batched launch "
+                         "per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="run one 1 GiB device-to-device copy before the timed loop "
@@ -396,14 +403,23 @@ def main():
                 16 * len(ids) + 8 * len(np.unique(miss_ids >> 6))), img, \
             int(sb[np.unique(miss_ids)].sum())
 
+    # launch groups: the weight matrices of a layer go in one batched call
+    # (layer-by-layer loading), every other step is a launch of its own
+    batch_layers = wl.layer_size > 1 and not args.per_tensor and pos_table is None and \
+        args.width == 32 and args.source == "device" and not args.cache_mib
+    if batch_layers:
+        groups = [list(range(g, min(g + wl.layer_size, len(plan))))
+                  for g in range(0, len(plan), wl.layer_size)]
+    else:
+        groups = [[k] for k in range(len(plan))]
     plan_split = [algo_bytes(ti, ids) for ti, _, _, ids in plan]
-    plan_bytes = [b for b, _, _ in plan_split]
-    plan_img = [i for _, i, _ in plan_split]
-    plan_link = [u for _, _, u in plan_split]
-    plan_out = [o.numel() for _, _, o, _ in plan]
+    plan_bytes = [sum(plan_split[k][0] for k in g) for g in groups]
+    plan_img = [sum(plan_split[k][1] for k in g) for g in groups]
+    plan_link = [sum(plan_split[k][2] for k in g) for g in groups]
+    plan_out = [sum(plan[k][2].numel() for k in g) for g in groups]
 
     launchers = []
-    for ti, idg, out, _ in plan:
+    for ti, idg, out, _ in (plan if not batch_layers else []):
         slots, flags, _ = images[ti]
         if pos_table is not None:
             if idg is None:
@@ -419,6 +435,12 @@ def main():
                 md, arena, cache_loc, slots, flags, idg, out))
         else:
             launchers.append(ibp.ibp_gather_decompress_launcher(md, slots, flags, idg, out))
+
+    if batch_layers:
+        for g in groups:
+            launchers.append(ibp.ibp_decompress_batch_launcher(
+                md, [(images[plan[k][0]][0], images[plan[k][0]][1]) for k in g],
+                [plan[k][2] for k in g]))
 
     def launch(k):
         launchers[k % len(launchers)]()
@@ -460,20 +482,21 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    out_bytes = sum(plan_out[k % len(plan)] for k in range(K))
-    a_bytes = sum(plan_bytes[k % len(plan)] for k in range(K)) / K
+    out_bytes = sum(plan_out[k % len(groups)] for k in range(K))
+    a_bytes = sum(plan_bytes[k % len(groups)] for k in range(K)) / K
     value = out_bytes / wall / 1e9
     mean_launch_s = region_s / K
     achieved = a_bytes / mean_launch_s / 1e9
 
     # correctness spot check of the timed path against the source rows
-    ti, idg, out, ids = plan[(K - 1) % len(plan)]
-    src = wl.tables[ti].reshape(wl.tables[ti].shape[0], -1).view(np.uint8)
-    pick = np.random.default_rng(0).integers(0, out.shape[0], 256)
-    got = out[torch.from_numpy(pick).to(dev)].cpu().numpy()
-    want = src[ids[pick]] if ids is not None else src[pick]
-    if not np.array_equal(got, want):
-        raise SystemExit("bench: decompressed rows differ from the source table")
+    for pk in groups[(K - 1) % len(groups)]:
+        ti, idg, out, ids = plan[pk]
+        src = wl.tables[ti].reshape(wl.tables[ti].shape[0], -1).view(np.uint8)
+        pick = np.random.default_rng(0).integers(0, out.shape[0], 256)
+        got = out[torch.from_numpy(pick).to(dev)].cpu().numpy()
+        want = src[ids[pick]] if ids is not None else src[pick]
+        if not np.array_equal(got, want):
+            raise SystemExit("bench: decompressed rows differ from the source table")
 
     if args.source == "host":
         # host-link ceiling: pinned host -> device copy of 1 GiB
@@ -489,8 +512,8 @@ def main():
         torch.cuda.synchronize()
         link = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
         del h, d
-        link_read = sum(plan_link[k % len(plan)] for k in range(K)) / K  # crosses the link
-        hbm_bytes = a_bytes - sum(plan_img[k % len(plan)] for k in range(K)) / K
+        link_read = sum(plan_link[k % len(groups)] for k in range(K)) / K  # crosses the link
+        hbm_bytes = a_bytes - sum(plan_img[k % len(groups)] for k in range(K)) / K
         if link_read / link >= hbm_bytes / HBM_PEAK_GBPS:
             roof = {"bound": "host_link", "achieved": round(link_read / mean_launch_s / 1e9, 2),
                     "peak": round(link, 2), "unit": "GB/s",
@@ -505,7 +528,8 @@ def main():
     else:
         traffic = None if cache or args.width != 32 else \
             traffic_from_profiles(decode_kernel_name(S, positional=args.positional,
-                                                     invariant_bits=md.invariant_bits), wl.name)
+                                                     invariant_bits=md.invariant_bits,
+                                                     batched=batch_layers), wl.name)
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic}
@@ -538,7 +562,8 @@ def main():
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
         "kernel": {"name": decode_kernel_name(S, args.width, args.positional, md.invariant_bits,
-                                              bool(args.cache_mib), args.source == "host"),
+                                              bool(args.cache_mib), args.source == "host",
+                                              batch_layers),
                    "mean_launch_us": round(mean_launch_s * 1e6, 3),
                    "event_pair_median_us": round(float(np.median(launch_ms)) * 1e3, 3),
                    "event_pair_min_us": round(float(launch_ms.min()) * 1e3, 3),

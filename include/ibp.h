@@ -146,6 +146,32 @@ int ibp_decompress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
                    void *stream);
 
 /*
+ * One tensor of a batched decompression: its image (slots, flags) and the
+ * device buffer its rows are restored into (n_rows x row_bytes bytes), with
+ * the same memory classes and alignment as ibp_decompress.
+ */
+typedef struct ibp_tensor {
+  uint64_t n_rows;
+  uint64_t row_bytes;
+  const void *slots;
+  const uint64_t *flags;
+  void *dst;
+} ibp_tensor;
+
+/*
+ * [IBP] Decompression of n_tensors whole tensors that share the metadata
+ * `md` (the weight matrices of a model layer, loaded layer by layer):
+ * tensors[t].dst = tensor t restored, as ibp_decompress would give it, in
+ * one launch per 16 tensors instead of one per tensor.  The descriptor array
+ * is host memory and is read before the call returns.  Every tensor is
+ * validated first; on an error nothing is enqueued.  n_tensors == 0 is a
+ * no-op.  Tensors must not overlap each other's outputs.  W = 32 in one
+ * launch; other widths decode tensor by tensor.  Asynchronous on `stream`.
+ */
+int ibp_decompress_batch(const ibp_metadata *md, const ibp_tensor *tensors,
+                         uint64_t n_tensors, void *stream);
+
+/*
  * Gather-decompress: dst row i = row row_ids[i] restored, for i < n_ids, in
  * id order; duplicate ids are allowed; an id outside [0, n_rows) gives a
  * zero row.  The fetch of a feature / embedding /

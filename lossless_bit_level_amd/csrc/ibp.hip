@@ -599,6 +599,112 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
 //   3. per 64-block chunk: header word -> per-lane bit offset (mbcnt + carry)
 //      -> two LDS words -> funnel shift -> deposit + Bitval -> store.
 // A raw row is a straight copy.
+// One decode task: segment s (blocks [s*seg, min(n, s*seg + seg))) of output
+// row i, whose source is row ids[i] of the image (row i for a full
+// decompress).  Rows of n blocks; `lds` is the wave's window.
+template <int MODE, int NR>
+__device__ __forceinline__ void decode_segment_task(
+    const Codec& cd, uint32_t n, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
+    uint64_t n_rows, uint64_t i, uint32_t s, uint32_t seg, uint32_t* __restrict__ dst, int vec,
+    uint32_t* lds, uint32_t lane) {
+  const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
+  uint32_t* out = dst + i * n;
+  const uint32_t lo = s * seg;
+  const uint32_t hi = min(n, lo + seg);
+  if (MODE != kModeTable && id >= n_rows) {  // an id outside the table gives a zero row
+    for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = 0u;
+    return;
+  }
+  const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
+  const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
+  const uint32_t* src = row_source<MODE>(slots, arena, id, n, loc);
+  const uint32_t lim = row_words<MODE>(n, loc);
+  const bool flag = row_flag<MODE>(fw, id, loc);
+
+  // The header words are requested together with the flag word (for a raw
+  // row they are row data inside the slot, read and then ignored): the
+  // segment's words one per lane, and the words before it, whose stripped
+  // count is the segment's carry, in batches of four per lane.
+  const uint32_t hw_n = (hi - lo + 31) / 32;
+  uint32_t hw = 0;
+  if (lane < hw_n) hw = src[lo / 32 + lane];
+  uint32_t acc = 0;
+  for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
+    uint32_t w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
+  }
+
+  if (!flag) {
+    if (vec) {
+      const uint4* a = reinterpret_cast<const uint4*>(src);
+      uint4* o = reinterpret_cast<uint4*>(out);
+      for (uint32_t j = lo / 4 + lane; j < hi / 4; j += kWave) o[j] = a[j];
+    } else {
+      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = src[j];
+    }
+    return;
+  }
+
+  // stripped blocks before the segment: header words [0, lo/32) (all header)
+  const uint32_t carry = lo ? wave_sum(acc) : 0u;
+  // the segment's header words, one per lane; bits at or past n belong to
+  // the payloads and are cleared
+  if (lane < hw_n) {
+    const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
+    if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
+  }
+  const uint32_t m_seg = wave_sum(__popc(hw));
+
+  // stream bit range of the segment's payloads, and its LDS window
+  // (for an image that ibp_compress wrote, wb <= ceil(C/32) <= n; the
+  // clamps only keep a corrupt header from reading past the slot or entry)
+  const uint32_t a = n + 32u * lo - cd.p * carry;
+  const uint32_t b = n + 32u * hi - cd.p * (carry + m_seg);
+  const uint32_t wb = min((b + 31u) >> 5, lim);
+  const uint32_t wa = min(a >> 5, wb);
+  uint32_t base;
+  if (vec) {
+    base = wa & ~3u;
+    stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
+                    (wb - base + 3u) / 4u, lane);
+  } else {
+    base = wa;
+    stage_window<4>(src + wa, lds, wb - wa, lane);
+  }
+  wave_lds_sync();
+
+  // u = bit offset, relative to the LDS window, of the payload of the
+  // chunk's first block; lane l's payload starts 32*l - p*(stripped blocks
+  // of the chunk below l) further on.
+  uint32_t u = n + 32u * lo - cd.p * carry - 32u * base;
+  const uint32_t l32 = lane * 32u;
+  const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
+  uint32_t k0 = lo;
+  for (; k0 < full_hi; k0 += kWave) {
+    const uint32_t q = (k0 - lo) / 32;
+    const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+    const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+    const uint32_t rel = u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi));
+    __builtin_nontemporal_store(decode_block<NR>(lds, rel, h_lo, h_hi, cd), out + k0 + lane);
+    u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+  }
+  if (k0 < hi) {  // ragged end of the row (n not a multiple of 64)
+    const uint32_t q = (k0 - lo) / 32;
+    const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+    const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+    const bool valid = k0 + lane < hi;
+    const uint32_t rel = valid ? u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi)) : 0u;
+    const uint32_t x = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
+    if (valid) out[k0 + lane] = x;
+  }
+  wave_lds_sync();
+}
+
 template <int MODE, int NR>
 __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     Codec cd, const uint32_t* __restrict__ slots,
@@ -610,108 +716,58 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
-  const uint32_t n = cd.n;
-
   const uint32_t g = gridDim.x;
   for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
     const uint64_t task = wg * kWavesPerBlock + wave;
     if (task >= n_tasks) break;
     const uint64_t i = task / nseg;
     const uint32_t s = (uint32_t)(task - i * nseg);
-    const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
-    uint32_t* out = dst + i * n;
-    const uint32_t lo = s * seg;
-    const uint32_t hi = min(n, lo + seg);
-    if (MODE != kModeTable && id >= n_rows) {  // an id outside the table gives a zero row
-      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = 0u;
-      continue;
-    }
-    const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
-    const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
-    const uint32_t* src = row_source<MODE>(slots, arena, id, n, loc);
-    const uint32_t lim = row_words<MODE>(n, loc);
-    const bool flag = row_flag<MODE>(fw, id, loc);
+    decode_segment_task<MODE, NR>(cd, cd.n, slots, flags, ids, arena, cache_loc, n_rows, i, s,
+                                  seg, dst, vec, lds, lane);
+  }
+}
 
-    // The header words are requested together with the flag word (for a raw
-    // row they are row data inside the slot, read and then ignored): the
-    // segment's words one per lane, and the words before it, whose stripped
-    // count is the segment's carry, in batches of four per lane.
-    const uint32_t hw_n = (hi - lo + 31) / 32;
-    uint32_t hw = 0;
-    if (lane < hw_n) hw = src[lo / 32 + lane];
-    uint32_t acc = 0;
-    for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
-      uint32_t w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
-    }
+// [IBP] Decompression of several tensors that share one Mask/Bitval (the
+// layers of a model are decompressed tensor group by tensor group) in one
+// launch: the segment tasks of every tensor, one after the other, each
+// mapped to its tensor by the running task counts.  One launch instead of
+// one per tensor keeps the GPU full across tensor boundaries.
+constexpr uint32_t kBatchMax = 16;
+struct BatchTensor {
+  const uint32_t* slots;
+  const unsigned long long* flags;
+  uint32_t* dst;
+  uint32_t n;     // blocks per row
+  uint32_t nseg;  // segments per row
+  uint32_t vec;   // 16-byte aligned rows and buffers
+  uint32_t pad;
+};
+struct Batch {
+  uint32_t count;
+  uint32_t pad;
+  uint64_t end[kBatchMax];  // tasks of tensors [0, t]
+  BatchTensor t[kBatchMax];
+};
 
-    if (!flag) {
-      if (vec) {
-        const uint4* a = reinterpret_cast<const uint4*>(src);
-        uint4* o = reinterpret_cast<uint4*>(out);
-        for (uint32_t j = lo / 4 + lane; j < hi / 4; j += kWave) o[j] = a[j];
-      } else {
-        for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = src[j];
-      }
-      continue;
-    }
-
-    // stripped blocks before the segment: header words [0, lo/32) (all header)
-    const uint32_t carry = lo ? wave_sum(acc) : 0u;
-    // the segment's header words, one per lane; bits at or past n belong to
-    // the payloads and are cleared
-    if (lane < hw_n) {
-      const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
-      if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
-    }
-    const uint32_t m_seg = wave_sum(__popc(hw));
-
-    // stream bit range of the segment's payloads, and its LDS window
-    // (for an image that ibp_compress wrote, wb <= ceil(C/32) <= n; the
-    // clamps only keep a corrupt header from reading past the slot or entry)
-    const uint32_t a = n + 32u * lo - cd.p * carry;
-    const uint32_t b = n + 32u * hi - cd.p * (carry + m_seg);
-    const uint32_t wb = min((b + 31u) >> 5, lim);
-    const uint32_t wa = min(a >> 5, wb);
-    uint32_t base;
-    if (vec) {
-      base = wa & ~3u;
-      stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
-                      (wb - base + 3u) / 4u, lane);
-    } else {
-      base = wa;
-      stage_window<4>(src + wa, lds, wb - wa, lane);
-    }
-    wave_lds_sync();
-
-    // u = bit offset, relative to the LDS window, of the payload of the
-    // chunk's first block; lane l's payload starts 32*l - p*(stripped blocks
-    // of the chunk below l) further on.
-    uint32_t u = n + 32u * lo - cd.p * carry - 32u * base;
-    const uint32_t l32 = lane * 32u;
-    const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
-    uint32_t k0 = lo;
-    for (; k0 < full_hi; k0 += kWave) {
-      const uint32_t q = (k0 - lo) / 32;
-      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
-      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-      const uint32_t rel = u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi));
-      __builtin_nontemporal_store(decode_block<NR>(lds, rel, h_lo, h_hi, cd), out + k0 + lane);
-      u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
-    }
-    if (k0 < hi) {  // ragged end of the row (n not a multiple of 64)
-      const uint32_t q = (k0 - lo) / 32;
-      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
-      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-      const bool valid = k0 + lane < hi;
-      const uint32_t rel = valid ? u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi)) : 0u;
-      const uint32_t x = decode_block<NR>(lds, rel, h_lo, h_hi, cd);
-      if (valid) out[k0 + lane] = x;
-    }
-    wave_lds_sync();
+template <int NR>
+__global__ __launch_bounds__(kBlockThreads) void decode_batch_kernel(Codec cd, Batch batch) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint64_t n_tasks = batch.end[batch.count - 1];
+  const uint32_t g = gridDim.x;
+  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+    const uint64_t task = wg * kWavesPerBlock + wave;
+    if (task >= n_tasks) break;
+    uint32_t t = 0;
+    while (task >= batch.end[t]) ++t;
+    const BatchTensor& bt = batch.t[t];
+    const uint64_t local = task - (t ? batch.end[t - 1] : 0ull);
+    const uint64_t i = local / bt.nseg;
+    const uint32_t s = (uint32_t)(local - i * bt.nseg);
+    decode_segment_task<kModeTable, NR>(cd, bt.n, bt.slots, bt.flags, nullptr, nullptr, nullptr,
+                                        0, i, s, kSegBlocks, bt.dst, (int)bt.vec, lds, lane);
   }
 }
 
@@ -2530,6 +2586,79 @@ int ibp_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
                    const void* slots, const uint64_t* flags, void* dst, void* stream) {
   return decode_common(md, n_rows, row_bytes, slots, flags, nullptr, n_rows, dst, stream,
                        kModeTable);
+}
+
+// Host checks of one tensor of a batch (those of decode_common for a full
+// decompress).
+static int check_batch_tensor(const ibp_metadata* md, const ibp_tensor& t) {
+  int rc = check_rows(t.n_rows, t.row_bytes, md->width_bits);
+  if (rc) return rc;
+  if (t.n_rows == 0) return IBP_OK;
+  if (!t.slots || !t.flags || !t.dst) return IBP_ERR_INVALID_ARGUMENT;
+  if (!aligned(t.slots, 4) || !aligned(t.dst, 4) || !aligned(t.flags, 8)) return IBP_ERR_LAYOUT;
+  if (md->width_bits == 64 && (!aligned(t.slots, 8) || !aligned(t.dst, 8))) return IBP_ERR_LAYOUT;
+  return IBP_OK;
+}
+
+int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint64_t n_tensors,
+                         void* stream) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  if (n_tensors == 0) return IBP_OK;
+  if (!tensors) return IBP_ERR_INVALID_ARGUMENT;
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    rc = check_batch_tensor(md, tensors[t]);
+    if (rc) return rc;
+  }
+  if (md->width_bits != 32) {  // other widths: tensor by tensor
+    for (uint64_t t = 0; t < n_tensors; ++t) {
+      const ibp_tensor& x = tensors[t];
+      if (x.n_rows == 0) continue;
+      rc = ibp_decompress(md, x.n_rows, x.row_bytes, x.slots, x.flags, x.dst, stream);
+      if (rc) return rc;
+    }
+    return IBP_OK;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const Codec cd = make_codec(md, tensors[0].row_bytes);  // n is per tensor
+  uint64_t t = 0;
+  while (t < n_tensors) {
+    Batch b{};
+    uint64_t tasks = 0;
+    for (; t < n_tensors && b.count < kBatchMax; ++t) {
+      const ibp_tensor& x = tensors[t];
+      if (x.n_rows == 0) continue;
+      const uint32_t n = (uint32_t)(x.row_bytes / 4);
+      const uint32_t nseg = (n + kSegBlocks - 1) / kSegBlocks;
+      if (x.n_rows > (UINT64_MAX >> 8) / nseg) return IBP_ERR_INVALID_ARGUMENT;
+      tasks += x.n_rows * nseg;
+      BatchTensor& bt = b.t[b.count];
+      bt.slots = (const uint32_t*)x.slots;
+      bt.flags = (const unsigned long long*)x.flags;
+      bt.dst = (uint32_t*)x.dst;
+      bt.n = n;
+      bt.nseg = nseg;
+      bt.vec = x.row_bytes % 16 == 0 && aligned(x.slots, 16) && aligned(x.dst, 16);
+      b.end[b.count] = tasks;
+      ++b.count;
+    }
+    if (b.count == 0) break;
+    const uint32_t grid = grid_for((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+#define IBP_BATCH(NR)                                                                      \
+  hipLaunchKernelGGL((decode_batch_kernel<NR>), dim3(grid), dim3(kBlockThreads), 0, st, cd, b)
+    switch (cd.runs.n) {
+      case 0: IBP_BATCH(0); break;
+      case 1: IBP_BATCH(1); break;
+      case 2: IBP_BATCH(2); break;
+      case 3: IBP_BATCH(3); break;
+      case 4: IBP_BATCH(4); break;
+      default: IBP_BATCH(-1); break;
+    }
+#undef IBP_BATCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return IBP_OK;
 }
 
 int ibp_gather_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,

@@ -28,6 +28,15 @@ IBP_LOC_WORDS_MASK = (1 << 26) - 1
 IBP_LOC_OFFSET_MASK = (1 << 36) - 1
 
 
+class ibp_tensor(ctypes.Structure):
+    """One tensor of ibp_decompress_batch (see include/ibp.h)."""
+    _fields_ = [("n_rows", ctypes.c_uint64),
+                ("row_bytes", ctypes.c_uint64),
+                ("slots", ctypes.c_void_p),
+                ("flags", ctypes.c_void_p),
+                ("dst", ctypes.c_void_p)]
+
+
 class ibp_metadata(ctypes.Structure):
     _fields_ = [("width_bits", ctypes.c_uint32),
                 ("invariant_bits", ctypes.c_uint32),
@@ -70,6 +79,7 @@ def lib() -> ctypes.CDLL:
         L.ibp_compress.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp]
         L.ibp_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, vp]
         L.ibp_gather_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp]
+        L.ibp_decompress_batch.argtypes = [mdp, ctypes.POINTER(ibp_tensor), u64, vp]
         L.ibp_cache_plan.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, ctypes.POINTER(u64), vp]
         L.ibp_cache_fill.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp, u64, vp, vp]
         L.ibp_gather_decompress_cached.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp, u64, vp, vp]
@@ -87,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.ibp_status_string.restype = ctypes.c_char_p
         L.ibp_last_hip_error.argtypes = []
         for f in ("ibp_metadata_from_counts", "ibp_build_metadata", "ibp_compress",
-                  "ibp_decompress", "ibp_gather_decompress", "ibp_host_device_pointer",
+                  "ibp_decompress", "ibp_decompress_batch", "ibp_gather_decompress",
+                  "ibp_host_device_pointer",
                   "ibp_last_hip_error", "ibp_cache_plan", "ibp_cache_fill",
                   "ibp_gather_decompress_cached", "ibp_positional_table",
                   "ibp_build_metadata_positional", "ibp_compress_positional",
@@ -221,6 +232,47 @@ def ibp_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
            lib().ibp_decompress(ctypes.byref(md), n_rows, row_bytes, _dptr(slots),
                                 flags.data_ptr(), out.data_ptr(), _stream(stream)))
     return out
+
+
+def _batch_args(images, outs):
+    arr = (ibp_tensor * max(1, len(images)))()
+    for k, ((slots, flags), out) in enumerate(zip(images, outs)):
+        n_rows, row_bytes = _rows(slots)
+        _need_cuda(flags, "flags")
+        _need_cuda(out, "out")
+        _need_size(out, n_rows * row_bytes, "out")
+        arr[k] = ibp_tensor(n_rows, row_bytes, _dptr(slots), flags.data_ptr(), out.data_ptr())
+    return arr
+
+
+def ibp_decompress_batch(md: ibp_metadata, images, outs=None, stream=None):
+    """Restore several tensors sharing `md` in one launch: images is a list of
+    (slots, flags); outs (optional) the matching uint8 [n_rows, row_bytes]
+    outputs.  Returns the outputs."""
+    images = list(images)
+    if outs is None:
+        outs = [torch.empty(_rows(sl), dtype=torch.uint8, device="cuda") for sl, _ in images]
+    if len(outs) != len(images):
+        raise ValueError("one output per image")
+    arr = _batch_args(images, outs)
+    _check("ibp_decompress_batch",
+           lib().ibp_decompress_batch(ctypes.byref(md), arr, len(images), _stream(stream)))
+    return outs
+
+
+def ibp_decompress_batch_launcher(md: ibp_metadata, images, outs, stream=None):
+    """ibp_decompress_batch with its arguments converted once."""
+    images = list(images)
+    arr = _batch_args(images, outs)
+    fn = lib().ibp_decompress_batch
+    args = (ctypes.byref(md), arr, ctypes.c_uint64(len(images)), ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_decompress_batch", rc)
+    launch.keep = (arr, images, outs)
+    return launch
 
 
 def ibp_gather_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,

@@ -60,6 +60,27 @@ def _md(ibp, mask=0x7C000000, bitval=0x3C000000, w=32, p=None):
     return md
 
 
+def test_batch_validation_before_enqueue(ibp):
+    """ibp_decompress_batch checks every tensor before it enqueues anything."""
+    L = ibp.lib()
+    md = _md(ibp)
+    byref = ctypes.byref
+    fake = 0x10000  # never dereferenced
+    T = ibp.ibp_tensor
+    good = T(4, 4096, fake, fake, fake)
+    arr = (T * 3)(good, T(4, 4098, fake, fake, fake), good)       # row_bytes % 4
+    assert L.ibp_decompress_batch(byref(md), arr, 3, None) == ibp.IBP_ERR_LAYOUT
+    arr = (T * 2)(good, T(4, 4096, fake, None, fake))              # null flags
+    assert L.ibp_decompress_batch(byref(md), arr, 2, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    arr = (T * 2)(good, T(4, 4096, fake, fake + 4, fake))          # misaligned flags
+    assert L.ibp_decompress_batch(byref(md), arr, 2, None) == ibp.IBP_ERR_LAYOUT
+    assert L.ibp_decompress_batch(byref(md), None, 1, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_decompress_batch(None, arr, 1, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_decompress_batch(byref(md), None, 0, None) == ibp.IBP_OK
+    empty = (T * 1)(T(0, 4096, None, None, None))                 # empty tensors: no-op
+    assert L.ibp_decompress_batch(byref(md), empty, 1, None) == ibp.IBP_OK
+
+
 def test_validation_before_enqueue(ibp):
     L = ibp.lib()
     md = _md(ibp)

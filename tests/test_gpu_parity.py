@@ -814,6 +814,38 @@ def test_full_llm_kv(ibp):
     assert torch.equal(a, to_gpu(x)[idg])
 
 
+@pytest.mark.parametrize("n_tensors", [7, 19])
+def test_decompress_batch(ibp, n_tensors):
+    """One launch per 16 tensors of different shapes sharing the metadata:
+    rows of 2 and 7 segments, a ragged row (n = 1025), raw rows, a tensor of
+    one row; against ibp_decompress of each tensor, the source rows, and the
+    oracle on sampled rows."""
+    rng = np.random.default_rng(n_tensors)
+    mask, bitval = 0x78007800, 0x38003800
+    md = gmd(ibp, mask, bitval)
+    shapes = [(64, 8192), (40, 28672), (70, 4100), (1, 8192), (33, 4096), (50, 512), (9, 98304)]
+    images, srcs = [], []
+    for k in range(n_tensors):
+        n_rows, S = shapes[k % len(shapes)]
+        x = make_rows(rng, n_rows, S, mask, bitval, match_p=0.9,
+                      raw_rows=(0,) if n_rows > 2 else ())
+        xg = to_gpu(x)
+        slots, flags, _ = ibp.ibp_compress(md, xg)
+        images.append((slots, flags))
+        srcs.append((x, xg))
+    say(f"batch of {n_tensors} tensors")
+    outs = ibp.ibp_decompress_batch(md, images)
+    torch.cuda.synchronize()
+    for (slots, flags), (x, xg), out in zip(images, srcs, outs):
+        assert torch.equal(out, xg)
+        assert torch.equal(out, ibp.ibp_decompress(md, slots, flags))
+    x, _ = srcs[1]
+    slots_o, flags_o, _ = orc.compress(omd(md), x)
+    ids = np.arange(0, x.shape[0], 7)
+    want = orc.gather_decompress(omd(md), slots_o, flags_o, ids)
+    assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("layer", [0, 31])
 def test_full_llm_weights_layer(ibp, layer):
     """Every matrix of one layer at full size: compress, full decompress,
