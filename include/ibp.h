@@ -48,9 +48,12 @@
  * row ids 8-byte aligned; with W = 64 src, slots and dst 8-byte aligned too);
  * 16-byte aligned slots/src/dst with row_bytes a multiple of 16 enable
  * 16-byte memory operations (W = 32).
- * ibp_compress, ibp_decompress and ibp_gather_decompress only enqueue work on
- * `stream` (a hipStream_t, NULL = the null stream) and return at once; they
- * allocate nothing, copy nothing on the host and never synchronise.
+ * ibp_compress, ibp_decompress, ibp_decompress_batch and the gathers only
+ * enqueue work on `stream` (a hipStream_t, NULL = the null stream) and
+ * return at once; they allocate nothing, copy nothing on the host and never
+ * synchronise.  The W = 32 decodes ask HIP (hipPointerGetAttributes) whether
+ * `slots` is host memory, and then cut rows of 1024 or more blocks into
+ * smaller tasks, which suits the host link; the result is the same.
  * ibp_build_metadata is synchronous.  The library keeps no state between
  * calls apart from the last HIP error code of the calling thread and the
  * compute-unit count of the device (read once, to size launches).
