@@ -1359,12 +1359,17 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     }
     wave_lds_sync();
     uint32_t u = a - 32u * base;
-    for (uint32_t k0 = lo; k0 < hi; k0 += kWave) {
+    const int negp = -(int)cd.p;
+    const uint32_t wl = W * lane;
+    // one 64-block chunk: lane l restores block k0 + l; `ragged` only for the
+    // last chunk of a segment shorter than a whole number of chunks
+    auto chunk = [&](uint32_t k0, bool ragged) {
       const uint32_t q = (k0 - lo) / 32;
       const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
       const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-      const bool valid = k0 + lane < hi;
-      const uint32_t rel = valid ? u + W * lane - __umul24(cd.p, bits_below_lane(h_lo, h_hi)) : 0u;
+      const bool valid = !ragged || k0 + lane < hi;
+      const uint32_t rel =
+          valid ? (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + wl) : 0u;
       const T v = lds_payload<T>(lds, rel);
       const bool stripped =
           __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
@@ -1376,11 +1381,24 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
         const uint32_t nb = __builtin_amdgcn_mov_dpp((uint32_t)x, 0xB1, 0xF, 0xF, false);
         if (valid && !(lane & 1u))
           __builtin_nontemporal_store((uint32_t)x | (nb << 16),
-                                      reinterpret_cast<uint32_t*>(out) + (k0 + lane) / 2);
+                                      reinterpret_cast<uint32_t*>(out + k0) + lane / 2);
       } else {
         if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
       }
-      u += W * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+      u += W * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+    };
+    // a whole segment (the decode launch cuts rows into segments of 1024
+    // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter chunk
+    // by chunk
+    constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+    if (hi - lo == kFull && seg == kFull) {
+#pragma unroll
+      for (uint32_t c = 0; c < kFull / kWave; ++c) chunk(lo + c * kWave, false);
+    } else {
+      const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
+      uint32_t k0 = lo;
+      for (; k0 < full_hi; k0 += kWave) chunk(k0, false);
+      if (k0 < hi) chunk(k0, true);
     }
     wave_lds_sync();
   }
