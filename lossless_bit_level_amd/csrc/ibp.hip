@@ -683,15 +683,23 @@ __device__ __forceinline__ void decode_segment_task(
   // of the chunk below l) further on.
   uint32_t u = n + 32u * lo - cd.p * carry - 32u * base;
   const uint32_t l32 = lane * 32u;
-  const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
-  uint32_t k0 = lo;
-  for (; k0 < full_hi; k0 += kWave) {
+  const int negp = -(int)cd.p;
+  auto chunk = [&](uint32_t k0) {  // a whole 64-block chunk
     const uint32_t q = (k0 - lo) / 32;
     const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
     const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-    const uint32_t rel = u + l32 - __umul24(cd.p, bits_below_lane(h_lo, h_hi));
+    const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
     __builtin_nontemporal_store(decode_block<NR>(lds, rel, h_lo, h_hi, cd), out + k0 + lane);
-    u += 32u * kWave - cd.p * (__popc(h_lo) + __popc(h_hi));
+    u += 32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+  };
+  const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
+  uint32_t k0 = lo;
+  if (hi - lo == kSegBlocks) {  // a whole segment: unrolled
+#pragma unroll
+    for (uint32_t c = 0; c < kSegBlocks / kWave; ++c) chunk(lo + c * kWave);
+    k0 = hi;
+  } else {
+    for (; k0 < full_hi; k0 += kWave) chunk(k0);
   }
   if (k0 < hi) {  // ragged end of the row (n not a multiple of 64)
     const uint32_t q = (k0 - lo) / 32;
