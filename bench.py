@@ -247,6 +247,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks, width_bits=args.width)
+    meta_first_ms = (time.perf_counter() - t0) * 1e3   # includes the library's first-use setup
+    t0 = time.perf_counter()
+    md, _ = ibp.ibp_build_metadata(samp, n_blocks=n_blocks, width_bits=args.width)
     meta_ms = (time.perf_counter() - t0) * 1e3
     del samp
     pos_table = pmask = pbitval = None
@@ -558,7 +561,8 @@ def main():
             pos_table.numel() if pos_table is not None else 32)), 4),
         "metadata": {"mask": f"0x{md.mask:0{args.width // 4}X}",
                      "bitval": f"0x{md.bitval:0{args.width // 4}X}",
-                     "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3)},
+                     "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3),
+                     "first_call_ms": round(meta_first_ms, 3)},
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
                      "in_place_pinned_host": inplace},
         "kernel": {"name": decode_kernel_name(S, args.width, args.positional, md.invariant_bits,
