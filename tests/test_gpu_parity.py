@@ -855,6 +855,7 @@ def test_full_llm_weights_layer(ibp, layer):
     md, _ = ibp.ibp_build_metadata(to_gpu(w0), n_blocks=min(w0.size // 2, 1 << 24))
     assert (md.mask, md.bitval) == (0x78007800, 0x38003800)
     rng = np.random.default_rng(layer)
+    images, sources = [], []
     for j in range(syn.LLM_MATRICES):
         w = syn.llm_weight(layer, j)
         say(f"layer {layer} matrix {j} shape {w.shape}")
@@ -862,6 +863,8 @@ def test_full_llm_weights_layer(ibp, layer):
         slots, flags, rb = ibp.ibp_compress(md, wg)
         back = ibp.ibp_decompress(md, slots, flags)
         assert torch.equal(back, wg)
+        images.append((slots, flags))
+        sources.append(wg)
         fl = flags_np(flags, w.shape[0])
         rbn = rb.cpu().numpy()
         for r in np.concatenate([[0, w.shape[0] - 1], rng.integers(0, w.shape[0], 24)]):
@@ -870,6 +873,11 @@ def test_full_llm_weights_layer(ibp, layer):
             assert flag_of(fl, r) == f_o
             nb = orc.stored_bytes(w.shape[1] * 2, c_o, f_o)
             assert np.array_equal(slots[int(r), :nb].cpu().numpy(), s_o[:nb])
+    # the whole layer in one batched launch, as bench.py times it
+    outs = ibp.ibp_decompress_batch(md, images)
+    torch.cuda.synchronize()
+    for out, wg in zip(outs, sources):
+        assert torch.equal(out, wg)
 
 
 def test_full_sparse_gnn_cache_of_whole_table(ibp):
