@@ -285,6 +285,97 @@ def test_metadata_matches_distribution_configs(name):
     assert (md.mask, md.bitval) == expected
 
 
+def _match_prob(cdf_abs, mask_e, val_e, mant, bf16):
+    """P((v & mask_e) == val_e) for one float v whose |x| has CDF cdf_abs,
+    when mask_e covers exponent bits only: the sum of P(|v| in binade E)
+    over the exponent values E that agree with val_e under the mask.  For
+    bf16 values rounded from a continuous x (nearest, ties to even), |v|
+    reaches 2^k once |x| passes 2^k less half a bf16 step, 2^k (1 - 2^-9)."""
+    assert mask_e & ((1 << mant) - 1) == 0 and mask_e >> (mant + 8) == 0
+    adj = 1.0 - 2.0 ** -(mant + 2) if bf16 else 1.0
+    q = 0.0
+    for e in range(255):
+        if ((e << mant) & mask_e) != val_e:
+            continue
+        lo = 0.0 if e == 0 else 2.0 ** (e - 127) * adj
+        hi = 2.0 ** (e - 126) * adj
+        q += cdf_abs(hi) - cdf_abs(lo)
+    return q
+
+
+def _page_savings():
+    """tests/golden/page_savings.txt: class -> (low, high) percent."""
+    bands = {}
+    with open(os.path.join(ROOT, "tests", "golden", "page_savings.txt")) as f:
+        for line in f:
+            line = line.split("#", 1)[0].split()
+            if line:
+                bands[line[0]] = (float(line[1]), float(line[2]))
+    return bands
+
+
+@pytest.mark.parametrize("name", ["tiny_dense", "dense_gnn", "dlrm_emb", "llm_weights",
+                                  "llm_kv"])
+def test_savings_closed_form_and_page_bands(name):
+    """Space saved by the oracle's image against a number computed without
+    it.  Every row of these tables is stored compressed, so its stored bits
+    are n(1 + W) - p m: the saving is (p q - 1) / W, where q, the chance that
+    a block matches Bitval under Mask, follows from the distribution the
+    table is drawn from (for a bf16 block, both halves must match).  A lost
+    header bit or a wrong p moves the saving by 1/32 or more, ~100 sigma
+    here.  The result is then held to the savings the IBP page reports for
+    real data of the same kind (Results section), within 1.5 points: the
+    tables are synthetic stand-ins, not the page's datasets."""
+    from scipy.stats import norm
+    gauss = lambda s: (lambda a: 2 * norm.cdf(a / s) - 1)
+    if name == "tiny_dense":
+        x, cls = syn.tiny_dense(), "dense_fp32"
+        q_of = lambda m, v: _match_prob(gauss(0.1), m, v, 23, False)
+    elif name == "dense_gnn":
+        x, cls = syn.dense_gnn_rows(0, 4096), "dense_fp32"
+        q_of = lambda m, v: _match_prob(gauss(0.5), m, v, 23, False)
+    elif name == "dlrm_emb":
+        x, cls = syn.dlrm_emb_rows(0, 8192), "dlrm_fp32"
+        q_of = lambda m, v: _match_prob(lambda a: min(a / 0.05, 1.0), m, v, 23, False)
+    elif name == "llm_weights":
+        x, cls = syn.llm_weight(0, 0, rows=slice(0, 512)), "bf16_llm"
+
+        def q_of(m, v):
+            assert m >> 16 == m & 0xFFFF and v >> 16 == v & 0xFFFF
+            return _match_prob(gauss(0.02), m & 0xFFFF, v & 0xFFFF, 7, True) ** 2
+    else:
+        x, cls = syn.llm_kv_pages(batches=[0], seq=256), "bf16_llm"
+
+        def q_of(m, v):
+            assert m >> 16 == m & 0xFFFF and v >> 16 == v & 0xFFFF
+            q1 = _match_prob(gauss(1.0), m & 0xFFFF, v & 0xFFFF, 7, True)
+            q20 = _match_prob(gauss(20.0), m & 0xFFFF, v & 0xFFFF, 7, True)
+            # every head owns the same number of pages; block k of a page
+            # holds channels 2k and 2k + 1 (k mod 64) of one token
+            tot = 0.0
+            for ch in syn.kv_outlier_channels():
+                out = np.zeros(syn.KV_D, bool)
+                out[ch] = True
+                qc = np.where(out, q20, q1)
+                tot += float(np.mean(qc[0::2] * qc[1::2]))
+            return tot / syn.KV_H
+    w = 32
+    md, _ = orc.build_metadata(x, w, t=0.9)
+    p = md.invariant_bits
+    q = q_of(md.mask, md.bitval)
+    _, flags, row_bits = orc.compress(md, x)
+    rows = x.shape[0]
+    n = x.nbytes // rows * 8 // w
+    assert all(bool(int(flags[r >> 6]) >> (r & 63) & 1) for r in range(rows))
+    blocks = rows * n
+    saved = 1.0 - float(row_bits.astype(np.float64).sum()) / (blocks * w)
+    predicted = (p * q - 1.0) / w
+    sigma = p * (q * (1 - q) / blocks) ** 0.5 / w
+    assert abs(saved - predicted) < 5 * sigma + 1e-6, (saved, predicted, sigma)
+    lo, hi = _page_savings()[cls]
+    assert lo - 1.5 <= 100 * saved <= hi + 1.5, (name, 100 * saved, lo, hi)
+
+
 # ------------------------------------------------------- layout pins ----
 
 def _numpy_stream(x_rows_u8, w, mask, bitval):
