@@ -39,6 +39,12 @@ def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     return r.astype(np.uint16)
 
 
+def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to IEEE fp16 (numpy's conversion: nearest, ties to even,
+    subnormals kept, overflow to infinity); uint16 bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
 def _chunked(n_rows: int, row_start: int, row_count: int, make_chunk):
     """Rows [row_start, row_start+row_count) of a table built from 65,536-row
     chunks, chunk c drawn by make_chunk(c, rows_in_chunk)."""
@@ -145,14 +151,16 @@ def llm_weight_shape(j: int):
     return (LLM_HIDDEN, LLM_HIDDEN) if j < 4 else (LLM_HIDDEN, LLM_FFN)
 
 
-def llm_weight(layer: int, j: int, rows: slice | None = None) -> np.ndarray:
-    """Matrix j of one layer, bf16 bits (uint16) ~ N(0, 0.02^2)."""
+def llm_weight(layer: int, j: int, rows: slice | None = None,
+               fp16: bool = False) -> np.ndarray:
+    """Matrix j of one layer, bf16 bits (uint16) ~ N(0, 0.02^2); with fp16
+    the same draw rounded to IEEE fp16 instead."""
     shape = llm_weight_shape(j)
     rng = np.random.default_rng([0, layer, j])
     w = rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02)
     if rows is not None:
         w = w[rows]
-    return f32_to_bf16_bits(w)
+    return f32_to_fp16_bits(w) if fp16 else f32_to_bf16_bits(w)
 
 
 KV_B, KV_H, KV_S, KV_D = 16, 32, 4096, 128
@@ -166,23 +174,23 @@ def kv_outlier_channels() -> np.ndarray:
     return np.stack([rng.choice(KV_D, 4, replace=False) for _ in range(KV_H)])
 
 
-def llm_kv_batch(b: int, seq: int = KV_S) -> np.ndarray:
+def llm_kv_batch(b: int, seq: int = KV_S, fp16: bool = False) -> np.ndarray:
     """One batch entry of the KV cache: [32, seq, 128] bf16 bits (uint16).
 
     Values ~ N(0, 1); the 4 outlier channels of every head are scaled by 20
-    before rounding to bf16."""
+    before rounding to bf16 (to IEEE fp16 with fp16)."""
     rng = np.random.default_rng([0, b])
     x = rng.standard_normal((KV_H, seq, KV_D), dtype=np.float32)
     ch = kv_outlier_channels()
     for h in range(KV_H):
         x[h][:, ch[h]] *= np.float32(20.0)
-    return f32_to_bf16_bits(x)
+    return f32_to_fp16_bits(x) if fp16 else f32_to_bf16_bits(x)
 
 
-def llm_kv_pages(batches=range(KV_B), seq: int = KV_S) -> np.ndarray:
+def llm_kv_pages(batches=range(KV_B), seq: int = KV_S, fp16: bool = False) -> np.ndarray:
     """KV cache as pages: [n_pages, 16*128] uint16, page id
     (b*32 + h) * (seq/16) + t; each page is contiguous in [B, H, S, D]."""
-    parts = [llm_kv_batch(b, seq).reshape(-1, KV_PAGE_TOKENS * KV_D)
+    parts = [llm_kv_batch(b, seq, fp16).reshape(-1, KV_PAGE_TOKENS * KV_D)
              for b in batches]
     return np.concatenate(parts)
 

@@ -497,6 +497,41 @@ def test_full_llm_kv_width16(ibp):
     say(f"llm_kv W=16: mask {md.mask:04x} bitval {md.bitval:04x}")
 
 
+@pytest.mark.parametrize("name,w", [("llm_weights_fp16", 16), ("llm_weights_fp16", 32),
+                                    ("llm_kv_fp16", 16), ("llm_kv_fp16", 32)])
+def test_fp16_tables(ibp, name, w):
+    """IEEE fp16 tables (5 exponent bits): metadata, image and decode against
+    the oracle.  Weights ~ N(0, 0.02^2) keep only the top exponent bit of a
+    value invariant, so at W = 16 every row has C = nW exactly and stays
+    raw; the KV pages keep two bits per value."""
+    if name == "llm_weights_fp16":
+        x = syn.llm_weight(0, 4, rows=slice(0, 96), fp16=True)   # 28 KiB rows
+    else:
+        x = syn.llm_kv_pages(batches=[0], seq=256, fp16=True)    # 512 pages of 4 KiB
+    n_rows, S = x.shape[0], x.nbytes // x.shape[0]
+    say(f"fp16 {name} W={w} rows={n_rows} row_bytes={S}")
+    xg = to_gpu(x)
+    md, ones = ibp.ibp_build_metadata(xg, width_bits=w)
+    md_o, ones_o = orc.build_metadata(x, w)
+    assert np.array_equal(np.array(ones, np.uint64), ones_o)
+    assert (md.mask, md.bitval) == (md_o.mask, md_o.bitval)
+    slots, flags, rb = ibp.ibp_compress(md, xg)
+    torch.cuda.synchronize()
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    if name == "llm_weights_fp16" and w == 16:
+        assert md.invariant_bits == 1 and not flags_o.any()
+    else:
+        assert all(flag_of(flags_o, r) for r in range(n_rows))
+    assert torch.equal(ibp.ibp_decompress(md, slots, flags), xg)
+    ids = np.random.default_rng(n_rows + w).integers(0, n_rows, 2 * n_rows).astype(np.int64)
+    idg = torch.from_numpy(ids).cuda()
+    out = ibp.ibp_gather_decompress(md, slots, flags, idg)
+    torch.cuda.synchronize()
+    assert torch.equal(out, xg[idg])
+
+
 # --------------------------------------------------- per-position metadata --
 
 def _pm_from_np(mask, bitval):

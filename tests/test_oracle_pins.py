@@ -7,7 +7,8 @@ layout, so the oracle is pinned by:
   * brute force over every tiny input (width 4 metadata, width 8 codec);
   * hand-derived worked examples (derivations written out below);
   * closed forms: per-row size n + nW - p*m, the sparse-feature image, the
-    fp32/bf16 exponent-bit probabilities of the synthetic distributions;
+    fp32/bf16/fp16 exponent-bit probabilities of the synthetic
+    distributions and the space saved, (p q - 1)/W;
   * special cases that reduce to memcpy / fill / numpy bit packing;
   * round-trip identity on adversarial rows.
 All tests here run on the CPU.
@@ -215,11 +216,17 @@ def _binade_bit_prob(cdf_abs, exp_bits, mant_bits, bit, bias):
     return tot
 
 
-def _predicted_mask(cdf_abs, w_field, t=0.9, n=None):
+# (exponent bits, mantissa bits, bias) of the float formats
+_FMT = {"f32": (8, 23, 127), "bf16": (8, 7, 127), "f16": (5, 10, 15)}
+
+
+def _predicted_mask(cdf_abs, w_field, t=0.9, n=None, fmt=None):
     """Predicted Mask/Bitval for the sign+exponent bits of fp32 (w_field=32)
-    or of each bf16 half (w_field=16), plus the bits whose majority margin
-    is too close to T to predict with n samples."""
-    exp_bits, mant, bias = (8, 23, 127) if w_field == 32 else (8, 7, 127)
+    or of each bf16 half (w_field=16; fmt="f16" for IEEE fp16 halves), plus
+    the bits whose majority margin is too close to T to predict with n
+    samples."""
+    fmt = fmt or ("f32" if w_field == 32 else "bf16")
+    exp_bits, mant, bias = _FMT[fmt]
     mask = val = 0
     unsure = 0
     for j in range(exp_bits):
@@ -252,12 +259,23 @@ def test_metadata_matches_distribution_tiny_dense():
     assert abs(ones[26] / n - p26) < 5 * sig
 
 
-@pytest.mark.parametrize("name", ["dense_gnn", "dlrm_emb", "llm_weights", "llm_kv"])
+@pytest.mark.parametrize("name", ["dense_gnn", "dlrm_emb", "llm_weights", "llm_kv",
+                                  "llm_weights_fp16", "llm_kv_fp16"])
 def test_metadata_matches_distribution_configs(name):
     """Predicted Mask/Bitval of the other synthetic workloads from their
-    CDFs, on a 2^20-block sample (first rows in storage order)."""
+    CDFs, on a 2^20-block sample (first rows in storage order).  Stored as
+    IEEE fp16 (5 exponent bits, bias 15), the weights keep only the top
+    exponent bit invariant (0: |x| < 2), the KV values also the next one."""
     from scipy.stats import norm
-    if name == "dense_gnn":
+    fmt = "f16" if name.endswith("_fp16") else None
+    if name == "llm_weights_fp16":
+        x, w = syn.llm_weight(0, 0, rows=slice(0, 512), fp16=True), 16
+        cdf = lambda a: 2 * norm.cdf(a / 0.02) - 1
+    elif name == "llm_kv_fp16":
+        x, w = syn.llm_kv_batch(0, seq=256, fp16=True).reshape(-1), 16
+        f = 4 / 128
+        cdf = lambda a: (1 - f) * (2 * norm.cdf(a) - 1) + f * (2 * norm.cdf(a / 20) - 1)
+    elif name == "dense_gnn":
         x, w = syn.dense_gnn_rows(0, 4096), 32
         cdf = lambda a: 2 * norm.cdf(a / 0.5) - 1
     elif name == "dlrm_emb":
@@ -272,8 +290,8 @@ def test_metadata_matches_distribution_configs(name):
         cdf = lambda a: (1 - f) * (2 * norm.cdf(a) - 1) + f * (2 * norm.cdf(a / 20) - 1)
     md, _ = orc.build_metadata(x, 32, t=0.9)
     n = x.nbytes // 4
-    mask, val, unsure = _predicted_mask(cdf, w, n=n)
-    if w == 16:  # both bf16 halves of a 32-bit block share the prediction
+    mask, val, unsure = _predicted_mask(cdf, w, n=n, fmt=fmt)
+    if w == 16:  # both 16-bit halves of a 32-bit block share the prediction
         mask, val, unsure = (mask | mask << 16, val | val << 16,
                              unsure | unsure << 16)
     assert unsure == 0
@@ -281,24 +299,28 @@ def test_metadata_matches_distribution_configs(name):
     expected = {"dense_gnn": (0x7C000000, 0x3C000000),
                 "dlrm_emb": (0x78000000, 0x38000000),
                 "llm_weights": (0x78007800, 0x38003800),
-                "llm_kv": (0x7C007C00, 0x3C003C00)}[name]
+                "llm_kv": (0x7C007C00, 0x3C003C00),
+                "llm_weights_fp16": (0x40004000, 0x00000000),
+                "llm_kv_fp16": (0x60006000, 0x20002000)}[name]
     assert (md.mask, md.bitval) == expected
 
 
-def _match_prob(cdf_abs, mask_e, val_e, mant, bf16):
+def _match_prob(cdf_abs, mask_e, val_e, fmt, rounded):
     """P((v & mask_e) == val_e) for one float v whose |x| has CDF cdf_abs,
     when mask_e covers exponent bits only: the sum of P(|v| in binade E)
-    over the exponent values E that agree with val_e under the mask.  For
-    bf16 values rounded from a continuous x (nearest, ties to even), |v|
-    reaches 2^k once |x| passes 2^k less half a bf16 step, 2^k (1 - 2^-9)."""
-    assert mask_e & ((1 << mant) - 1) == 0 and mask_e >> (mant + 8) == 0
-    adj = 1.0 - 2.0 ** -(mant + 2) if bf16 else 1.0
+    over the exponent values E that agree with val_e under the mask (E = 0:
+    zero and subnormals).  For 16-bit values rounded from a continuous x
+    (nearest, ties to even), |v| reaches 2^k once |x| passes 2^k less half
+    a step, 2^k (1 - 2^-(mantissa bits + 2))."""
+    exp_bits, mant, bias = _FMT[fmt]
+    assert mask_e & ((1 << mant) - 1) == 0 and mask_e >> (mant + exp_bits) == 0
+    adj = 1.0 - 2.0 ** -(mant + 2) if rounded else 1.0
     q = 0.0
-    for e in range(255):
+    for e in range((1 << exp_bits) - 1):
         if ((e << mant) & mask_e) != val_e:
             continue
-        lo = 0.0 if e == 0 else 2.0 ** (e - 127) * adj
-        hi = 2.0 ** (e - 126) * adj
+        lo = 0.0 if e == 0 else 2.0 ** (e - bias) * adj
+        hi = 2.0 ** (e + 1 - bias) * adj
         q += cdf_abs(hi) - cdf_abs(lo)
     return q
 
@@ -314,9 +336,11 @@ def _page_savings():
     return bands
 
 
-@pytest.mark.parametrize("name", ["tiny_dense", "dense_gnn", "dlrm_emb", "llm_weights",
-                                  "llm_kv"])
-def test_savings_closed_form_and_page_bands(name):
+@pytest.mark.parametrize("name,w", [("tiny_dense", 32), ("dense_gnn", 32), ("dlrm_emb", 32),
+                                    ("llm_weights", 32), ("llm_kv", 32),
+                                    ("llm_weights_fp16", 32), ("llm_kv_fp16", 32),
+                                    ("llm_kv_fp16", 16)])
+def test_savings_closed_form_and_page_bands(name, w):
     """Space saved by the oracle's image against a number computed without
     it.  Every row of these tables is stored compressed, so its stored bits
     are n(1 + W) - p m: the saving is (p q - 1) / W, where q, the chance that
@@ -325,41 +349,53 @@ def test_savings_closed_form_and_page_bands(name):
     header bit or a wrong p moves the saving by 1/32 or more, ~100 sigma
     here.  The result is then held to the savings the IBP page reports for
     real data of the same kind (Results section), within 1.5 points: the
-    tables are synthetic stand-ins, not the page's datasets."""
+    tables are synthetic stand-ins, not the page's datasets.  The page gives
+    no figure for fp16 tables, which are held to the closed form only."""
     from scipy.stats import norm
     gauss = lambda s: (lambda a: 2 * norm.cdf(a / s) - 1)
+    fp16 = name.endswith("_fp16")
+    fmt16 = "f16" if fp16 else "bf16"
+
+    def pair(q_elem):
+        """Per 32-bit block of two 16-bit values: both must match (at W =
+        16 a block is one value)."""
+        def q_of(m, v):
+            if w == 16:
+                return q_elem(m, v)
+            assert m >> 16 == m & 0xFFFF and v >> 16 == v & 0xFFFF
+            return q_elem(m & 0xFFFF, v & 0xFFFF) ** 2
+        return q_of
+
     if name == "tiny_dense":
         x, cls = syn.tiny_dense(), "dense_fp32"
-        q_of = lambda m, v: _match_prob(gauss(0.1), m, v, 23, False)
+        q_of = lambda m, v: _match_prob(gauss(0.1), m, v, "f32", False)
     elif name == "dense_gnn":
         x, cls = syn.dense_gnn_rows(0, 4096), "dense_fp32"
-        q_of = lambda m, v: _match_prob(gauss(0.5), m, v, 23, False)
+        q_of = lambda m, v: _match_prob(gauss(0.5), m, v, "f32", False)
     elif name == "dlrm_emb":
         x, cls = syn.dlrm_emb_rows(0, 8192), "dlrm_fp32"
-        q_of = lambda m, v: _match_prob(lambda a: min(a / 0.05, 1.0), m, v, 23, False)
-    elif name == "llm_weights":
-        x, cls = syn.llm_weight(0, 0, rows=slice(0, 512)), "bf16_llm"
-
-        def q_of(m, v):
-            assert m >> 16 == m & 0xFFFF and v >> 16 == v & 0xFFFF
-            return _match_prob(gauss(0.02), m & 0xFFFF, v & 0xFFFF, 7, True) ** 2
+        q_of = lambda m, v: _match_prob(lambda a: min(a / 0.05, 1.0), m, v, "f32", False)
+    elif name.startswith("llm_weights"):
+        x, cls = syn.llm_weight(0, 0, rows=slice(0, 512), fp16=fp16), "bf16_llm"
+        q_of = pair(lambda m, v: _match_prob(gauss(0.02), m, v, fmt16, True))
     else:
-        x, cls = syn.llm_kv_pages(batches=[0], seq=256), "bf16_llm"
+        x, cls = syn.llm_kv_pages(batches=[0], seq=256, fp16=fp16), "bf16_llm"
 
         def q_of(m, v):
-            assert m >> 16 == m & 0xFFFF and v >> 16 == v & 0xFFFF
-            q1 = _match_prob(gauss(1.0), m & 0xFFFF, v & 0xFFFF, 7, True)
-            q20 = _match_prob(gauss(20.0), m & 0xFFFF, v & 0xFFFF, 7, True)
-            # every head owns the same number of pages; block k of a page
-            # holds channels 2k and 2k + 1 (k mod 64) of one token
+            halves = [(m, v)] if w == 16 else [(m >> 16, v >> 16), (m & 0xFFFF, v & 0xFFFF)]
+            assert all(h == halves[0] for h in halves)
+            q1 = _match_prob(gauss(1.0), *halves[0], fmt16, True)
+            q20 = _match_prob(gauss(20.0), *halves[0], fmt16, True)
+            # every head owns the same number of pages; a 32-bit block of a
+            # page holds channels 2k and 2k + 1 of one token, a 16-bit one
+            # a single channel
             tot = 0.0
             for ch in syn.kv_outlier_channels():
                 out = np.zeros(syn.KV_D, bool)
                 out[ch] = True
                 qc = np.where(out, q20, q1)
-                tot += float(np.mean(qc[0::2] * qc[1::2]))
+                tot += float(np.mean(qc if w == 16 else qc[0::2] * qc[1::2]))
             return tot / syn.KV_H
-    w = 32
     md, _ = orc.build_metadata(x, w, t=0.9)
     p = md.invariant_bits
     q = q_of(md.mask, md.bitval)
@@ -372,8 +408,9 @@ def test_savings_closed_form_and_page_bands(name):
     predicted = (p * q - 1.0) / w
     sigma = p * (q * (1 - q) / blocks) ** 0.5 / w
     assert abs(saved - predicted) < 5 * sigma + 1e-6, (saved, predicted, sigma)
-    lo, hi = _page_savings()[cls]
-    assert lo - 1.5 <= 100 * saved <= hi + 1.5, (name, 100 * saved, lo, hi)
+    if not fp16:
+        lo, hi = _page_savings()[cls]
+        assert lo - 1.5 <= 100 * saved <= hi + 1.5, (name, 100 * saved, lo, hi)
 
 
 # ------------------------------------------------------- layout pins ----
