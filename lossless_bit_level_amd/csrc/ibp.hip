@@ -988,9 +988,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
 // whose range is the row's stream, and every iteration issues the same
 // vector memory instructions (one window load, RV stream loads, NCH stores),
 // so the waits at the top of an iteration leave the previous row's stores in
-// flight.  Ids and flag words are scalar loads, one clamped id per row (slot
-// 0 stands in for a row outside the table, so every address is in bounds).
-// A wave takes rows i, i + stride, ...; ids past the table give zero rows.
+// flight.  Ids and flag words are loaded per group of 64 rows, one lane per
+// row, with one clamped id per row (slot 0 stands in for a row outside the
+// table, so every address is in bounds).  A wave takes rows i, i + stride,
+// ...; ids past the table give zero rows.  Launches size the grid so that a
+// wave has at most 64 rows: a further group restarts the pipeline.
 //   stream_words(win): words of a compressed row's stream, from its window
 //   decode(win, x):    the row's n words from the LDS window, x[c] = word
 //                      c * 64 + lane (every lane of the wave calls it)
@@ -1017,89 +1019,111 @@ __device__ __forceinline__ void run_row_pipeline(
   constexpr int RV = P::RV;
   const uint32_t lane = lane_id();
   u32x4* l4 = reinterpret_cast<u32x4*>(lds);
-  struct Row {
-    const uint32_t* src;
-    bool ok;                // a row of the table
-    unsigned long long fw;  // its flag word
-    uint32_t bit;           // id & 63
-  };
-  auto id_of = [&](uint32_t r) -> uint64_t {
-    return GATHER ? (uint64_t)ids[min(r, n_out - 1)] : (uint64_t)r;
-  };
-  // row r with id `id`: slot, flag word (scalar load) and window (buffer load)
-  auto open_row = [&](uint32_t r, uint64_t id, uint32_t& win) -> Row {
-    const bool ok = r < n_out && id < n_rows;
-    const uint64_t idc = ok ? id : 0ull;
-    Row w{slots + idc * n, ok, flags[idc >> 6], (uint32_t)idc & 63u};
-    win = __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(w.src, ok ? kWin * 4 : 0u), lane * 4,
-                                               0, 0);
-    return w;
-  };
-  auto flagged = [&](const Row& w) { return w.ok && ((w.fw >> w.bit) & 1ull); };
-  // words of the row's stored form: the stream for a compressed row, the
-  // whole slot for a raw one, nothing for a row outside the table
-  auto stored = [&](const Row& w, uint32_t win) -> uint32_t {
-    if (!w.ok) return 0u;
-    if (!flagged(w)) return n;
-    return min(stream_words(win), n);
-  };
-  auto load_rest = [&](const Row& w, uint32_t words, u32x4* r) {
-    const __amdgpu_buffer_rsrc_t rs = row_rsrc(w.src, ((words + 3u) & ~3u) * 4u);
-#pragma unroll
-    for (int c = 0; c < RV; ++c)
-      r[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
-  };
 
-  // prologue: windows of rows 0 and 1, the stream of row 0, the id of row 2
-  uint32_t win0, win1;
-  Row w0 = open_row(i, id_of(i), win0);
-  Row w1 = open_row(i + stride, id_of(i + stride), win1);
-  uint64_t id2 = id_of(i + 2 * stride);
-  u32x4 rest0[RV];
-  load_rest(w0, stored(w0, win0), rest0);
-  // wait for all of it here: at the loop top the compiler merges this state
-  // with the back edge's, where the previous row's stores are still pending
-  asm volatile("" ::"v"(win1));
-#pragma unroll
-  for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
+  // The wave's rows are i + k * stride, k = 0, 1, ..., taken in groups of up
+  // to 64.  Their bookkeeping is vector work done once per group: lane k
+  // loads row k's id and flag word and forms its slot address; two ballots
+  // hold "in the table" and "stored compressed" for the group.  Per row the
+  // scalar unit then only reads the address out of two lanes and tests a bit
+  // (rows of 512 bytes are otherwise bound by the CU's one scalar unit).
+  for (uint32_t g = i; g < n_out;) {
+    const uint32_t K = (uint32_t)min<uint64_t>(kWave, ((uint64_t)n_out - g + stride - 1) / stride);
+    const uint64_t r = (uint64_t)g + (uint64_t)lane * stride;
+    const bool in = lane < K;
+    const uint64_t id = in ? (GATHER ? (uint64_t)ids[r] : r) : 0ull;
+    const bool ok = in && id < n_rows;
+    const uint64_t idc = ok ? id : 0ull;  // slot 0 stands in for a row outside the table
+    const unsigned long long fw = flags[idc >> 6];
+    const uint64_t src_v = reinterpret_cast<uint64_t>(slots + idc * n);
+    // bit j: row k + j of the group is in the table / stored compressed;
+    // shifted down by one row per iteration, so that every test below is of
+    // a fixed bit
+    unsigned long long ok_m = __ballot(ok);
+    unsigned long long fl_m = __ballot(ok && ((fw >> (idc & 63u)) & 1ull));
 
-  while (true) {
-    // (1) row 0's stream has arrived: stage it in the wave's LDS window (the
-    //     window's lanes 32-63 are zeros that the stream units overwrite)
-    lds[lane] = win0;
+    auto src_of = [&](uint32_t k) -> const uint32_t* {
+      const uint32_t kk = min(k, (uint32_t)kWave - 1u);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)src_v, kk);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(src_v >> 32), kk);
+      return reinterpret_cast<const uint32_t*>(((uint64_t)hi << 32) | lo);
+    };
+    auto ok_of = [&](int j) { return ((uint32_t)ok_m >> j) & 1u; };
+    auto fl_of = [&](int j) { return ((uint32_t)fl_m >> j) & 1u; };
+    // window (first 32 words) of row k + j: a buffer load, empty past the group
+    auto window = [&](int j, const uint32_t* src) -> uint32_t {
+      return __builtin_amdgcn_raw_buffer_load_b32(row_rsrc(src, ok_of(j) ? kWin * 4 : 0u),
+                                                  lane * 4, 0, 0);
+    };
+    // words of row k + j's stored form: the stream for a compressed row, the
+    // whole slot for a raw one, nothing for a row outside the table
+    auto stored = [&](int j, uint32_t win) -> uint32_t {
+      if (!ok_of(j)) return 0u;
+      if (!fl_of(j)) return n;
+      return min(stream_words(win), n);
+    };
+    auto load_rest = [&](const uint32_t* src, uint32_t words, u32x4* rr) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, ((words + 3u) & ~3u) * 4u);
 #pragma unroll
-    for (int c = 0; c < RV; ++c) l4[kWin / 4 + c * kWave + lane] = rest0[c];
-    wave_lds_sync();
-    // (2) row 1: its header gives its stream length; the rest of its stream
-    //     goes in flight now
-    u32x4 rest1[RV];
-    load_rest(w1, stored(w1, win1), rest1);
-    // (3) window and flag word of row 2, id of row 3
-    uint32_t win2;
-    const Row w2 = open_row(i + 2 * stride, id2, win2);
-    const uint64_t id3 = id_of(i + 3 * stride);
-    // (4) decode row 0: exactly NCH stores on every path
-    uint32_t x[NCH];
-    if (!w0.ok) {
+      for (int c = 0; c < RV; ++c)
+        rr[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
+    };
+
+    // prologue: windows of rows 0 and 1, the stream of row 0
+    const uint32_t* src0 = src_of(0);
+    const uint32_t* src1 = src_of(1);
+    uint32_t win0 = window(0, src0);
+    uint32_t win1 = window(1, src1);
+    u32x4 rest0[RV];
+    load_rest(src0, stored(0, win0), rest0);
+    // wait for all of it here: at the loop top the compiler merges this state
+    // with the back edge's, where the previous row's stores are still pending
+    asm volatile("" ::"v"(win1));
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) x[c] = 0u;
-    } else if (!flagged(w0)) {
+    for (int c = 0; c < RV; ++c) asm volatile("" ::"v"(rest0[c]));
+
+    uint32_t* out = dst + (uint64_t)g * n;
+    const uint64_t out_step = (uint64_t)stride * n;
+    for (uint32_t k = 0;;) {
+      // (1) row k's stream has arrived: stage it in the wave's LDS window
+      //     (the window's lanes 32-63 are zeros that the stream units
+      //     overwrite)
+      lds[lane] = win0;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
-    } else {
-      decode(win0, x);
+      for (int c = 0; c < RV; ++c) l4[kWin / 4 + c * kWave + lane] = rest0[c];
+      wave_lds_sync();
+      // (2) row k+1: its header gives its stream length; the rest of its
+      //     stream goes in flight now
+      u32x4 rest1[RV];
+      load_rest(src1, stored(1, win1), rest1);
+      // (3) window of row k+2
+      const uint32_t* src2 = src_of(k + 2);
+      const uint32_t win2 = window(2, src2);
+      // (4) decode row k: exactly NCH stores on every path
+      uint32_t x[NCH];
+      if (!ok_of(0)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = 0u;
+      } else if (!fl_of(0)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+      } else {
+        decode(win0, x);
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+      __builtin_amdgcn_sched_barrier(0);
+      wave_lds_sync();
+      if (++k >= K) break;
+      ok_m >>= 1;
+      fl_m >>= 1;
+      out += out_step;
+      win0 = win1;
+      for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
+      src1 = src2;
+      win1 = win2;
     }
-    uint32_t* out = dst + (uint64_t)i * n;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
-    __builtin_amdgcn_sched_barrier(0);
-    wave_lds_sync();
-    i += stride;
-    if (i >= n_out) break;
-    w0 = w1; win0 = win1;
-    for (int c = 0; c < RV; ++c) rest0[c] = rest1[c];
-    w1 = w2; win1 = win2;
-    id2 = id3;
+    if ((uint64_t)g + (uint64_t)kWave * stride >= n_out) break;
+    g += kWave * stride;
   }
 }
 
@@ -2144,6 +2168,17 @@ uint32_t workgroups_per_device(uint32_t mult) {
   return mult * (uint32_t)g_cu_count;
 }
 
+// Grid of a row-pipeline launch over `rows` rows: as many workgroups of `wpb`
+// waves as stay resident (`per_cu` per CU), but enough that no wave has more
+// than 64 rows (one group of row bookkeeping), and no more than one row per
+// wave.
+uint32_t row_pipe_grid(uint32_t rows, uint32_t wpb, uint32_t per_cu) {
+  const uint64_t one_per_wave = (rows + wpb - 1) / wpb;
+  const uint64_t groups = (rows + 64ull * wpb - 1) / (64ull * wpb);
+  return (uint32_t)std::min<uint64_t>(
+      one_per_wave, std::max<uint64_t>(groups, workgroups_per_device(per_cu)));
+}
+
 template <int NR, uint32_t MAXW>
 void launch_compress_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
                        uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
@@ -2254,8 +2289,7 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
       // decode_rows_kernel on a larger grid is as fast or faster)
       if constexpr (MODE != kModeCached && NR != 0) {
         if (a.vec && (cd.n == 128 || cd.n == 256 || cd.n == 512)) {
-          const uint32_t pipe_grid =
-              (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(8));
+          const uint32_t pipe_grid = row_pipe_grid(cnt, kWavesPerBlock, 8);
           switch (cd.n) {
             case 128: IBP_PIPE(2); break;
             case 256: IBP_PIPE(4); break;
@@ -2955,9 +2989,7 @@ static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_by
       // workgroups of 4 waves (8 for 4 KiB rows, whose 32 KiB table is then
       // shared by more waves); as many as stay resident
 #define IBP_PP(G, NCH, WPB, PER_CU)                                                             \
-  hipLaunchKernelGGL((decode_pos_pipe_kernel<G, NCH, WPB>),                                     \
-                     dim3((uint32_t)std::min<uint64_t>((cnt + WPB - 1) / WPB,                  \
-                                                       workgroups_per_device(PER_CU))),        \
+  hipLaunchKernelGGL((decode_pos_pipe_kernel<G, NCH, WPB>), dim3(row_pipe_grid(cnt, WPB, PER_CU)), \
                      dim3(WPB * kWave), 0, st, (const PosEntry*)table, sl, fl, id_p,           \
                      gather ? n_rows : (uint64_t)cnt, cnt, out_p)
 #define IBP_PP_N(G)                                         \
