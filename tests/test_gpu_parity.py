@@ -610,6 +610,53 @@ def test_positional_codec_parity(ibp, case):
         assert flags_o.any()
 
 
+@pytest.mark.parametrize("row_bytes", [512, 1024, 2048, 4096])
+@pytest.mark.parametrize("mask,bitval", [(0x7C000000, 0x3C000000), (0x78007800, 0x38003800),
+                                         (0xFFFFFFFF, 0x00000000), (0xFFFFFFFF, 0x3F800000)])
+def test_positional_uniform_table(ibp, row_bytes, mask, bitval):
+    """A position table whose entries are all one (Mask, Bitval): the image
+    is the global one byte for byte (the decoder then uses its uniform-table
+    paths), and a table with a single position changed takes the general
+    path; both decode to the source, through gathers with many rows per
+    wave and ids outside the table."""
+    rng = np.random.default_rng(row_bytes + mask % 997 + bitval % 991)
+    n = row_bytes // 4
+    n_rows = 600
+    x = make_rows(rng, n_rows, row_bytes, mask, bitval, 0.9, raw_rows=(3,)).view(np.uint32)
+    ids = rng.integers(0, n_rows, 20_000).astype(np.int64)
+    ids[:2] = [-1, n_rows]
+    inside = (ids >= 0) & (ids < n_rows)
+    want = np.zeros((ids.size, row_bytes), np.uint8)
+    want[inside] = x[ids[inside]].view(np.uint8)
+    xg = to_gpu(x)
+    md = gmd(ibp, mask, bitval)
+    g_slots, g_flags, g_rb = ibp.ibp_compress(md, xg)
+    for changed in (False, True):
+        m = np.full(n, mask, np.uint64)
+        b = np.full(n, bitval, np.uint64)
+        if changed:
+            m[n // 2 + 1] = 0x7F800000
+            b[n // 2 + 1] = 0x3F800000
+        say(f"positional uniform table row_bytes={row_bytes} mask={mask:08x} changed={changed}")
+        table = ibp.ibp_positional_table(m, b).cuda()
+        slots, flags, rb = ibp.ibp_compress_positional(table, xg)
+        torch.cuda.synchronize()
+        slots_o, flags_o, rb_o = orc.compress_positional(_pm_from_np(m, b), x)
+        assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                           rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+        if not changed:
+            assert torch.equal(flags, g_flags) and torch.equal(rb, g_rb)
+            assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                               rb.cpu().numpy()[:n_rows].view(np.uint32),
+                               g_slots.cpu().numpy(), flags_np(g_flags, n_rows),
+                               g_rb.cpu().numpy()[:n_rows].astype(np.uint64))
+        assert torch.equal(ibp.ibp_decompress_positional(table, slots, flags), xg)
+        out = ibp.ibp_gather_decompress_positional(table, slots, flags,
+                                                   torch.from_numpy(ids).cuda())
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want)
+
+
 @pytest.mark.parametrize("row_bytes,n_ids", [(512, 60_000), (1024, 60_000), (2048, 40_000),
                                                (4096, 40_000)])
 def test_positional_gather_many_rows_per_wave(ibp, row_bytes, n_ids):
