@@ -862,6 +862,34 @@ def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     return md, slots, flags
 
 
+def test_largest_decode_row(ibp):
+    """Rows of the largest size the decoders take, 64 MiB (2^24 blocks, bit
+    offsets below 2^29): one stored compressed, one raw, imaged by the oracle
+    (the library's compressor takes rows up to 96 KiB), decoded in full and
+    gathered, with an id outside the table giving a zero row."""
+    S = 1 << 26
+    n = S // 4
+    mask, bitval = 0x7C000000, 0x3C000000
+    rng = np.random.default_rng(3)
+    x = rng.integers(0, 2**32, (2, n), dtype=np.uint32)
+    force = rng.random(x.shape, dtype=np.float32) < 0.9
+    x = np.where(force, (x & np.uint32(~mask & 0xFFFFFFFF)) | np.uint32(bitval), x).astype(np.uint32)
+    x[1] = rng.integers(0, 2**32, n, dtype=np.uint32)
+    md = gmd(ibp, mask, bitval)
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    assert [flag_of(flags_o, r) for r in (0, 1)] == [1, 0]
+    say(f"largest row: {S} bytes, C = {int(rb_o[0])} bits")
+    slots = torch.from_numpy(slots_o).cuda()
+    flags = torch.from_numpy(flags_o.view(np.int64).copy()).cuda()
+    xg = to_gpu(x)
+    assert torch.equal(ibp.ibp_decompress(md, slots, flags), xg)
+    ids = torch.tensor([1, 0, 2, 0], dtype=torch.int64, device="cuda")
+    out = ibp.ibp_gather_decompress(md, slots, flags, ids)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], xg[1]) and torch.equal(out[1], xg[0])
+    assert torch.equal(out[3], xg[0]) and not bool(out[2].any())
+
+
 def test_full_sparse_gnn(ibp):
     x = syn.sparse_gnn_rows()
     ids = syn.uniform_ids(syn.SPARSE_GNN_ROWS, 8, 65536)
