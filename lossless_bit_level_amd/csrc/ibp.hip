@@ -185,6 +185,12 @@ __device__ __forceinline__ uint32_t lds_bits(const uint32_t* lds, uint32_t rel) 
   return __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], rel & 31u);
 }
 
+// v_bitop3 with truth table 0xE4 is a bitwise select, S2 ? S0 : S1 (one
+// instruction, whether the mask sits in a vector or a scalar register).
+__device__ __forceinline__ uint32_t select_bits(uint32_t mask, uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_bitop3_b32(a, b, mask, 0xE4);
+}
+
 template <int NR>
 __device__ __forceinline__ uint32_t decode_block(const uint32_t* lds, uint32_t rel,
                                                  uint32_t h_lo, uint32_t h_hi,
@@ -1392,6 +1398,65 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     wave_lds_sync();
     uint32_t u = a - 32u * base;
     const int negp = -(int)cd.p;
+    // a whole segment (the decode launch cuts rows into segments of 1024
+    // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter step
+    // by step
+    constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+    if constexpr (sizeof(T) == 2) {
+      // Two blocks per lane: lane l restores blocks k0 + 2l and k0 + 2l + 1
+      // of a 128-block step and stores them as one word.  Their header bits
+      // are bits 2(l mod 16) and 2(l mod 16) + 1 of header word q + l/16;
+      // two ballots (first / second block of a pair stripped) give the
+      // stripped blocks before the pair through v_mbcnt.  Both payloads lie
+      // in the 32 stream bits at the pair's offset (16 - p or 16 bits each),
+      // and one deposit over the packed pair, with the run masks repeated in
+      // both halves, restores both blocks' invariant bits: run j moves bits
+      // up by shift_j, and a half's bits never reach the other half's places
+      // (the lowest upper-half place of run j is bit 16 + shift_j + its
+      // source bit), so a raw half or the bits past a payload cannot leak.
+      const uint32_t bv2 = (uint32_t)cd.bitval * 0x10001u;
+      const uint32_t sh = 2u * (lane & 15u);
+      const uint32_t hsel = 4u * (lane >> 4);
+      const uint32_t l32 = 32u * lane;
+      uint32_t* out_w = reinterpret_cast<uint32_t*>(out);
+      auto pair = [&](uint32_t k0, bool ragged) {
+        // the lane's header word, q + l/16, from the lane of hw holding it
+        const uint32_t q = (k0 - lo) / 32;
+        const uint32_t hs = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * q + hsel), (int)hw);
+        const uint32_t b2 = __builtin_amdgcn_ubfe(hs, sh, 2);
+        const bool s0 = (b2 & 1u) != 0u, s1 = b2 > 1u;
+        const unsigned long long e = __ballot(s0), o = __ballot(s1);
+        const bool valid = !ragged || k0 + 2u * lane < hi;
+        const uint32_t below = bits_below_lane_acc((uint32_t)o, (uint32_t)(o >> 32),
+                                                   bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
+        const uint32_t rel = valid ? (uint32_t)__mul24(negp, (int)below) + (u + l32) : 0u;
+        const uint32_t v = lds_bits(lds, rel);
+        const uint32_t l0 = s0 ? 16u - cd.p : 16u;
+        const uint32_t y = (v & 0xFFFFu) | ((v >> l0) << 16);
+        uint32_t dep = bv2;
+        if constexpr (NR >= 0) {
+#pragma unroll
+          for (int j = 0; j < NR; ++j) dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
+        } else {
+          for (uint32_t j = 0; j < cd.nruns; ++j)
+            dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
+        }
+        const uint32_t sel = (s0 ? 0x0000FFFFu : 0u) | (s1 ? 0xFFFF0000u : 0u);
+        if (valid) __builtin_nontemporal_store(select_bits(sel, dep, y), out_w + k0 / 2 + lane);
+        u += 16u * 2u * kWave - cd.p * (uint32_t)(__popcll(e) + __popcll(o));
+      };
+      if (hi - lo == kFull && seg == kFull) {
+#pragma unroll
+        for (uint32_t c = 0; c < kFull / (2 * kWave); ++c) pair(lo + c * 2 * kWave, false);
+      } else {
+        const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(2 * kWave - 1));
+        uint32_t k0 = lo;
+        for (; k0 < full_hi; k0 += 2 * kWave) pair(k0, false);
+        if (k0 < hi) pair(k0, true);
+      }
+      wave_lds_sync();
+      continue;
+    }
     const uint32_t wl = W * lane;
     // one 64-block chunk: lane l restores block k0 + l; `ragged` only for the
     // last chunk of a segment shorter than a whole number of chunks
@@ -1406,23 +1471,9 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
       const bool stripped =
           __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
       const T x = stripped ? deposit_wide<T, NR>(v, cd) : v;
-      if constexpr (sizeof(T) == 2) {
-        // an even lane takes its odd neighbour's block (DPP quad_perm 1,0,3,2)
-        // and stores the pair as one word; rows and segments hold an even
-        // number of blocks, so both blocks of a pair are valid or neither
-        const uint32_t nb = __builtin_amdgcn_mov_dpp((uint32_t)x, 0xB1, 0xF, 0xF, false);
-        if (valid && !(lane & 1u))
-          __builtin_nontemporal_store((uint32_t)x | (nb << 16),
-                                      reinterpret_cast<uint32_t*>(out + k0) + lane / 2);
-      } else {
-        if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
-      }
+      if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
       u += W * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
     };
-    // a whole segment (the decode launch cuts rows into segments of 1024
-    // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter chunk
-    // by chunk
-    constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
     if (hi - lo == kFull && seg == kFull) {
 #pragma unroll
       for (uint32_t c = 0; c < kFull / kWave; ++c) chunk(lo + c * kWave, false);
@@ -1469,12 +1520,6 @@ __device__ __forceinline__ uint32_t extract_pos(uint32_t x, const PosEntry& e) {
     x = (x ^ t) | (t >> (1u << i));
   }
   return x;
-}
-
-// v_bitop3 with truth table 0xE4 is a bitwise select, S2 ? S0 : S1 (one
-// instruction per step whether the masks sit in vector or scalar registers).
-__device__ __forceinline__ uint32_t select_bits(uint32_t mask, uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_bitop3_b32(a, b, mask, 0xE4);
 }
 
 __device__ __forceinline__ uint32_t deposit_pos(uint32_t v, const PosEntry& e) {
