@@ -21,8 +21,10 @@
 //   * invariant bits go back in with a run decomposition of ~Mask
 //     (v_bfe_u32 + v_lshl_or_b32 per run) and an OR with Bitval; the run
 //     count is a template parameter for the common masks;
-//   * workgroup ids are remapped so that consecutive tasks land on the same
-//     XCD (each of the 8 XCDs has its own L2).
+//   * workgroups keep the dispatcher's order (round robin over the 8 XCDs):
+//     renumbering them so that consecutive tasks share an XCD and its L2
+//     made every decode from HBM slower, by 4-11%; only segment decodes from
+//     a host image renumber (xcd_remap).
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
@@ -168,21 +170,23 @@ __device__ __forceinline__ void stage_window(const U* __restrict__ g, U* l, uint
   }
 }
 
-// Workgroups are handed to the 8 XCDs round robin; renumber them so that
-// logical neighbours (segments of one row, rows of one batch) share an XCD
-// and its L2.  A bijection on [0, G).
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t g) {
-  const uint32_t x = 8;
-  uint32_t q = g / x, r = g % x, xcd = b % x, idx = b / x;
-  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
-}
-
 // One block per lane: pull the payload at bit `rel` of the LDS window out of
 // two words with a funnel shift; a stripped block (its bit set in the 64-bit
 // chunk header, used directly as a lane mask) gets its invariant bits back.
 __device__ __forceinline__ uint32_t lds_bits(const uint32_t* lds, uint32_t rel) {
   const uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
   return __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], rel & 31u);
+}
+
+// Workgroups are handed to the 8 XCDs round robin; this renumbering gives
+// each XCD a contiguous range of logical workgroups (a bijection on [0, G)).
+// Only decodes from a host image use it: there the segments of one row then
+// read their shared header words across the host link once per XCD L2, not
+// once per segment.  From HBM the dispatcher's order is faster.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t g) {
+  const uint32_t x = 8;
+  uint32_t q = g / x, r = g % x, xcd = b % x, idx = b / x;
+  return xcd < r ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
 }
 
 // v_bitop3 with truth table 0xE4 is a bitwise select, S2 ? S0 : S1 (one
@@ -725,13 +729,13 @@ __global__ __launch_bounds__(kBlockThreads) void decode_segments_kernel(
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
     uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, uint32_t* __restrict__ dst,
-    int vec) {
+    int vec, int remap) {
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
   const uint32_t g = gridDim.x;
-  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+  for (uint64_t wg = remap ? xcd_remap(blockIdx.x, g) : blockIdx.x; ; wg += g) {
     const uint64_t task = wg * kWavesPerBlock + wave;
     if (task >= n_tasks) break;
     const uint64_t i = task / nseg;
@@ -771,7 +775,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_batch_kernel(Codec cd, B
   uint32_t* lds = lds_all[wave];
   const uint64_t n_tasks = batch.end[batch.count - 1];
   const uint32_t g = gridDim.x;
-  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+  for (uint64_t wg = blockIdx.x; ; wg += g) {
     const uint64_t task = wg * kWavesPerBlock + wave;
     if (task >= n_tasks) break;
     uint32_t t = 0;
@@ -820,7 +824,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
   const uint32_t l32 = 32u * lane;
   const uint32_t full = n & ~(uint32_t)(kWave - 1);
 
-  uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  uint32_t i = blockIdx.x * kWavesPerBlock + wave;
   if (i >= n_out) return;
 
   auto row_id = [&](uint32_t r) -> uint64_t { return MODE != kModeTable ? (uint64_t)ids[r] : r; };
@@ -1149,7 +1153,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
   const uint32_t stride = gridDim.x * kWavesPerBlock;
-  const uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  const uint32_t i = blockIdx.x * kWavesPerBlock + wave;
   if (i >= n_out) return;
   const int negp = -(int)cd.p;
   const uint32_t l32 = 32u * lane;
@@ -1327,7 +1331,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
     const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
     uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, T* __restrict__ dst,
-    int vec) {
+    int vec, int remap) {
   constexpr uint32_t W = WideCodec<T>::W;
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
@@ -1335,7 +1339,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
   uint32_t* lds = lds_all[wave];
   const uint32_t n = cd.n, nw = cd.nw;
   const uint32_t g = gridDim.x;
-  for (uint64_t wg = xcd_remap(blockIdx.x, g); ; wg += g) {
+  for (uint64_t wg = remap ? xcd_remap(blockIdx.x, g) : blockIdx.x; ; wg += g) {
     const uint64_t task = wg * kWavesPerBlock + wave;
     if (task >= n_tasks) break;
     const uint64_t i = task / nseg;
@@ -1702,7 +1706,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
       return load_entry(table, k);
   };
   const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t i = (uint64_t)xcd_remap(blockIdx.x, gridDim.x) * kWavesPerBlock + wave;
+  for (uint64_t i = (uint64_t)blockIdx.x * kWavesPerBlock + wave;
        i < n_out; i += stride) {
     const uint64_t id = GATHER ? (uint64_t)ids[i] : i;
     uint32_t* out = dst + i * n;
@@ -1931,7 +1935,7 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
   auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
   auto entry = [&](uint32_t k) { return pos_entry<n>(tf, k); };
   const uint32_t stride = gridDim.x * WPB;
-  const uint32_t i = xcd_remap(blockIdx.x, gridDim.x) * WPB + wave;
+  const uint32_t i = blockIdx.x * WPB + wave;
   if (i >= n_out) return;
   const uint32_t l32 = 32u * lane;
 
@@ -2436,7 +2440,7 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_segments_kernel<MODE, NR>), dim3(grid_for(wgs)),
                      dim3(kBlockThreads), 0, st, cd, (const uint32_t*)a.slots,
                      (const unsigned long long*)a.flags, a.ids, arena, cloc, a.n_rows, n_tasks,
-                     nseg, (uint32_t)seg, (uint32_t*)a.dst, a.vec);
+                     nseg, (uint32_t)seg, (uint32_t*)a.dst, a.vec, (int)a.host_image);
 }
 
 template <int MODE>
@@ -2491,7 +2495,7 @@ void launch_decode_wide_nr(const WideCodec<T>& cd, const DecodeArgs& a, hipStrea
   hipLaunchKernelGGL((decode_wide_kernel<T, MODE, NR>), dim3(grid_for(wgs)), dim3(kBlockThreads),
                      0, st, cd, (const uint32_t*)a.slots, (const unsigned long long*)a.flags,
                      a.ids, (const uint32_t*)a.arena, (const unsigned long long*)a.cache_loc,
-                     a.n_rows, n_tasks, nseg, seg, (T*)a.dst, a.vec);
+                     a.n_rows, n_tasks, nseg, seg, (T*)a.dst, a.vec, (int)a.host_image);
 }
 
 template <typename T, int MODE>
@@ -2736,7 +2740,8 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
     // 16-byte staging and raw copies need 16-byte rows (segments are
     // multiples of 64 blocks, so their bounds are 16-byte aligned too)
     const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
-    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec, false};
+    const DecodeArgs a{slots, flags, ids, arena, cache_loc, n_rows, n_out, dst, vec,
+                       is_host_memory(slots)};
     if (md->width_bits == 16)
       launch_decode_wide_mode<uint16_t>(md, row_bytes, a, mode, st);
     else
