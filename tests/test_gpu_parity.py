@@ -172,6 +172,11 @@ CODEC_CASES = [
     (20, 2048, 0x00000000, 0x00000000),            # p = 0: everything raw
     (1, 4, 0xFFFFFFFE, 0x00000000),                # one block
     (3, 98304, 0x7F800000, 0x3F800000),            # largest compressible row
+    # rows of 2048, 4096, 7168 and 8192 blocks: the register-resident
+    # workgroup compressor
+    (24, 16384, 0x55555555, 0x11111111),           # 16 runs, n = 4096
+    (12, 32768, 0x7C000000, 0x3C000000),           # n = 8192
+    (6, 32768, 0x00000000, 0x00000000),            # p = 0: raw rows from registers
     # nearly every block stripped: whole chunks of stripped blocks
     (64, 4096, 0xFFFFFFFF, 0x3F800000, 0.998),     # p = 32, n = 1024
     (96, 2048, 0xFFFFFFFF, 0x00000000, 0.995),     # p = 32, n = 512
@@ -347,7 +352,9 @@ def test_pinned_host_image_small_tasks(ibp, row_bytes, mask, bitval):
 @pytest.mark.parametrize("where", ["device", "pinned_host"])
 @pytest.mark.parametrize("row_bytes,mask,bitval", [(4096, 0x7C007C00, 0x3C003C00),
                                                   (2048, 0xFFFFFFFF, 0x00000000),
-                                                  (8192, 0x78007800, 0x38003800)])
+                                                  (8192, 0x78007800, 0x38003800),
+                                                  (16384, 0x78007800, 0x38003800),
+                                                  (28672, 0x7C007C00, 0x3C003C00)])
 def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
     """In-place compression (each row into its own buffer, as for host tensors
     compressed before transfer): same flags, sizes and image bytes as the
