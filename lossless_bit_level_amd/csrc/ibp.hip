@@ -525,6 +525,86 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
   }
 }
 
+// [IBP] Compression of rows of exactly 4 * 64 * CPW blocks (the long rows of
+// LLM weight matrices), one workgroup per row: each wave holds a quarter of
+// the row in registers (chunks wave * CPW ... + CPW - 1, one block per lane
+// each), so the row is read once.  The chunk ballots are the header words;
+// the waves' match totals, exchanged through LDS, give each wave its carry;
+// payloads are ORed into the workgroup's LDS stream, which is then written
+// with coalesced stores (a raw row straight from the registers).  Three
+// barriers per row.  In place (src == slots) is safe: every wave has read its
+// part of the row before the first barrier, and nothing is written before it.
+template <int NR, int CPW>
+__global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
+    Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t n = (uint32_t)CPW * kWave * kWavesPerBlock;
+  __shared__ uint32_t buf[n + 4];
+  __shared__ uint32_t wtot[kWavesPerBlock];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t c0 = wave * CPW;  // the wave's first chunk
+  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const uint32_t* x_row = src + row * n;
+    uint32_t* s_row = slots + row * n;
+    uint32_t x[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) x[c] = x_row[(c0 + c) * kWave + lane];
+    uint32_t mw = 0;
+    uint32_t hword = 0;  // lane 2c / 2c + 1: low / high half of chunk c's ballot
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
+      mw += (uint32_t)__popcll(h);
+      if (lane == 2u * c) hword = (uint32_t)h;
+      if (lane == 2u * c + 1) hword = (uint32_t)(h >> 32);
+    }
+    // the payload part of the stream starts zeroed; header words are whole
+    for (uint32_t j = n / 32 + threadIdx.x; j < n + 4; j += kBlockThreads) buf[j] = 0u;
+    if (lane < 2u * CPW) buf[2u * c0 + lane] = hword;
+    if (lane == 0) wtot[wave] = mw;
+    __syncthreads();
+    uint32_t carry = 0, m = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const uint32_t t = wtot[w];
+      carry += (uint32_t)w < wave ? t : 0u;
+      m += t;
+    }
+    const uint32_t c_bits = n + 32u * n - cd.p * m;
+    const bool flag = c_bits < 32u * n;
+    if (!flag) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) s_row[(c0 + c) * kWave + lane] = x[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
+        const bool match = __builtin_amdgcn_inverse_ballot_w64(h);
+        const uint32_t k = (c0 + c) * kWave + lane;
+        const uint32_t off =
+            n + 32u * k - __umul24(cd.p, carry + bits_below_lane((uint32_t)h, (uint32_t)(h >> 32)));
+        const uint32_t len = match ? 32u - cd.p : 32u;
+        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+        if (len) {
+          const uint32_t sh = off & 31u, wi = off >> 5;
+          atomicOr(&buf[wi], pay << sh);
+          if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+        }
+        carry += (uint32_t)__popcll(h);
+      }
+      __syncthreads();
+      const uint32_t nw = (c_bits + 31u) >> 5;
+      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+    __syncthreads();
+  }
+}
+
 // [IBP] Compression of rows of exactly 64*NCH blocks, one wave per row: the
 // row is read once into registers (NCH blocks per lane), each chunk's match
 // ballot is its 64-bit header word, the chunk prefixes are a scalar running
@@ -2328,6 +2408,20 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
     case 1024: return launch_compress_rows_t<NR, 16>(cd, n_rows, src, slots, flags, row_bits, st);
     default: break;
   }
+  // rows of 256 * CPW blocks for the common long-row sizes (LLM weight rows
+  // of 4096 or 14336 bf16 values): the register-resident workgroup kernel
+#define IBP_CWG(CPW)                                                                     \
+  hipLaunchKernelGGL((compress_wg_kernel<NR, CPW>), dim3(grid_for(n_rows)),                \
+                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,          \
+                     (uint32_t*)slots, (unsigned long long*)flags, row_bits)
+  switch (cd.n) {
+    case 2048: IBP_CWG(8); return;
+    case 4096: IBP_CWG(16); return;
+    case 7168: IBP_CWG(28); return;
+    case 8192: IBP_CWG(32); return;
+    default: break;
+  }
+#undef IBP_CWG
   // LDS window tiers: the whole row stream (<= n words) lives in LDS
   if (cd.n <= 1024)
     launch_compress_t<NR, 1024>(cd, n_rows, src, slots, flags, row_bits, vec, st);
