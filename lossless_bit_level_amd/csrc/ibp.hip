@@ -1924,6 +1924,85 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
   pack_pos_p<NCH>(tf, lane, pp);
   auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
   const uint64_t stride = (uint64_t)gridDim.x * WPB;
+
+  // Every position with one (Mask, Bitval): the image is the global one, and
+  // the rows are compressed with the global arithmetic (offsets from the
+  // stripped count by v_mbcnt, no scan; the extract masks in scalar
+  // registers).  As in the decoder, only the kernels for rows of up to 512
+  // blocks carry this path.
+  if constexpr (NCH <= 8) {
+    const uint32_t m0 = uniform(tf[0][0]), b0 = uniform(tf[1][0]);
+    bool same = true;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      same = same && tf[0][c * kWave + lane] == m0 && tf[1][c * kWave + lane] == b0;
+    if (__ballot(!same) == 0ull) {
+      const uint32_t p = (uint32_t)__popc(m0);
+      PosEntry e = pos_entry<n>(tf, 0);
+      e.mask = m0;
+      e.bitval = b0;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) e.sfx[j] = uniform(e.sfx[j]);
+      for (uint64_t row = (uint64_t)blockIdx.x * WPB + wave; row < n_rows; row += stride) {
+        const uint32_t* x_row = src + row * n;
+        uint32_t* s_row = slots + row * n;
+        uint32_t x[NCH];
+        unsigned long long h[NCH];
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+        uint32_t m = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          h[c] = __ballot((x[c] & m0) == b0);
+          m += (uint32_t)__popcll(h[c]);
+        }
+        const uint32_t c_bits = n + 32u * n - p * m;
+        const bool flag = c_bits < 32u * n;
+        if (!flag) {
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) s_row[c * kWave + lane] = x[c];
+        } else {
+          const uint32_t nw = (c_bits + 31u) >> 5;
+          for (uint32_t j = n / 32 + lane; j < nw + 1; j += kWave) buf[j] = 0u;
+          if (lane < 2 * NCH) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+              if (lane == 2u * c) w = (uint32_t)h[c];
+              if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
+            }
+            buf[lane] = w;
+          }
+          wave_lds_sync();
+          uint32_t carry = 0;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
+            const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+            const uint32_t off =
+                n + 32u * (c * kWave + lane) - __umul24(p, carry + bits_below_lane(lo, hi));
+            const uint32_t len = match ? 32u - p : 32u;
+            const uint32_t pay = match ? extract_pos(x[c], e) : x[c];
+            if (len) {
+              const uint32_t sh = off & 31u, wi = off >> 5;
+              atomicOr(&buf[wi], pay << sh);
+              if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+            }
+            carry += (uint32_t)__popcll(h[c]);
+          }
+          wave_lds_sync();
+          for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+          wave_lds_sync();
+        }
+        if (lane == 0) {
+          if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+          if (row_bits) row_bits[row] = c_bits;
+        }
+      }
+      return;
+    }
+  }
+
   for (uint64_t row = (uint64_t)blockIdx.x * WPB + wave; row < n_rows; row += stride) {
     const uint32_t* x_row = src + row * n;
     uint32_t* s_row = slots + row * n;
