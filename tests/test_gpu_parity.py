@@ -429,6 +429,8 @@ WIDE_CASES = [
     (16, 20, 1024, 0x0000, 0x0000, 0.0),                  # p = 0: all raw
     (16, 50, 260, 0x5555, 0x1111, 0.9),                   # 8 runs
     (16, 3, 98304, 0x7C00, 0x3C00, 0.9),                  # largest row
+    (16, 64, 1024, 0x5555, 0x1111, 0.9),                  # 8 runs, wave-per-row pairs
+    (16, 50, 4096, 0x7800, 0x3800, 0.95),                 # 2 runs, wave-per-row pairs
     (64, 130, 1024, 0x7FF0000000000000, 0x3FF0000000000000, 0.85),  # fp64 exponent
     (64, 70, 8200, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 1025 blocks, 3 segments
     (64, 40, 24, 0xFFFF0000FFFF0000, 0x1234000056780000, 0.9),      # n = 3
@@ -472,6 +474,24 @@ def test_codec_parity_other_widths(ibp, case):
     assert np.array_equal(out.cpu().numpy(), want)
     if bin(mask).count("1") >= 2 and match_p > 0.5:
         assert flags_o.any()
+
+
+@pytest.mark.parametrize("row_bytes", [4096, 28672])
+def test_compress_in_place_width16(ibp, row_bytes):
+    """16-bit blocks compressed in place (each row into its own buffer):
+    flags, sizes and image bytes equal the oracle's, and the image decodes to
+    the source."""
+    rng = np.random.default_rng(row_bytes + 16)
+    n_rows = 300
+    x = make_rows_w(rng, 16, n_rows, row_bytes, 0x7C00, 0x3C00, 0.9, raw_rows=(2, 200))
+    md = gmd(ibp, 0x7C00, 0x3C00, w=16)
+    buf = to_gpu(x)
+    _, flags, rb = ibp.ibp_compress(md, buf, slots=buf)
+    torch.cuda.synchronize()
+    slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+    assert_image_equal(buf.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    assert torch.equal(ibp.ibp_decompress(md, buf, flags), to_gpu(x))
 
 
 def test_full_llm_kv_width16(ibp):
