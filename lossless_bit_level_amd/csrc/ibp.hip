@@ -1403,6 +1403,111 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
   }
 }
 
+// [IBP] Compression with 16-bit blocks of rows of exactly 128 * NWL blocks
+// (64 * NWL words), one wave per row with the row in registers: lane l holds
+// word 64 t + l, blocks 2 (64 t + l) and 2 (64 t + l) + 1 of the 128-block
+// step t.  Two ballots per step (first / second block of the pair matches)
+// count the stripped blocks and, through v_mbcnt, give each pair's offset;
+// the step's four header words are the pairs' two bits ORed across each row
+// of 16 lanes (DPP).  One extract over the packed pair, with the run masks
+// repeated in both halves, strips both blocks (run j moves bits down by
+// shift_j, and a half's bits never leave it); the pair's payloads, joined,
+// take at most 32 bits, ORed into the wave's LDS stream.  In place is safe:
+// the row is read whole before the first store.
+template <int NR, int NWL>
+__global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
+    WideCodec<uint16_t> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t nw = (uint32_t)NWL * kWave;  // words of a row
+  constexpr uint32_t n = 2u * nw;                 // 16-bit blocks of a row
+  __shared__ uint32_t lds_all[kWavesPerBlock][nw + 4];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds_all[wave];
+  const uint32_t m2 = (uint32_t)cd.mask * 0x10001u, b2 = (uint32_t)cd.bitval * 0x10001u;
+  const uint32_t sh = 2u * (lane & 15u);
+  auto extract2 = [&](uint32_t y) -> uint32_t {
+    uint32_t v = 0;
+    if constexpr (NR >= 0) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
+    } else {
+      for (uint32_t j = 0; j < cd.nruns; ++j)
+        v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
+    }
+    return v;
+  };
+  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
+    const uint32_t* x_row = src + row * nw;
+    uint32_t* s_row = slots + row * nw;
+    uint32_t x[NWL];
+    unsigned long long e[NWL], o[NWL];
+#pragma unroll
+    for (int t = 0; t < NWL; ++t) x[t] = x_row[t * kWave + lane];
+    uint32_t m = 0;
+#pragma unroll
+    for (int t = 0; t < NWL; ++t) {
+      const uint32_t d = (x[t] & m2) ^ b2;
+      e[t] = __ballot((d & 0xFFFFu) == 0u);
+      o[t] = __ballot((d >> 16) == 0u);
+      m += (uint32_t)(__popcll(e[t]) + __popcll(o[t]));
+    }
+    const uint32_t c_bits = n + 16u * n - cd.p * m;
+    const bool flag = c_bits < 16u * n;
+    if (!flag) {
+#pragma unroll
+      for (int t = 0; t < NWL; ++t) s_row[t * kWave + lane] = x[t];
+    } else {
+      const uint32_t nwc = (c_bits + 31u) >> 5;
+      for (uint32_t j = n / 32 + lane; j < nwc + 1; j += kWave) buf[j] = 0u;
+#pragma unroll
+      for (int t = 0; t < NWL; ++t) {
+        uint32_t v = (__builtin_amdgcn_inverse_ballot_w64(e[t]) ? 1u : 0u) |
+                     (__builtin_amdgcn_inverse_ballot_w64(o[t]) ? 2u : 0u);
+        v <<= sh;
+        v |= __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+        v |= __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+        v |= __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+        v |= __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+        if ((lane & 15u) == 15u) buf[4 * t + (lane >> 4)] = v;
+      }
+      wave_lds_sync();
+      uint32_t carry = 0;
+#pragma unroll
+      for (int t = 0; t < NWL; ++t) {
+        const bool s0 = __builtin_amdgcn_inverse_ballot_w64(e[t]);
+        const bool s1 = __builtin_amdgcn_inverse_ballot_w64(o[t]);
+        const uint32_t below = bits_below_lane_acc(
+            (uint32_t)o[t], (uint32_t)(o[t] >> 32),
+            bits_below_lane((uint32_t)e[t], (uint32_t)(e[t] >> 32)));
+        const uint32_t off =
+            n + 16u * (2u * (t * kWave + lane)) - __umul24(cd.p, carry + below);
+        const uint32_t l0 = s0 ? 16u - cd.p : 16u;
+        const uint32_t l1 = s1 ? 16u - cd.p : 16u;
+        const uint32_t ext = extract2(x[t]);
+        const uint32_t pay0 = (s0 ? ext : x[t]) & 0xFFFFu;
+        const uint32_t pay1 = (s1 ? ext : x[t]) >> 16;
+        const uint32_t pay = pay0 | (pay1 << l0);
+        const uint32_t len = l0 + l1;
+        if (len) {
+          const uint32_t sw = off & 31u, wi = off >> 5;
+          atomicOr(&buf[wi], pay << sw);
+          if (sw + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sw));
+        }
+        carry += (uint32_t)(__popcll(e[t]) + __popcll(o[t]));
+      }
+      wave_lds_sync();
+      for (uint32_t j = lane; j < nwc; j += kWave) s_row[j] = buf[j];
+      wave_lds_sync();
+    }
+    if (lane == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+  }
+}
+
 // [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
 // blocks), in the three row-source modes of the 32-bit kernels.
 template <typename T, int MODE, int NR>
@@ -2631,6 +2736,23 @@ void launch_decode(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
 template <typename T, int NR>
 void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void* src,
                              void* slots, uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    // rows of 128 * NWL 16-bit blocks (512 bytes to 4 KiB): one wave per row
+    const uint64_t wgs = (n_rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(32));
+#define IBP_PAIR(NWL)                                                                       \
+  hipLaunchKernelGGL((compress_pair_rows_kernel<NR, NWL>), dim3(grid), dim3(kBlockThreads), 0, \
+                     st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,                 \
+                     (unsigned long long*)flags, row_bits)
+    switch (cd.nw) {
+      case 128: IBP_PAIR(2); return;
+      case 256: IBP_PAIR(4); return;
+      case 512: IBP_PAIR(8); return;
+      case 1024: IBP_PAIR(16); return;
+      default: break;
+    }
+#undef IBP_PAIR
+  }
 #define IBP_WIDE(MAXW)                                                                    \
   hipLaunchKernelGGL((compress_wide_kernel<T, NR, MAXW>), dim3(grid_for(n_rows)),         \
                      dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,         \
