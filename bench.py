@@ -271,20 +271,24 @@ def main():
     raw_bytes = stored = 0
     bits_total = 0
     side_bytes = 0   # flag words of every table
-    def compress(tg):
+    def compress(tg, out=(None, None, None)):
+        slots, flags, rb = out
         if pos_table is not None:
-            return ibp.ibp_compress_positional(pos_table, tg)
-        return ibp.ibp_compress(md, tg)
+            return ibp.ibp_compress_positional(pos_table, tg, slots=slots, flags=flags, row_bits=rb)
+        return ibp.ibp_compress(md, tg, slots=slots, flags=flags, row_bits=rb)
 
     for tg in tables_g:
-        compress(tg)                          # warm
+        out = compress(tg)                    # warm; allocates the image buffers
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        slots, flags, rb = compress(tg)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        comp_ms += e0.elapsed_time(e1)
+        times = []
+        for _ in range(3):                    # the median of three calls into those buffers
+            e0.record(stream)
+            slots, flags, rb = compress(tg, out)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        comp_ms += sorted(times)[1]
         rbn = rb.cpu().numpy()[:tg.shape[0]]
         sb = stored_bytes_per_row(rbn, tg.shape[1])
         images.append((slots, flags, sb))
