@@ -104,6 +104,8 @@ def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False
     if positional:
         return ("decode_pos_pipe_kernel" if row_bytes in (512, 1024, 2048, 4096)
                 else "decode_positional_kernel")
+    if width == 64 and row_bytes in (512, 1024, 2048) and not cached:
+        return "decode_pipe64_kernel"
     if width != 32:
         return "decode_wide_kernel"
     if batched:

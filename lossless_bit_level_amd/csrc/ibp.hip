@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <vector>
 
 #include "ibp.h"
@@ -1085,7 +1086,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
 // wave has at most 64 rows: a further group restarts the pipeline.
 //   stream_words(win): words of a compressed row's stream, from its window
 //   decode(win, x):    the row's n words from the LDS window, x[c] = word
-//                      c * 64 + lane (every lane of the wave calls it)
+//                      c * 64 + lane, or with Q = 2 the 64-bit word c * 64 +
+//                      lane (every lane of the wave calls it)
 template <int NCH>
 struct RowPipe {
   static constexpr uint32_t n = NCH * kWave;  // blocks = words of a row
@@ -1098,7 +1100,7 @@ struct RowPipe {
   static_assert(kLdsWords >= n + 4, "window too small");
 };
 
-template <int NCH, bool GATHER, typename StreamWords, typename Decode>
+template <int NCH, bool GATHER, int Q = 1, typename StreamWords, typename Decode>
 __device__ __forceinline__ void run_row_pipeline(
     const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
     const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
@@ -1188,19 +1190,22 @@ __device__ __forceinline__ void run_row_pipeline(
       // (3) window of row k+2
       const uint32_t* src2 = src_of(k + 2);
       const uint32_t win2 = window(2, src2);
-      // (4) decode row k: exactly NCH stores on every path
-      uint32_t x[NCH];
+      // (4) decode row k: exactly NCH / Q stores of Q words on every path
+      using XT = std::conditional_t<Q == 2, unsigned long long, uint32_t>;
+      constexpr int NX = NCH / Q;
+      XT x[NX];
       if (!ok_of(0)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) x[c] = 0u;
+        for (int c = 0; c < NX; ++c) x[c] = 0u;
       } else if (!fl_of(0)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+        for (int c = 0; c < NX; ++c) x[c] = reinterpret_cast<const XT*>(lds)[c * kWave + lane];
       } else {
         decode(win0, x);
       }
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+      for (int c = 0; c < NX; ++c)
+        __builtin_nontemporal_store(x[c], reinterpret_cast<XT*>(out) + c * kWave + lane);
       __builtin_amdgcn_sched_barrier(0);
       wave_lds_sync();
       if (++k >= K) break;
@@ -1674,6 +1679,51 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     }
     wave_lds_sync();
   }
+}
+
+// [IBP] Decompression with 64-bit blocks of rows of 512 bytes to 2 KiB (32 * NCH
+// blocks, NCH = 2, 4, 8), 16-byte aligned: the row pipeline of the 32-bit
+// decoder with 64-bit stores.  A compressed row's stream is nb + 64 nb - p m
+// bits (nb blocks, m stripped); per 64-block chunk a lane's payload starts at
+// u + 64 lane - p * (stripped blocks of the chunk below the lane) and is read
+// from three LDS words with two funnel shifts.
+template <int MODE, int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void decode_pipe64_kernel(
+    WideCodec<uint64_t> cd, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    uint64_t n_rows, uint32_t n_out, uint32_t* __restrict__ dst) {
+  using P = RowPipe<NCH>;
+  constexpr uint32_t n = P::n;   // words of a row
+  constexpr uint32_t nb = n / 2;  // 64-bit blocks of a row
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][P::kLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint32_t stride = gridDim.x * kWavesPerBlock;
+  const uint32_t i = blockIdx.x * kWavesPerBlock + wave;
+  if (i >= n_out) return;
+  const int negp = -(int)cd.p;
+  const uint32_t l64 = 64u * lane;
+  auto stream_words = [&](uint32_t win) -> uint32_t {
+    const uint32_t m = wave_sum(__popc(lane < nb / 32 ? win : 0u));
+    return (nb + 64u * nb - cd.p * m + 31u) >> 5;
+  };
+  auto decode = [&](uint32_t win, unsigned long long* x) {
+    uint32_t u = nb;
+#pragma unroll
+    for (int c = 0; c < NCH / 2; ++c) {
+      const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+      const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+      const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l64);
+      const uint64_t v = lds_payload<uint64_t>(lds, rel);
+      const bool stripped =
+          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+      x[c] = stripped ? deposit_wide<uint64_t, NR>(v, cd) : v;
+      u += 64u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+    }
+  };
+  run_row_pipeline<NCH, MODE == kModeGather, 2>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                                stride, stream_words, decode);
 }
 
 // ---------------------------------------------------- per-position metadata --
@@ -2782,6 +2832,35 @@ void launch_compress_wide(const ibp_metadata* md, uint64_t n_rows, uint64_t row_
 
 template <typename T, int MODE, int NR>
 void launch_decode_wide_nr(const WideCodec<T>& cd, const DecodeArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) == 8 && MODE != kModeCached) {
+    // 64-bit blocks in 16-byte aligned rows of 512 bytes to 2 KiB: the row
+    // pipeline, in launches of at most 2^30 rows (32-bit row indices)
+    if (a.vec && (cd.nw == 128 || cd.nw == 256 || cd.nw == 512)) {
+      const uint64_t piece = 1ull << 30;
+      for (uint64_t off = 0; off < a.n_out; off += piece) {
+        const uint32_t cnt = (uint32_t)std::min<uint64_t>(piece, a.n_out - off);
+        const uint32_t* sl = (const uint32_t*)a.slots;
+        const unsigned long long* fl = (const unsigned long long*)a.flags;
+        if (MODE == kModeTable) {  // flags stay word aligned (piece % 64 == 0)
+          sl += off * cd.nw;
+          fl += off / 64;
+        }
+        const int64_t* id_p = MODE != kModeTable ? a.ids + off : a.ids;
+        uint32_t* out_p = (uint32_t*)a.dst + off * cd.nw;
+        const uint32_t grid = row_pipe_grid(cnt, kWavesPerBlock, 8);
+#define IBP_P64(NCH)                                                                          \
+  hipLaunchKernelGGL((decode_pipe64_kernel<MODE, NR, NCH>), dim3(grid), dim3(kBlockThreads), 0, \
+                     st, cd, sl, fl, id_p, a.n_rows, cnt, out_p)
+        switch (cd.nw) {
+          case 128: IBP_P64(2); break;
+          case 256: IBP_P64(4); break;
+          default: IBP_P64(8); break;
+        }
+#undef IBP_P64
+      }
+      return;
+    }
+  }
   // a segment's stream stays within the LDS window: <= seg * W / 32 + 3 words
   const uint32_t seg = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
   const uint32_t nseg = (cd.n + seg - 1) / seg;
