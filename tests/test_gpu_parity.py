@@ -437,6 +437,7 @@ WIDE_CASES = [
     (64, 20, 2048, 0xFFFFFFFFFFFFFFFF, 0x0, 0.99),                  # p = 64
     (64, 30, 512, 0x5555555555555555, 0x1111111111111111, 0.9),     # 32 runs
     (64, 3, 98304, 0x7FF0000000000000, 0x3FF0000000000000, 0.9),    # largest row
+    (64, 48, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 512 blocks, wave per row
 ]
 
 
@@ -476,15 +477,18 @@ def test_codec_parity_other_widths(ibp, case):
         assert flags_o.any()
 
 
-@pytest.mark.parametrize("row_bytes", [4096, 28672])
-def test_compress_in_place_width16(ibp, row_bytes):
-    """16-bit blocks compressed in place (each row into its own buffer):
-    flags, sizes and image bytes equal the oracle's, and the image decodes to
-    the source."""
-    rng = np.random.default_rng(row_bytes + 16)
+@pytest.mark.parametrize("w,row_bytes,mask,bitval", [
+    (16, 4096, 0x7C00, 0x3C00), (16, 28672, 0x7C00, 0x3C00),
+    (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000),
+    (64, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00)])
+def test_compress_in_place_other_widths(ibp, w, row_bytes, mask, bitval):
+    """16- and 64-bit blocks compressed in place (each row into its own
+    buffer): flags, sizes and image bytes equal the oracle's, and the image
+    decodes to the source."""
+    rng = np.random.default_rng(row_bytes + w)
     n_rows = 300
-    x = make_rows_w(rng, 16, n_rows, row_bytes, 0x7C00, 0x3C00, 0.9, raw_rows=(2, 200))
-    md = gmd(ibp, 0x7C00, 0x3C00, w=16)
+    x = make_rows_w(rng, w, n_rows, row_bytes, mask, bitval, 0.9, raw_rows=(2, 200))
+    md = gmd(ibp, mask, bitval, w=w)
     buf = to_gpu(x)
     _, flags, rb = ibp.ibp_compress(md, buf, slots=buf)
     torch.cuda.synchronize()
