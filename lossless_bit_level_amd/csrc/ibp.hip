@@ -1513,6 +1513,84 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
   }
 }
 
+// [IBP] Compression with 64-bit blocks of rows of exactly 64 * NCH blocks
+// (512 bytes to 4 KiB), one wave per row with the row in registers (lane l
+// holds block 64 c + l of chunk c): each chunk's match ballot is its header
+// word pair, the chunk prefixes are a scalar running sum, and a payload of up
+// to 64 bits is ORed into the wave's LDS stream in up to three words.  In
+// place is safe: the row is read whole before the first store.
+template <int NR, int NCH>
+__global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
+    WideCodec<uint64_t> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t nb = (uint32_t)NCH * kWave;  // blocks of a row
+  constexpr uint32_t nw = 2u * nb;                // words of a row
+  __shared__ uint32_t lds_all[kWavesPerBlock][nw + 4];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* buf = lds_all[wave];
+  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
+  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
+    const uint64_t* x_row = reinterpret_cast<const uint64_t*>(src + row * nw);
+    uint64_t* s_row64 = reinterpret_cast<uint64_t*>(slots + row * nw);
+    uint32_t* s_row = slots + row * nw;
+    uint64_t x[NCH];
+    unsigned long long h[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
+      m += (uint32_t)__popcll(h[c]);
+    }
+    const uint32_t c_bits = nb + 64u * nb - cd.p * m;
+    const bool flag = c_bits < 64u * nb;
+    if (!flag) {
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) s_row64[c * kWave + lane] = x[c];
+    } else {
+      const uint32_t nwc = (c_bits + 31u) >> 5;
+      for (uint32_t j = nb / 32 + lane; j < nwc + 2; j += kWave) buf[j] = 0u;
+      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
+        uint32_t w = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          if (lane == 2u * c) w = (uint32_t)h[c];
+          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
+        }
+        buf[lane] = w;
+      }
+      wave_lds_sync();
+      uint32_t carry = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
+        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+        const uint32_t off =
+            nb + 64u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
+        const uint32_t len = match ? 64u - cd.p : 64u;
+        const uint64_t pay = match ? extract_wide<uint64_t, NR>(x[c], cd) : x[c];
+        if (len) {
+          const uint32_t sh = off & 31u, wi = off >> 5;
+          const uint64_t placed = pay << sh;  // bits [0, 64) of the placed payload
+          atomicOr(&buf[wi], (uint32_t)placed);
+          if (sh + len > 32u) atomicOr(&buf[wi + 1], (uint32_t)(placed >> 32));
+          if (sh + len > 64u) atomicOr(&buf[wi + 2], (uint32_t)(pay >> (64u - sh)));
+        }
+        carry += (uint32_t)__popcll(h[c]);
+      }
+      wave_lds_sync();
+      for (uint32_t j = lane; j < nwc; j += kWave) s_row[j] = buf[j];
+      wave_lds_sync();
+    }
+    if (lane == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+  }
+}
+
 // [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
 // blocks), in the three row-source modes of the 32-bit kernels.
 template <typename T, int MODE, int NR>
@@ -2802,6 +2880,23 @@ void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void
       default: break;
     }
 #undef IBP_PAIR
+  }
+  if constexpr (sizeof(T) == 8) {
+    // rows of 64 * NCH 64-bit blocks (512 bytes to 4 KiB): one wave per row
+    const uint64_t wgs = (n_rows + kWavesPerBlock - 1) / kWavesPerBlock;
+    const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(32));
+#define IBP_W64(NCH)                                                                         \
+  hipLaunchKernelGGL((compress_w64_rows_kernel<NR, NCH>), dim3(grid), dim3(kBlockThreads), 0, \
+                     st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,                  \
+                     (unsigned long long*)flags, row_bits)
+    switch (cd.nw) {
+      case 128: IBP_W64(1); return;
+      case 256: IBP_W64(2); return;
+      case 512: IBP_W64(4); return;
+      case 1024: IBP_W64(8); return;
+      default: break;
+    }
+#undef IBP_W64
   }
 #define IBP_WIDE(MAXW)                                                                    \
   hipLaunchKernelGGL((compress_wide_kernel<T, NR, MAXW>), dim3(grid_for(n_rows)),         \
