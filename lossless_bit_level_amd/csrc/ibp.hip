@@ -144,6 +144,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data format).
+// A buffer load past `bytes` returns zeros and moves no data, and a store
+// past it is dropped, so an access whose lanes partly or wholly fall outside
+// a row's stream needs no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // 16 bytes as a native vector (kept in registers; HIP's uint4 struct is not
 // always promoted out of private memory when it is assigned conditionally).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -606,13 +615,17 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
   }
 }
 
-// [IBP] Compression of rows of exactly 64*NCH blocks, one wave per row: the
-// row is read once into registers (NCH blocks per lane), each chunk's match
+// [IBP] Compression of rows of exactly 64*NCH blocks, one wave per row.  A
+// wave takes a contiguous range of rows (the launch gives every wave the
+// same number), in pieces of up to 64 rows whose flag bits it ORs into their
+// flag words at once and whose C values it stores with one instruction.  A
+// row is read into registers (NCH blocks per lane); each chunk's match
 // ballot is its 64-bit header word, the chunk prefixes are a scalar running
-// sum, and the payloads are ORed into a wave-private LDS stream buffer that
-// is then written out with coalesced stores.  No workgroup barriers.  In
-// place (src == slots) is safe: the row decision needs every block, so all
-// of a row's loads complete before its first store.
+// sum, and the payloads are ORed into a wave-private LDS stream buffer,
+// written out with NCH buffer stores whose range is the row's stored words
+// (the same instructions for a raw row).  No workgroup barriers.  In place
+// (src == slots) is safe: a row's stores depend on all of its loads, and no
+// other row's stores touch it.
 template <int NR, int NCH>
 __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
     Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
@@ -622,60 +635,83 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* buf = lds_all[wave];
-  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
-    const uint32_t* x_row = src + row * n;
-    uint32_t* s_row = slots + row * n;
-    uint32_t x[NCH];
-    unsigned long long h[NCH];
+  const uint64_t waves = (uint64_t)gridDim.x * kWavesPerBlock;
+  const uint64_t per = (n_rows + waves - 1) / waves;
+  const uint64_t r0 = min(n_rows, ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * per);
+  const uint64_t r1 = min(n_rows, r0 + per);
+  for (uint64_t base = r0; base < r1; base += 64) {
+    const uint32_t K = (uint32_t)min<uint64_t>(64, r1 - base);
+    uint32_t cb = 0u;              // lane k: C of row k of the piece
+    unsigned long long fl = 0ull;  // bit k: row k stored compressed
+    for (uint32_t k = 0; k < K; ++k) {
+      const __amdgpu_buffer_rsrc_t in = row_rsrc(src + (base + k) * n, n * 4u);
+      uint32_t x[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
-    uint32_t m = 0;
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
-      m += (uint32_t)__popcll(h[c]);
-    }
-    const uint32_t c_bits = n + 32u * n - cd.p * m;
-    const bool flag = c_bits < 32u * n;
-    if (!flag) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) s_row[c * kWave + lane] = x[c];
-    } else {
-      const uint32_t nw = (c_bits + 31u) >> 5;
-      for (uint32_t j = n / 32 + lane; j < nw + 1; j += kWave) buf[j] = 0u;
-      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          if (lane == 2u * c) w = (uint32_t)h[c];
-          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
-        }
-        buf[lane] = w;
-      }
-      wave_lds_sync();
-      uint32_t carry = 0;
+      for (int c = 0; c < NCH; ++c)
+        x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, (c * kWave + lane) * 4u, 0, 0);
+      unsigned long long h[NCH];
+      uint32_t m = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
-        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
-        const uint32_t off = n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
-        const uint32_t len = match ? 32u - cd.p : 32u;
-        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
-        if (len) {
-          const uint32_t sh = off & 31u, wi = off >> 5;
-          atomicOr(&buf[wi], pay << sh);
-          if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
-        }
-        carry += (uint32_t)__popcll(h[c]);
+        h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
+        m += (uint32_t)__popcll(h[c]);
       }
-      wave_lds_sync();
-      for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+      const uint32_t c_bits = n + 32u * n - cd.p * m;
+      const bool flag = c_bits < 32u * n;
+      cb = lane == k ? c_bits : cb;
+      fl |= (unsigned long long)flag << k;
+      uint32_t v[NCH];
+      uint32_t words = n;
+      if (!flag) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) v[c] = x[c];
+      } else {
+        words = (c_bits + 31u) >> 5;
+        for (uint32_t j = n / 32 + lane; j < words + 1; j += kWave) buf[j] = 0u;
+        if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
+          uint32_t w = 0;
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            if (lane == 2u * c) w = (uint32_t)h[c];
+            if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
+          }
+          buf[lane] = w;
+        }
+        wave_lds_sync();
+        uint32_t carry = 0;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
+          const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+          const uint32_t off =
+              n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
+          const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+          // the payload's bits in its first word and the next (zero when it
+          // ends in the first).  With p = 32 a matched block has no payload,
+          // and only the other lanes take part (many empty payloads at one
+          // offset would all hit one LDS word); otherwise no branch.
+          const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
+          if (cd.p < 32u || !match) {
+            atomicOr(&buf[off >> 5], (uint32_t)w2);
+            atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
+          }
+          carry += (uint32_t)__popcll(h[c]);
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) v[c] = c * kWave < words ? buf[c * kWave + lane] : 0u;
+      }
+      const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + (base + k) * n, words * 4u);
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(v[c], out, (c * kWave + lane) * 4u, 0, 0);
       wave_lds_sync();
     }
-    if (lane == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
-      if (row_bits) row_bits[row] = c_bits;
+    if (row_bits && lane < K) row_bits[base + lane] = cb;
+    if (fl && lane < 2u) {  // the piece's bits span one or two flag words
+      const uint32_t sh = (uint32_t)(base & 63u);
+      const unsigned long long part = lane == 0 ? fl << sh : (sh ? fl >> (64u - sh) : 0ull);
+      if (part) atomicOr(&flags[(base >> 6) + lane], part);
     }
   }
 }
@@ -1059,14 +1095,6 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
     loc = loc_next;
     win = win_next;
   }
-}
-
-// Buffer resource over `bytes` bytes at p (gfx9 word 3: 32-bit data format).
-// A buffer load past `bytes` returns zeros and moves no data, so a load whose
-// lanes partly or wholly fall outside a row's stream needs no branch.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                           0x00020000);
 }
 
 // The row pipeline shared by decode_pipe_kernel and decode_pos_pipe_kernel,
@@ -2700,6 +2728,8 @@ void launch_compress_t(const Codec& cd, uint64_t n_rows, const void* src, void* 
                      (uint32_t*)slots, (unsigned long long*)flags, row_bits, vec);
 }
 
+// 32 workgroups per compute unit (four times what stays resident), so the
+// dispatcher balances the ranges; every wave gets the same number of rows.
 template <int NR, int NCH>
 void launch_compress_rows_t(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
                             uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
