@@ -615,6 +615,40 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
   }
 }
 
+// Rows of one compressing wave: a contiguous range, as long for every wave
+// of the launch (wpb waves per workgroup), taken in pieces of up to 64 rows.
+// encode(row) compresses a row and returns its C; a row is stored compressed
+// when C < raw_bits.  A piece's flag bits are ORed into their one or two flag
+// words at once, and its C values stored with one instruction.
+template <typename Encode>
+__device__ __forceinline__ void compress_row_range(uint64_t n_rows, uint32_t wave, uint32_t wpb,
+                                                   uint32_t raw_bits,
+                                                   unsigned long long* __restrict__ flags,
+                                                   uint32_t* __restrict__ row_bits,
+                                                   Encode encode) {
+  const uint32_t lane = lane_id();
+  const uint64_t waves = (uint64_t)gridDim.x * wpb;
+  const uint64_t per = (n_rows + waves - 1) / waves;
+  const uint64_t r0 = min(n_rows, ((uint64_t)blockIdx.x * wpb + wave) * per);
+  const uint64_t r1 = min(n_rows, r0 + per);
+  for (uint64_t base = r0; base < r1; base += 64) {
+    const uint32_t K = (uint32_t)min<uint64_t>(64, r1 - base);
+    uint32_t cb = 0u;              // lane k: C of row k of the piece
+    unsigned long long fl = 0ull;  // bit k: row k stored compressed
+    for (uint32_t k = 0; k < K; ++k) {
+      const uint32_t c_bits = encode(base + k);
+      cb = lane == k ? c_bits : cb;
+      fl |= (unsigned long long)(c_bits < raw_bits) << k;
+    }
+    if (row_bits && lane < K) row_bits[base + lane] = cb;
+    if (fl && lane < 2u) {  // the piece's bits span one or two flag words
+      const uint32_t sh = (uint32_t)(base & 63u);
+      const unsigned long long part = lane == 0 ? fl << sh : (sh ? fl >> (64u - sh) : 0ull);
+      if (part) atomicOr(&flags[(base >> 6) + lane], part);
+    }
+  }
+}
+
 // [IBP] Compression of rows of exactly 64*NCH blocks, one wave per row.  A
 // wave takes a contiguous range of rows (the launch gives every wave the
 // same number), in pieces of up to 64 rows whose flag bits it ORs into their
@@ -635,85 +669,69 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* buf = lds_all[wave];
-  const uint64_t waves = (uint64_t)gridDim.x * kWavesPerBlock;
-  const uint64_t per = (n_rows + waves - 1) / waves;
-  const uint64_t r0 = min(n_rows, ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * per);
-  const uint64_t r1 = min(n_rows, r0 + per);
-  for (uint64_t base = r0; base < r1; base += 64) {
-    const uint32_t K = (uint32_t)min<uint64_t>(64, r1 - base);
-    uint32_t cb = 0u;              // lane k: C of row k of the piece
-    unsigned long long fl = 0ull;  // bit k: row k stored compressed
-    for (uint32_t k = 0; k < K; ++k) {
-      const __amdgpu_buffer_rsrc_t in = row_rsrc(src + (base + k) * n, n * 4u);
-      uint32_t x[NCH];
+  compress_row_range(n_rows, wave, kWavesPerBlock, 32u * n, flags, row_bits, [&](uint64_t row) {
+    const __amdgpu_buffer_rsrc_t in = row_rsrc(src + row * n, n * 4u);
+    uint32_t x[NCH];
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, (c * kWave + lane) * 4u, 0, 0);
-      unsigned long long h[NCH];
-      uint32_t m = 0;
+    for (int c = 0; c < NCH; ++c)
+      x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, (c * kWave + lane) * 4u, 0, 0);
+    unsigned long long h[NCH];
+    uint32_t m = 0;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
-        m += (uint32_t)__popcll(h[c]);
-      }
-      const uint32_t c_bits = n + 32u * n - cd.p * m;
-      const bool flag = c_bits < 32u * n;
-      cb = lane == k ? c_bits : cb;
-      fl |= (unsigned long long)flag << k;
-      uint32_t v[NCH];
-      uint32_t words = n;
-      if (!flag) {
+    for (int c = 0; c < NCH; ++c) {
+      h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
+      m += (uint32_t)__popcll(h[c]);
+    }
+    const uint32_t c_bits = n + 32u * n - cd.p * m;
+    const bool flag = c_bits < 32u * n;
+    uint32_t v[NCH];
+    uint32_t words = n;
+    if (!flag) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) v[c] = x[c];
-      } else {
-        words = (c_bits + 31u) >> 5;
-        for (uint32_t j = n / 32 + lane; j < words + 1; j += kWave) buf[j] = 0u;
-        if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
-          uint32_t w = 0;
-#pragma unroll
-          for (int c = 0; c < NCH; ++c) {
-            if (lane == 2u * c) w = (uint32_t)h[c];
-            if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
-          }
-          buf[lane] = w;
-        }
-        wave_lds_sync();
-        uint32_t carry = 0;
+      for (int c = 0; c < NCH; ++c) v[c] = x[c];
+    } else {
+      words = (c_bits + 31u) >> 5;
+      for (uint32_t j = n / 32 + lane; j < words + 1; j += kWave) buf[j] = 0u;
+      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
+        uint32_t w = 0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
-          const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
-          const uint32_t off =
-              n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
-          const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
-          // the payload's bits in its first word and the next (zero when it
-          // ends in the first).  With p = 32 a matched block has no payload,
-          // and only the other lanes take part (many empty payloads at one
-          // offset would all hit one LDS word); otherwise no branch.
-          const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
-          if (cd.p < 32u || !match) {
-            atomicOr(&buf[off >> 5], (uint32_t)w2);
-            atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
-          }
-          carry += (uint32_t)__popcll(h[c]);
+          if (lane == 2u * c) w = (uint32_t)h[c];
+          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
         }
-        wave_lds_sync();
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) v[c] = c * kWave < words ? buf[c * kWave + lane] : 0u;
+        buf[lane] = w;
       }
-      const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + (base + k) * n, words * 4u);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        __builtin_amdgcn_raw_buffer_store_b32(v[c], out, (c * kWave + lane) * 4u, 0, 0);
       wave_lds_sync();
+      uint32_t carry = 0;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
+        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
+        const uint32_t off =
+            n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
+        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+        // the payload's bits in its first word and the next (zero when it
+        // ends in the first).  With p = 32 a matched block has no payload,
+        // and only the other lanes take part (many empty payloads at one
+        // offset would all hit one LDS word); otherwise no branch.
+        const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
+        if (cd.p < 32u || !match) {
+          atomicOr(&buf[off >> 5], (uint32_t)w2);
+          atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
+        }
+        carry += (uint32_t)__popcll(h[c]);
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) v[c] = c * kWave < words ? buf[c * kWave + lane] : 0u;
     }
-    if (row_bits && lane < K) row_bits[base + lane] = cb;
-    if (fl && lane < 2u) {  // the piece's bits span one or two flag words
-      const uint32_t sh = (uint32_t)(base & 63u);
-      const unsigned long long part = lane == 0 ? fl << sh : (sh ? fl >> (64u - sh) : 0ull);
-      if (part) atomicOr(&flags[(base >> 6) + lane], part);
-    }
-  }
+    const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * n, words * 4u);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      __builtin_amdgcn_raw_buffer_store_b32(v[c], out, (c * kWave + lane) * 4u, 0, 0);
+    wave_lds_sync();
+    return c_bits;
+  });
 }
 
 // [IBP] Decompression.  One wave per task = (output row, segment of `seg`
@@ -1470,14 +1488,13 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
     }
     return v;
   };
-  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
-    const uint32_t* x_row = src + row * nw;
-    uint32_t* s_row = slots + row * nw;
+  compress_row_range(n_rows, wave, kWavesPerBlock, 16u * n, flags, row_bits, [&](uint64_t row) {
+    const __amdgpu_buffer_rsrc_t in = row_rsrc(src + row * nw, nw * 4u);
     uint32_t x[NWL];
     unsigned long long e[NWL], o[NWL];
 #pragma unroll
-    for (int t = 0; t < NWL; ++t) x[t] = x_row[t * kWave + lane];
+    for (int t = 0; t < NWL; ++t)
+      x[t] = __builtin_amdgcn_raw_buffer_load_b32(in, (t * kWave + lane) * 4u, 0, 0);
     uint32_t m = 0;
 #pragma unroll
     for (int t = 0; t < NWL; ++t) {
@@ -1488,11 +1505,9 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
     }
     const uint32_t c_bits = n + 16u * n - cd.p * m;
     const bool flag = c_bits < 16u * n;
-    if (!flag) {
-#pragma unroll
-      for (int t = 0; t < NWL; ++t) s_row[t * kWave + lane] = x[t];
-    } else {
-      const uint32_t nwc = (c_bits + 31u) >> 5;
+    uint32_t nwc = nw;
+    if (flag) {
+      nwc = (c_bits + 31u) >> 5;
       for (uint32_t j = n / 32 + lane; j < nwc + 1; j += kWave) buf[j] = 0u;
 #pragma unroll
       for (int t = 0; t < NWL; ++t) {
@@ -1531,14 +1546,16 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
         carry += (uint32_t)(__popcll(e[t]) + __popcll(o[t]));
       }
       wave_lds_sync();
-      for (uint32_t j = lane; j < nwc; j += kWave) s_row[j] = buf[j];
-      wave_lds_sync();
+#pragma unroll
+      for (int t = 0; t < NWL; ++t) x[t] = t * kWave < nwc ? buf[t * kWave + lane] : 0u;
     }
-    if (lane == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
-      if (row_bits) row_bits[row] = c_bits;
-    }
-  }
+    const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * nw, nwc * 4u);
+#pragma unroll
+    for (int t = 0; t < NWL; ++t)
+      __builtin_amdgcn_raw_buffer_store_b32(x[t], out, (t * kWave + lane) * 4u, 0, 0);
+    wave_lds_sync();
+    return c_bits;
+  });
 }
 
 // [IBP] Compression with 64-bit blocks of rows of exactly 64 * NCH blocks
@@ -1557,11 +1574,9 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* buf = lds_all[wave];
-  const uint64_t stride = (uint64_t)gridDim.x * kWavesPerBlock;
-  for (uint64_t row = (uint64_t)blockIdx.x * kWavesPerBlock + wave; row < n_rows; row += stride) {
+  compress_row_range(n_rows, wave, kWavesPerBlock, 64u * nb, flags, row_bits, [&](uint64_t row) {
     const uint64_t* x_row = reinterpret_cast<const uint64_t*>(src + row * nw);
     uint64_t* s_row64 = reinterpret_cast<uint64_t*>(slots + row * nw);
-    uint32_t* s_row = slots + row * nw;
     uint64_t x[NCH];
     unsigned long long h[NCH];
 #pragma unroll
@@ -1609,14 +1624,17 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
         carry += (uint32_t)__popcll(h[c]);
       }
       wave_lds_sync();
-      for (uint32_t j = lane; j < nwc; j += kWave) s_row[j] = buf[j];
+      uint32_t v[2 * NCH];
+#pragma unroll
+      for (int t = 0; t < 2 * NCH; ++t) v[t] = t * kWave < nwc ? buf[t * kWave + lane] : 0u;
+      const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * nw, nwc * 4u);
+#pragma unroll
+      for (int t = 0; t < 2 * NCH; ++t)
+        __builtin_amdgcn_raw_buffer_store_b32(v[t], out, (t * kWave + lane) * 4u, 0, 0);
       wave_lds_sync();
     }
-    if (lane == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
-      if (row_bits) row_bits[row] = c_bits;
-    }
-  }
+    return c_bits;
+  });
 }
 
 // [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
@@ -2184,7 +2202,6 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
   uint32_t pp[(NCH + 3) / 4];
   pack_pos_p<NCH>(tf, lane, pp);
   auto p_of = [&](int c) { return __builtin_amdgcn_ubfe(pp[c / 4], 8 * (c % 4), 8); };
-  const uint64_t stride = (uint64_t)gridDim.x * WPB;
 
   // Every position with one (Mask, Bitval): the image is the global one, and
   // the rows are compressed with the global arithmetic (offsets from the
@@ -2204,7 +2221,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
       e.bitval = b0;
 #pragma unroll
       for (int j = 0; j < 5; ++j) e.sfx[j] = uniform(e.sfx[j]);
-      for (uint64_t row = (uint64_t)blockIdx.x * WPB + wave; row < n_rows; row += stride) {
+      compress_row_range(n_rows, wave, WPB, 32u * n, flags, row_bits, [&](uint64_t row) {
         const uint32_t* x_row = src + row * n;
         uint32_t* s_row = slots + row * n;
         uint32_t x[NCH];
@@ -2255,16 +2272,13 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
           for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
           wave_lds_sync();
         }
-        if (lane == 0) {
-          if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
-          if (row_bits) row_bits[row] = c_bits;
-        }
-      }
+        return c_bits;
+      });
       return;
     }
   }
 
-  for (uint64_t row = (uint64_t)blockIdx.x * WPB + wave; row < n_rows; row += stride) {
+  compress_row_range(n_rows, wave, WPB, 32u * n, flags, row_bits, [&](uint64_t row) {
     const uint32_t* x_row = src + row * n;
     uint32_t* s_row = slots + row * n;
     uint32_t x[NCH];
@@ -2318,11 +2332,8 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
       for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
       wave_lds_sync();
     }
-    if (lane == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
-      if (row_bits) row_bits[row] = c_bits;
-    }
-  }
+    return c_bits;
+  });
 }
 
 // [IBP] Decompression with per-position metadata for rows of exactly
