@@ -378,6 +378,56 @@ def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
     assert np.array_equal(back.cpu().numpy(), x)
 
 
+@pytest.mark.parametrize("kind", ["w32", "w16", "w64", "positional"])
+def test_compress_row_ranges_across_flag_words(ibp, kind):
+    """Rows of 512 bytes, 2 V + 777 of them, V = the waves of a row
+    compression launch (32 workgroups of four waves per compute unit): every
+    wave compresses three consecutive rows (nine on the per-position kernel's
+    resident grid), so wave ranges start inside flag words and some span two,
+    and the last waves get fewer rows or none.  Flags, sizes and image bytes
+    equal the oracle's, and the image decodes to the source."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n_rows = 2 * 128 * cus + 777
+    rng = np.random.default_rng(n_rows + len(kind))
+    say(f"compress row ranges kind={kind} rows={n_rows}")
+    raw = (5, 63, 64, 65, n_rows - 1)
+    if kind == "positional":
+        n = 128
+        mask = np.full(n, 0x7C000000, np.uint64)
+        mask[:4] = [0, 0xFFFFFFFF, 0x7F800000, 0x78007800]
+        bitval = mask & rng.integers(0, 2**32, n, dtype=np.uint64)
+        x = rng.integers(0, 2**32, (n_rows, n), dtype=np.uint64).astype(np.uint32)
+        force = rng.random(x.shape) < 0.9
+        x = np.where(force, (x & ~mask.astype(np.uint32)) | bitval.astype(np.uint32), x)
+        x = x.astype(np.uint32)
+        for r in raw:
+            x[r] = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
+        table = ibp.ibp_positional_table(mask, bitval).cuda()
+        xg = to_gpu(x)
+        slots, flags, rb = ibp.ibp_compress_positional(table, xg)
+        torch.cuda.synchronize()
+        slots_o, flags_o, rb_o = orc.compress_positional(_pm_from_np(mask, bitval), x)
+        back = ibp.ibp_decompress_positional(table, slots, flags)
+    else:
+        w = int(kind[1:])
+        mask, bitval = {32: (0x7C000000, 0x3C000000), 16: (0x7C00, 0x3C00),
+                        64: (0x7C0000007C000000, 0x3C0000003C000000)}[w]
+        if w == 32:
+            x = make_rows(rng, n_rows, 512, mask, bitval, match_p=0.9, raw_rows=raw)
+        else:
+            x = make_rows_w(rng, w, n_rows, 512, mask, bitval, 0.9, raw_rows=raw)
+        md = gmd(ibp, mask, bitval, w=w)
+        xg = to_gpu(x)
+        slots, flags, rb = ibp.ibp_compress(md, xg)
+        torch.cuda.synchronize()
+        slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+        back = ibp.ibp_decompress(md, slots, flags)
+    assert_image_equal(slots.cpu().numpy(), flags_np(flags, n_rows),
+                       rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    assert torch.equal(back, xg)
+    assert flags_o.any() and not all(flag_of(flags_o, r) for r in raw)
+
+
 # ----------------------------------------------------- full-size workloads --
 
 # ------------------------------------------------------ other block widths --
