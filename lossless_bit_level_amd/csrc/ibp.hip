@@ -1558,6 +1558,116 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
   });
 }
 
+// [IBP] Compression with 16-bit blocks of rows of exactly 256 * CPW words
+// (512 * CPW blocks; the 8 and 28 KiB rows of bf16 weight matrices), one
+// workgroup per row.  Each wave holds a quarter of the row in registers, one
+// word (two blocks) per lane per chunk, as in compress_pair_rows_kernel: the
+// pairs' two header bits are ORed into the chunk's four header words across
+// each row of 16 lanes, the waves' match totals meet in LDS to give each wave
+// its carry, and the joined payloads of a pair are ORed into the
+// workgroup's LDS stream, which is then written with coalesced stores (a raw
+// row straight from the registers).  Three barriers per row.  In place is
+// safe: every wave has read its part of the row before the first barrier.
+template <int NR, int CPW>
+__global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
+    WideCodec<uint16_t> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+  constexpr uint32_t nw = (uint32_t)CPW * kWave * kWavesPerBlock;  // words of a row
+  constexpr uint32_t n = 2u * nw;                                   // blocks of a row
+  __shared__ uint32_t buf[nw + 4];
+  __shared__ uint32_t wtot[kWavesPerBlock];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t c0 = wave * CPW;  // the wave's first chunk of 64 words
+  const uint32_t m2 = (uint32_t)cd.mask * 0x10001u, b2 = (uint32_t)cd.bitval * 0x10001u;
+  const uint32_t sh = 2u * (lane & 15u);
+  auto extract2 = [&](uint32_t y) -> uint32_t {
+    uint32_t v = 0;
+    if constexpr (NR >= 0) {
+#pragma unroll
+      for (int j = 0; j < NR; ++j) v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
+    } else {
+      for (uint32_t j = 0; j < cd.nruns; ++j)
+        v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
+    }
+    return v;
+  };
+  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
+    const uint32_t* x_row = src + row * nw;
+    uint32_t* s_row = slots + row * nw;
+    uint32_t x[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) x[c] = x_row[(c0 + c) * kWave + lane];
+    // the payload part of the stream starts zeroed; header words are whole
+    for (uint32_t j = n / 32 + threadIdx.x; j < nw + 4; j += kBlockThreads) buf[j] = 0u;
+    uint32_t mw = 0;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const uint32_t d = (x[c] & m2) ^ b2;
+      const unsigned long long e = __ballot((d & 0xFFFFu) == 0u);
+      const unsigned long long o = __ballot((d >> 16) == 0u);
+      mw += (uint32_t)(__popcll(e) + __popcll(o));
+      uint32_t v = (__builtin_amdgcn_inverse_ballot_w64(e) ? 1u : 0u) |
+                   (__builtin_amdgcn_inverse_ballot_w64(o) ? 2u : 0u);
+      v <<= sh;
+      v |= __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+      v |= __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+      v |= __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+      v |= __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+      if ((lane & 15u) == 15u) buf[4u * (c0 + c) + (lane >> 4)] = v;
+    }
+    if (lane == 0) wtot[wave] = mw;
+    __syncthreads();
+    uint32_t carry = 0, m = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const uint32_t t = wtot[w];
+      carry += (uint32_t)w < wave ? t : 0u;
+      m += t;
+    }
+    const uint32_t c_bits = n + 16u * n - cd.p * m;
+    const bool flag = c_bits < 16u * n;
+    if (!flag) {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) s_row[(c0 + c) * kWave + lane] = x[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const uint32_t d = (x[c] & m2) ^ b2;
+        const unsigned long long e = __ballot((d & 0xFFFFu) == 0u);
+        const unsigned long long o = __ballot((d >> 16) == 0u);
+        const bool s0 = __builtin_amdgcn_inverse_ballot_w64(e);
+        const bool s1 = __builtin_amdgcn_inverse_ballot_w64(o);
+        const uint32_t below = bits_below_lane_acc(
+            (uint32_t)o, (uint32_t)(o >> 32), bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
+        const uint32_t off =
+            n + 32u * ((c0 + c) * kWave + lane) - __umul24(cd.p, carry + below);
+        const uint32_t l0 = s0 ? 16u - cd.p : 16u;
+        const uint32_t l1 = s1 ? 16u - cd.p : 16u;
+        const uint32_t ext = extract2(x[c]);
+        const uint32_t pay0 = (s0 ? ext : x[c]) & 0xFFFFu;
+        const uint32_t pay1 = (s1 ? ext : x[c]) >> 16;
+        const uint32_t pay = pay0 | (pay1 << l0);
+        const uint32_t len = l0 + l1;
+        if (len) {
+          const uint32_t sw = off & 31u, wi = off >> 5;
+          atomicOr(&buf[wi], pay << sw);
+          if (sw + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sw));
+        }
+        carry += (uint32_t)(__popcll(e) + __popcll(o));
+      }
+      __syncthreads();
+      const uint32_t nwc = (c_bits + 31u) >> 5;
+      for (uint32_t j = threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0) {
+      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      if (row_bits) row_bits[row] = c_bits;
+    }
+    __syncthreads();
+  }
+}
+
 // [IBP] Compression with 64-bit blocks of rows of exactly 64 * NCH blocks
 // (512 bytes to 4 KiB), one wave per row with the row in registers (lane l
 // holds block 64 c + l of chunk c): each chunk's match ballot is its header
@@ -2921,6 +3031,19 @@ void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void
       default: break;
     }
 #undef IBP_PAIR
+    // rows of 512 * CPW blocks (the 8 and 28 KiB weight rows): one workgroup per row
+#define IBP_PAIR_WG(CPW)                                                                    \
+  hipLaunchKernelGGL((compress_pair_wg_kernel<NR, CPW>), dim3(grid_for(n_rows)),            \
+                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,           \
+                     (uint32_t*)slots, (unsigned long long*)flags, row_bits)
+    switch (cd.nw) {
+      case 2048: IBP_PAIR_WG(8); return;
+      case 4096: IBP_PAIR_WG(16); return;
+      case 7168: IBP_PAIR_WG(28); return;
+      case 8192: IBP_PAIR_WG(32); return;
+      default: break;
+    }
+#undef IBP_PAIR_WG
   }
   if constexpr (sizeof(T) == 8) {
     // rows of 64 * NCH 64-bit blocks (512 bytes to 4 KiB): one wave per row

@@ -481,6 +481,11 @@ WIDE_CASES = [
     (16, 3, 98304, 0x7C00, 0x3C00, 0.9),                  # largest row
     (16, 64, 1024, 0x5555, 0x1111, 0.9),                  # 8 runs, wave-per-row pairs
     (16, 50, 4096, 0x7800, 0x3800, 0.95),                 # 2 runs, wave-per-row pairs
+    # rows of 2048, 4096, 7168 (above) and 8192 words: workgroup per row
+    (16, 20, 8192, 0x7800, 0x3800, 0.9),                  # 2 runs
+    (16, 9, 16384, 0x5555, 0x1111, 0.9),                  # 8 runs (generic path)
+    (16, 5, 32768, 0xFFFF, 0x0000, 0.995),                # p = 16: empty pair payloads
+    (16, 6, 8192, 0x0000, 0x0000, 0.0),                   # p = 0: raw rows from registers
     (64, 130, 1024, 0x7FF0000000000000, 0x3FF0000000000000, 0.85),  # fp64 exponent
     (64, 70, 8200, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 1025 blocks, 3 segments
     (64, 40, 24, 0xFFFF0000FFFF0000, 0x1234000056780000, 0.9),      # n = 3
