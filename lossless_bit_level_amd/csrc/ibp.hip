@@ -535,22 +535,22 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
   }
 }
 
-// [IBP] Compression of rows of exactly 4 * 64 * CPW blocks (the long rows of
-// LLM weight matrices), one workgroup per row: each wave holds a quarter of
-// the row in registers (chunks wave * CPW ... + CPW - 1, one block per lane
-// each), so the row is read once.  The chunk ballots are the header words;
+// [IBP] Compression of rows of exactly WPB * 64 * CPW blocks (the long rows
+// of LLM weight matrices), one workgroup of WPB waves per row: each wave
+// holds its share of the row in registers (chunks wave * CPW ... + CPW - 1,
+// one block per lane each), so the row is read once.  The chunk ballots are the header words;
 // the waves' match totals, exchanged through LDS, give each wave its carry;
 // payloads are ORed into the workgroup's LDS stream, which is then written
 // with coalesced stores (a raw row straight from the registers).  Three
 // barriers per row.  In place (src == slots) is safe: every wave has read its
 // part of the row before the first barrier, and nothing is written before it.
-template <int NR, int CPW>
-__global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
+template <int NR, int CPW, int WPB>
+__global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
     Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
     unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
-  constexpr uint32_t n = (uint32_t)CPW * kWave * kWavesPerBlock;
+  constexpr uint32_t n = (uint32_t)CPW * kWave * WPB;
   __shared__ uint32_t buf[n + 4];
-  __shared__ uint32_t wtot[kWavesPerBlock];
+  __shared__ uint32_t wtot[WPB];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t c0 = wave * CPW;  // the wave's first chunk
@@ -570,13 +570,13 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
       if (lane == 2u * c + 1) hword = (uint32_t)(h >> 32);
     }
     // the payload part of the stream starts zeroed; header words are whole
-    for (uint32_t j = n / 32 + threadIdx.x; j < n + 4; j += kBlockThreads) buf[j] = 0u;
+    for (uint32_t j = n / 32 + threadIdx.x; j < n + 4; j += WPB * kWave) buf[j] = 0u;
     if (lane < 2u * CPW) buf[2u * c0 + lane] = hword;
     if (lane == 0) wtot[wave] = mw;
     __syncthreads();
     uint32_t carry = 0, m = 0;
 #pragma unroll
-    for (int w = 0; w < kWavesPerBlock; ++w) {
+    for (int w = 0; w < WPB; ++w) {
       const uint32_t t = wtot[w];
       carry += (uint32_t)w < wave ? t : 0u;
       m += t;
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wg_kernel(
       }
       __syncthreads();
       const uint32_t nw = (c_bits + 31u) >> 5;
-      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = threadIdx.x; j < nw; j += WPB * kWave) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
       if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
@@ -2873,15 +2873,15 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
   }
   // rows of 256 * CPW blocks for the common long-row sizes (LLM weight rows
   // of 4096 or 14336 bf16 values): the register-resident workgroup kernel
-#define IBP_CWG(CPW)                                                                     \
-  hipLaunchKernelGGL((compress_wg_kernel<NR, CPW>), dim3(grid_for(n_rows)),                \
-                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,          \
+#define IBP_CWG(CPW, WPB)                                                                \
+  hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>), dim3(grid_for(n_rows)),           \
+                     dim3(WPB * kWave), 0, st, cd, n_rows, (const uint32_t*)src,            \
                      (uint32_t*)slots, (unsigned long long*)flags, row_bits)
   switch (cd.n) {
-    case 2048: IBP_CWG(8); return;
-    case 4096: IBP_CWG(16); return;
-    case 7168: IBP_CWG(28); return;
-    case 8192: IBP_CWG(32); return;
+    case 2048: IBP_CWG(8, 4); return;
+    case 4096: IBP_CWG(16, 4); return;
+    case 7168: IBP_CWG(28, 4); return;
+    case 8192: IBP_CWG(32, 4); return;
     default: break;
   }
 #undef IBP_CWG
