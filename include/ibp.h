@@ -129,9 +129,12 @@ int ibp_build_metadata(const void *sample, uint64_t n_blocks,
  * row_bits[r] = C of row r (also for rows stored raw).  src and slots may be
  * device memory or mapped pinned host memory (zero-copy).  src == slots
  * compresses in place, each row into its own fixed-size buffer ([IBP] System
- * integration: in-place compression of host tensors before transfer); the
- * slot bytes past a compressed row's stream then keep raw bytes, which are
- * not part of the image.  Any other overlap of src and slots is
+ * integration: in-place compression of host tensors before transfer).  Slot
+ * bytes past a compressed row's stream are not part of the image: on device
+ * memory the kernels may write zeros there up to the next 64-byte boundary
+ * (a write ending inside a 64-byte unit costs HBM a read-modify-write); the
+ * rest is not written (in place it keeps raw bytes).  Any other overlap of
+ * src and slots is
  * INVALID_ARGUMENT.  Asynchronous on `stream`.  row_bytes <=
  * IBP_MAX_COMPRESS_ROW_BYTES.  Equal inputs give equal bytes.
  */
