@@ -376,6 +376,22 @@ def test_compress_in_place(ibp, where, row_bytes, mask, bitval):
     back = ibp.ibp_decompress(md, buf, flags)
     torch.cuda.synchronize()
     assert np.array_equal(back.cpu().numpy(), x)
+    # past a compressed row's stream: on device slots at most up to the next
+    # 64-byte boundary may be zeroed, and nothing after it is written; on
+    # host slots nothing past the stream is written
+    got = buf.cpu().numpy()
+    base = buf.data_ptr()
+    for r in range(n_rows):
+        f = flag_of(flags_o, r)
+        if not f:
+            continue
+        nb = orc.stored_bytes(row_bytes, int(rb_o[r]), f)
+        end = nb
+        if where == "device":
+            a = (base + r * row_bytes) % 64
+            end = min(row_bytes, (a + nb + 63) // 64 * 64 - a)
+            assert not got[r, nb:end].any() or np.array_equal(got[r, nb:end], x[r, nb:end])
+        assert np.array_equal(got[r, end:], x[r, end:]), r
 
 
 @pytest.mark.parametrize("kind", ["w32", "w16", "w64", "positional"])
