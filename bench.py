@@ -570,6 +570,8 @@ def main():
                      "invariant_bits": md.invariant_bits, "build_ms": round(meta_ms, 3),
                      "first_call_ms": round(meta_first_ms, 3)},
         "compress": {"ms": round(comp_ms, 3), "GB_per_s_raw_in": round(comp_GBps, 1),
+                     # raw bytes read plus stored bytes written, against the HBM peak
+                     "frac": round((raw_bytes + stored) / (comp_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "in_place_pinned_host": inplace},
         "kernel": {"name": decode_kernel_name(S, args.width, args.positional, md.invariant_bits,
                                               bool(args.cache_mib), args.source == "host",
