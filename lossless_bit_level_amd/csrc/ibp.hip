@@ -2954,10 +2954,13 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
       const uint64_t wgs = (cnt + kWavesPerBlock - 1) / kWavesPerBlock;
       // Grid size (measured on MI355X): with Mask = all ones (p = 32) the
       // streams of sparse rows fit the prefetched window and one row per wave
-      // with many workgroups in flight is fastest; rows of 1024 blocks do best
-      // with 16 workgroups per CU; shorter dense rows, which need a second
-      // load per row, profit most from the pipeline of a resident grid.
-      const uint32_t mult = cd.p == 32 ? 64u : (cd.n >= 1024 ? 16u : 8u);
+      // with many workgroups in flight is fastest, except through the cache,
+      // whose locator adds a dependent load that two rows per wave overlap
+      // (all-hit sparse gather: 22.2 against 23.2 us); rows of 1024 blocks do
+      // best with 16 workgroups per CU; shorter dense rows, which need a
+      // second load per row, profit most from the pipeline of a resident grid.
+      const uint32_t mult =
+          cd.p == 32 ? (MODE == kModeCached ? 32u : 64u) : (cd.n >= 1024 ? 16u : 8u);
       const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, workgroups_per_device(mult));
       // a full decompress is the identity gather: row `off + r` of the table
       const uint32_t* sl = (const uint32_t*)a.slots;
