@@ -548,24 +548,33 @@ def test_codec_parity_other_widths(ibp, case):
         assert flags_o.any()
 
 
-@pytest.mark.parametrize("w,row_bytes,mask,bitval", [
-    (16, 4096, 0x7C00, 0x3C00), (16, 28672, 0x7C00, 0x3C00),
-    (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000),
-    (64, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00)])
-def test_compress_in_place_other_widths(ibp, w, row_bytes, mask, bitval):
+@pytest.mark.parametrize("w,row_bytes,mask,bitval,where", [
+    (16, 4096, 0x7C00, 0x3C00, "device"), (16, 28672, 0x7C00, 0x3C00, "device"),
+    (16, 8192, 0x7800, 0x3800, "host"),
+    (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000, "device"),
+    (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000, "host"),
+    (64, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00, "device")])
+def test_compress_in_place_other_widths(ibp, w, row_bytes, mask, bitval, where):
     """16- and 64-bit blocks compressed in place (each row into its own
-    buffer): flags, sizes and image bytes equal the oracle's, and the image
-    decodes to the source."""
+    buffer, in device or pinned host memory): flags, sizes and image bytes
+    equal the oracle's, nothing past a stream is written on host slots, and
+    the image decodes to the source."""
     rng = np.random.default_rng(row_bytes + w)
     n_rows = 300
     x = make_rows_w(rng, w, n_rows, row_bytes, mask, bitval, 0.9, raw_rows=(2, 200))
     md = gmd(ibp, mask, bitval, w=w)
-    buf = to_gpu(x)
+    buf = to_gpu(x) if where == "device" else torch.from_numpy(x.copy()).pin_memory()
     _, flags, rb = ibp.ibp_compress(md, buf, slots=buf)
     torch.cuda.synchronize()
     slots_o, flags_o, rb_o = orc.compress(omd(md), x)
-    assert_image_equal(buf.cpu().numpy(), flags_np(flags, n_rows),
+    got = buf.cpu().numpy()
+    assert_image_equal(got, flags_np(flags, n_rows),
                        rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
+    if where == "host":
+        for r in range(n_rows):
+            f = flag_of(flags_o, r)
+            nb = orc.stored_bytes(row_bytes, int(rb_o[r]), f) if f else row_bytes
+            assert np.array_equal(got[r, nb:], x[r, nb:]), r
     assert torch.equal(ibp.ibp_decompress(md, buf, flags), to_gpu(x))
 
 
