@@ -55,14 +55,18 @@
  * `slots` is host memory, and then cut rows of 1024 or more blocks into
  * smaller tasks, which suits the host link; the result is the same.
  * ibp_build_metadata is synchronous.  The library keeps no state between
- * calls apart from the last HIP error code of the calling thread and the
- * compute-unit count of the device (read once, to size launches).
+ * calls apart from the last HIP error code of the calling thread, the
+ * compute-unit count of each device (read once per device, to size
+ * launches).
  *
  * Errors
  * ------
  * Every entry point validates its arguments on the host before it enqueues
  * anything; a negative status means nothing was enqueued.  IBP_ERR_HIP means
  * a HIP call or launch failed; ibp_last_hip_error() gives its hipError_t.
+ * A HIP error already pending on the calling thread when an entry point is
+ * called (hipPeekAtLastError) is returned as IBP_ERR_HIP before any work is
+ * enqueued and is left pending for its owner.
  * A row id outside [0, n_rows) (negative ids included) yields an all-zero
  * output row; the kernels never read outside the image for it.
  */
@@ -323,7 +327,8 @@ uint64_t ibp_flag_words(uint64_t n_rows);
  * Device-visible address of pinned host memory (hipHostMalloc'd, e.g. a
  * torch pin_memory tensor), for zero-copy sample/slots arguments.
  * Errors: INVALID_ARGUMENT on null, IBP_ERR_HIP when the memory is not
- * mapped for the current device.
+ * mapped for the current device (the failed query's HIP error is cleared;
+ * ibp_last_hip_error() keeps it).
  */
 int ibp_host_device_pointer(const void *host_ptr, void **device_ptr);
 

@@ -1,0 +1,74 @@
+/*
+ * ibp_ceiling.h -- C ABI of libibp_ceiling, a measuring instrument for
+ * libibp on AMD Instinct MI355X (gfx950): a plain gather-copy kernel that
+ * moves exactly the bytes a decompression moves, with none of its work.
+ *
+ * The explainer page "Reducing the GPU Memory Bottleneck with Lossless
+ * Compression for ML -- Extended" (Kamath, Krishnamurthy, Canini, Peter)
+ * judges its decompressor against the ideal rate of the same transfer
+ * without decoding (section "Results": throughput above 95% of the ideal
+ * uncompressed rate), and its decompression reads only the compressed part
+ * of each fixed-size buffer (section "System integration").  This copy is
+ * that ideal for the library's device and host images: for each output row
+ * it reads the stored bytes of the requested slot and writes the whole row,
+ * so that its time is the floor of the access pattern (random slot reads of
+ * the stored length, streaming row writes) on the machine at hand.
+ *
+ * It is not part of the compression method: the benchmark times it beside
+ * the decompression on the same ids, images and outputs.
+ */
+#ifndef IBP_CEILING_H_
+#define IBP_CEILING_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of tensors one ibp_ceiling_gather_copy call takes. */
+#define IBP_CEILING_MAX_TENSORS 16u
+
+/*
+ * One tensor of a gather copy.
+ *   n_rows     rows of the source table (slots)
+ *   row_bytes  S, bytes of a slot and of an output row; a multiple of 16
+ *   src        the slots, row r at byte r*S: device memory or pinned host
+ *              memory mapped for the device (its device address); 16-byte
+ *              aligned
+ *   src_bytes  device, n_rows uint32: how many leading bytes of slot r to
+ *              copy (the stored length of row r); values above S count as S;
+ *              each is rounded up to a multiple of 16 (16-byte loads)
+ *   ids        device, n_out int64 row ids; NULL: row i of the output is
+ *              row i of the table (then n_out <= n_rows)
+ *   n_out      output rows
+ *   dst        device, n_out x S bytes, 16-byte aligned
+ * Output row i = the first src_bytes[r] bytes (rounded up to 16) of slot r
+ * = ids[i], then zeros to S; an id outside [0, n_rows) gives a zero row.
+ */
+typedef struct ibp_copy_tensor {
+  uint64_t n_rows;
+  uint64_t row_bytes;
+  const void *src;
+  const uint32_t *src_bytes;
+  const int64_t *ids;
+  uint64_t n_out;
+  void *dst;
+} ibp_copy_tensor;
+
+/*
+ * Enqueues one launch on `stream` (a hipStream_t; NULL = the null stream)
+ * that copies every tensor as described above, n_tensors <=
+ * IBP_CEILING_MAX_TENSORS.  Asynchronous; allocates nothing.  Returns 0, or
+ * -1 (null or misaligned pointer, row_bytes not a multiple of 16 or above
+ * 2^26, n_out > n_rows without ids, too many tensors; nothing enqueued) or
+ * -5 (launch failure).  Tensors with n_out == 0 are skipped.
+ */
+int ibp_ceiling_gather_copy(const ibp_copy_tensor *tensors, uint64_t n_tensors,
+                            void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IBP_CEILING_H_ */

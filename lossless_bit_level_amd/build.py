@@ -1,4 +1,5 @@
-"""Build libibp.so in-tree with hipcc for gfx950.
+"""Build libibp.so (the IBP library) and libibp_ceiling.so (the gather-copy
+floor the benchmark measures it against) in-tree with hipcc for gfx950.
 
 Usage: python -m lossless_bit_level_amd.build
 """
@@ -13,6 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "ibp.hip")
 LIB = os.path.join(PKG, "libibp.so")
+CEILING_SRC = os.path.join(PKG, "csrc", "ceiling.hip")
+CEILING_LIB = os.path.join(PKG, "libibp_ceiling.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 
@@ -23,25 +26,34 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libibp)")
 
 
-def command(out: str = LIB, extra=()) -> list[str]:
+def command(out: str = LIB, extra=(), src: str = SRC) -> list[str]:
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Wall", "-I", INCLUDE,
             # packed fp32 instructions are kept out of every kernel
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            *extra, SRC, "-o", out]
+            *extra, src, "-o", out]
 
 
 def build(verbose: bool = False) -> str:
-    """Compile libibp.so (always recompiles; a few tens of seconds)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed to build libibp.so")
-    os.replace(tmp, LIB)
+    """Compile both libraries, side by side (always recompiles; the IBP
+    library takes about a minute)."""
+    jobs = []
+    for src, lib in ((SRC, LIB), (CEILING_SRC, CEILING_LIB)):
+        cmd = command(lib + ".tmp", src=src)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((lib, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                           stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for lib, proc in jobs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(os.path.basename(lib))
+        else:
+            os.replace(lib + ".tmp", lib)
+    if failed:
+        raise RuntimeError(f"hipcc failed to build {', '.join(failed)}")
     return LIB
 
 

@@ -1,0 +1,155 @@
+// libibp_ceiling: the gather-copy floor against which libibp's decompression
+// is measured (include/ibp_ceiling.h).  For every output row it reads the
+// stored bytes of the requested slot and writes the whole row: the reads and
+// writes of a decompression without its decode, so that the ratio of the two
+// times says how much the decode itself costs on top of the memory traffic
+// (explainer page "Reducing the GPU Memory Bottleneck with Lossless
+// Compression for ML -- Extended", section "Results", which compares the
+// decompressor with the ideal rate of the same transfer).
+//
+// Work is cut into tasks of 256 16-byte units (4 KiB of output), one task per
+// wave at a time, four units per lane issued as four loads and then four
+// non-temporal stores.  Rows of up to 4 KiB whose unit count is a power of
+// two pack several rows into a task; longer rows are split into 4 KiB chunks.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "ibp_ceiling.h"
+
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr uint32_t kTaskUnits = 256;  // 16-byte units per task
+constexpr int kPerLane = kTaskUnits / kWave;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct CopyTensor {
+  const u32x4* src;
+  const uint32_t* src_bytes;
+  const int64_t* ids;
+  u32x4* dst;
+  uint64_t n_rows;
+  uint64_t n_out;
+  uint64_t task_end;  // tasks of tensors [0, this one]
+  uint32_t units;     // 16-byte units per row
+  uint32_t shift;     // packed: log2(units)
+  uint32_t cpr;       // chunked: 4 KiB chunks per row; 0 = packed
+  uint32_t pad;
+};
+
+struct CopyBatch {
+  uint32_t count;
+  uint32_t pad;
+  uint64_t tasks;
+  CopyTensor t[IBP_CEILING_MAX_TENSORS];
+};
+
+__global__ __launch_bounds__(kThreads) void gather_copy_kernel(CopyBatch b) {
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint64_t nwaves = (uint64_t)gridDim.x * kWaves;
+  uint64_t task = (uint64_t)blockIdx.x * kWaves +
+                  __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  for (; task < b.tasks; task += nwaves) {
+    uint32_t k = 0;
+    uint64_t begin = 0;
+    while (k + 1 < b.count && task >= b.t[k].task_end) begin = b.t[k++].task_end;
+    const CopyTensor& t = b.t[k];
+    const uint64_t local = task - begin;
+    uint64_t row[kPerLane];
+    uint32_t col[kPerLane];
+    bool live[kPerLane];
+    if (t.cpr == 0) {
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        const uint64_t g = local * kTaskUnits + (uint32_t)j * kWave + lane;
+        row[j] = g >> t.shift;
+        col[j] = (uint32_t)(g & (t.units - 1));
+        live[j] = row[j] < t.n_out;
+      }
+    } else {
+      const uint64_t r = local / t.cpr;
+      const uint32_t chunk = (uint32_t)(local - r * t.cpr);
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) {
+        row[j] = r;
+        col[j] = chunk * kTaskUnits + (uint32_t)j * kWave + lane;
+        live[j] = col[j] < t.units;
+      }
+    }
+    uint64_t src_row[kPerLane];
+    uint32_t limit[kPerLane];  // units of the slot to read
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      src_row[j] = 0;
+      limit[j] = 0;
+      if (live[j]) {
+        const int64_t id = t.ids ? t.ids[row[j]] : (int64_t)row[j];
+        if (id >= 0 && (uint64_t)id < t.n_rows) {
+          src_row[j] = (uint64_t)id;
+          limit[j] = std::min<uint32_t>((t.src_bytes[id] + 15) / 16, t.units);
+        }
+      }
+    }
+    u32x4 v[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (live[j] && col[j] < limit[j]) v[j] = t.src[src_row[j] * t.units + col[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j)
+      if (live[j]) __builtin_nontemporal_store(v[j], &t.dst[row[j] * t.units + col[j]]);
+  }
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+}  // namespace
+
+extern "C" int ibp_ceiling_gather_copy(const ibp_copy_tensor* tensors, uint64_t n_tensors,
+                                       void* stream) {
+  if (n_tensors > IBP_CEILING_MAX_TENSORS || (n_tensors && !tensors)) return -1;
+  CopyBatch b{};
+  uint64_t tasks = 0;
+  for (uint64_t i = 0; i < n_tensors; ++i) {
+    const ibp_copy_tensor& x = tensors[i];
+    if (x.n_out == 0) continue;
+    if (x.row_bytes == 0 || x.row_bytes % 16 || x.row_bytes > (1ull << 26)) return -1;
+    if (!x.src || !x.src_bytes || !x.dst || x.n_rows == 0) return -1;
+    if (!aligned16(x.src) || !aligned16(x.dst) || ((uintptr_t)x.src_bytes & 3) ||
+        ((uintptr_t)x.ids & 7))
+      return -1;
+    if (!x.ids && x.n_out > x.n_rows) return -1;
+    if (x.n_out > (1ull << 40)) return -1;
+    CopyTensor& t = b.t[b.count];
+    t.src = (const u32x4*)x.src;
+    t.src_bytes = x.src_bytes;
+    t.ids = x.ids;
+    t.dst = (u32x4*)x.dst;
+    t.n_rows = x.n_rows;
+    t.n_out = x.n_out;
+    t.units = (uint32_t)(x.row_bytes / 16);
+    if (t.units <= kTaskUnits && (t.units & (t.units - 1)) == 0) {
+      t.shift = (uint32_t)__builtin_ctz(t.units);
+      t.cpr = 0;
+      tasks += (x.n_out * t.units + kTaskUnits - 1) / kTaskUnits;
+    } else {
+      t.cpr = (t.units + kTaskUnits - 1) / kTaskUnits;
+      tasks += x.n_out * t.cpr;
+    }
+    t.task_end = tasks;
+    ++b.count;
+  }
+  if (b.count == 0) return 0;
+  b.tasks = tasks;
+  const uint64_t wgs = (tasks + kWaves - 1) / kWaves;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(wgs, 1u << 20);
+  hipLaunchKernelGGL(gather_copy_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, b);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}

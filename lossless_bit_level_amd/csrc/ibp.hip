@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 #include <vector>
 
@@ -2747,6 +2748,15 @@ int hip_fail(hipError_t e) {
   return IBP_ERR_HIP;
 }
 
+// A HIP error already pending on the calling thread (left by earlier work) is
+// reported as IBP_ERR_HIP and left pending.  Every entry point checks this
+// before its first HIP call, so the errors it reads back afterwards, and the
+// one it clears in is_host_memory, are its own.
+int pending_hip_error() {
+  const hipError_t e = hipPeekAtLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
 int popcount32(uint64_t x) {
   int c = 0;
   for (; x; x &= x - 1) ++c;
@@ -2829,20 +2839,28 @@ uint32_t grid_for(uint64_t work_groups) {
   return (uint32_t)(work_groups < kMaxGrid ? work_groups : kMaxGrid);
 }
 
-int g_cu_count = 0;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // per device, read once (0: not yet)
 
-// Workgroups for a launch: mult per CU (8 workgroups of 4 waves fill a CU).
+// Workgroups for a launch on the current device: mult per CU (8 workgroups of
+// 4 waves fill a CU).
 uint32_t workgroups_per_device(uint32_t mult) {
-  if (!g_cu_count) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus > 0)
-      g_cu_count = cus;
-    else
-      g_cu_count = 256;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();  // the failed query's own error
+    return mult * 256u;
   }
-  return mult * (uint32_t)g_cu_count;
+  if (dev < 0 || dev >= kMaxDevices) return mult * 256u;
+  int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (!cus) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+    }
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  }
+  return mult * (uint32_t)cus;
 }
 
 // Grid of a row-pipeline launch over `rows` rows: as many workgroups of `wpb`
@@ -2932,7 +2950,10 @@ struct DecodeArgs {
 bool is_host_memory(const void* p) {
   hipPointerAttribute_t at;
   if (hipPointerGetAttributes(&at, p) != hipSuccess) {
-    (void)hipGetLastError();  // unregistered memory: clear the error, treat as device
+    // memory HIP does not know: treat it as device memory.  The entry point
+    // checked that no error was pending before this query, so this clears
+    // only the query's own error.
+    (void)hipGetLastError();
     return false;
   }
   return at.type == hipMemoryTypeHost;
@@ -3251,9 +3272,12 @@ int ibp_metadata_from_counts(const uint64_t* ones, uint64_t n_blocks, uint32_t w
   return IBP_OK;
 }
 
-int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bits,
-                       uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
-                       void* stream) {
+// [IBP] Preprocessing on the GPU.  scratch: device buffer of at least
+// (grid + 1) * 64 counters for the count kernel's partials and the totals,
+// with grid <= max_grid; nullptr: allocate one for the call.
+static int build_metadata_impl(const void* sample, uint64_t n_blocks, uint32_t width_bits,
+                               uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
+                               void* stream, unsigned long long* scratch, uint64_t max_grid) {
   if (!sample || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
   if (!width_supported(width_bits)) return IBP_ERR_UNSUPPORTED;
   if (n_blocks == 0) return IBP_ERR_EMPTY;
@@ -3275,15 +3299,23 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
     const uint64_t steps = (words + kCountGroup - 1) / kCountGroup;
     uint64_t wgs = std::min<uint64_t>((steps + kWavesPerBlock - 1) / kWavesPerBlock,
                                       workgroups_per_device(2));
+    if (scratch) wgs = std::min<uint64_t>(wgs, max_grid);
     const uint64_t per_wg = kCountMaxSteps * kWavesPerBlock;
     wgs = std::max<uint64_t>({wgs, (steps + per_wg - 1) / per_wg, 1});
     if (wgs > kMaxGrid) return IBP_ERR_INVALID_ARGUMENT;
+    if (scratch && wgs > max_grid) return IBP_ERR_UNSUPPORTED;  // sample too large
     const uint32_t grid = (uint32_t)wgs;
     const uint64_t lane_max =
         (steps + wgs * kWavesPerBlock - 1) / (wgs * kWavesPerBlock) * kCountWords;
+    int rc = pending_hip_error();
+    if (rc) return rc;
     // partial counts (npos columns of grid) followed by the npos totals
-    e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * npos * sizeof(unsigned long long));
-    if (e != hipSuccess) return hip_fail(e);
+    if (scratch) {
+      d_buf = scratch;
+    } else {
+      e = hipMalloc((void**)&d_buf, ((size_t)grid + 1) * npos * sizeof(unsigned long long));
+      if (e != hipSuccess) return hip_fail(e);
+    }
     unsigned long long* d_counts = d_buf + (size_t)grid * npos;
     const uint32_t* smp = (const uint32_t*)sample;
 #define IBP_COUNT(P, NPOS)                                                              \
@@ -3306,12 +3338,15 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
     e = hipGetLastError();
     if (e == hipSuccess)
       e = hipMemcpyAsync(counts, d_counts, npos * sizeof(uint64_t), hipMemcpyDeviceToHost, st);
+  } else {
+    int rc = pending_hip_error();
+    if (rc) return rc;
   }
   if (e == hipSuccess && width_bits == 16 && (n_blocks & 1))
     e = hipMemcpyAsync(&odd_block, (const uint16_t*)sample + (n_blocks - 1), 2,
                        hipMemcpyDefault, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (d_buf) {
+  if (d_buf && !scratch) {
     hipError_t ef = hipFree(d_buf);
     if (e == hipSuccess) e = ef;
   }
@@ -3322,6 +3357,13 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
   if (out_ones)
     for (uint32_t b = 0; b < width_bits; ++b) out_ones[b] = ones[b];
   return ibp_metadata_from_counts(ones, n_blocks, width_bits, t_ppm, out);
+}
+
+int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bits,
+                       uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
+                       void* stream) {
+  return build_metadata_impl(sample, n_blocks, width_bits, t_ppm, out, out_ones, stream,
+                             nullptr, 0);
 }
 
 int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, const void* src,
@@ -3341,6 +3383,8 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
     const uintptr_t a = (uintptr_t)src, b = (uintptr_t)slots, len = n_rows * row_bytes;
     if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
   }
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   const uint64_t fw = ibp_flag_words(n_rows);
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
@@ -3387,9 +3431,11 @@ static int decode_common(const ibp_metadata* md, uint64_t n_rows, uint64_t row_b
     return IBP_ERR_LAYOUT;
   if (mode == kModeCached && (!aligned(arena, 16) || !aligned(cache_loc, 8)))
     return IBP_ERR_LAYOUT;
+  if (md->width_bits == 64 && (!aligned(slots, 8) || !aligned(dst, 8))) return IBP_ERR_LAYOUT;
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (md->width_bits != 32) {
-    if (md->width_bits == 64 && (!aligned(slots, 8) || !aligned(dst, 8))) return IBP_ERR_LAYOUT;
     // 16-byte staging and raw copies need 16-byte rows (segments are
     // multiples of 64 blocks, so their bounds are 16-byte aligned too)
     const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
@@ -3432,6 +3478,10 @@ static int check_batch_tensor(const ibp_metadata* md, const ibp_tensor& t) {
   if (!t.slots || !t.flags || !t.dst) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(t.slots, 4) || !aligned(t.dst, 4) || !aligned(t.flags, 8)) return IBP_ERR_LAYOUT;
   if (md->width_bits == 64 && (!aligned(t.slots, 8) || !aligned(t.dst, 8))) return IBP_ERR_LAYOUT;
+  if (md->width_bits == 32) {  // task counts of the batched launch fit their 56 bits
+    const uint64_t nseg = (t.row_bytes / 4 + kSegBlocks - 1) / kSegBlocks;
+    if (t.n_rows > (UINT64_MAX >> 8) / nseg) return IBP_ERR_INVALID_ARGUMENT;
+  }
   return IBP_OK;
 }
 
@@ -3441,10 +3491,15 @@ int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint
   if (rc) return rc;
   if (n_tensors == 0) return IBP_OK;
   if (!tensors) return IBP_ERR_INVALID_ARGUMENT;
+  bool work = false;
   for (uint64_t t = 0; t < n_tensors; ++t) {
     rc = check_batch_tensor(md, tensors[t]);
     if (rc) return rc;
+    work = work || tensors[t].n_rows != 0;
   }
+  if (!work) return IBP_OK;
+  rc = pending_hip_error();
+  if (rc) return rc;
   if (md->width_bits != 32) {  // other widths: tensor by tensor
     for (uint64_t t = 0; t < n_tensors; ++t) {
       const ibp_tensor& x = tensors[t];
@@ -3464,8 +3519,7 @@ int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint
       const ibp_tensor& x = tensors[t];
       if (x.n_rows == 0) continue;
       const uint32_t n = (uint32_t)(x.row_bytes / 4);
-      const uint32_t nseg = (n + kSegBlocks - 1) / kSegBlocks;
-      if (x.n_rows > (UINT64_MAX >> 8) / nseg) return IBP_ERR_INVALID_ARGUMENT;
+      const uint32_t nseg = (n + kSegBlocks - 1) / kSegBlocks;  // checked above
       tasks += x.n_rows * nseg;
       BatchTensor& bt = b.t[b.count];
       bt.slots = (const uint32_t*)x.slots;
@@ -3529,6 +3583,8 @@ int ibp_cache_plan(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
   }
   if (!entry_loc) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(entry_loc, 8)) return IBP_ERR_LAYOUT;
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   const uint64_t n_tiles = (n_ids + kScanTile - 1) / kScanTile;  // <= 2^24
   unsigned long long* d_sums = nullptr;
@@ -3572,6 +3628,8 @@ int ibp_cache_fill(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
   if (!aligned(cache_loc, 8) || (entry_loc && !aligned(entry_loc, 8)) ||
       (arena && !aligned(arena, 16)))
     return IBP_ERR_LAYOUT;
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((n_rows + 255) / 256)), dim3(256), 0, st,
                      (unsigned long long*)cache_loc, n_rows, 0ull);
@@ -3631,6 +3689,8 @@ int ibp_build_metadata_positional(const void* sample, uint64_t n_sample_rows,
   if (n_sample_rows == 0) return IBP_ERR_EMPTY;
   if (n_sample_rows >= (1ull << 32) || row_bytes / 4 > (1u << 24)) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(sample, 4) || !aligned(table, 16)) return IBP_ERR_LAYOUT;
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   const uint32_t n = (uint32_t)(row_bytes / 4);
   const uint32_t n_chunks = (n + kWave - 1) / kWave;
@@ -3699,6 +3759,8 @@ int ibp_compress_positional(const void* table, uint64_t n_rows, uint64_t row_byt
     const uintptr_t a = (uintptr_t)src, b = (uintptr_t)slots, len = n_rows * row_bytes;
     if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
   }
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   const uint64_t fw = ibp_flag_words(n_rows);
   hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
@@ -3750,6 +3812,8 @@ static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_by
   if (!aligned(table, 16) || !aligned(slots, 4) || !aligned(dst, 4) || !aligned(flags, 8) ||
       (gather && !aligned(ids, 8)))
     return IBP_ERR_LAYOUT;
+  rc = pending_hip_error();
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   const uint32_t n = (uint32_t)(row_bytes / 4);
   const int vec = row_bytes % 16 == 0 && aligned(slots, 16) && aligned(dst, 16);
@@ -3823,8 +3887,12 @@ int ibp_gather_decompress_positional(const void* table, uint64_t n_rows, uint64_
 
 int ibp_host_device_pointer(const void* host_ptr, void** device_ptr) {
   if (!host_ptr || !device_ptr) return IBP_ERR_INVALID_ARGUMENT;
+  const int rc = pending_hip_error();
+  if (rc) return rc;
   hipError_t e = hipHostGetDevicePointer(device_ptr, const_cast<void*>(host_ptr), 0);
-  return e == hipSuccess ? IBP_OK : hip_fail(e);
+  if (e == hipSuccess) return IBP_OK;
+  (void)hipGetLastError();  // the status carries it; later HIP calls start clean
+  return hip_fail(e);
 }
 
 }  // extern "C"

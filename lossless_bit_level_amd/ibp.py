@@ -173,7 +173,7 @@ def ibp_metadata_from_counts(ones, n_blocks: int, t_ppm: int = 900000,
 
 def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 32,
                        n_blocks: int | None = None, t_ppm: int | None = None,
-                       stream=None):
+                       stream=None, _fn: str = "ibp_build_metadata"):
     """Mask/Bitval over the width_bits-bit blocks of `sample` (GPU or pinned
     host memory).
 
@@ -189,8 +189,7 @@ def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 3
     ppm = int(round(t * 1_000_000)) if t_ppm is None else int(t_ppm)
     md = ibp_metadata()
     ones = (ctypes.c_uint64 * width_bits)()
-    _check("ibp_build_metadata",
-           lib().ibp_build_metadata(_dptr(sample), n_blocks, width_bits, ppm,
+    _check(_fn, getattr(lib(), _fn)(_dptr(sample), n_blocks, width_bits, ppm,
                                     ctypes.byref(md), ones, _stream(stream)))
     return md, list(ones)
 

@@ -24,6 +24,8 @@ distribution family:
 """
 from __future__ import annotations
 
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 CHUNK_ROWS = 65536
@@ -45,22 +47,38 @@ def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
 
 
-def _chunked(n_rows: int, row_start: int, row_count: int, make_chunk):
+def _chunked(n_rows: int, row_start: int, row_count: int, make_chunk, threads: int = 1):
     """Rows [row_start, row_start+row_count) of a table built from 65,536-row
-    chunks, chunk c drawn by make_chunk(c, rows_in_chunk)."""
+    chunks, chunk c drawn by make_chunk(c, rows_in_chunk).  With threads > 1
+    the chunks are drawn concurrently (each has its own generator, so the
+    values do not depend on the thread count)."""
     assert 0 <= row_start and row_start + row_count <= n_rows
-    parts = []
     c0 = row_start // CHUNK_ROWS
     c1 = (row_start + row_count + CHUNK_ROWS - 1) // CHUNK_ROWS
-    for c in range(c0, c1):
+    if c1 <= c0:
+        return make_chunk(0, 0)[:0]
+
+    def piece(c):
         rows = min(CHUNK_ROWS, n_rows - c * CHUNK_ROWS)
-        chunk = make_chunk(c, rows)
         lo = max(row_start - c * CHUNK_ROWS, 0)
         hi = min(row_start + row_count - c * CHUNK_ROWS, rows)
-        parts.append(chunk[lo:hi])
-    if not parts:
-        return make_chunk(0, 0)[:0]
-    return np.concatenate(parts) if len(parts) > 1 else parts[0]
+        return lo, hi, make_chunk(c, rows)
+
+    if threads <= 1 or c1 - c0 == 1:
+        parts = [p[2][p[0]:p[1]] for p in map(piece, range(c0, c1))]
+        return np.concatenate(parts) if len(parts) > 1 else parts[0]
+    first = piece(c0)
+    out = np.empty((row_count,) + first[2].shape[1:], first[2].dtype)
+
+    def place(c, p=None):
+        lo, hi, chunk = p if p is not None else piece(c)
+        at = c * CHUNK_ROWS + lo - row_start
+        out[at:at + hi - lo] = chunk[lo:hi]
+
+    place(c0, first)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(place, range(c0 + 1, c1)))
+    return out
 
 
 # ------------------------------------------------------------ workloads --
@@ -75,7 +93,7 @@ SPARSE_GNN_ROWS, SPARSE_GNN_COLS = 1 << 20, 512
 
 
 def sparse_gnn_rows(row_start: int = 0, row_count: int | None = None,
-                    n_rows: int = SPARSE_GNN_ROWS) -> np.ndarray:
+                    n_rows: int = SPARSE_GNN_ROWS, threads: int = 1) -> np.ndarray:
     """Bag-of-words features: 1.0 with probability 0.01, else 0.0."""
     if row_count is None:
         row_count = n_rows - row_start
@@ -84,7 +102,7 @@ def sparse_gnn_rows(row_start: int = 0, row_count: int | None = None,
         rng = np.random.default_rng([0, c])
         u = rng.random((rows, SPARSE_GNN_COLS), dtype=np.float32)
         return (u < np.float32(0.01)).astype(np.float32)
-    return _chunked(n_rows, row_start, row_count, make)
+    return _chunked(n_rows, row_start, row_count, make, threads)
 
 
 def uniform_ids(n_rows: int, batches: int, per_batch: int, seed: int = 1):
@@ -98,7 +116,7 @@ DLRM_EMB_ROWS, DLRM_EMB_COLS = 1 << 22, 128
 
 
 def dense_gnn_rows(row_start: int = 0, row_count: int | None = None,
-                   n_rows: int = DENSE_GNN_ROWS) -> np.ndarray:
+                   n_rows: int = DENSE_GNN_ROWS, threads: int = 1) -> np.ndarray:
     """Dense node features ~ N(0, 1) * 0.5, fp32."""
     if row_count is None:
         row_count = n_rows - row_start
@@ -107,11 +125,11 @@ def dense_gnn_rows(row_start: int = 0, row_count: int | None = None,
         rng = np.random.default_rng([0, c])
         return rng.standard_normal((rows, DENSE_GNN_COLS),
                                    dtype=np.float32) * np.float32(0.5)
-    return _chunked(n_rows, row_start, row_count, make)
+    return _chunked(n_rows, row_start, row_count, make, threads)
 
 
 def dlrm_emb_rows(row_start: int = 0, row_count: int | None = None,
-                  n_rows: int = DLRM_EMB_ROWS) -> np.ndarray:
+                  n_rows: int = DLRM_EMB_ROWS, threads: int = 1) -> np.ndarray:
     """Embedding table ~ U(-0.05, 0.05), drawn in fp64 and stored as fp32."""
     if row_count is None:
         row_count = n_rows - row_start
@@ -119,7 +137,7 @@ def dlrm_emb_rows(row_start: int = 0, row_count: int | None = None,
     def make(c, rows):
         rng = np.random.default_rng([1, c])
         return rng.uniform(-0.05, 0.05, (rows, DLRM_EMB_COLS)).astype(np.float32)
-    return _chunked(n_rows, row_start, row_count, make)
+    return _chunked(n_rows, row_start, row_count, make, threads)
 
 
 def zipf_ids(n_rows: int, batches: int, per_batch: int, a: float = 1.05,
@@ -187,11 +205,17 @@ def llm_kv_batch(b: int, seq: int = KV_S, fp16: bool = False) -> np.ndarray:
     return f32_to_fp16_bits(x) if fp16 else f32_to_bf16_bits(x)
 
 
-def llm_kv_pages(batches=range(KV_B), seq: int = KV_S, fp16: bool = False) -> np.ndarray:
+def llm_kv_pages(batches=range(KV_B), seq: int = KV_S, fp16: bool = False,
+                 threads: int = 1) -> np.ndarray:
     """KV cache as pages: [n_pages, 16*128] uint16, page id
     (b*32 + h) * (seq/16) + t; each page is contiguous in [B, H, S, D]."""
-    parts = [llm_kv_batch(b, seq, fp16).reshape(-1, KV_PAGE_TOKENS * KV_D)
-             for b in batches]
+    def one(b):
+        return llm_kv_batch(b, seq, fp16).reshape(-1, KV_PAGE_TOKENS * KV_D)
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            parts = list(ex.map(one, batches))
+    else:
+        parts = [one(b) for b in batches]
     return np.concatenate(parts)
 
 

@@ -45,6 +45,33 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, n), n
 
 
+def test_ceiling_library_exports_and_validation():
+    """libibp_ceiling (the benchmark's gather-copy floor) exports what
+    include/ibp_ceiling.h declares and rejects bad layouts before any HIP
+    call."""
+    lib = os.path.join(ROOT, "lossless_bit_level_amd", "libibp_ceiling.so")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ibp_ceiling.h")).read(),
+                  flags=re.S)
+    names = sorted(set(re.findall(r"\b(ibp_[a-z_]+)\s*\(", text)))
+    assert names == ["ibp_ceiling_gather_copy"]
+    L = ctypes.CDLL(lib)
+    for n in names:
+        assert hasattr(L, n), n
+    from lossless_bit_level_amd import ceiling
+    T = ceiling.ibp_copy_tensor
+    f = ceiling.lib().ibp_ceiling_gather_copy
+    fake = 0x10000
+    assert f(None, 0, None) == 0
+    assert f((T * 1)(T(4, 4096, fake, fake, None, 0, fake)), 1, None) == 0   # nothing to copy
+    for bad in [T(4, 4100, fake, fake, None, 4, fake),       # row_bytes % 16
+                T(4, 4096, fake + 4, fake, None, 4, fake),   # misaligned src
+                T(4, 4096, fake, fake, None, 5, fake),       # n_out > n_rows without ids
+                T(4, 4096, fake, None, None, 4, fake),       # no src_bytes
+                T(4, 4096, fake, fake, fake + 4, 4, fake)]:  # misaligned ids
+        assert f((T * 1)(bad), 1, None) == -1
+    assert f((T * 17)(), 17, None) == -1
+
+
 def test_flag_words_and_status_strings(ibp):
     assert [ibp.ibp_flag_words(n) for n in (0, 1, 63, 64, 65, 128, 129)] == \
         [0, 1, 1, 1, 2, 2, 3]

@@ -2,10 +2,15 @@
 
 Small cases compare everything (metadata, per-bit counts, flags, row_bits,
 every image byte that belongs to the image, every decompressed byte).  The
-full-size workloads run in the launch configuration the benchmark times and
-compare sampled rows with the oracle plus properties that hold at any size
-(closed-form row sizes, round trip against the source table).
+full-size workloads run in the launch configuration the benchmark times: the
+whole image of every table (every row's stored words, flag and C) is
+compared with the oracle's, which compresses the table on every host thread
+of the box's share, and every gather batch or layer decode is compared with
+the source rows; closed-form row sizes are checked independently of both.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
@@ -816,7 +821,8 @@ def test_positional_gather_many_rows_per_wave(ibp, row_bytes, n_ids):
 
 def test_full_llm_kv_positional(ibp):
     """KV pages with per-position metadata from the first 2^24 blocks:
-    masks against the oracle, sampled image rows, every gather batch."""
+    masks against the oracle, the whole image against the oracle's, every
+    gather batch."""
     x = syn.llm_kv_pages()
     n_rows, S = x.shape[0], x.nbytes // x.shape[0]
     xg = to_gpu(x)
@@ -827,15 +833,10 @@ def test_full_llm_kv_positional(ibp):
     assert np.array_equal(b.astype(np.uint64), pm.bitval)
     slots, flags, rb = ibp.ibp_compress_positional(table, xg)
     fl = flags_np(flags, n_rows)
-    rbn = rb.cpu().numpy()
-    rng = np.random.default_rng(5)
-    rows = rng.integers(0, n_rows, 40)
-    sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
-    for j, r in enumerate(rows):
-        s_o, c_o, f_o = orc.compress_row_positional(pm, x[r])
-        assert (c_o, f_o) == (int(rbn[r]), flag_of(fl, r))
-        nb = orc.stored_bytes(S, c_o, f_o)
-        assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
+    slots_o, flags_o, rb_o = oracle_image(pm, x.view(np.uint8),
+                                          compress=orc.compress_positional)
+    assert_images_equal("llm_kv per-position", slots.cpu().numpy(), fl,
+                        rb.cpu().numpy()[:n_rows], slots_o, flags_o, rb_o)
     ids = syn.kv_page_ids()
     out = torch.empty((ids.shape[1], S), dtype=torch.uint8, device="cuda")
     for bi, bt in enumerate(ids):
@@ -916,11 +917,70 @@ def test_cache_parity(ibp, case, where):
         assert np.array_equal(out.cpu().numpy(), want), name
 
 
-def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
+def host_threads() -> int:
+    """Threads for the oracle: the affinity mask, capped at the host share
+    OMP_NUM_THREADS announces and at 16."""
+    allowed = len(os.sched_getaffinity(0))
+    share = int(os.environ.get("OMP_NUM_THREADS") or allowed)
+    return max(1, min(allowed, share, 16))
+
+
+def oracle_image(md_o, x_u8: np.ndarray, compress=None):
+    """The oracle's image of a whole table, compressed in row ranges (a
+    multiple of 64 rows, so flag words never straddle two ranges; at least
+    four per thread) on a thread pool; ctypes releases the GIL for each
+    range.  compress: the oracle's table compressor (default: the
+    global-metadata one)."""
+    compress = compress or orc.compress
+    n_rows, S = x_u8.shape
+    threads = host_threads()
+    chunk = min(8192, max(64, n_rows // (4 * threads) // 64 * 64))
+    slots = np.empty((n_rows, S), np.uint8)
+    flags = np.zeros((n_rows + 63) // 64, np.uint64)
+    rb = np.empty(n_rows, np.uint64)
+
+    def job(r0):
+        r1 = min(n_rows, r0 + chunk)
+        s_, f_, b_ = compress(md_o, x_u8[r0:r1])
+        slots[r0:r1] = s_
+        flags[r0 // 64:r0 // 64 + f_.size] = f_
+        rb[r0:r1] = b_
+
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(job, range(0, n_rows, chunk)))
+    return slots, flags, rb
+
+
+def assert_images_equal(name, slots_g: np.ndarray, flags_g: np.ndarray, rb_g: np.ndarray,
+                        slots_o: np.ndarray, flags_o: np.ndarray, rb_o: np.ndarray):
+    """Every row: flag, C and the stored 32-bit words (ceil(C/32) of a
+    compressed row, all of a raw one) equal; zero mismatching rows."""
+    n_rows, S = slots_o.shape
+    n = S // 4
+    assert np.array_equal(flags_g, flags_o), f"{name}: flags differ"
+    assert np.array_equal(rb_g.astype(np.uint64), rb_o), f"{name}: row_bits differ"
+    bits = np.unpackbits(flags_o.view(np.uint8), bitorder="little")[:n_rows].astype(bool)
+    words = np.where(bits, (rb_o.astype(np.int64) + 31) // 32, n)
+    col = np.arange(n)[None, :]
+    bad = []
+    step = max(1, (1 << 24) // n)
+    for r0 in range(0, n_rows, step):
+        r1 = min(n_rows, r0 + step)
+        a = slots_g[r0:r1].view(np.uint32)
+        b = slots_o[r0:r1].view(np.uint32)
+        rows = np.nonzero(((a != b) & (col < words[r0:r1, None])).any(1))[0]
+        bad.extend((r0 + rows[:4]).tolist())
+        if len(bad) > 8:
+            break
+    assert not bad, f"{name}: stored words differ from the oracle in rows {bad[:8]}"
+    return int(bits.sum())
+
+
+def check_full_table(ibp, name, x_np, ids_batches):
     """Metadata over the first min(N, 2^24) blocks, compress the whole table,
-    closed-form sizes for every row, sampled image rows against the oracle,
+    closed-form sizes for every row, the whole image against the oracle's,
     every gather batch against the source rows, sampled outputs against the
-    oracle's gather."""
+    oracle's decode."""
     n_rows, S = x_np.shape[0], x_np.nbytes // x_np.shape[0]
     n = S // 4
     say(f"{name}: table {n_rows} x {S} B")
@@ -944,17 +1004,12 @@ def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     bits[:n_rows] = cc < 32 * n
     want_flags = np.packbits(bits, bitorder="little").view(np.uint64)
     assert np.array_equal(fl, want_flags)
-    # sampled rows of the image against the oracle
-    rng = np.random.default_rng(123)
-    rows = np.unique(np.concatenate([[0, n_rows - 1], rng.integers(0, n_rows, sample_rows)]))
-    sl = slots[torch.from_numpy(rows).cuda()].cpu().numpy()
-    for j, r in enumerate(rows):
-        s_o, c_o, f_o = orc.compress_row(omd(md), x_np[r])
-        f = flag_of(fl, r)
-        assert (c_o, f_o) == (int(cc[r]), f)
-        nb = orc.stored_bytes(S, c_o, f_o)
-        assert np.array_equal(sl[j, :nb], s_o[:nb]), f"row {r}"
+    # the whole image against the oracle's
+    slots_o, flags_o, rb_o = oracle_image(omd(md), x_np.reshape(n_rows, -1).view(np.uint8))
+    n_comp = assert_images_equal(name, slots.cpu().numpy(), fl, rb.cpu().numpy()[:n_rows],
+                                 slots_o, flags_o, rb_o)
     # every gather batch against the source rows; sampled outputs vs oracle
+    rng = np.random.default_rng(123)
     out = torch.empty((ids_batches.shape[1], S), dtype=torch.uint8, device="cuda")
     for bi, ids in enumerate(ids_batches):
         idg = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
@@ -963,13 +1018,10 @@ def check_full_table(ibp, name, x_np, ids_batches, sample_rows=192):
     pick = rng.integers(0, ids_batches.shape[1], 64)
     last = ids_batches[-1][pick]
     got = out[torch.from_numpy(pick).cuda()].cpu().numpy()
-    for j, r in enumerate(last):
-        f = flag_of(fl, r)
-        row = orc.decompress_row(omd(md), slots[int(r)].cpu().numpy(), f)
-        assert np.array_equal(got[j], row)
-    stored = sum(orc.stored_bytes(S, int(cc[r]), int(cc[r] < 32 * n)) for r in range(n_rows)) \
-        if n_rows <= 8192 else None
-    say(f"{name}: ok" + (f", ratio {n_rows * S / stored:.3f}" if stored else ""))
+    assert np.array_equal(got, orc.gather_decompress(omd(md), slots_o, flags_o, last))
+    stored = int(np.where(bits[:n_rows].astype(bool), 4 * ((rb_o.astype(np.int64) + 31) // 32),
+                          S).sum())
+    say(f"{name}: {n_rows} rows bit-exact ({n_comp} compressed), ratio {n_rows * S / stored:.4f}")
     return md, slots, flags
 
 
@@ -1025,14 +1077,19 @@ def test_full_dlrm_emb(ibp):
 def test_full_llm_kv(ibp):
     x = syn.llm_kv_pages()
     ids = syn.kv_page_ids()
-    md, slots, flags = check_full_table(ibp, "llm_kv", x, ids, sample_rows=96)
+    md, slots, flags = check_full_table(ibp, "llm_kv", x, ids)
     assert (md.mask, md.bitval) == (0x7C007C00, 0x3C003C00)
-    # the same gather from a pinned host copy of the image
+    # every gather batch again from a pinned host copy of the image (the
+    # page-granular fetch across the host link)
     host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
     host.copy_(slots)
-    idg = torch.from_numpy(ids[3]).cuda()
-    a = ibp.ibp_gather_decompress(md, host, flags, idg)
-    assert torch.equal(a, to_gpu(x)[idg])
+    xg = to_gpu(x)
+    out = torch.empty((ids.shape[1], x.shape[1] * 2), dtype=torch.uint8, device="cuda")
+    for bi, b in enumerate(ids):
+        idg = torch.from_numpy(np.ascontiguousarray(b)).cuda()
+        ibp.ibp_gather_decompress(md, host, flags, idg, out=out)
+        assert torch.equal(out, xg[idg]), f"host batch {bi}"
+    del host
 
 
 @pytest.mark.parametrize("n_tensors", [7, 19])
@@ -1067,38 +1124,54 @@ def test_decompress_batch(ibp, n_tensors):
     assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("layer", [0, 31])
-def test_full_llm_weights_layer(ibp, layer):
-    """Every matrix of one layer at full size: compress, full decompress,
-    sampled rows against the oracle.  Metadata of the whole model is the one
-    of layer 0's first matrix sample (same distribution everywhere)."""
-    w0 = syn.llm_weight(0, 0)
-    md, _ = ibp.ibp_build_metadata(to_gpu(w0), n_blocks=min(w0.size // 2, 1 << 24))
-    assert (md.mask, md.bitval) == (0x78007800, 0x38003800)
-    rng = np.random.default_rng(layer)
-    images, sources = [], []
-    for j in range(syn.LLM_MATRICES):
-        w = syn.llm_weight(layer, j)
-        say(f"layer {layer} matrix {j} shape {w.shape}")
-        wg = to_gpu(w)
-        slots, flags, rb = ibp.ibp_compress(md, wg)
-        back = ibp.ibp_decompress(md, slots, flags)
-        assert torch.equal(back, wg)
-        images.append((slots, flags))
-        sources.append(wg)
-        fl = flags_np(flags, w.shape[0])
-        rbn = rb.cpu().numpy()
-        for r in np.concatenate([[0, w.shape[0] - 1], rng.integers(0, w.shape[0], 24)]):
-            s_o, c_o, f_o = orc.compress_row(omd(md), w[r])
-            assert int(rbn[r]) == c_o
-            assert flag_of(fl, r) == f_o
-            nb = orc.stored_bytes(w.shape[1] * 2, c_o, f_o)
-            assert np.array_equal(slots[int(r), :nb].cpu().numpy(), s_o[:nb])
-    # the whole layer in one batched launch, as bench.py times it
-    outs = ibp.ibp_decompress_batch(md, images)
-    torch.cuda.synchronize()
-    for out, wg in zip(outs, sources):
-        assert torch.equal(out, wg)
+@pytest.fixture(scope="module")
+def llm_metadata(ibp):
+    """Metadata of the whole model: the first 2^24 blocks in storage order,
+    layer 0's first two matrices; GPU and oracle agree on it."""
+    sample = np.concatenate([syn.llm_weight(0, 0).reshape(-1), syn.llm_weight(0, 1).reshape(-1)])
+    md, ones = ibp.ibp_build_metadata(to_gpu(sample[None]), n_blocks=1 << 24)
+    md_o, ones_o = orc.build_metadata(sample.view(np.uint8), 32)
+    assert (md.mask, md.bitval) == (md_o.mask, md_o.bitval) == (0x78007800, 0x38003800)
+    assert np.array_equal(np.array(ones, np.uint64), ones_o)
+    return md
+
+
+@pytest.mark.parametrize("first_layer", [0, 8, 16, 24])
+def test_full_llm_weights(ibp, llm_metadata, first_layer):
+    """Eight layers of the 32-layer model at full size (the four cases cover
+    every matrix of every layer): each matrix compressed on the GPU and its
+    whole image compared with the oracle's; each layer decoded in the one
+    batched launch the benchmark times and compared with the source; the
+    first layer of the eight also decoded matrix by matrix from a pinned host
+    copy of its images (the zero-copy load)."""
+    md = llm_metadata
+    with ThreadPoolExecutor(syn.LLM_MATRICES) as ex:
+        for layer in range(first_layer, first_layer + 8):
+            mats = list(ex.map(lambda j: syn.llm_weight(layer, j), range(syn.LLM_MATRICES)))
+            images, sources = [], []
+            for j, w in enumerate(mats):
+                wg = to_gpu(w)
+                slots, flags, rb = ibp.ibp_compress(md, wg)
+                slots_o, flags_o, rb_o = oracle_image(omd(md), w.view(np.uint8))
+                assert_images_equal(f"layer {layer} matrix {j}", slots.cpu().numpy(),
+                                    flags_np(flags, w.shape[0]), rb.cpu().numpy()[:w.shape[0]],
+                                    slots_o, flags_o, rb_o)
+                images.append((slots, flags))
+                sources.append(wg)
+            outs = ibp.ibp_decompress_batch(md, images)
+            torch.cuda.synchronize()
+            for j, (out, wg) in enumerate(zip(outs, sources)):
+                assert torch.equal(out, wg), f"layer {layer} matrix {j}"
+            if layer == first_layer:
+                for j, ((slots, flags), wg) in enumerate(zip(images, sources)):
+                    host = torch.empty(slots.shape, dtype=torch.uint8, pin_memory=True)
+                    host.copy_(slots)
+                    back = ibp.ibp_decompress(md, host, flags)
+                    torch.cuda.synchronize()
+                    assert torch.equal(back, wg), f"host layer {layer} matrix {j}"
+                    del host
+            say(f"layer {layer}: 7 matrices bit-exact")
+            del images, sources, outs
 
 
 def test_full_sparse_gnn_cache_of_whole_table(ibp):
