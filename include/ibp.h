@@ -57,7 +57,8 @@
  * ibp_build_metadata is synchronous.  The library keeps no state between
  * calls apart from the last HIP error code of the calling thread, the
  * compute-unit count of each device (read once per device, to size
- * launches).
+ * launches) and, for ibp_build_metadata_noalloc only, one static scratch
+ * array per device.
  *
  * Errors
  * ------
@@ -126,6 +127,28 @@ int ibp_metadata_from_counts(const uint64_t *ones, uint64_t n_blocks,
 int ibp_build_metadata(const void *sample, uint64_t n_blocks,
                        uint32_t width_bits, uint32_t t_ppm, ibp_metadata *out,
                        uint64_t *out_ones, void *stream);
+
+/*
+ * ibp_build_metadata for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, result and synchronisation, but the
+ * partial counts live in a static device array of the library
+ * ((IBP_NOALLOC_COUNT_GRID + 1) * 64 uint64 counters, 513 KiB, one copy per
+ * device, held until the process ends) instead of a per-call hipMalloc.  It
+ * calls no hipMalloc or hipFree.  Samples of up to IBP_NOALLOC_MAX_WORDS
+ * 32-bit words (n_blocks / 2 words for W = 16, n_blocks for W = 32,
+ * 2 * n_blocks for W = 64); a larger sample returns IBP_ERR_UNSUPPORTED.
+ * Every call on a device uses that device's one array (every counter it
+ * reads is written by the same call first): calls that overlap on one
+ * device, from several threads or streams, race and must be serialised by
+ * the caller.
+ */
+#define IBP_NOALLOC_COUNT_GRID 1024u
+#define IBP_NOALLOC_MAX_WORDS (1024ull * 4ull * 524287ull * 2048ull)
+int ibp_build_metadata_noalloc(const void *sample, uint64_t n_blocks,
+                               uint32_t width_bits, uint32_t t_ppm,
+                               ibp_metadata *out, uint64_t *out_ones,
+                               void *stream);
 
 /*
  * [IBP] Compression.  src: the n_rows x row_bytes table.  Writes the image

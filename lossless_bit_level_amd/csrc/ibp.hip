@@ -32,6 +32,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <vector>
 
@@ -3225,6 +3226,40 @@ void launch_compress_positional_t(const void* table, uint32_t n, uint64_t n_rows
                      row_bits);
 }
 
+// Scratch of ibp_build_metadata_noalloc: the count kernel's partial counts
+// (up to IBP_NOALLOC_COUNT_GRID workgroups x 64 positions) and the 64
+// totals, 513 KiB.  Every device the library runs on holds its own copy
+// until the process ends; calls on one device share it.
+static __device__ __align__(256) unsigned long long
+    scratch[((size_t)IBP_NOALLOC_COUNT_GRID + 1) * 64];
+static_assert(IBP_NOALLOC_MAX_WORDS ==
+                  (uint64_t)IBP_NOALLOC_COUNT_GRID * kWavesPerBlock * kCountMaxSteps * kCountGroup,
+              "the largest no-alloc sample is what IBP_NOALLOC_COUNT_GRID workgroups can count");
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current).  In host code the array's name is
+// only a host-side stand-in; kernels get this address instead.
+int count_scratch(unsigned long long** out) {
+  int rc = pending_hip_error();
+  if (rc) return rc;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return IBP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = (unsigned long long*)g_scratch_ptr[dev];
+  return IBP_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI ----
@@ -3364,6 +3399,20 @@ int ibp_build_metadata(const void* sample, uint64_t n_blocks, uint32_t width_bit
                        void* stream) {
   return build_metadata_impl(sample, n_blocks, width_bits, t_ppm, out, out_ones, stream,
                              nullptr, 0);
+}
+
+int ibp_build_metadata_noalloc(const void* sample, uint64_t n_blocks, uint32_t width_bits,
+                               uint32_t t_ppm, ibp_metadata* out, uint64_t* out_ones,
+                               void* stream) {
+  // argument errors first, as ibp_build_metadata reports them
+  if (!sample || !out || t_ppm > 1000000u) return IBP_ERR_INVALID_ARGUMENT;
+  if (!width_supported(width_bits)) return IBP_ERR_UNSUPPORTED;
+  if (n_blocks == 0) return IBP_ERR_EMPTY;
+  unsigned long long* buf = nullptr;
+  const int rc = count_scratch(&buf);
+  if (rc) return rc;
+  return build_metadata_impl(sample, n_blocks, width_bits, t_ppm, out, out_ones, stream, buf,
+                             IBP_NOALLOC_COUNT_GRID);
 }
 
 int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, const void* src,

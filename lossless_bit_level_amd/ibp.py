@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         mdp = ctypes.POINTER(ibp_metadata)
         L.ibp_metadata_from_counts.argtypes = [vp, u64, u32, u32, mdp]
         L.ibp_build_metadata.argtypes = [vp, u64, u32, u32, mdp, vp, vp]
+        L.ibp_build_metadata_noalloc.argtypes = [vp, u64, u32, u32, mdp, vp, vp]
         L.ibp_compress.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp]
         L.ibp_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, vp]
         L.ibp_gather_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp]
@@ -96,7 +97,8 @@ def lib() -> ctypes.CDLL:
         L.ibp_status_string.argtypes = [i32]
         L.ibp_status_string.restype = ctypes.c_char_p
         L.ibp_last_hip_error.argtypes = []
-        for f in ("ibp_metadata_from_counts", "ibp_build_metadata", "ibp_compress",
+        for f in ("ibp_metadata_from_counts", "ibp_build_metadata",
+                  "ibp_build_metadata_noalloc", "ibp_compress",
                   "ibp_decompress", "ibp_decompress_batch", "ibp_gather_decompress",
                   "ibp_host_device_pointer",
                   "ibp_last_hip_error", "ibp_cache_plan", "ibp_cache_fill",
@@ -192,6 +194,15 @@ def ibp_build_metadata(sample: torch.Tensor, t: float = 0.9, width_bits: int = 3
     _check(_fn, getattr(lib(), _fn)(_dptr(sample), n_blocks, width_bits, ppm,
                                     ctypes.byref(md), ones, _stream(stream)))
     return md, list(ones)
+
+
+def ibp_build_metadata_noalloc(sample: torch.Tensor, t: float = 0.9, width_bits: int = 32,
+                               n_blocks: int | None = None, t_ppm: int | None = None,
+                               stream=None):
+    """ibp_build_metadata with the library's static scratch instead of a
+    per-call device allocation (for callers that cannot allocate)."""
+    return ibp_build_metadata(sample, t, width_bits, n_blocks, t_ppm, stream,
+                              _fn="ibp_build_metadata_noalloc")
 
 
 def ibp_compress(md: ibp_metadata, src: torch.Tensor, slots: torch.Tensor | None = None,

@@ -38,8 +38,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert {"ibp_build_metadata", "ibp_compress", "ibp_decompress",
-            "ibp_gather_decompress"} <= set(names)
+    assert {"ibp_build_metadata", "ibp_build_metadata_noalloc", "ibp_compress",
+            "ibp_decompress", "ibp_gather_decompress"} <= set(names)
     L = ctypes.CDLL(LIB)
     for n in names:
         assert hasattr(L, n), n
@@ -61,15 +61,15 @@ def test_ceiling_library_exports_and_validation():
     T = ceiling.ibp_copy_tensor
     f = ceiling.lib().ibp_ceiling_gather_copy
     fake = 0x10000
-    assert f(None, 0, None) == 0
-    assert f((T * 1)(T(4, 4096, fake, fake, None, 0, fake)), 1, None) == 0   # nothing to copy
+    assert f(None, 0, 0, None) == 0
+    assert f((T * 1)(T(4, 4096, fake, fake, None, 0, fake)), 1, 0, None) == 0   # nothing to copy
     for bad in [T(4, 4100, fake, fake, None, 4, fake),       # row_bytes % 16
                 T(4, 4096, fake + 4, fake, None, 4, fake),   # misaligned src
                 T(4, 4096, fake, fake, None, 5, fake),       # n_out > n_rows without ids
                 T(4, 4096, fake, None, None, 4, fake),       # no src_bytes
                 T(4, 4096, fake, fake, fake + 4, 4, fake)]:  # misaligned ids
-        assert f((T * 1)(bad), 1, None) == -1
-    assert f((T * 17)(), 17, None) == -1
+        assert f((T * 1)(bad), 1, 0, None) == -1
+    assert f((T * 17)(), 17, 0, None) == -1
 
 
 def test_flag_words_and_status_strings(ibp):
@@ -154,6 +154,13 @@ def test_validation_before_enqueue(ibp):
     assert L.ibp_build_metadata(fake, 10, 32, 1000001, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_build_metadata(None, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_build_metadata(fake + 1, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_LAYOUT
+    # the no-allocation variant reports the same argument errors, before any HIP call
+    nl = L.ibp_build_metadata_noalloc
+    assert nl(fake, 0, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_EMPTY
+    assert nl(fake, 10, 8, 900000, byref(out), None, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert nl(fake, 10, 32, 1000001, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert nl(None, 10, 32, 900000, byref(out), None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert nl(fake, 10, 32, 900000, None, None, None) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_host_device_pointer(None, byref(ctypes.c_void_p())) == ibp.IBP_ERR_INVALID_ARGUMENT
     assert L.ibp_last_hip_error() == 0
 
