@@ -53,6 +53,7 @@ HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "lossless_bit_level_amd", "csrc", "ibp.hip")
 ROTATE_BYTES = 1 << 30           # outputs rotate over at least this much memory
+CEILING_GRIDS = (2, 4, 8, 16, 64)   # workgroups per CU tried for the gather-copy ceiling
 GiB = float(1 << 30)
 
 
@@ -67,6 +68,11 @@ def cpu_threads():
     allowed = len(os.sched_getaffinity(0))
     share = int(os.environ.get("OMP_NUM_THREADS") or allowed)
     return max(1, min(allowed, share)), allowed
+
+
+def cu_count() -> int:
+    import torch
+    return torch.cuda.get_device_properties(0).multi_processor_count
 
 
 def cpu_model() -> str:
@@ -542,13 +548,20 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
                                                              idg, out)
         return ibp.ibp_gather_decompress_launcher(md, slots, flags, idg, out)
 
-    def make_copy(gi, oi):
+    # stored bytes of each output row's source row, the copy's read lengths
+    out_sb = []
+    for ti, ids in steps:
+        sb = images[ti][2]
+        out_sb.append(images[ti][3] if ids is None else
+                      torch.from_numpy(sb[ids].astype(np.int32)).to(dev))
+
+    def make_copy(gi, oi, cap, pack):
         parts = []
         for j, k in enumerate(groups[gi]):
-            slots, _, _, sbg = images[steps[k][0]]
+            slots = images[steps[k][0]][0]
             n, S = group_shapes[gi][j]
-            parts.append((slots, sbg, ids_g[k], out_sets[oi][j].view(-1)[:n * S].view(n, S)))
-        return ceiling.gather_copy_launcher(parts)
+            parts.append((slots, out_sb[k], ids_g[k], out_sets[oi][j].view(-1)[:n * S].view(n, S)))
+        return ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack)
 
     def launcher(make):
         # every (group, output set) pair the warm-up, the timed region and
@@ -565,7 +578,6 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
         return launch
 
     decode = launcher(make_decode)
-    copy = launcher(make_copy) if arena is None else None
     G = len(groups)
     for k in range(W):
         decode(k)
@@ -601,15 +613,27 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
         if not np.array_equal(got, want):
             raise SystemExit(f"bench: decompressed rows of {wl.name} differ from the source")
 
-    # the gather-copy ceiling on the same ids, images and output rotation
+    # the gather-copy ceiling on the same ids, images and output rotation:
+    # the best of a few grid sizes (the copy's waves loop over their work)
     ceil_rec = None
-    if copy is not None:
-        for k in range(W):
-            copy(k)
-        torch.cuda.synchronize()
-        _, c_region = time_region(stream, copy, K)
-        c_s = c_region / K
-        ceil_rec = {"kernel": "gather_copy_kernel", "mean_launch_us": round(c_s * 1e6, 3),
+    if arena is None:
+        best = None
+        short = min(s[1] for s in shapes) < 4096
+        for pack in ((False, True) if short else (False,)):
+            for per_cu in CEILING_GRIDS:
+                cap = per_cu * cu_count()
+                copy = launcher(lambda gi, oi, c=cap, p=pack: make_copy(gi, oi, c, p))
+                for k in range(W):
+                    copy(k)
+                torch.cuda.synchronize()
+                _, c_region = time_region(stream, copy, K)
+                if best is None or c_region < best[0]:
+                    best = (c_region, per_cu, pack)
+                del copy
+        c_s = best[0] / K
+        ceil_rec = {"kernel": "gather_copy_kernel", "workgroups_per_cu": best[1],
+                    "rows_per_task": "4 KiB of rows" if best[2] else "one",
+                    "mean_launch_us": round(c_s * 1e6, 3),
                     "achieved": round(a_bytes / c_s / 1e9, 2),
                     "frac_of_peak": round(a_bytes / c_s / 1e9 / HBM_PEAK_GBPS, 4),
                     "decode_frac_of_ceiling": round(c_s / mean_launch_s, 4)}

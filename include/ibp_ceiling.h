@@ -36,15 +36,18 @@ extern "C" {
  *   src        the slots, row r at byte r*S: device memory or pinned host
  *              memory mapped for the device (its device address); 16-byte
  *              aligned
- *   src_bytes  device, n_rows uint32: how many leading bytes of slot r to
- *              copy (the stored length of row r); values above S count as S;
- *              each is rounded up to a multiple of 16 (16-byte loads)
+ *   src_bytes  device, n_out uint32: how many leading bytes of the slot of
+ *              output row i to copy (the stored length of row ids[i]); values
+ *              above S count as S; each is rounded up to a multiple of 16
+ *              (16-byte loads)
  *   ids        device, n_out int64 row ids; NULL: row i of the output is
  *              row i of the table (then n_out <= n_rows)
  *   n_out      output rows
  *   dst        device, n_out x S bytes, 16-byte aligned
- * Output row i = the first src_bytes[r] bytes (rounded up to 16) of slot r
- * = ids[i], then zeros to S; an id outside [0, n_rows) gives a zero row.
+ * Output row i = the first src_bytes[i] bytes (rounded up to 16) of slot
+ * ids[i], then zeros to S; an id outside [0, n_rows) gives a zero row.  The
+ * byte counts are indexed by the output row so that they load alongside the
+ * ids: a floor must not wait for a lookup the decompression does not pay.
  */
 typedef struct ibp_copy_tensor {
   uint64_t n_rows;
@@ -59,13 +62,18 @@ typedef struct ibp_copy_tensor {
 /*
  * Enqueues one launch on `stream` (a hipStream_t; NULL = the null stream)
  * that copies every tensor as described above, n_tensors <=
- * IBP_CEILING_MAX_TENSORS.  Asynchronous; allocates nothing.  Returns 0, or
- * -1 (null or misaligned pointer, row_bytes not a multiple of 16 or above
- * 2^26, n_out > n_rows without ids, too many tensors; nothing enqueued) or
- * -5 (launch failure).  Tensors with n_out == 0 are skipped.
+ * IBP_CEILING_MAX_TENSORS.  A task is 4 KiB of output: a row or a 4 KiB
+ * chunk of a longer row; with pack != 0, rows shorter than 4 KiB whose size
+ * is a power of two times 16 bytes go 4 KiB / S to a task instead.
+ * max_workgroups caps the grid (workgroups of 256 threads; each wave loops
+ * over its share of the tasks), 0 = one wave per task.  The result is the
+ * same either way.  Asynchronous; allocates nothing.  Returns 0, or -1 (null
+ * or misaligned pointer, row_bytes not a multiple of 16 or above 2^26,
+ * n_out > n_rows without ids, too many tensors; nothing enqueued) or -5
+ * (launch failure).  Tensors with n_out == 0 are skipped.
  */
 int ibp_ceiling_gather_copy(const ibp_copy_tensor *tensors, uint64_t n_tensors,
-                            void *stream);
+                            uint32_t max_workgroups, uint32_t pack, void *stream);
 
 #ifdef __cplusplus
 }

@@ -35,28 +35,31 @@ def lib() -> ctypes.CDLL:
                                "`python -m lossless_bit_level_amd.build`")
         L = ctypes.CDLL(_LIB_PATH)
         L.ibp_ceiling_gather_copy.argtypes = [ctypes.POINTER(ibp_copy_tensor), ctypes.c_uint64,
-                                              ctypes.c_void_p]
+                                              ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
         L.ibp_ceiling_gather_copy.restype = ctypes.c_int
         _lib = L
     return _lib
 
 
-def gather_copy_launcher(parts, stream=None):
+def gather_copy_launcher(parts, max_workgroups: int = 0, pack: bool = False, stream=None):
     """parts: list of (slots, src_bytes, ids or None, out) with slots a
     [n_rows, S] uint8 tensor (GPU or pinned host), src_bytes an int32 GPU
-    tensor of n_rows stored lengths, ids an int64 GPU tensor and out a GPU
-    tensor of n_out x S bytes.  Returns a no-argument callable that enqueues
-    the copy (one launch) on the current stream."""
+    tensor of the n_out stored lengths of the output rows' source rows, ids
+    an int64 GPU tensor and out a GPU tensor of n_out x S bytes;
+    max_workgroups caps the grid (0: none); pack puts several short rows in
+    one 4 KiB task.
+    Returns a no-argument callable that enqueues the copy (one launch) on
+    the current stream."""
     if not 0 < len(parts) <= IBP_CEILING_MAX_TENSORS:
         raise ValueError("1 to 16 tensors per copy")
     arr = (ibp_copy_tensor * len(parts))()
     for k, (slots, src_bytes, ids, out) in enumerate(parts):
         n_rows, row_bytes = ibp._rows(slots)
-        if src_bytes.dtype != torch.int32 or not src_bytes.is_cuda or src_bytes.numel() < n_rows:
-            raise ValueError("src_bytes must be an int32 GPU tensor of n_rows entries")
         if ids is not None:
             ibp._ids(ids)
         n_out = ids.numel() if ids is not None else n_rows
+        if src_bytes.dtype != torch.int32 or not src_bytes.is_cuda or src_bytes.numel() < n_out:
+            raise ValueError("src_bytes must be an int32 GPU tensor of n_out entries")
         ibp._need_cuda(out, "out")
         ibp._need_size(out, n_out * row_bytes, "out")
         arr[k] = ibp_copy_tensor(n_rows, row_bytes, ibp._dptr(slots), src_bytes.data_ptr(),
@@ -65,9 +68,11 @@ def gather_copy_launcher(parts, stream=None):
     fn = lib().ibp_ceiling_gather_copy
     s = ctypes.c_void_p((torch.cuda.current_stream() if stream is None else stream).cuda_stream)
     n = ctypes.c_uint64(len(parts))
+    cap = ctypes.c_uint32(max_workgroups)
+    pk = ctypes.c_uint32(1 if pack else 0)
 
     def launch():
-        rc = fn(arr, n, s)
+        rc = fn(arr, n, cap, pk, s)
         if rc:
             raise RuntimeError(f"ibp_ceiling_gather_copy failed ({rc})")
     launch.keep = (arr, parts)

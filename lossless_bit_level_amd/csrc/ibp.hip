@@ -49,6 +49,7 @@ constexpr uint64_t kMaxRowBytes = 1ull << 26;  // bit offsets fit 32 bits, count
 constexpr int kMaxRuns = 16;                   // runs of ~Mask for W = 32
 constexpr uint32_t kMaxGrid = 1u << 24;
 constexpr uint32_t kSpecWords = 32;            // first slot words fetched with the header
+constexpr uint32_t kSlotPipeMaxP = 8;          // row pipelines fetch whole slots up to this p
 
 // Run decomposition of the kept (non-invariant) bit positions ~Mask.  Run j
 // is a maximal stretch of kept block bits; `place[j]` is its mask in the
@@ -1284,18 +1285,132 @@ __device__ __forceinline__ void run_row_pipeline(
   }
 }
 
+// The same pipeline fetching each row's whole slot (S = 4n bytes) in one
+// step instead of a window and then the rest of the stream: for rows of 512
+// bytes to 2 KiB whose stored form is most of the slot (ratios near 1.1) the
+// few extra bytes cost less than the dependent second fetch and the stream
+// length it needs.  While row j is decoded, the slots of rows j+1 and j+2
+// are in flight (FV 16-byte loads per lane each).  Every iteration issues the
+// same vector memory instructions (FV loads, NCH stores), so the wait at the
+// top of an iteration leaves the next row's loads and this row's stores in
+// flight.  Same bookkeeping and id rules as run_row_pipeline.
+//   decode(hdr, x): the row's n words from the LDS copy of its slot, x[c] =
+//                   word c * 64 + lane; hdr holds header word q in lane q
+template <int NCH, bool GATHER, typename Decode>
+__device__ __forceinline__ void run_slot_pipeline(
+    const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
+    uint32_t* __restrict__ dst, uint32_t* lds, uint32_t i, uint32_t stride, Decode decode) {
+  constexpr uint32_t n = NCH * kWave;
+  constexpr int FV = NCH >= 4 ? NCH / 4 : 1;  // 16-byte loads per lane for a slot
+  const uint32_t lane = lane_id();
+  u32x4* l4 = reinterpret_cast<u32x4*>(lds);
+  for (uint32_t g = i; g < n_out;) {
+    const uint32_t K = (uint32_t)min<uint64_t>(kWave, ((uint64_t)n_out - g + stride - 1) / stride);
+    const uint64_t r = (uint64_t)g + (uint64_t)lane * stride;
+    const bool in = lane < K;
+    const uint64_t id = in ? (GATHER ? (uint64_t)ids[r] : r) : 0ull;
+    const bool ok = in && id < n_rows;
+    const uint64_t idc = ok ? id : 0ull;
+    const unsigned long long fw = flags[idc >> 6];
+    const uint64_t src_v = reinterpret_cast<uint64_t>(slots + idc * n);
+    unsigned long long ok_m = __ballot(ok);
+    unsigned long long fl_m = __ballot(ok && ((fw >> (idc & 63u)) & 1ull));
+    auto src_of = [&](uint32_t k) -> const uint32_t* {
+      const uint32_t kk = min(k, (uint32_t)kWave - 1u);
+      const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)src_v, kk);
+      const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(src_v >> 32), kk);
+      return reinterpret_cast<const uint32_t*>(((uint64_t)hi << 32) | lo);
+    };
+    auto ok_of = [&](int j) { return ((uint32_t)ok_m >> j) & 1u; };
+    auto fl_of = [&](int j) { return ((uint32_t)fl_m >> j) & 1u; };
+    // the whole slot of row k + j (nothing past the group)
+    auto load_slot = [&](int j, const uint32_t* src, u32x4* v) {
+      const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, ok_of(j) ? n * 4u : 0u);
+#pragma unroll
+      for (int c = 0; c < FV; ++c)
+        v[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (c * kWave + lane) * 16u, 0, 0);
+    };
+    uint32_t* out = dst + (uint64_t)g * n;
+    const uint64_t out_step = (uint64_t)stride * n;
+    uint32_t k = 0;
+    // One row: its slot `cur` has arrived; the slot of row k+2 goes into
+    // `nxt`.  The loop below is unrolled three times so that the three slot
+    // buffers change roles without register copies (a copy of a buffer whose
+    // load is in flight would wait for that load), and it has no exit inside
+    // a round (an exit block shared with the back edge would make the
+    // compiler's wait at the loop top cover the latest load); the last K % 3
+    // rows follow the loop.
+    auto row = [&](u32x4 (&cur)[FV], u32x4 (&nxt)[FV]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int c = 0; c < FV; ++c) l4[c * kWave + lane] = cur[c];
+      wave_lds_sync();
+      load_slot(2, src_of(k + 2), nxt);
+      uint32_t x[NCH];
+      if (!ok_of(0)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = 0u;
+      } else if (!fl_of(0)) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+      } else {
+        decode(lds[lane], x);
+      }
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+      __builtin_amdgcn_sched_barrier(0);
+      wave_lds_sync();
+      ++k;
+      ok_m >>= 1;
+      fl_m >>= 1;
+      out += out_step;
+    };
+    u32x4 sa[FV], sb[FV], sc[FV];
+    load_slot(0, src_of(0), sa);
+    load_slot(1, src_of(1), sb);
+    // wait for both here: at the loop top the compiler merges this state
+    // with the back edge's, where the last rows' stores are pending
+#pragma unroll
+    for (int c = 0; c < FV; ++c) asm volatile("" ::"v"(sa[c]), "v"(sb[c]));
+    for (uint32_t rounds = K / 3; rounds; --rounds) {
+      row(sa, sc);
+      row(sb, sa);
+      row(sc, sb);
+    }
+    if (K % 3 >= 1) row(sa, sc);
+    if (K % 3 == 2) row(sb, sa);
+    if ((uint64_t)g + (uint64_t)kWave * stride >= n_out) break;
+    g += kWave * stride;
+  }
+}
+
+// The row pipeline of a kernel: whole slots (SLOT) or window + rest.
+template <int NCH, bool GATHER, bool SLOT, typename StreamWords, typename Decode>
+__device__ __forceinline__ void row_pipeline(
+    const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
+    const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
+    uint32_t* __restrict__ dst, uint32_t* lds, uint32_t i, uint32_t stride,
+    StreamWords stream_words, Decode decode) {
+  if constexpr (SLOT)
+    run_slot_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride, decode);
+  else
+    run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                  stream_words, decode);
+}
+
 // [IBP] Decompression of rows of 64 * NCH blocks with one global Mask/Bitval
-// (p < 32): the row pipeline above.  A compressed row's stream length is
+// (p < 32): one of the row pipelines above (SLOT: whole slots).  A compressed row's stream length is
 // n + 32 n - p m bits (m = its header popcount); a payload's bit offset is
 // u + 32 lane - p * (stripped blocks of the chunk below the lane).
-template <int MODE, int NR, int NCH>
+template <int MODE, int NR, int NCH, bool SLOT = false>
 __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
     Codec cd, const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
     const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
     uint32_t* __restrict__ dst) {
   using P = RowPipe<NCH>;
   constexpr uint32_t n = P::n;
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][P::kLdsWords];
+  __shared__ __attribute__((aligned(16)))
+  uint32_t lds_all[kWavesPerBlock][SLOT ? (NCH >= 4 ? n : 256u) + 4u : P::kLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
@@ -1319,8 +1434,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe_kernel(
       u += 32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
     }
   };
-  run_row_pipeline<NCH, MODE == kModeGather>(slots, flags, ids, n_rows, n_out, dst, lds, i,
-                                             stride, stream_words, decode);
+  row_pipeline<NCH, MODE == kModeGather, SLOT>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                               stride, stream_words, decode);
 }
 
 // ---------------------------------------------------- other block widths --
@@ -2534,8 +2649,8 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
             uw += (uint32_t)__popcll(kept);
           }
         };
-        run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
-                                      stream_words, decode);
+        row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                         stream_words, decode);
       } else {
         PosEntry e = pos_entry<n>(tf, 0);
         e.mask = m0;
@@ -2556,8 +2671,13 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
             u += 32u * kWave - p * (uint32_t)__popcll(h);
           }
         };
-        run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
-                                      stream_words, decode);
+        // few invariant bits: whole slots, as the global decoder fetches them
+        if (p <= kSlotPipeMaxP)
+          row_pipeline<NCH, GATHER, true>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                          stream_words, decode);
+        else
+          row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                           stream_words, decode);
       }
       return;
     }
@@ -2591,8 +2711,8 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
       u += 32u * kWave - __builtin_amdgcn_readlane(incl, kWave - 1);
     }
   };
-  run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
-                                stream_words, decode);
+  row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                   stream_words, decode);
 }
 
 // ------------------------------------------------------ packed cache ----
@@ -2997,17 +3117,28 @@ void launch_decode_t(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_rows_kernel<MODE, NR, NCH>), dim3(grid), dim3(kBlockThreads), \
                      0, st, cd, sl, fl, id_p, arena, cloc, a.n_rows, cnt, out_p, a.vec)
 #define IBP_PIPE(NCH)                                                                      \
-  hipLaunchKernelGGL((decode_pipe_kernel<MODE, NR, NCH>),                                   \
-                     dim3(pipe_grid), dim3(kBlockThreads), 0, st, cd, sl, fl, id_p, a.n_rows, \
-                     cnt, out_p)
+  if (slot_pipe)                                                                            \
+    hipLaunchKernelGGL((decode_pipe_kernel<MODE, NR, NCH, true>),                           \
+                       dim3(pipe_grid), dim3(kBlockThreads), 0, st, cd, sl, fl, id_p, a.n_rows, \
+                       cnt, out_p);                                                           \
+  else                                                                                      \
+    hipLaunchKernelGGL((decode_pipe_kernel<MODE, NR, NCH>),                                 \
+                       dim3(pipe_grid), dim3(kBlockThreads), 0, st, cd, sl, fl, id_p, a.n_rows, \
+                       cnt, out_p)
       // rows of 128-512 blocks with some invariant bits kept, 16-byte
       // aligned, not through the cache: the pipelined kernel on a resident
       // grid (measured: dense 1 KiB feature rows 21.1 -> 20.2 us per 65,536
       // ids; for 4 KiB rows, of which a launch gives each wave about two,
-      // decode_rows_kernel on a larger grid is as fast or faster)
+      // decode_rows_kernel on a larger grid is as fast or faster, with either
+      // pipeline).  With at most 8 invariant bits a stored row is at least
+      // about three quarters of its slot, and the pipeline fetches whole
+      // slots, 6 workgroups per CU (measured with the Zipf ids: embeddings
+      // 12.2 -> 10.2 us, dense features 21.2 -> 18.9 us); otherwise the
+      // header window and then the rest of the stream, 8 per CU.
       if constexpr (MODE != kModeCached && NR != 0) {
         if (a.vec && (cd.n == 128 || cd.n == 256 || cd.n == 512)) {
-          const uint32_t pipe_grid = row_pipe_grid(cnt, kWavesPerBlock, 8);
+          const bool slot_pipe = cd.p <= kSlotPipeMaxP;
+          const uint32_t pipe_grid = row_pipe_grid(cnt, kWavesPerBlock, slot_pipe ? 6u : 8u);
           switch (cd.n) {
             case 128: IBP_PIPE(2); break;
             case 256: IBP_PIPE(4); break;

@@ -2,9 +2,14 @@
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU
 baseline of the benchmark use this module; the product library never does.
-The arithmetic lives in ``ibp_oracle.c`` (plain bit-serial C, see its
-header for the method's source and the readings of it); this file only
-compiles it with gcc, loads it with ctypes and moves numpy arrays in and out.
+The method's arithmetic (metadata, compression, decompression, gather,
+global and per-position) lives in ``ibp_oracle.c`` (plain bit-serial C, see
+its header for the method's source and the readings of it); for those this
+file only compiles the C with gcc, loads it with ctypes and moves numpy
+arrays in and out.  One part is written here in Python instead: the packed
+layout of the compressed GPU cache (cache_pack, cache_gather), which is plain
+byte bookkeeping around the C decoder -- each cached row's stored words
+copied back to back at 16-byte boundaries, with a 64-bit locator per row.
 """
 from __future__ import annotations
 

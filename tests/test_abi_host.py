@@ -61,15 +61,15 @@ def test_ceiling_library_exports_and_validation():
     T = ceiling.ibp_copy_tensor
     f = ceiling.lib().ibp_ceiling_gather_copy
     fake = 0x10000
-    assert f(None, 0, 0, None) == 0
-    assert f((T * 1)(T(4, 4096, fake, fake, None, 0, fake)), 1, 0, None) == 0   # nothing to copy
+    assert f(None, 0, 0, 0, None) == 0
+    assert f((T * 1)(T(4, 4096, fake, fake, None, 0, fake)), 1, 0, 0, None) == 0   # nothing to copy
     for bad in [T(4, 4100, fake, fake, None, 4, fake),       # row_bytes % 16
                 T(4, 4096, fake + 4, fake, None, 4, fake),   # misaligned src
                 T(4, 4096, fake, fake, None, 5, fake),       # n_out > n_rows without ids
                 T(4, 4096, fake, None, None, 4, fake),       # no src_bytes
                 T(4, 4096, fake, fake, fake + 4, 4, fake)]:  # misaligned ids
-        assert f((T * 1)(bad), 1, 0, None) == -1
-    assert f((T * 17)(), 17, 0, None) == -1
+        assert f((T * 1)(bad), 1, 0, 0, None) == -1
+    assert f((T * 17)(), 17, 0, 0, None) == -1
 
 
 def test_flag_words_and_status_strings(ibp):

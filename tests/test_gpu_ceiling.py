@@ -1,8 +1,8 @@
 """The gather-copy ceiling (libibp_ceiling) moves the bytes it claims: output
-row i = the first src_bytes[r] bytes (rounded up to 16) of slot r = ids[i],
-zeros after; an id outside the table gives a zero row.  Packed rows (several
-per 4 KiB task), chunked rows (8 and 28 KiB), several tensors in one launch,
-a pinned host source.  The benchmark times this copy as the floor of each
+row i = the first src_bytes[i] bytes (rounded up to 16) of slot ids[i],
+zeros after; an id outside the table gives a zero row.  Rows of 16 B to
+4 KiB (one task each), chunked rows (8 and 28 KiB), several tensors in one
+launch, a capped grid, a pinned host source.  The benchmark times this copy as the floor of each
 decompression, so it has to read and write exactly that."""
 import numpy as np
 import pytest
@@ -27,26 +27,29 @@ def expected(table: np.ndarray, src_bytes: np.ndarray, ids) -> np.ndarray:
     out = np.zeros((len(rows), S), np.uint8)
     for i, r in enumerate(rows):
         if 0 <= r < n_rows:
-            nb = min(S, (int(src_bytes[r]) + 15) // 16 * 16)
+            nb = min(S, (int(src_bytes[i]) + 15) // 16 * 16)
             out[i, :nb] = table[r, :nb]
     return out
 
 
 def case(rng, n_rows, S, n_ids):
     table = rng.integers(0, 256, (n_rows, S), dtype=np.uint8)
-    src_bytes = (rng.integers(0, S // 4 + 40, n_rows) * 4).astype(np.int32)
-    src_bytes[:3] = [0, S, 4]
     ids = None
     if n_ids is not None:
         ids = rng.integers(-2, n_rows + 3, n_ids).astype(np.int64)
+    n_out = n_rows if ids is None else n_ids
+    src_bytes = (rng.integers(0, S // 4 + 40, n_out) * 4).astype(np.int32)
+    src_bytes[:3] = [0, S, 4]
     return table, src_bytes, ids
 
 
+@pytest.mark.parametrize("pack", [False, True])
+@pytest.mark.parametrize("cap", [0, 1, 7])
 @pytest.mark.parametrize("S,n_rows,n_ids", [(512, 3000, 5000), (1024, 700, 4097),
                                             (2048, 513, 1000), (4096, 300, 999),
                                             (16, 100, 77), (8192, 65, None),
                                             (28672, 33, None), (1040, 40, 90)])
-def test_gather_copy_single(ceiling, S, n_rows, n_ids):
+def test_gather_copy_single(ceiling, S, n_rows, n_ids, cap, pack):
     rng = np.random.default_rng(S + n_rows)
     table, sb, ids = case(rng, n_rows, S, n_ids)
     tg = torch.from_numpy(table).cuda()
@@ -54,7 +57,7 @@ def test_gather_copy_single(ceiling, S, n_rows, n_ids):
     idg = torch.from_numpy(ids).cuda() if ids is not None else None
     n_out = len(ids) if ids is not None else n_rows
     out = torch.full((n_out, S), 0xAB, dtype=torch.uint8, device="cuda")
-    ceiling.gather_copy_launcher([(tg, sbg, idg, out)])()
+    ceiling.gather_copy_launcher([(tg, sbg, idg, out)], max_workgroups=cap, pack=pack)()
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), expected(table, sb, ids))
 
@@ -72,7 +75,10 @@ def test_gather_copy_batch_and_host_source(ceiling):
         out = torch.full((n_out, S), 0xCD, dtype=torch.uint8, device="cuda")
         parts.append((tg, torch.from_numpy(sb).cuda(), idg, out))
         want.append(expected(table, sb, ids))
-    ceiling.gather_copy_launcher(parts)()
-    torch.cuda.synchronize()
-    for (_, _, _, out), w in zip(parts, want):
-        assert np.array_equal(out.cpu().numpy(), w)
+    for cap, pack in ((0, False), (3, False), (0, True), (5, True)):
+        for _, _, _, out in parts:
+            out.fill_(0xCD)
+        ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack)()
+        torch.cuda.synchronize()
+        for (_, _, _, out), w in zip(parts, want):
+            assert np.array_equal(out.cpu().numpy(), w)
