@@ -453,6 +453,41 @@ __global__ __launch_bounds__(kBlockThreads) void reduce_counts_kernel(
   if (lane == 0) counts[b] = t;
 }
 
+// Flag bits of rows [base, base + k) (bit j of fl: row base + j is stored
+// compressed), 1 <= k <= 64, written into their one or two flag words
+// without assuming the words were cleared: the piece's bits are cleared with
+// an atomic AND, then the set ones ORed in (one row alone: a single OR or
+// AND).  No other piece touches these bits, so pieces that share a word
+// commute.  The piece that ends the table also clears the bits of its word
+// past the table (they must read 0).
+__device__ __forceinline__ void put_flag_bits(unsigned long long* flags, uint64_t base,
+                                              uint32_t k, unsigned long long fl,
+                                              uint64_t n_rows) {
+  const uint32_t sh = (uint32_t)(base & 63u);
+  const uint32_t end = sh + k;  // one past the piece's last bit, counted from word 0
+  const bool last = base + k == n_rows;
+  unsigned long long* w0 = flags + (base >> 6);
+  const unsigned long long tail = last && end < 64u ? ~0ull << end : 0ull;
+  if (k == 1u) {  // rows compressed one per workgroup: one atomic per row
+    if (fl & 1ull)
+      atomicOr(w0, 1ull << sh);
+    else
+      atomicAnd(w0, ~(1ull << sh));
+    if (tail) atomicAnd(w0, ~tail);
+    return;
+  }
+  const unsigned long long span = k == 64u ? ~0ull : ((1ull << k) - 1ull);
+  atomicAnd(w0, ~((span << sh) | tail));
+  if (fl << sh) atomicOr(w0, fl << sh);
+  if (end > 64u) {  // the piece continues in the next word (sh > 0 here)
+    unsigned long long clear1 = span >> (64u - sh);
+    if (last) clear1 |= ~0ull << (end - 64u);
+    atomicAnd(w0 + 1, ~clear1);
+    const unsigned long long set1 = fl >> (64u - sh);
+    if (set1) atomicOr(w0 + 1, set1);
+  }
+}
+
 // [IBP] Compression, one workgroup per row.  The row's stream is assembled
 // in LDS: header words from per-chunk ballots, a workgroup scan of the chunk
 // match counts, then every lane ORs its payload (<= 2 words) into place with
@@ -545,10 +580,12 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
       for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
       if (row_bits) row_bits[row] = c_bits;
     }
-    __syncthreads();
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + gridDim.x < n_rows) __syncthreads();
   }
 }
 
@@ -586,8 +623,13 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
       if (lane == 2u * c) hword = (uint32_t)h;
       if (lane == 2u * c + 1) hword = (uint32_t)(h >> 32);
     }
-    // the payload part of the stream starts zeroed; header words are whole
-    for (uint32_t j = n / 32 + threadIdx.x; j < n + 4; j += WPB * kWave) buf[j] = 0u;
+    // the payload part of the stream starts zeroed (16-byte LDS stores: n/32
+    // and n + 4 are multiples of 4); header words are whole
+    {
+      u32x4* b4 = reinterpret_cast<u32x4*>(buf);
+      for (uint32_t j = n / 128 + threadIdx.x; j < (n + 4) / 4; j += WPB * kWave)
+        b4[j] = u32x4{0u, 0u, 0u, 0u};
+    }
     if (lane < 2u * CPW) buf[2u * c0 + lane] = hword;
     if (lane == 0) wtot[wave] = mw;
     __syncthreads();
@@ -606,29 +648,49 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
     } else {
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
+        // the ballot again (two instructions, cheaper than keeping CPW of
+        // them in scalar registers, which spill)
         const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
         const bool match = __builtin_amdgcn_inverse_ballot_w64(h);
         const uint32_t k = (c0 + c) * kWave + lane;
         const uint32_t off =
             n + 32u * k - __umul24(cd.p, carry + bits_below_lane((uint32_t)h, (uint32_t)(h >> 32)));
-        const uint32_t len = match ? 32u - cd.p : 32u;
-        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
-        if (len) {
-          const uint32_t sh = off & 31u, wi = off >> 5;
-          atomicOr(&buf[wi], pay << sh);
-          if (sh + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sh));
+        if constexpr (NR != 0) {
+          // p < 32: every block has a payload of 32 - p or 32 bits; its two
+          // stream words get their bits with no branch (the second OR is of
+          // zero when the payload ends in the first word)
+          const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+          const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
+          atomicOr(&buf[off >> 5], (uint32_t)w2);
+          atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
+        } else {
+          // p = 32: a stripped block has no payload
+          if (!match) {
+            const uint32_t sh = off & 31u, wi = off >> 5;
+            atomicOr(&buf[wi], x[c] << sh);
+            if (sh) atomicOr(&buf[wi + 1], x[c] >> (32u - sh));
+          }
         }
         carry += (uint32_t)__popcll(h);
       }
       __syncthreads();
       const uint32_t nw = store_words(s_row, (c_bits + 31u) >> 5, n, cd.pad);
-      for (uint32_t j = threadIdx.x; j < nw; j += WPB * kWave) s_row[j] = buf[j];
+      uint32_t j0 = 0;
+      if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
+        const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
+        u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
+        for (uint32_t j = threadIdx.x; j < nw / 4; j += WPB * kWave) o4[j] = b4[j];
+        j0 = nw & ~3u;
+      }
+      for (uint32_t j = j0 + threadIdx.x; j < nw; j += WPB * kWave) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
       if (row_bits) row_bits[row] = c_bits;
     }
-    __syncthreads();
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + gridDim.x < n_rows) __syncthreads();
   }
 }
 
@@ -658,11 +720,7 @@ __device__ __forceinline__ void compress_row_range(uint64_t n_rows, uint32_t wav
       fl |= (unsigned long long)(c_bits < raw_bits) << k;
     }
     if (row_bits && lane < K) row_bits[base + lane] = cb;
-    if (fl && lane < 2u) {  // the piece's bits span one or two flag words
-      const uint32_t sh = (uint32_t)(base & 63u);
-      const unsigned long long part = lane == 0 ? fl << sh : (sh ? fl >> (64u - sh) : 0ull);
-      if (part) atomicOr(&flags[(base >> 6) + lane], part);
-    }
+    if (lane == 0) put_flag_bits(flags, base, K, fl, n_rows);
   }
 }
 
@@ -1579,10 +1637,12 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
       for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
       if (row_bits) row_bits[row] = c_bits;
     }
-    __syncthreads();
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + gridDim.x < n_rows) __syncthreads();
   }
 }
 
@@ -1793,10 +1853,12 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
       for (uint32_t j = threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
       if (row_bits) row_bits[row] = c_bits;
     }
-    __syncthreads();
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + gridDim.x < n_rows) __syncthreads();
   }
 }
 
@@ -2269,10 +2331,12 @@ __global__ __launch_bounds__(kBlockThreads) void compress_positional_kernel(
       for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
     }
     if (threadIdx.x == 0) {
-      if (flag) atomicOr(&flags[row >> 6], 1ull << (row & 63));
+      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
       if (row_bits) row_bits[row] = c_bits;
     }
-    __syncthreads();
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + gridDim.x < n_rows) __syncthreads();
   }
 }
 
@@ -3566,9 +3630,8 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
   rc = pending_hip_error();
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const uint64_t fw = ibp_flag_words(n_rows);
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
-                     (unsigned long long*)flags, fw, 0ull);
+  // no clearing launch: every row's flag bit is cleared or set by the
+  // kernel that compresses the row (put_flag_bits)
   if (md->width_bits != 32) {
     if (md->width_bits == 16)
       launch_compress_wide<uint16_t>(md, n_rows, row_bytes, src, slots, flags, row_bits, st);
@@ -3942,9 +4005,8 @@ int ibp_compress_positional(const void* table, uint64_t n_rows, uint64_t row_byt
   rc = pending_hip_error();
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  const uint64_t fw = ibp_flag_words(n_rows);
-  hipLaunchKernelGGL(fill_u64_kernel, dim3(grid_for((fw + 255) / 256)), dim3(256), 0, st,
-                     (unsigned long long*)flags, fw, 0ull);
+  // no clearing launch: every row's flag bit is cleared or set by the
+  // kernel that compresses the row (put_flag_bits)
   const uint32_t n = (uint32_t)(row_bytes / 4);
   if (n == 128 || n == 256 || n == 512 || n == 1024) {
     // one wave per row, the table in LDS per workgroup; four times as many

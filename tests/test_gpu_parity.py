@@ -425,7 +425,8 @@ def test_compress_row_ranges_across_flag_words(ibp, kind):
             x[r] = rng.integers(0, 2**32, n, dtype=np.uint64).astype(np.uint32)
         table = ibp.ibp_positional_table(mask, bitval).cuda()
         xg = to_gpu(x)
-        slots, flags, rb = ibp.ibp_compress_positional(table, xg)
+        flags0 = torch.full((ibp.ibp_flag_words(n_rows),), -1, dtype=torch.int64, device="cuda")
+        slots, flags, rb = ibp.ibp_compress_positional(table, xg, flags=flags0)
         torch.cuda.synchronize()
         slots_o, flags_o, rb_o = orc.compress_positional(_pm_from_np(mask, bitval), x)
         back = ibp.ibp_decompress_positional(table, slots, flags)
@@ -439,7 +440,9 @@ def test_compress_row_ranges_across_flag_words(ibp, kind):
             x = make_rows_w(rng, w, n_rows, 512, mask, bitval, 0.9, raw_rows=raw)
         md = gmd(ibp, mask, bitval, w=w)
         xg = to_gpu(x)
-        slots, flags, rb = ibp.ibp_compress(md, xg)
+        # flag words start as all ones: every bit is cleared or set by its row
+        flags0 = torch.full((ibp.ibp_flag_words(n_rows),), -1, dtype=torch.int64, device="cuda")
+        slots, flags, rb = ibp.ibp_compress(md, xg, flags=flags0)
         torch.cuda.synchronize()
         slots_o, flags_o, rb_o = orc.compress(omd(md), x)
         back = ibp.ibp_decompress(md, slots, flags)
@@ -447,6 +450,50 @@ def test_compress_row_ranges_across_flag_words(ibp, kind):
                        rb.cpu().numpy()[:n_rows].view(np.uint32), slots_o, flags_o, rb_o)
     assert torch.equal(back, xg)
     assert flags_o.any() and not all(flag_of(flags_o, r) for r in raw)
+
+
+@pytest.mark.parametrize("kind,row_bytes", [
+    ("w32", 128), ("w32", 512), ("w32", 8192), ("w32", 4100), ("w16", 8192), ("w16", 512),
+    ("w64", 2048), ("w64", 4104), ("positional", 512), ("positional", 4100)])
+def test_flags_written_over_any_prior_contents(ibp, kind, row_bytes):
+    """Every compression kernel writes each row's flag bit itself (no clearing
+    launch): flag words that start as all ones, or as the flags of another
+    table, end equal to the oracle's, with the bits past the table zero.
+    Ragged row counts end inside a flag word; half the rows are raw."""
+    rng = np.random.default_rng(row_bytes + len(kind))
+    w = 32 if kind == "positional" else int(kind[1:])
+    mask, bitval = {32: (0x7C000000, 0x3C000000), 16: (0x7C00, 0x3C00),
+                    64: (0x7C0000007C000000, 0x3C0000003C000000)}[w]
+    for n_rows, prior in ((1, "ones"), (65, "ones"), (200, "ones"), (200, "other")):
+        raw = tuple(range(1, n_rows, 2))
+        x = make_rows(rng, n_rows, row_bytes, mask, bitval, match_p=0.95, raw_rows=raw) \
+            if w == 32 else make_rows_w(rng, w, n_rows, row_bytes, mask, bitval, 0.95, raw_rows=raw)
+        fw = ibp.ibp_flag_words(n_rows)
+        if prior == "ones":
+            flags = torch.full((fw,), -1, dtype=torch.int64, device="cuda")
+        else:  # the flags of the same rows with the raw ones swapped
+            flags = torch.from_numpy(rng.integers(-2**63, 2**63 - 1, fw, dtype=np.int64)).cuda()
+        xg = to_gpu(x)
+        if kind == "positional":
+            n = row_bytes // 4
+            m = np.full(n, mask, np.uint64)
+            b = np.full(n, bitval, np.uint64)
+            m[1] = 0xFFFFFFFF
+            b[1] = 0
+            table = ibp.ibp_positional_table(m, b).cuda()
+            slots, flags, rb = ibp.ibp_compress_positional(table, xg, flags=flags)
+            slots_o, flags_o, rb_o = orc.compress_positional(_pm_from_np(m, b), x)
+        else:
+            md = gmd(ibp, mask, bitval, w=w)
+            slots, flags, rb = ibp.ibp_compress(md, xg, flags=flags)
+            slots_o, flags_o, rb_o = orc.compress(omd(md), x)
+        torch.cuda.synchronize()
+        got = flags.cpu().numpy().view(np.uint64)[:fw]
+        assert np.array_equal(got, flags_o), (n_rows, prior)
+        assert_image_equal(slots.cpu().numpy(), got, rb.cpu().numpy()[:n_rows].view(np.uint32),
+                           slots_o, flags_o, rb_o)
+        assert flags_o.any()
+        assert n_rows == 1 or not all(flag_of(flags_o, r) for r in range(n_rows))
 
 
 # ----------------------------------------------------- full-size workloads --
