@@ -105,6 +105,13 @@ __device__ __forceinline__ uint32_t lane_id() {
   return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
 }
 
+// v_writelane_b32: `old` with lane `lane` (a constant) set to the scalar v
+// (the intrinsic, which this compiler has no builtin for).
+__device__ int lane_write(int v, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// v_mul_i32_i24: the product of the low 24 bits of a and b, as signed values.
+__device__ int mul_i24(int a, int b) __asm("llvm.amdgcn.mul.i24.i32");
+
 __device__ __forceinline__ uint32_t uniform(uint32_t v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
@@ -488,6 +495,22 @@ __device__ __forceinline__ void put_flag_bits(unsigned long long* flags, uint64_
   }
 }
 
+// Flag bits of rows [base, base + k) written as whole bytes with plain
+// stores, base a multiple of 8 and 1 <= k <= 64, by a whole wave (lane j
+// writes byte j).  The caller owns every row of these bytes: k is a multiple
+// of 8 or the piece ends the table, so no other piece shares a byte and no
+// atomic is needed.  The piece that ends the table also zeroes the bytes of
+// its word past the table (they must read 0).
+__device__ __forceinline__ void put_flag_bytes(unsigned long long* flags, uint64_t base,
+                                               uint32_t k, unsigned long long fl,
+                                               uint64_t n_rows, uint32_t lane) {
+  unsigned char* fb = reinterpret_cast<unsigned char*>(flags) + base / 8;
+  const uint32_t nb = (k + 7u) / 8u;
+  const uint32_t last =
+      base + k == n_rows ? (uint32_t)((n_rows + 63u) / 64u * 8u - base / 8u) : nb;
+  if (lane < last) fb[lane] = lane < nb ? (unsigned char)(fl >> (8u * lane)) : (unsigned char)0;
+}
+
 // [IBP] Compression, one workgroup per row.  The row's stream is assembled
 // in LDS: header words from per-chunk ballots, a workgroup scan of the chunk
 // match counts, then every lane ORs its payload (<= 2 words) into place with
@@ -590,38 +613,72 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
 }
 
 // [IBP] Compression of rows of exactly WPB * 64 * CPW blocks (the long rows
-// of LLM weight matrices), one workgroup of WPB waves per row: each wave
-// holds its share of the row in registers (chunks wave * CPW ... + CPW - 1,
-// one block per lane each), so the row is read once.  The chunk ballots are the header words;
-// the waves' match totals, exchanged through LDS, give each wave its carry;
-// payloads are ORed into the workgroup's LDS stream, which is then written
-// with coalesced stores (a raw row straight from the registers).  Three
-// barriers per row.  In place (src == slots) is safe: every wave has read its
-// part of the row before the first barrier, and nothing is written before it.
+// of LLM weight matrices), a workgroup of WPB waves per row: each wave holds
+// its share of the row in registers (chunks wave * CPW ... + CPW - 1, one
+// block per lane each), so the row is read once.  A workgroup takes a
+// contiguous range of `per_wg` rows (at most 64) and loads its next row while
+// it encodes one.  The chunk ballots are the header words (each placed
+// in its lane with a lane write); the waves' match totals, exchanged through
+// LDS, give each wave its carry; payloads are ORed into the workgroup's LDS
+// stream, which is then written with coalesced stores (a raw row straight
+// from the registers).  Three barriers per row.  The range's flag bits are
+// written once at its end: as whole bytes with plain stores when per_wg is a
+// multiple of 8 (the workgroup owns those bytes), else with an atomic AND and
+// OR; per-row atomics on the few flag words of a matrix serialize (one per
+// row cost a third of the time of a 4096 x 8 KiB matrix).  In place
+// (src == slots) is safe: every wave has read its part of the row before the
+// first barrier and nothing is written before it, and the rows loaded ahead
+// are other rows, whose slots no store of this one touches.
 template <int NR, int CPW, int WPB>
 __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
     Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
-    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits, uint32_t per_wg) {
   constexpr uint32_t n = (uint32_t)CPW * kWave * WPB;
   __shared__ uint32_t buf[n + 4];
-  __shared__ uint32_t wtot[WPB];
+  __shared__ uint32_t wtot[WPB];  // the waves' match totals
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t c0 = wave * CPW;  // the wave's first chunk
-  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
-    const uint32_t* x_row = src + row * n;
-    uint32_t* s_row = slots + row * n;
-    uint32_t x[CPW];
+  const uint32_t lane_byte = (c0 * kWave + lane) * 4u;
+  // a run's kept bits at their payload position: extract = OR of
+  // (x >> shift) & kept, a shift and an and-or per run
+  constexpr int NK = NR > 0 ? NR : 1;
+  uint32_t kept[NK];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) x[c] = x_row[(c0 + c) * kWave + lane];
+  for (int j = 0; j < NK; ++j) kept[j] = NR > 0 ? cd.runs.place[j] >> cd.runs.shift[j] : 0u;
+  // this lane's first payload offset in bits, less the carry: the stream's
+  // n header bits, then 32 bits per block before it
+  const uint32_t off0 = n + 8u * lane_byte;
+  const int negp = -(int)cd.p;
+  const uint64_t r0 = (uint64_t)blockIdx.x * per_wg;
+  const uint64_t r1 = min(n_rows, r0 + per_wg);
+  // a row past the range loads as zeros (empty range), never out of bounds
+  auto load = [&](uint32_t (&v)[CPW], uint64_t r) {
+    const __amdgpu_buffer_rsrc_t in =
+        row_rsrc(src + (r < r1 ? r : r0) * n, r < r1 ? n * 4u : 0u);
+    // the lane's offset as an opaque value: the chunks' offsets are then
+    // immediates on it, not CPW precomputed registers
+    uint32_t lb = lane_byte;
+    asm volatile("" : "+v"(lb));
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+  };
+  uint32_t x[CPW];
+  load(x, r0);
+  unsigned long long fl = 0;  // bit j: row r0 + j is stored compressed
+  for (uint64_t row = r0; row < r1; ++row) {
+    uint32_t* s_row = slots + row * n;
+    uint32_t y[CPW];  // the next row, in flight
+    load(y, row + 1);
     uint32_t mw = 0;
     uint32_t hword = 0;  // lane 2c / 2c + 1: low / high half of chunk c's ballot
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
       mw += (uint32_t)__popcll(h);
-      if (lane == 2u * c) hword = (uint32_t)h;
-      if (lane == 2u * c + 1) hword = (uint32_t)(h >> 32);
+      hword = (uint32_t)lane_write((int)(uint32_t)h, 2 * c, (int)hword);
+      hword = (uint32_t)lane_write((int)(uint32_t)(h >> 32), 2 * c + 1, (int)hword);
     }
     // the payload part of the stream starts zeroed (16-byte LDS stores: n/32
     // and n + 4 are multiples of 4); header words are whole
@@ -642,24 +699,41 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
     }
     const uint32_t c_bits = n + 32u * n - cd.p * m;
     const bool flag = c_bits < 32u * n;
-    if (!flag) {
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) s_row[(c0 + c) * kWave + lane] = x[c];
-    } else {
+    fl |= (unsigned long long)flag << (row - r0);
+    if (flag) {
+      // off0 as an opaque value of this row: folded into CPW loop-invariant
+      // chunk bases it would hold as many registers
+      uint32_t ob = off0;
+      asm volatile("" : "+v"(ob));
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
-        // the ballot again (two instructions, cheaper than keeping CPW of
-        // them in scalar registers, which spill)
-        const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
-        const bool match = __builtin_amdgcn_inverse_ballot_w64(h);
-        const uint32_t k = (c0 + c) * kWave + lane;
-        const uint32_t off =
-            n + 32u * k - __umul24(cd.p, carry + bits_below_lane((uint32_t)h, (uint32_t)(h >> 32)));
+        // the match test again: two instructions, where reusing the first
+        // pass's masks keeps CPW of them in scalar registers and costs as
+        // many to turn back into lane masks
+        asm volatile("" : "+v"(x[c]));
+        const bool match = (x[c] & cd.mask) == cd.bitval;
+        const unsigned long long h = __ballot(match);
+        // offset = this lane's 32-bit slots before it less p per stripped
+        // block before it: one multiply-add on the lane's count and a scalar
+        // for the chunk (kept opaque so that it is not split into per-chunk
+        // vector constants)
+        const uint32_t below = bits_below_lane((uint32_t)h, (uint32_t)(h >> 32));
+        uint32_t t = (uint32_t)(c * kWave * 32) - cd.p * carry;
+        asm volatile("" : "+s"(t));
+        const uint32_t off = (uint32_t)mul_i24((int)below, negp) + ob + t;
         if constexpr (NR != 0) {
           // p < 32: every block has a payload of 32 - p or 32 bits; its two
           // stream words get their bits with no branch (the second OR is of
           // zero when the payload ends in the first word)
-          const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+          uint32_t e;
+          if constexpr (NR > 0) {
+            e = (x[c] >> cd.runs.shift[0]) & kept[0];
+#pragma unroll
+            for (int j = 1; j < NR; ++j) e |= (x[c] >> cd.runs.shift[j]) & kept[j];
+          } else {
+            e = extract_kept<NR>(x[c], cd.runs);
+          }
+          const uint32_t pay = match ? e : x[c];
           const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
           atomicOr(&buf[off >> 5], (uint32_t)w2);
           atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
@@ -673,7 +747,16 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
         }
         carry += (uint32_t)__popcll(h);
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    if (!flag) {
+      const __amdgpu_buffer_rsrc_t out = row_rsrc(s_row, n * 4u);
+      uint32_t lb = lane_byte;
+      asm volatile("" : "+v"(lb));
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
+    } else {
       const uint32_t nw = store_words(s_row, (c_bits + 31u) >> 5, n, cd.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
@@ -684,13 +767,19 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
       }
       for (uint32_t j = j0 + threadIdx.x; j < nw; j += WPB * kWave) s_row[j] = buf[j];
     }
-    if (threadIdx.x == 0) {
-      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
-      if (row_bits) row_bits[row] = c_bits;
-    }
+    if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) x[c] = y[c];
     // the LDS stream is reused only by a next row; after the last one the
     // workgroup ends without waiting for its stores (a barrier would)
-    if (row + gridDim.x < n_rows) __syncthreads();
+    if (row + 1 < r1) __syncthreads();
+  }
+  if (wave == 0 && r0 < r1) {
+    const uint32_t k = (uint32_t)(r1 - r0);
+    if (per_wg % 8u == 0)
+      put_flag_bytes(flags, r0, k, fl, n_rows, lane);
+    else if (lane == 0)
+      put_flag_bits(flags, r0, k, fl, n_rows);
   }
 }
 
@@ -729,12 +818,12 @@ __device__ __forceinline__ void compress_row_range(uint64_t n_rows, uint32_t wav
 // same number), in pieces of up to 64 rows whose flag bits it ORs into their
 // flag words at once and whose C values it stores with one instruction.  A
 // row is read into registers (NCH blocks per lane); each chunk's match
-// ballot is its 64-bit header word, the chunk prefixes are a scalar running
-// sum, and the payloads are ORed into a wave-private LDS stream buffer,
-// written out with NCH buffer stores whose range is the row's stored words
-// (the same instructions for a raw row).  No workgroup barriers.  In place
-// (src == slots) is safe: a row's stores depend on all of its loads, and no
-// other row's stores touch it.
+// ballot is its 64-bit header word (placed in its lane with a lane write),
+// the chunk prefixes are a scalar running sum, and the payloads are ORed into
+// a wave-private LDS stream buffer, written out with NCH buffer stores whose
+// range is the row's stored words (the same instructions for a raw row).  No
+// workgroup barriers.  In place (src == slots) is safe: a row's stores depend
+// on all of its loads, and no other row's stores touch it.
 template <int NR, int NCH>
 __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
     Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
@@ -744,66 +833,82 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* buf = lds_all[wave];
-  compress_row_range(n_rows, wave, kWavesPerBlock, 32u * n, flags, row_bits, [&](uint64_t row) {
-    const __amdgpu_buffer_rsrc_t in = row_rsrc(src + row * n, n * 4u);
-    uint32_t x[NCH];
+  constexpr int NK = NR > 0 ? NR : 1;
+  uint32_t kept[NK];  // a run's kept bits at their payload position
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
-      x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, (c * kWave + lane) * 4u, 0, 0);
-    unsigned long long h[NCH];
+  for (int j = 0; j < NK; ++j) kept[j] = NR > 0 ? cd.runs.place[j] >> cd.runs.shift[j] : 0u;
+  const int negp = -(int)cd.p;
+  compress_row_range(n_rows, wave, kWavesPerBlock, 32u * n, flags, row_bits, [&](uint64_t row) {
+    uint32_t x[NCH];
+    {
+      const __amdgpu_buffer_rsrc_t in = row_rsrc(src + row * n, n * 4u);
+      uint32_t lb = lane * 4u;  // opaque: the chunks' offsets are immediates on it
+      asm volatile("" : "+v"(lb));
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+    }
     uint32_t m = 0;
+    uint32_t hword = 0;  // lane 2c / 2c + 1: low / high half of chunk c's ballot
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      h[c] = __ballot((x[c] & cd.mask) == cd.bitval);
-      m += (uint32_t)__popcll(h[c]);
+      const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
+      m += (uint32_t)__popcll(h);
+      hword = (uint32_t)lane_write((int)(uint32_t)h, 2 * c, (int)hword);
+      hword = (uint32_t)lane_write((int)(uint32_t)(h >> 32), 2 * c + 1, (int)hword);
     }
     const uint32_t c_bits = n + 32u * n - cd.p * m;
     const bool flag = c_bits < 32u * n;
-    uint32_t v[NCH];
     uint32_t words = n;
-    if (!flag) {
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) v[c] = x[c];
-    } else {
+    if (flag) {
       words = store_words(slots + row * n, (c_bits + 31u) >> 5, n, cd.pad);
       for (uint32_t j = n / 32 + lane; j < words + 1; j += kWave) buf[j] = 0u;
-      if (lane < 2 * NCH) {  // header word q = half (q & 1) of chunk q / 2's ballot
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          if (lane == 2u * c) w = (uint32_t)h[c];
-          if (lane == 2u * c + 1) w = (uint32_t)(h[c] >> 32);
-        }
-        buf[lane] = w;
-      }
+      if (lane < 2 * NCH) buf[lane] = hword;
       wave_lds_sync();
+      uint32_t ob = n + 32u * lane;  // opaque, as the load offsets
+      asm volatile("" : "+v"(ob));
       uint32_t carry = 0;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
-        const uint32_t lo = (uint32_t)h[c], hi = (uint32_t)(h[c] >> 32);
-        const bool match = __builtin_amdgcn_inverse_ballot_w64(h[c]);
-        const uint32_t off =
-            n + 32u * (c * kWave + lane) - __umul24(cd.p, carry + bits_below_lane(lo, hi));
-        const uint32_t pay = match ? extract_kept<NR>(x[c], cd.runs) : x[c];
+        // the match test again (two instructions, where keeping NCH ballots
+        // in scalar registers costs as many to turn back into lane masks)
+        asm volatile("" : "+v"(x[c]));
+        const bool match = (x[c] & cd.mask) == cd.bitval;
+        const unsigned long long h = __ballot(match);
+        const uint32_t below = bits_below_lane((uint32_t)h, (uint32_t)(h >> 32));
+        uint32_t t = (uint32_t)(c * kWave * 32) - cd.p * carry;
+        asm volatile("" : "+s"(t));
+        const uint32_t off = (uint32_t)mul_i24((int)below, negp) + ob + t;
+        uint32_t e;
+        if constexpr (NR > 0) {
+          e = (x[c] >> cd.runs.shift[0]) & kept[0];
+#pragma unroll
+          for (int j = 1; j < NR; ++j) e |= (x[c] >> cd.runs.shift[j]) & kept[j];
+        } else {
+          e = extract_kept<NR>(x[c], cd.runs);
+        }
+        const uint32_t pay = match ? e : x[c];
         // the payload's bits in its first word and the next (zero when it
         // ends in the first).  With p = 32 a matched block has no payload,
         // and only the other lanes take part (many empty payloads at one
         // offset would all hit one LDS word); otherwise no branch.
         const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
-        if (cd.p < 32u || !match) {
+        if (NR != 0 || !match) {
           atomicOr(&buf[off >> 5], (uint32_t)w2);
           atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
         }
-        carry += (uint32_t)__popcll(h[c]);
+        carry += (uint32_t)__popcll(h);
       }
       wave_lds_sync();
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) v[c] = c * kWave < words ? buf[c * kWave + lane] : 0u;
+      for (int c = 0; c < NCH; ++c) x[c] = c * kWave < words ? buf[c * kWave + lane] : 0u;
     }
     const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * n, words * 4u);
+    uint32_t lb = lane * 4u;
+    asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
-      __builtin_amdgcn_raw_buffer_store_b32(v[c], out, (c * kWave + lane) * 4u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
     wave_lds_sync();
     return c_bits;
   });
@@ -1758,12 +1863,16 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
 // each row of 16 lanes, the waves' match totals meet in LDS to give each wave
 // its carry, and the joined payloads of a pair are ORed into the
 // workgroup's LDS stream, which is then written with coalesced stores (a raw
-// row straight from the registers).  Three barriers per row.  In place is
-// safe: every wave has read its part of the row before the first barrier.
+// row straight from the registers).  Three barriers per row.  As in
+// compress_wg_kernel, a workgroup takes a contiguous range of `per_wg` rows
+// (at most 64), loads its next row while it encodes one and writes the
+// range's flag bits once at its end (whole bytes when per_wg is a multiple
+// of 8).  In place is safe: every wave has read its part of the row before
+// the first barrier, and the row loaded ahead is another row.
 template <int NR, int CPW>
 __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
     WideCodec<uint16_t> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
-    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits) {
+    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits, uint32_t per_wg) {
   constexpr uint32_t nw = (uint32_t)CPW * kWave * kWavesPerBlock;  // words of a row
   constexpr uint32_t n = 2u * nw;                                   // blocks of a row
   __shared__ uint32_t buf[nw + 4];
@@ -1771,25 +1880,46 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t c0 = wave * CPW;  // the wave's first chunk of 64 words
+  const uint32_t lane_byte = (c0 * kWave + lane) * 4u;
   const uint32_t m2 = (uint32_t)cd.mask * 0x10001u, b2 = (uint32_t)cd.bitval * 0x10001u;
   const uint32_t sh = 2u * (lane & 15u);
+  // a run's kept bits at their payload position, in both halves of a word:
+  // extract = OR of (y >> shift) & kept2, a shift and an and-or per run
+  constexpr int NK = NR > 0 ? NR : 1;
+  uint32_t kept2[NK];
+#pragma unroll
+  for (int j = 0; j < NK; ++j)
+    kept2[j] = NR > 0 ? ((uint32_t)cd.place[j] >> cd.shift[j]) * 0x10001u : 0u;
   auto extract2 = [&](uint32_t y) -> uint32_t {
     uint32_t v = 0;
     if constexpr (NR >= 0) {
 #pragma unroll
-      for (int j = 0; j < NR; ++j) v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
+      for (int j = 0; j < NR; ++j) v |= (y >> cd.shift[j]) & kept2[j];
     } else {
       for (uint32_t j = 0; j < cd.nruns; ++j)
         v |= (y & ((uint32_t)cd.place[j] * 0x10001u)) >> cd.shift[j];
     }
     return v;
   };
-  for (uint64_t row = blockIdx.x; row < n_rows; row += gridDim.x) {
-    const uint32_t* x_row = src + row * nw;
-    uint32_t* s_row = slots + row * nw;
-    uint32_t x[CPW];
+  const uint64_t r0 = (uint64_t)blockIdx.x * per_wg;
+  const uint64_t r1 = min(n_rows, r0 + per_wg);
+  // a row past the range loads as zeros (empty range), never out of bounds
+  auto load = [&](uint32_t (&v)[CPW], uint64_t r) {
+    const __amdgpu_buffer_rsrc_t in =
+        row_rsrc(src + (r < r1 ? r : r0) * nw, r < r1 ? nw * 4u : 0u);
+    uint32_t lb = lane_byte;  // opaque: the chunks' offsets are immediates on it
+    asm volatile("" : "+v"(lb));
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) x[c] = x_row[(c0 + c) * kWave + lane];
+    for (int c = 0; c < CPW; ++c)
+      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+  };
+  uint32_t x[CPW];
+  load(x, r0);
+  unsigned long long fl = 0;  // bit j: row r0 + j is stored compressed
+  for (uint64_t row = r0; row < r1; ++row) {
+    uint32_t* s_row = slots + row * nw;
+    uint32_t y[CPW];  // the next row, in flight
+    load(y, row + 1);
     // the payload part of the stream starts zeroed; header words are whole
     for (uint32_t j = n / 32 + threadIdx.x; j < nw + 4; j += kBlockThreads) buf[j] = 0u;
     uint32_t mw = 0;
@@ -1819,46 +1949,77 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
     }
     const uint32_t c_bits = n + 16u * n - cd.p * m;
     const bool flag = c_bits < 16u * n;
-    if (!flag) {
-#pragma unroll
-      for (int c = 0; c < CPW; ++c) s_row[(c0 + c) * kWave + lane] = x[c];
-    } else {
+    fl |= (unsigned long long)flag << (row - r0);
+    if (flag) {
+      // the lane's first pair offset less the carry, opaque (folded into CPW
+      // loop-invariant chunk bases it would hold as many registers)
+      uint32_t ob = n + 8u * lane_byte;
+      asm volatile("" : "+v"(ob));
+      const int negp = -(int)cd.p;
 #pragma unroll
       for (int c = 0; c < CPW; ++c) {
+        // the match tests again (cheaper than turning kept ballots back
+        // into lane masks)
+        asm volatile("" : "+v"(x[c]));
         const uint32_t d = (x[c] & m2) ^ b2;
-        const unsigned long long e = __ballot((d & 0xFFFFu) == 0u);
-        const unsigned long long o = __ballot((d >> 16) == 0u);
-        const bool s0 = __builtin_amdgcn_inverse_ballot_w64(e);
-        const bool s1 = __builtin_amdgcn_inverse_ballot_w64(o);
+        const bool s0 = (d & 0xFFFFu) == 0u;
+        const bool s1 = (d >> 16) == 0u;
+        const unsigned long long e = __ballot(s0);
+        const unsigned long long o = __ballot(s1);
         const uint32_t below = bits_below_lane_acc(
             (uint32_t)o, (uint32_t)(o >> 32), bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
-        const uint32_t off =
-            n + 32u * ((c0 + c) * kWave + lane) - __umul24(cd.p, carry + below);
+        uint32_t t = (uint32_t)(c * kWave * 32) - cd.p * carry;
+        asm volatile("" : "+s"(t));
+        const uint32_t off = (uint32_t)mul_i24((int)below, negp) + ob + t;
         const uint32_t l0 = s0 ? 16u - cd.p : 16u;
-        const uint32_t l1 = s1 ? 16u - cd.p : 16u;
         const uint32_t ext = extract2(x[c]);
         const uint32_t pay0 = (s0 ? ext : x[c]) & 0xFFFFu;
         const uint32_t pay1 = (s1 ? ext : x[c]) >> 16;
         const uint32_t pay = pay0 | (pay1 << l0);
-        const uint32_t len = l0 + l1;
-        if (len) {
-          const uint32_t sw = off & 31u, wi = off >> 5;
-          atomicOr(&buf[wi], pay << sw);
-          if (sw + len > 32u) atomicOr(&buf[wi + 1], pay >> (32u - sw));
+        // the pair's bits in its first stream word and the next (zero when
+        // they end in the first).  With p = 16 a pair of stripped blocks has
+        // no payload and takes no part (many empty payloads at one offset
+        // would all hit one LDS word); otherwise no branch.
+        const unsigned long long w2 = (unsigned long long)pay << (off & 31u);
+        if (NR != 0 || !(s0 && s1)) {
+          atomicOr(&buf[off >> 5], (uint32_t)w2);
+          atomicOr(&buf[(off >> 5) + 1u], (uint32_t)(w2 >> 32));
         }
         carry += (uint32_t)(__popcll(e) + __popcll(o));
       }
-      __syncthreads();
+    }
+    __syncthreads();
+    if (!flag) {
+      const __amdgpu_buffer_rsrc_t out = row_rsrc(s_row, nw * 4u);
+      uint32_t lb = lane_byte;
+      asm volatile("" : "+v"(lb));
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
+    } else {
       const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, cd.pad);
-      for (uint32_t j = threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
+      uint32_t j0 = 0;
+      if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
+        const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
+        u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
+        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) o4[j] = b4[j];
+        j0 = nwc & ~3u;
+      }
+      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
     }
-    if (threadIdx.x == 0) {
-      put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
-      if (row_bits) row_bits[row] = c_bits;
-    }
+    if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) x[c] = y[c];
     // the LDS stream is reused only by a next row; after the last one the
     // workgroup ends without waiting for its stores (a barrier would)
-    if (row + gridDim.x < n_rows) __syncthreads();
+    if (row + 1 < r1) __syncthreads();
+  }
+  if (wave == 0 && r0 < r1) {
+    const uint32_t k = (uint32_t)(r1 - r0);
+    if (per_wg % 8u == 0)
+      put_flag_bytes(flags, r0, k, fl, n_rows, lane);
+    else if (lane == 0)
+      put_flag_bits(flags, r0, k, fl, n_rows);
   }
 }
 
@@ -3079,6 +3240,15 @@ void launch_compress_rows_t(const Codec& cd, uint64_t n_rows, const void* src, v
                      (unsigned long long*)flags, row_bits);
 }
 
+// Rows per workgroup of compress_wg_kernel over n_rows rows with `cap`
+// resident workgroups: enough that every workgroup is resident, at most 64;
+// with `bytes`, a multiple of 8 (whole flag bytes, no atomics), else any
+// (fewer rows per workgroup, two flag atomics each).
+uint32_t cwg_rows_per_wg(uint64_t n_rows, uint64_t cap, bool bytes) {
+  const uint64_t fill = (n_rows + cap - 1) / cap;
+  return (uint32_t)std::min<uint64_t>(64, bytes ? 8 * ((fill + 7) / 8) : fill);
+}
+
 template <int NR>
 void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
                         uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
@@ -3090,16 +3260,26 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
     default: break;
   }
   // rows of 256 * CPW blocks for the common long-row sizes (LLM weight rows
-  // of 4096 or 14336 bf16 values): the register-resident workgroup kernel
-#define IBP_CWG(CPW, WPB)                                                                \
-  hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>), dim3(grid_for(n_rows)),           \
-                     dim3(WPB * kWave), 0, st, cd, n_rows, (const uint32_t*)src,            \
-                     (uint32_t*)slots, (unsigned long long*)flags, row_bits)
+  // of 4096 or 14336 bf16 values): the register-resident workgroup kernel,
+  // as many workgroups as stay resident (a CU holds 8 workgroups of 4 waves
+  // and 160 KiB of LDS, which holds their rows' streams).  Measured on a
+  // 4096-row matrix: 8 rows per workgroup (flag bytes) for 8 KiB rows, and
+  // for 28 KiB rows 4 (atomics; 8 leave too few workgroups).
+#define IBP_CWG(CPW, WPB, BYTES)                                                           \
+  {                                                                                         \
+    constexpr uint32_t lds = (CPW * kWave * WPB + 4u + WPB) * 4u;                           \
+    constexpr uint32_t per_cu = std::min(32u / WPB, (160u * 1024u) / lds);                  \
+    const uint32_t per_wg = cwg_rows_per_wg(n_rows, workgroups_per_device(per_cu), BYTES);  \
+    hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>),                                  \
+                       dim3(grid_for((n_rows + per_wg - 1) / per_wg)), dim3(WPB * kWave), 0, \
+                       st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,              \
+                       (unsigned long long*)flags, row_bits, per_wg);                       \
+  }
   switch (cd.n) {
-    case 2048: IBP_CWG(8, 4); return;
-    case 4096: IBP_CWG(16, 4); return;
-    case 7168: IBP_CWG(28, 4); return;
-    case 8192: IBP_CWG(32, 4); return;
+    case 2048: IBP_CWG(8, 4, true); return;
+    case 4096: IBP_CWG(16, 4, true); return;
+    case 7168: IBP_CWG(28, 4, false); return;
+    case 8192: IBP_CWG(32, 4, false); return;
     default: break;
   }
 #undef IBP_CWG
@@ -3266,16 +3446,23 @@ void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void
       default: break;
     }
 #undef IBP_PAIR
-    // rows of 512 * CPW blocks (the 8 and 28 KiB weight rows): one workgroup per row
-#define IBP_PAIR_WG(CPW)                                                                    \
-  hipLaunchKernelGGL((compress_pair_wg_kernel<NR, CPW>), dim3(grid_for(n_rows)),            \
-                     dim3(kBlockThreads), 0, st, cd, n_rows, (const uint32_t*)src,           \
-                     (uint32_t*)slots, (unsigned long long*)flags, row_bits)
+    // rows of 512 * CPW blocks (the 8 and 28 KiB weight rows): a workgroup
+    // per row, ranges of rows per workgroup as for compress_wg_kernel
+#define IBP_PAIR_WG(CPW, BYTES)                                                             \
+  {                                                                                         \
+    constexpr uint32_t lds = (CPW * kWave * kWavesPerBlock + 4u + kWavesPerBlock) * 4u;      \
+    constexpr uint32_t per_cu = std::min(8u, (160u * 1024u) / lds);                         \
+    const uint32_t per_wg = cwg_rows_per_wg(n_rows, workgroups_per_device(per_cu), BYTES);  \
+    hipLaunchKernelGGL((compress_pair_wg_kernel<NR, CPW>),                                  \
+                       dim3(grid_for((n_rows + per_wg - 1) / per_wg)), dim3(kBlockThreads), \
+                       0, st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,           \
+                       (unsigned long long*)flags, row_bits, per_wg);                       \
+  }
     switch (cd.nw) {
-      case 2048: IBP_PAIR_WG(8); return;
-      case 4096: IBP_PAIR_WG(16); return;
-      case 7168: IBP_PAIR_WG(28); return;
-      case 8192: IBP_PAIR_WG(32); return;
+      case 2048: IBP_PAIR_WG(8, true); return;
+      case 4096: IBP_PAIR_WG(16, true); return;
+      case 7168: IBP_PAIR_WG(28, false); return;
+      case 8192: IBP_PAIR_WG(32, false); return;
       default: break;
     }
 #undef IBP_PAIR_WG

@@ -182,6 +182,11 @@ CODEC_CASES = [
     (24, 16384, 0x55555555, 0x11111111),           # 16 runs, n = 4096
     (12, 32768, 0x7C000000, 0x3C000000),           # n = 8192
     (6, 32768, 0x00000000, 0x00000000),            # p = 0: raw rows from registers
+    # more rows than stay resident: each workgroup takes several rows and
+    # loads the next while it encodes one; a ragged last workgroup
+    (2600, 8192, 0x78007800, 0x38003800),          # n = 2048, 2 rows per workgroup
+    (1283, 28672, 0x7C007C00, 0x3C003C00),         # n = 7168
+    (2100, 16384, 0x55555555, 0x11111111),         # 16 runs, n = 4096
     # nearly every block stripped: whole chunks of stripped blocks
     (64, 4096, 0xFFFFFFFF, 0x3F800000, 0.998),     # p = 32, n = 1024
     (96, 2048, 0xFFFFFFFF, 0x00000000, 0.995),     # p = 32, n = 512
