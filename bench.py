@@ -54,6 +54,8 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "lossless_bit_level_amd", "csrc", "ibp.hip")
 ROTATE_BYTES = 1 << 30           # outputs rotate over at least this much memory
 CEILING_GRIDS = (2, 4, 8, 16, 64)   # workgroups per CU tried for the gather-copy ceiling
+COMPRESS_GROUP_BYTES = 400 << 20  # compression timed over groups of this much raw input (a layer)
+COMPRESS_SPIN_CYCLES = 1_000_000  # spin before a timed compress group (~0.5 ms of GPU clock)
 GiB = float(1 << 30)
 
 
@@ -310,27 +312,44 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
                                                row_bits=rb)
         return ibp.ibp_compress(md, tg, slots=slots, flags=flags, row_bits=rb)
 
-    # upload and compress every table (out of place from a staging upload);
-    # for a one-table workload the median of three calls into the same buffers
+    def time_compress(calls):
+        """GPU seconds of the compress calls (staged table, outputs) back to
+        back on the stream.  A spin kernel runs first, so that the calls are
+        queued before the region starts and the host's own per-call work is
+        not timed (the GPU time of a pipeline of such calls)."""
+        torch.cuda.synchronize()
+        torch.cuda._sleep(COMPRESS_SPIN_CYCLES)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for tg, out in calls:
+            compress(tg, out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    # upload and compress every table (out of place from a staging upload),
+    # then time its compression again into the same buffers: the tables of a
+    # layer (up to COMPRESS_GROUP_BYTES of raw input) back to back, a
+    # one-table workload three times back to back
     images = []          # (slots, flags, stored bytes per row numpy, stored bytes int32 GPU)
     shapes = []
     comp_s = 0.0
     raw_bytes = stored = bits_total = side_bytes = 0
     t_up = time.perf_counter()
+    group, group_bytes = [], 0
     for i, x in iter_tables(wl, threads):
         tg = torch.from_numpy(x.reshape(x.shape[0], -1).view(np.uint8)).to(dev)
         shapes.append(tuple(tg.shape))
         out = compress(tg)
-        torch.cuda.synchronize()
-        times = []
-        for _ in range(3 if wl.n_tables == 1 else 1):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            slots, flags, rb = compress(tg, out)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1) / 1e3)
-        comp_s += sorted(times)[len(times) // 2]
+        slots, flags, rb = out
+        group.append((tg, out))
+        group_bytes += tg.numel()
+        if wl.n_tables == 1:
+            comp_s += time_compress(group * 3) / 3
+            group, group_bytes = [], 0
+        elif group_bytes >= COMPRESS_GROUP_BYTES or i == wl.n_tables - 1:
+            comp_s += time_compress(group)
+            group, group_bytes = [], 0
         del tg
         rbn = rb.cpu().numpy()[:shapes[-1][0]]
         sb = stored_bytes_per_row(rbn, shapes[-1][1])
