@@ -184,9 +184,10 @@ CODEC_CASES = [
     (6, 32768, 0x00000000, 0x00000000),            # p = 0: raw rows from registers
     # more rows than stay resident: each workgroup takes several rows and
     # loads the next while it encodes one; a ragged last workgroup
-    (2600, 8192, 0x78007800, 0x38003800),          # n = 2048, 2 rows per workgroup
-    (1283, 28672, 0x7C007C00, 0x3C003C00),         # n = 7168
+    (2600, 8192, 0x78007800, 0x38003800),          # n = 2048, flag bytes owned
+    (1283, 28672, 0x7C007C00, 0x3C003C00),         # n = 7168, flag atomics per range
     (2100, 16384, 0x55555555, 0x11111111),         # 16 runs, n = 4096
+    (1100, 32768, 0x7C000000, 0x3C000000),         # n = 8192, flag atomics per range
     # nearly every block stripped: whole chunks of stripped blocks
     (64, 4096, 0xFFFFFFFF, 0x3F800000, 0.998),     # p = 32, n = 1024
     (96, 2048, 0xFFFFFFFF, 0x00000000, 0.995),     # p = 32, n = 512
@@ -558,6 +559,9 @@ WIDE_CASES = [
     (16, 20, 8192, 0x7800, 0x3800, 0.9),                  # 2 runs
     (16, 9, 16384, 0x5555, 0x1111, 0.9),                  # 8 runs (generic path)
     (16, 5, 32768, 0xFFFF, 0x0000, 0.995),                # p = 16: empty pair payloads
+    # more rows than stay resident: ranges of several rows per workgroup
+    (16, 2600, 8192, 0x7800, 0x3800, 0.9),                # flag bytes owned
+    (16, 1300, 28672, 0x7800, 0x3800, 0.9),               # flag atomics per range
     (16, 6, 8192, 0x0000, 0x0000, 0.0),                   # p = 0: raw rows from registers
     (64, 130, 1024, 0x7FF0000000000000, 0x3FF0000000000000, 0.85),  # fp64 exponent
     (64, 70, 8200, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 1025 blocks, 3 segments
