@@ -194,7 +194,7 @@ def decode_kernel_name(row_bytes: int, width: int = 32, positional: bool = False
     if width == 64 and row_bytes in (512, 1024, 2048) and not cached:
         return "decode_pipe64_kernel"
     if width != 32:
-        return "decode_wide_kernel"
+        return "decode_wide_batch_kernel" if batched else "decode_wide_kernel"
     if batched:
         return "decode_batch_kernel"
     if host_image and invariant_bits < 32 and row_bytes >= 4096 and not cached:
@@ -484,8 +484,7 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
     # the host link).  Every other step is one launch.
     steps = wl.steps
     layered = wl.layer_size > 1 and not opt.per_tensor
-    batched = layered and not host and pos_table is None and opt.width == 32 and \
-        not opt.cache_mib
+    batched = layered and not host and pos_table is None and not opt.cache_mib
     if layered:
         groups = [list(range(g, min(g + wl.layer_size, len(steps))))
                   for g in range(0, len(steps), wl.layer_size)]

@@ -198,8 +198,10 @@ typedef struct ibp_tensor {
  * one launch per 16 tensors instead of one per tensor.  The descriptor array
  * is host memory and is read before the call returns.  Every tensor is
  * validated first; on an error nothing is enqueued.  n_tensors == 0 is a
- * no-op.  Tensors must not overlap each other's outputs.  W = 32 in one
- * launch; other widths decode tensor by tensor.  Asynchronous on `stream`.
+ * no-op.  Tensors must not overlap each other's outputs.  Every width in
+ * one launch per 16 tensors, except W = 64 batches that hold a tensor of
+ * 512-byte to 2 KiB rows (those rows decode faster through their own
+ * kernel), which decode tensor by tensor.  Asynchronous on `stream`.
  */
 int ibp_decompress_batch(const ibp_metadata *md, const ibp_tensor *tensors,
                          uint64_t n_tensors, void *stream);

@@ -1073,7 +1073,7 @@ struct BatchTensor {
   uint32_t n;     // blocks per row
   uint32_t nseg;  // segments per row
   uint32_t vec;   // 16-byte aligned rows and buffers
-  uint32_t pad;
+  uint32_t nw;    // 32-bit words per row
 };
 struct Batch {
   uint32_t count;
@@ -2102,6 +2102,163 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
   });
 }
 
+// [IBP] Decompression for W = 16 / 64 of one task: segment s (blocks
+// [s * seg, min(n, (s + 1) * seg))) of output row i (rows of n blocks, slots
+// of nw words), in the three row-source modes of the 32-bit kernels.
+template <typename T, int MODE, int NR>
+__device__ __forceinline__ void decode_wide_task(
+    const WideCodec<T>& cd, uint32_t n, uint32_t nw, const uint32_t* __restrict__ slots,
+    const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
+    const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
+    uint64_t n_rows, uint64_t i, uint32_t s, uint32_t seg, T* __restrict__ dst, int vec,
+    uint32_t* lds, uint32_t lane) {
+  constexpr uint32_t W = WideCodec<T>::W;
+  const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
+  T* out = dst + i * n;
+  const uint32_t lo = s * seg;
+  const uint32_t hi = min(n, lo + seg);
+  if (MODE != kModeTable && id >= n_rows) {
+    for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = (T)0;
+    return;
+  }
+  const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
+  const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
+  const uint32_t* src = row_source<MODE>(slots, arena, id, nw, loc);
+  const uint32_t lim = row_words<MODE>(nw, loc);
+  // header words requested with the flag word (see decode_segments_kernel)
+  const uint32_t hw_n = (hi - lo + 31) / 32;
+  uint32_t hw = 0;
+  if (lane < hw_n) hw = src[lo / 32 + lane];
+  uint32_t acc = 0;
+  for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
+    uint32_t w[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
+  }
+  if (!row_flag<MODE>(fw, id, loc)) {
+    if (vec) {  // 16-byte units of the segment (lo and hi are multiples of 16 bytes)
+      const uint4* a = reinterpret_cast<const uint4*>(src);
+      uint4* o = reinterpret_cast<uint4*>(out);
+      constexpr uint32_t per = 16 / sizeof(T);
+      for (uint32_t j = lo / per + lane; j < hi / per; j += kWave) o[j] = a[j];
+    } else {
+      const T* a = reinterpret_cast<const T*>(src);
+      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = a[j];
+    }
+    return;
+  }
+  // stripped blocks before the segment (lo is a multiple of 64)
+  const uint32_t carry = lo ? wave_sum(acc) : 0u;
+  if (lane < hw_n) {
+    const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
+    if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
+  }
+  const uint32_t m_seg = wave_sum(__popc(hw));
+  const uint32_t a = n + W * lo - cd.p * carry;
+  const uint32_t b = n + W * hi - cd.p * (carry + m_seg);
+  const uint32_t wb = min((b + 31u) >> 5, lim);
+  const uint32_t wa = min(a >> 5, wb);
+  uint32_t base = wa;
+  if (vec) {  // 16-byte loads from the 16-byte unit holding word wa
+    base = wa & ~3u;
+    stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
+                    (wb - base + 3u) / 4u, lane);
+  } else {
+    stage_window<4>(src + wa, lds, wb - wa, lane);
+  }
+  wave_lds_sync();
+  uint32_t u = a - 32u * base;
+  const int negp = -(int)cd.p;
+  // a whole segment (the decode launch cuts rows into segments of 1024
+  // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter step
+  // by step
+  constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+  if constexpr (sizeof(T) == 2) {
+    // Two blocks per lane: lane l restores blocks k0 + 2l and k0 + 2l + 1
+    // of a 128-block step and stores them as one word.  Their header bits
+    // are bits 2(l mod 16) and 2(l mod 16) + 1 of header word q + l/16;
+    // two ballots (first / second block of a pair stripped) give the
+    // stripped blocks before the pair through v_mbcnt.  Both payloads lie
+    // in the 32 stream bits at the pair's offset (16 - p or 16 bits each),
+    // and one deposit over the packed pair, with the run masks repeated in
+    // both halves, restores both blocks' invariant bits: run j moves bits
+    // up by shift_j, and a half's bits never reach the other half's places
+    // (the lowest upper-half place of run j is bit 16 + shift_j + its
+    // source bit), so a raw half or the bits past a payload cannot leak.
+    const uint32_t bv2 = (uint32_t)cd.bitval * 0x10001u;
+    const uint32_t sh = 2u * (lane & 15u);
+    const uint32_t hsel = 4u * (lane >> 4);
+    const uint32_t l32 = 32u * lane;
+    uint32_t* out_w = reinterpret_cast<uint32_t*>(out);
+    auto pair = [&](uint32_t k0, bool ragged) {
+      // the lane's header word, q + l/16, from the lane of hw holding it
+      const uint32_t q = (k0 - lo) / 32;
+      const uint32_t hs = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * q + hsel), (int)hw);
+      const uint32_t b2 = __builtin_amdgcn_ubfe(hs, sh, 2);
+      const bool s0 = (b2 & 1u) != 0u, s1 = b2 > 1u;
+      const unsigned long long e = __ballot(s0), o = __ballot(s1);
+      const bool valid = !ragged || k0 + 2u * lane < hi;
+      const uint32_t below = bits_below_lane_acc((uint32_t)o, (uint32_t)(o >> 32),
+                                                 bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
+      const uint32_t rel = valid ? (uint32_t)__mul24(negp, (int)below) + (u + l32) : 0u;
+      const uint32_t v = lds_bits(lds, rel);
+      const uint32_t l0 = s0 ? 16u - cd.p : 16u;
+      const uint32_t y = (v & 0xFFFFu) | ((v >> l0) << 16);
+      uint32_t dep = bv2;
+      if constexpr (NR >= 0) {
+#pragma unroll
+        for (int j = 0; j < NR; ++j) dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
+      } else {
+        for (uint32_t j = 0; j < cd.nruns; ++j)
+          dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
+      }
+      const uint32_t sel = (s0 ? 0x0000FFFFu : 0u) | (s1 ? 0xFFFF0000u : 0u);
+      if (valid) __builtin_nontemporal_store(select_bits(sel, dep, y), out_w + k0 / 2 + lane);
+      u += 16u * 2u * kWave - cd.p * (uint32_t)(__popcll(e) + __popcll(o));
+    };
+    if (hi - lo == kFull && seg == kFull) {
+#pragma unroll
+      for (uint32_t c = 0; c < kFull / (2 * kWave); ++c) pair(lo + c * 2 * kWave, false);
+    } else {
+      const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(2 * kWave - 1));
+      uint32_t k0 = lo;
+      for (; k0 < full_hi; k0 += 2 * kWave) pair(k0, false);
+      if (k0 < hi) pair(k0, true);
+    }
+    wave_lds_sync();
+    return;
+  }
+  const uint32_t wl = W * lane;
+  // one 64-block chunk: lane l restores block k0 + l; `ragged` only for the
+  // last chunk of a segment shorter than a whole number of chunks
+  auto chunk = [&](uint32_t k0, bool ragged) {
+    const uint32_t q = (k0 - lo) / 32;
+    const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
+    const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
+    const bool valid = !ragged || k0 + lane < hi;
+    const uint32_t rel =
+        valid ? (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + wl) : 0u;
+    const T v = lds_payload<T>(lds, rel);
+    const bool stripped =
+        __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+    const T x = stripped ? deposit_wide<T, NR>(v, cd) : v;
+    if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
+    u += W * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+  };
+  if (hi - lo == kFull && seg == kFull) {
+#pragma unroll
+    for (uint32_t c = 0; c < kFull / kWave; ++c) chunk(lo + c * kWave, false);
+  } else {
+    const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
+    uint32_t k0 = lo;
+    for (; k0 < full_hi; k0 += kWave) chunk(k0, false);
+    if (k0 < hi) chunk(k0, true);
+  }
+  wave_lds_sync();
+}
+
 // [IBP] Decompression for W = 16 / 64: one wave per (row, segment of `seg`
 // blocks), in the three row-source modes of the 32-bit kernels.
 template <typename T, int MODE, int NR>
@@ -2111,162 +2268,47 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_kernel(
     const uint32_t* __restrict__ arena, const unsigned long long* __restrict__ cache_loc,
     uint64_t n_rows, uint64_t n_tasks, uint32_t nseg, uint32_t seg, T* __restrict__ dst,
     int vec, int remap) {
-  constexpr uint32_t W = WideCodec<T>::W;
   __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
-  const uint32_t n = cd.n, nw = cd.nw;
   const uint32_t g = gridDim.x;
   for (uint64_t wg = remap ? xcd_remap(blockIdx.x, g) : blockIdx.x; ; wg += g) {
     const uint64_t task = wg * kWavesPerBlock + wave;
     if (task >= n_tasks) break;
     const uint64_t i = task / nseg;
     const uint32_t s = (uint32_t)(task - i * nseg);
-    const uint64_t id = MODE != kModeTable ? (uint64_t)ids[i] : i;
-    T* out = dst + i * n;
-    const uint32_t lo = s * seg;
-    const uint32_t hi = min(n, lo + seg);
-    if (MODE != kModeTable && id >= n_rows) {
-      for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = (T)0;
-      continue;
-    }
-    const unsigned long long loc = MODE == kModeCached ? cache_loc[id] : 0ull;
-    const unsigned long long fw = (loc & IBP_LOC_RESIDENT) ? 0ull : flags[id >> 6];
-    const uint32_t* src = row_source<MODE>(slots, arena, id, nw, loc);
-    const uint32_t lim = row_words<MODE>(nw, loc);
-    // header words requested with the flag word (see decode_segments_kernel)
-    const uint32_t hw_n = (hi - lo + 31) / 32;
-    uint32_t hw = 0;
-    if (lane < hw_n) hw = src[lo / 32 + lane];
-    uint32_t acc = 0;
-    for (uint32_t t0 = 0; t0 < lo / 32; t0 += 4 * kWave) {
-      uint32_t w[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) w[c] = src[min(t0 + c * kWave + lane, lo / 32 - 1)];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc += t0 + c * kWave + lane < lo / 32 ? __popc(w[c]) : 0u;
-    }
-    if (!row_flag<MODE>(fw, id, loc)) {
-      if (vec) {  // 16-byte units of the segment (lo and hi are multiples of 16 bytes)
-        const uint4* a = reinterpret_cast<const uint4*>(src);
-        uint4* o = reinterpret_cast<uint4*>(out);
-        constexpr uint32_t per = 16 / sizeof(T);
-        for (uint32_t j = lo / per + lane; j < hi / per; j += kWave) o[j] = a[j];
-      } else {
-        const T* a = reinterpret_cast<const T*>(src);
-        for (uint32_t j = lo + lane; j < hi; j += kWave) out[j] = a[j];
-      }
-      continue;
-    }
-    // stripped blocks before the segment (lo is a multiple of 64)
-    const uint32_t carry = lo ? wave_sum(acc) : 0u;
-    if (lane < hw_n) {
-      const uint32_t valid_bits = min(32u, hi - 32u * (lo / 32 + lane));
-      if (valid_bits < 32u) hw &= (1u << valid_bits) - 1u;
-    }
-    const uint32_t m_seg = wave_sum(__popc(hw));
-    const uint32_t a = n + W * lo - cd.p * carry;
-    const uint32_t b = n + W * hi - cd.p * (carry + m_seg);
-    const uint32_t wb = min((b + 31u) >> 5, lim);
-    const uint32_t wa = min(a >> 5, wb);
-    uint32_t base = wa;
-    if (vec) {  // 16-byte loads from the 16-byte unit holding word wa
-      base = wa & ~3u;
-      stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
-                      (wb - base + 3u) / 4u, lane);
-    } else {
-      stage_window<4>(src + wa, lds, wb - wa, lane);
-    }
-    wave_lds_sync();
-    uint32_t u = a - 32u * base;
-    const int negp = -(int)cd.p;
-    // a whole segment (the decode launch cuts rows into segments of 1024
-    // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter step
-    // by step
-    constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
-    if constexpr (sizeof(T) == 2) {
-      // Two blocks per lane: lane l restores blocks k0 + 2l and k0 + 2l + 1
-      // of a 128-block step and stores them as one word.  Their header bits
-      // are bits 2(l mod 16) and 2(l mod 16) + 1 of header word q + l/16;
-      // two ballots (first / second block of a pair stripped) give the
-      // stripped blocks before the pair through v_mbcnt.  Both payloads lie
-      // in the 32 stream bits at the pair's offset (16 - p or 16 bits each),
-      // and one deposit over the packed pair, with the run masks repeated in
-      // both halves, restores both blocks' invariant bits: run j moves bits
-      // up by shift_j, and a half's bits never reach the other half's places
-      // (the lowest upper-half place of run j is bit 16 + shift_j + its
-      // source bit), so a raw half or the bits past a payload cannot leak.
-      const uint32_t bv2 = (uint32_t)cd.bitval * 0x10001u;
-      const uint32_t sh = 2u * (lane & 15u);
-      const uint32_t hsel = 4u * (lane >> 4);
-      const uint32_t l32 = 32u * lane;
-      uint32_t* out_w = reinterpret_cast<uint32_t*>(out);
-      auto pair = [&](uint32_t k0, bool ragged) {
-        // the lane's header word, q + l/16, from the lane of hw holding it
-        const uint32_t q = (k0 - lo) / 32;
-        const uint32_t hs = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * q + hsel), (int)hw);
-        const uint32_t b2 = __builtin_amdgcn_ubfe(hs, sh, 2);
-        const bool s0 = (b2 & 1u) != 0u, s1 = b2 > 1u;
-        const unsigned long long e = __ballot(s0), o = __ballot(s1);
-        const bool valid = !ragged || k0 + 2u * lane < hi;
-        const uint32_t below = bits_below_lane_acc((uint32_t)o, (uint32_t)(o >> 32),
-                                                   bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
-        const uint32_t rel = valid ? (uint32_t)__mul24(negp, (int)below) + (u + l32) : 0u;
-        const uint32_t v = lds_bits(lds, rel);
-        const uint32_t l0 = s0 ? 16u - cd.p : 16u;
-        const uint32_t y = (v & 0xFFFFu) | ((v >> l0) << 16);
-        uint32_t dep = bv2;
-        if constexpr (NR >= 0) {
-#pragma unroll
-          for (int j = 0; j < NR; ++j) dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
-        } else {
-          for (uint32_t j = 0; j < cd.nruns; ++j)
-            dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
-        }
-        const uint32_t sel = (s0 ? 0x0000FFFFu : 0u) | (s1 ? 0xFFFF0000u : 0u);
-        if (valid) __builtin_nontemporal_store(select_bits(sel, dep, y), out_w + k0 / 2 + lane);
-        u += 16u * 2u * kWave - cd.p * (uint32_t)(__popcll(e) + __popcll(o));
-      };
-      if (hi - lo == kFull && seg == kFull) {
-#pragma unroll
-        for (uint32_t c = 0; c < kFull / (2 * kWave); ++c) pair(lo + c * 2 * kWave, false);
-      } else {
-        const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(2 * kWave - 1));
-        uint32_t k0 = lo;
-        for (; k0 < full_hi; k0 += 2 * kWave) pair(k0, false);
-        if (k0 < hi) pair(k0, true);
-      }
-      wave_lds_sync();
-      continue;
-    }
-    const uint32_t wl = W * lane;
-    // one 64-block chunk: lane l restores block k0 + l; `ragged` only for the
-    // last chunk of a segment shorter than a whole number of chunks
-    auto chunk = [&](uint32_t k0, bool ragged) {
-      const uint32_t q = (k0 - lo) / 32;
-      const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
-      const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-      const bool valid = !ragged || k0 + lane < hi;
-      const uint32_t rel =
-          valid ? (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + wl) : 0u;
-      const T v = lds_payload<T>(lds, rel);
-      const bool stripped =
-          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-      const T x = stripped ? deposit_wide<T, NR>(v, cd) : v;
-      if (valid) __builtin_nontemporal_store(x, out + k0 + lane);
-      u += W * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
-    };
-    if (hi - lo == kFull && seg == kFull) {
-#pragma unroll
-      for (uint32_t c = 0; c < kFull / kWave; ++c) chunk(lo + c * kWave, false);
-    } else {
-      const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
-      uint32_t k0 = lo;
-      for (; k0 < full_hi; k0 += kWave) chunk(k0, false);
-      if (k0 < hi) chunk(k0, true);
-    }
-    wave_lds_sync();
+    decode_wide_task<T, MODE, NR>(cd, cd.n, cd.nw, slots, flags, ids, arena, cache_loc, n_rows,
+                                  i, s, seg, dst, vec, lds, lane);
+  }
+}
+
+// [IBP] Decompression for W = 16 / 64 of several tensors that share one
+// Mask/Bitval in one launch, as decode_batch_kernel for W = 32: the segment
+// tasks of every tensor one after the other, each mapped to its tensor by the
+// running task counts.
+template <typename T, int NR>
+__global__ __launch_bounds__(kBlockThreads) void decode_wide_batch_kernel(WideCodec<T> cd,
+                                                                          Batch batch,
+                                                                          uint32_t seg) {
+  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][kSegLdsWords];
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  uint32_t* lds = lds_all[wave];
+  const uint64_t n_tasks = batch.end[batch.count - 1];
+  const uint32_t g = gridDim.x;
+  for (uint64_t wg = blockIdx.x; ; wg += g) {
+    const uint64_t task = wg * kWavesPerBlock + wave;
+    if (task >= n_tasks) break;
+    uint32_t t = 0;
+    while (task >= batch.end[t]) ++t;
+    const BatchTensor& bt = batch.t[t];
+    const uint64_t local = task - (t ? batch.end[t - 1] : 0ull);
+    const uint64_t i = local / bt.nseg;
+    const uint32_t s = (uint32_t)(local - i * bt.nseg);
+    decode_wide_task<T, kModeTable, NR>(cd, bt.n, bt.nw, bt.slots, bt.flags, nullptr, nullptr,
+                                        nullptr, 0, i, s, seg, reinterpret_cast<T*>(bt.dst),
+                                        (int)bt.vec, lds, lane);
   }
 }
 
@@ -3580,6 +3622,27 @@ void launch_decode_wide_mode(const ibp_metadata* md, uint64_t row_bytes, const D
     launch_decode_wide<T, kModeTable>(md, row_bytes, a, st);
 }
 
+// A batched W = 16 / 64 decode (decode_wide_batch_kernel); n and the slot
+// words are per tensor, the rest of the codec is shared.
+template <typename T>
+void launch_decode_wide_batch(const ibp_metadata* md, const Batch& b, uint32_t grid,
+                              uint32_t seg, hipStream_t st) {
+  const WideCodec<T> cd = make_wide_codec<T>(md, b.t[0].nw * 4ull);
+#define IBP_WBATCH(NR)                                                                      \
+  hipLaunchKernelGGL((decode_wide_batch_kernel<T, NR>), dim3(grid), dim3(kBlockThreads), 0, st, \
+                     cd, b, seg)
+  switch (cd.nruns) {
+    case 0: IBP_WBATCH(0); break;
+    case 1: IBP_WBATCH(1); break;
+    case 2: IBP_WBATCH(2); break;
+    case 3: IBP_WBATCH(3); break;
+    case 4: IBP_WBATCH(4); break;
+    case 5: IBP_WBATCH(5); break;
+    default: IBP_WBATCH(-1); break;
+  }
+#undef IBP_WBATCH
+}
+
 // Shift masks for extracting / depositing the bits of `keep` (parallel
 // suffix method, Hacker's Delight sections 7-4 and 7-5): step i moves by 2^i
 // the kept bits whose count of dropped bits below them has bit i set.
@@ -3899,6 +3962,12 @@ int ibp_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
                        kModeTable);
 }
 
+// Blocks per task of a batched decode: a segment's stream stays within the
+// LDS window (<= seg * W / 32 + 3 words).
+static uint32_t batch_seg(uint32_t width_bits) {
+  return width_bits == 64 ? kSegBlocks / 2 : kSegBlocks;
+}
+
 // Host checks of one tensor of a batch (those of decode_common for a full
 // decompress).
 static int check_batch_tensor(const ibp_metadata* md, const ibp_tensor& t) {
@@ -3908,10 +3977,10 @@ static int check_batch_tensor(const ibp_metadata* md, const ibp_tensor& t) {
   if (!t.slots || !t.flags || !t.dst) return IBP_ERR_INVALID_ARGUMENT;
   if (!aligned(t.slots, 4) || !aligned(t.dst, 4) || !aligned(t.flags, 8)) return IBP_ERR_LAYOUT;
   if (md->width_bits == 64 && (!aligned(t.slots, 8) || !aligned(t.dst, 8))) return IBP_ERR_LAYOUT;
-  if (md->width_bits == 32) {  // task counts of the batched launch fit their 56 bits
-    const uint64_t nseg = (t.row_bytes / 4 + kSegBlocks - 1) / kSegBlocks;
-    if (t.n_rows > (UINT64_MAX >> 8) / nseg) return IBP_ERR_INVALID_ARGUMENT;
-  }
+  // task counts of the batched launch fit their 56 bits
+  const uint64_t nseg = (t.row_bytes * 8 / md->width_bits + batch_seg(md->width_bits) - 1) /
+                        batch_seg(md->width_bits);
+  if (t.n_rows > (UINT64_MAX >> 8) / nseg) return IBP_ERR_INVALID_ARGUMENT;
   return IBP_OK;
 }
 
@@ -3930,17 +3999,25 @@ int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint
   if (!work) return IBP_OK;
   rc = pending_hip_error();
   if (rc) return rc;
-  if (md->width_bits != 32) {  // other widths: tensor by tensor
+  const uint32_t W = md->width_bits;
+  if (W == 64) {  // rows of 512 B to 2 KiB decode faster through the row pipeline
+    bool pipe = false;
     for (uint64_t t = 0; t < n_tensors; ++t) {
-      const ibp_tensor& x = tensors[t];
-      if (x.n_rows == 0) continue;
-      rc = ibp_decompress(md, x.n_rows, x.row_bytes, x.slots, x.flags, x.dst, stream);
-      if (rc) return rc;
+      const uint64_t rb = tensors[t].row_bytes;
+      pipe = pipe || (tensors[t].n_rows && (rb == 512 || rb == 1024 || rb == 2048));
     }
-    return IBP_OK;
+    if (pipe) {  // tensor by tensor
+      for (uint64_t t = 0; t < n_tensors; ++t) {
+        const ibp_tensor& x = tensors[t];
+        if (x.n_rows == 0) continue;
+        rc = ibp_decompress(md, x.n_rows, x.row_bytes, x.slots, x.flags, x.dst, stream);
+        if (rc) return rc;
+      }
+      return IBP_OK;
+    }
   }
   hipStream_t st = (hipStream_t)stream;
-  const Codec cd = make_codec(md, tensors[0].row_bytes);  // n is per tensor
+  const uint32_t seg = batch_seg(W);
   uint64_t t = 0;
   while (t < n_tensors) {
     Batch b{};
@@ -3948,8 +4025,8 @@ int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint
     for (; t < n_tensors && b.count < kBatchMax; ++t) {
       const ibp_tensor& x = tensors[t];
       if (x.n_rows == 0) continue;
-      const uint32_t n = (uint32_t)(x.row_bytes / 4);
-      const uint32_t nseg = (n + kSegBlocks - 1) / kSegBlocks;  // checked above
+      const uint32_t n = (uint32_t)(x.row_bytes * 8 / W);
+      const uint32_t nseg = (n + seg - 1) / seg;  // checked above
       tasks += x.n_rows * nseg;
       BatchTensor& bt = b.t[b.count];
       bt.slots = (const uint32_t*)x.slots;
@@ -3958,22 +4035,30 @@ int ibp_decompress_batch(const ibp_metadata* md, const ibp_tensor* tensors, uint
       bt.n = n;
       bt.nseg = nseg;
       bt.vec = x.row_bytes % 16 == 0 && aligned(x.slots, 16) && aligned(x.dst, 16);
+      bt.nw = (uint32_t)(x.row_bytes / 4);
       b.end[b.count] = tasks;
       ++b.count;
     }
     if (b.count == 0) break;
     const uint32_t grid = grid_for((tasks + kWavesPerBlock - 1) / kWavesPerBlock);
+    if (W == 32) {
+      const Codec cd = make_codec(md, tensors[0].row_bytes);  // n is per tensor
 #define IBP_BATCH(NR)                                                                      \
   hipLaunchKernelGGL((decode_batch_kernel<NR>), dim3(grid), dim3(kBlockThreads), 0, st, cd, b)
-    switch (cd.runs.n) {
-      case 0: IBP_BATCH(0); break;
-      case 1: IBP_BATCH(1); break;
-      case 2: IBP_BATCH(2); break;
-      case 3: IBP_BATCH(3); break;
-      case 4: IBP_BATCH(4); break;
-      default: IBP_BATCH(-1); break;
-    }
+      switch (cd.runs.n) {
+        case 0: IBP_BATCH(0); break;
+        case 1: IBP_BATCH(1); break;
+        case 2: IBP_BATCH(2); break;
+        case 3: IBP_BATCH(3); break;
+        case 4: IBP_BATCH(4); break;
+        default: IBP_BATCH(-1); break;
+      }
 #undef IBP_BATCH
+    } else if (W == 16) {
+      launch_decode_wide_batch<uint16_t>(md, b, grid, seg, st);
+    } else {
+      launch_decode_wide_batch<uint64_t>(md, b, grid, seg, st);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e);
   }

@@ -1180,6 +1180,41 @@ def test_decompress_batch(ibp, n_tensors):
     assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("w,shapes,mask,bitval", [
+    # 16-bit blocks: rows of 1 and 14 segments, a ragged one (n = 1026), raw
+    # rows, a tensor of one row; one batched launch
+    (16, [(64, 2048), (40, 28672), (70, 2052), (1, 8192), (33, 4096), (9, 98304)], 0x7800, 0x3800),
+    # 64-bit blocks in rows above 2 KiB: one batched launch
+    (64, [(64, 8192), (40, 28672), (70, 4104), (1, 4096), (9, 98304)],
+     0x7FF0000000000000, 0x3FF0000000000000),
+    # 64-bit blocks with a row of 512 bytes among them: tensor by tensor
+    (64, [(64, 8192), (50, 512), (40, 28672)], 0x7FF0000000000000, 0x3FF0000000000000),
+], ids=["w16", "w64", "w64_small_rows"])
+def test_decompress_batch_other_widths(ibp, w, shapes, mask, bitval):
+    """ibp_decompress_batch at W = 16 and 64: against ibp_decompress of each
+    tensor, the source rows, and the oracle on sampled rows."""
+    rng = np.random.default_rng(w + len(shapes))
+    md = gmd(ibp, mask, bitval, w=w)
+    images, srcs = [], []
+    for n_rows, S in shapes:
+        x = make_rows_w(rng, w, n_rows, S, mask, bitval, 0.9, raw_rows=(0,) if n_rows > 2 else ())
+        xg = to_gpu(x)
+        slots, flags, _ = ibp.ibp_compress(md, xg)
+        images.append((slots, flags))
+        srcs.append((x, xg))
+    say(f"batch W={w} of {len(shapes)} tensors")
+    outs = ibp.ibp_decompress_batch(md, images)
+    torch.cuda.synchronize()
+    for (slots, flags), (x, xg), out in zip(images, srcs, outs):
+        assert torch.equal(out, xg)
+        assert torch.equal(out, ibp.ibp_decompress(md, slots, flags))
+    x, _ = srcs[1]
+    slots_o, flags_o, _ = orc.compress(omd(md), x)
+    ids = np.arange(0, x.shape[0], 7)
+    want = orc.gather_decompress(omd(md), slots_o, flags_o, ids)
+    assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
+
+
 @pytest.fixture(scope="module")
 def llm_metadata(ibp):
     """Metadata of the whole model: the first 2^24 blocks in storage order,
