@@ -2102,6 +2102,13 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
   });
 }
 
+// Blocks per decode task for W = 16 / 64: a segment's stream stays within
+// the LDS window of a 32-bit segment (seg * W / 32 <= kSegBlocks words).
+template <typename T>
+constexpr uint32_t wide_seg_blocks() {
+  return kSegBlocks * 32u / (8u * (uint32_t)sizeof(T));
+}
+
 // [IBP] Decompression for W = 16 / 64 of one task: segment s (blocks
 // [s * seg, min(n, (s + 1) * seg))) of output row i (rows of n blocks, slots
 // of nw words), in the three row-source modes of the 32-bit kernels.
@@ -2171,10 +2178,10 @@ __device__ __forceinline__ void decode_wide_task(
   wave_lds_sync();
   uint32_t u = a - 32u * base;
   const int negp = -(int)cd.p;
-  // a whole segment (the decode launch cuts rows into segments of 1024
+  // a whole segment (the decode launch cuts rows into segments of 2048
   // blocks for W = 16 and 512 for W = 64) unrolled, anything shorter step
   // by step
-  constexpr uint32_t kFull = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+  constexpr uint32_t kFull = wide_seg_blocks<T>();
   if constexpr (sizeof(T) == 2) {
     // Two blocks per lane: lane l restores blocks k0 + 2l and k0 + 2l + 1
     // of a 128-block step and stores them as one word.  Their header bits
@@ -3586,7 +3593,7 @@ void launch_decode_wide_nr(const WideCodec<T>& cd, const DecodeArgs& a, hipStrea
     }
   }
   // a segment's stream stays within the LDS window: <= seg * W / 32 + 3 words
-  const uint32_t seg = sizeof(T) == 8 ? kSegBlocks / 2 : kSegBlocks;
+  const uint32_t seg = wide_seg_blocks<T>();
   const uint32_t nseg = (cd.n + seg - 1) / seg;
   const uint64_t n_tasks = a.n_out * nseg;
   const uint64_t wgs = (n_tasks + kWavesPerBlock - 1) / kWavesPerBlock;
@@ -3965,7 +3972,8 @@ int ibp_decompress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
 // Blocks per task of a batched decode: a segment's stream stays within the
 // LDS window (<= seg * W / 32 + 3 words).
 static uint32_t batch_seg(uint32_t width_bits) {
-  return width_bits == 64 ? kSegBlocks / 2 : kSegBlocks;
+  return width_bits == 64 ? wide_seg_blocks<uint64_t>()
+                          : width_bits == 16 ? wide_seg_blocks<uint16_t>() : kSegBlocks;
 }
 
 // Host checks of one tensor of a batch (those of decode_common for a full
