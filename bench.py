@@ -312,24 +312,28 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
                                                row_bits=rb)
         return ibp.ibp_compress(md, tg, slots=slots, flags=flags, row_bits=rb)
 
-    def time_compress(calls):
+    def time_compress(calls, batch=False):
         """GPU seconds of the compress calls (staged table, outputs) back to
-        back on the stream.  A spin kernel runs first, so that the calls are
-        queued before the region starts and the host's own per-call work is
-        not timed (the GPU time of a pipeline of such calls)."""
+        back on the stream, or with batch of one ibp_compress_batch over them.
+        A spin kernel runs first, so that the calls are queued before the
+        region starts and the host's own per-call work is not timed (the GPU
+        time of a pipeline of such calls)."""
         torch.cuda.synchronize()
         torch.cuda._sleep(COMPRESS_SPIN_CYCLES)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for tg, out in calls:
-            compress(tg, out)
+        if batch:
+            ibp.ibp_compress_batch(md, [tg for tg, _ in calls], [out for _, out in calls])
+        else:
+            for tg, out in calls:
+                compress(tg, out)
         e1.record(stream)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3
 
     # upload and compress every table (out of place from a staging upload),
     # then time its compression again into the same buffers: the tables of a
-    # layer (up to COMPRESS_GROUP_BYTES of raw input) back to back, a
+    # layer (up to COMPRESS_GROUP_BYTES of raw input) in one batched call, a
     # one-table workload three times back to back
     images = []          # (slots, flags, stored bytes per row numpy, stored bytes int32 GPU)
     shapes = []
@@ -348,7 +352,8 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
             comp_s += time_compress(group * 3) / 3
             group, group_bytes = [], 0
         elif group_bytes >= COMPRESS_GROUP_BYTES or i == wl.n_tables - 1:
-            comp_s += time_compress(group)
+            # a layer's tables in one ibp_compress_batch (global metadata)
+            comp_s += time_compress(group, batch=pos_table is None)
             group, group_bytes = [], 0
         del tg
         rbn = rb.cpu().numpy()[:shapes[-1][0]]

@@ -170,6 +170,35 @@ int ibp_compress(const ibp_metadata *md, uint64_t n_rows, uint64_t row_bytes,
                  uint32_t *row_bits, void *stream);
 
 /*
+ * One tensor of a batched compression: its n_rows x row_bytes table `src`,
+ * its image (slots, flags) and optional row_bits, with the meaning, memory
+ * classes and alignment of ibp_compress's arguments.
+ */
+typedef struct ibp_compress_tensor {
+  uint64_t n_rows;
+  uint64_t row_bytes;
+  const void *src;
+  void *slots;
+  uint64_t *flags;
+  uint32_t *row_bits;
+} ibp_compress_tensor;
+
+/*
+ * [IBP] Compression of n_tensors tensors that share the metadata `md` (the
+ * weight matrices of a model layer): each tensor's image exactly as
+ * ibp_compress would write it.  With W = 32, the tensors whose rows are 8,
+ * 16, 28 or 32 KiB (2048, 4096, 7168 or 8192 blocks) are compressed in one
+ * launch per row length and 16 tensors; any other tensor is compressed as by
+ * ibp_compress.  The descriptor array is host memory and is read before the
+ * call returns.  Every tensor is checked first (the rules of ibp_compress);
+ * on an error nothing is enqueued.  n_tensors == 0 is a no-op.  Tensors must
+ * not overlap each other's buffers (each may compress in place).
+ * Asynchronous on `stream`.
+ */
+int ibp_compress_batch(const ibp_metadata *md, const ibp_compress_tensor *tensors,
+                       uint64_t n_tensors, void *stream);
+
+/*
  * [IBP] Decompression of the whole table: dst row r = row r restored.
  * slots: device memory or mapped pinned host memory; flags, dst: device.
  * Asynchronous on `stream`.

@@ -612,6 +612,24 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
   }
 }
 
+// One tensor of a batched compression launch (compress_wg_kernel).
+constexpr uint32_t kCompressBatchMax = 16;
+struct CompressTensor {
+  const uint32_t* src;
+  uint32_t* slots;
+  unsigned long long* flags;
+  uint32_t* row_bits;
+  uint64_t n_rows;
+  uint32_t pad;  // stored rows padded to 64-byte units (device slots)
+  uint32_t unused;
+};
+struct CompressBatch {
+  uint32_t count;
+  uint32_t unused;
+  uint32_t wg_end[kCompressBatchMax];  // workgroups of tensors [0, t]
+  CompressTensor t[kCompressBatchMax];
+};
+
 // [IBP] Compression of rows of exactly WPB * 64 * CPW blocks (the long rows
 // of LLM weight matrices), a workgroup of WPB waves per row: each wave holds
 // its share of the row in registers (chunks wave * CPW ... + CPW - 1, one
@@ -628,12 +646,23 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
 // row cost a third of the time of a 4096 x 8 KiB matrix).  In place
 // (src == slots) is safe: every wave has read its part of the row before the
 // first barrier and nothing is written before it, and the rows loaded ahead
-// are other rows, whose slots no store of this one touches.
+// are other rows, whose slots no store of this one touches.  One launch
+// takes up to kCompressBatchMax tensors of the same row length (the matrices
+// of a layer): each workgroup finds its tensor from the running workgroup
+// counts, and no range spans two tensors.
 template <int NR, int CPW, int WPB>
-__global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
-    Codec cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
-    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits, uint32_t per_wg) {
+__global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, CompressBatch batch,
+                                                                  uint32_t per_wg) {
   constexpr uint32_t n = (uint32_t)CPW * kWave * WPB;
+  uint32_t t = 0;
+  while (blockIdx.x >= batch.wg_end[t]) ++t;
+  const CompressTensor& ct = batch.t[t];
+  const uint64_t n_rows = ct.n_rows;
+  const uint32_t* src = ct.src;
+  uint32_t* slots = ct.slots;
+  unsigned long long* flags = ct.flags;
+  uint32_t* row_bits = ct.row_bits;
+  const uint32_t wg = blockIdx.x - (t ? batch.wg_end[t - 1] : 0u);  // within the tensor
   __shared__ uint32_t buf[n + 4];
   __shared__ uint32_t wtot[WPB];  // the waves' match totals
   const uint32_t lane = lane_id();
@@ -650,7 +679,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
   // n header bits, then 32 bits per block before it
   const uint32_t off0 = n + 8u * lane_byte;
   const int negp = -(int)cd.p;
-  const uint64_t r0 = (uint64_t)blockIdx.x * per_wg;
+  const uint64_t r0 = (uint64_t)wg * per_wg;
   const uint64_t r1 = min(n_rows, r0 + per_wg);
   // a row past the range loads as zeros (empty range), never out of bounds
   auto load = [&](uint32_t (&v)[CPW], uint64_t r) {
@@ -757,7 +786,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(
       for (int c = 0; c < CPW; ++c)
         __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
     } else {
-      const uint32_t nw = store_words(s_row, (c_bits + 31u) >> 5, n, cd.pad);
+      const uint32_t nw = store_words(s_row, (c_bits + 31u) >> 5, n, ct.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
         const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
@@ -3298,6 +3327,71 @@ uint32_t cwg_rows_per_wg(uint64_t n_rows, uint64_t cap, bool bytes) {
   return (uint32_t)std::min<uint64_t>(64, bytes ? 8 * ((fill + 7) / 8) : fill);
 }
 
+// Row lengths (in blocks) that compress_wg_kernel takes.
+bool cwg_row(uint32_t n) { return n == 2048 || n == 4096 || n == 7168 || n == 8192; }
+
+// Rows of one entry of a batched compression launch at most.  Longer
+// tensors (2^29 rows of 8 KiB are 4 TiB) are cut into entries of this many
+// rows, a multiple of 64, so that each entry's flag bits start a flag word; a
+// launch then has at most 16 * 2^29 rows and, with up to 64 rows per
+// workgroup once the rows outnumber the resident workgroups, fewer than 2^28
+// workgroups.
+constexpr uint64_t kCompressEntryRows = 1ull << 29;
+
+// One launch of compress_wg_kernel over the entries of `b` (rows of cd.n
+// blocks, b.count >= 1, total_rows rows), as many workgroups as stay resident
+// (a CU holds 8 workgroups of 4 waves and 160 KiB of LDS, which holds their
+// rows' streams).  Measured on 4096-row matrices: 8 rows per workgroup (flag
+// bytes) for 8 KiB rows, and for 28 KiB rows fewer (atomics; 8 leave too few
+// workgroups).
+template <int NR>
+void launch_compress_wg(const Codec& cd, CompressBatch& b, uint64_t total_rows, hipStream_t st) {
+#define IBP_CWG(CPW, WPB, BYTES)                                                           \
+  {                                                                                         \
+    constexpr uint32_t lds = (CPW * kWave * WPB + 4u + WPB) * 4u;                           \
+    constexpr uint32_t per_cu = std::min(32u / WPB, (160u * 1024u) / lds);                  \
+    const uint32_t per_wg =                                                                 \
+        cwg_rows_per_wg(total_rows, workgroups_per_device(per_cu), BYTES);                  \
+    uint32_t wgs = 0;                                                                       \
+    for (uint32_t e = 0; e < b.count; ++e) {                                                \
+      wgs += (uint32_t)((b.t[e].n_rows + per_wg - 1) / per_wg);                             \
+      b.wg_end[e] = wgs;                                                                    \
+    }                                                                                       \
+    hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>), dim3(wgs), dim3(WPB * kWave), 0,  \
+                       st, cd, b, per_wg);                                                  \
+  }
+  switch (cd.n) {
+    case 2048: IBP_CWG(8, 4, true); return;
+    case 4096: IBP_CWG(16, 4, true); return;
+    case 7168: IBP_CWG(28, 4, false); return;
+    default: IBP_CWG(32, 4, false); return;  // 8192
+  }
+#undef IBP_CWG
+}
+
+// Appends the rows of one tensor (rows of cd.n blocks) to a batch of
+// compress_wg_kernel entries, launching whenever the batch is full.
+template <int NR>
+void add_compress_wg(const Codec& cd, CompressBatch& b, uint64_t& total_rows, uint64_t n_rows,
+                     const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
+                     uint32_t pad, hipStream_t st) {
+  for (uint64_t off = 0; off < n_rows; off += kCompressEntryRows) {
+    if (b.count == kCompressBatchMax) {
+      launch_compress_wg<NR>(cd, b, total_rows, st);
+      b.count = 0;
+      total_rows = 0;
+    }
+    CompressTensor& e = b.t[b.count++];
+    e.src = (const uint32_t*)src + off * cd.n;
+    e.slots = (uint32_t*)slots + off * cd.n;
+    e.flags = (unsigned long long*)flags + off / 64;
+    e.row_bits = row_bits ? row_bits + off : nullptr;
+    e.n_rows = std::min(kCompressEntryRows, n_rows - off);
+    e.pad = pad;
+    total_rows += e.n_rows;
+  }
+}
+
 template <int NR>
 void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
                         uint64_t* flags, uint32_t* row_bits, int vec, hipStream_t st) {
@@ -3309,29 +3403,14 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
     default: break;
   }
   // rows of 256 * CPW blocks for the common long-row sizes (LLM weight rows
-  // of 4096 or 14336 bf16 values): the register-resident workgroup kernel,
-  // as many workgroups as stay resident (a CU holds 8 workgroups of 4 waves
-  // and 160 KiB of LDS, which holds their rows' streams).  Measured on a
-  // 4096-row matrix: 8 rows per workgroup (flag bytes) for 8 KiB rows, and
-  // for 28 KiB rows 4 (atomics; 8 leave too few workgroups).
-#define IBP_CWG(CPW, WPB, BYTES)                                                           \
-  {                                                                                         \
-    constexpr uint32_t lds = (CPW * kWave * WPB + 4u + WPB) * 4u;                           \
-    constexpr uint32_t per_cu = std::min(32u / WPB, (160u * 1024u) / lds);                  \
-    const uint32_t per_wg = cwg_rows_per_wg(n_rows, workgroups_per_device(per_cu), BYTES);  \
-    hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>),                                  \
-                       dim3(grid_for((n_rows + per_wg - 1) / per_wg)), dim3(WPB * kWave), 0, \
-                       st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,              \
-                       (unsigned long long*)flags, row_bits, per_wg);                       \
+  // of 4096 or 14336 bf16 values): the register-resident workgroup kernel
+  if (cwg_row(cd.n)) {
+    CompressBatch b{};
+    uint64_t total = 0;
+    add_compress_wg<NR>(cd, b, total, n_rows, src, slots, flags, row_bits, cd.pad, st);
+    launch_compress_wg<NR>(cd, b, total, st);
+    return;
   }
-  switch (cd.n) {
-    case 2048: IBP_CWG(8, 4, true); return;
-    case 4096: IBP_CWG(16, 4, true); return;
-    case 7168: IBP_CWG(28, 4, false); return;
-    case 8192: IBP_CWG(32, 4, false); return;
-    default: break;
-  }
-#undef IBP_CWG
   // LDS window tiers: the whole row stream (<= n words) lives in LDS
   if (cd.n <= 1024)
     launch_compress_t<NR, 1024>(cd, n_rows, src, slots, flags, row_bits, vec, st);
@@ -3712,6 +3791,22 @@ int count_scratch(unsigned long long** out) {
   return IBP_OK;
 }
 
+// The tensors of a batch whose rows compress_wg_kernel takes, of one row
+// length, in launches of up to kCompressBatchMax entries.
+template <int NR>
+void compress_wg_batch(const Codec& cd, const ibp_compress_tensor* tensors, uint64_t n_tensors,
+                       uint64_t row_bytes, hipStream_t st) {
+  CompressBatch b{};
+  uint64_t total = 0;
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    const ibp_compress_tensor& x = tensors[t];
+    if (x.n_rows == 0 || x.row_bytes != row_bytes) continue;
+    add_compress_wg<NR>(cd, b, total, x.n_rows, x.src, x.slots, x.flags, x.row_bits,
+                        is_host_memory(x.slots) ? 0u : 1u, st);
+  }
+  if (b.count) launch_compress_wg<NR>(cd, b, total, st);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------ C ABI ----
@@ -3867,11 +3962,11 @@ int ibp_build_metadata_noalloc(const void* sample, uint64_t n_blocks, uint32_t w
                              IBP_NOALLOC_COUNT_GRID);
 }
 
-int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, const void* src,
-                 void* slots, uint64_t* flags, uint32_t* row_bits, void* stream) {
-  int rc = check_metadata(md);
-  if (rc) return rc;
-  rc = check_rows(n_rows, row_bytes, md->width_bits);
+// Host checks of ibp_compress's arguments (n_rows == 0 passes).
+static int check_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                          const void* src, const void* slots, const uint64_t* flags,
+                          const uint32_t* row_bits) {
+  int rc = check_rows(n_rows, row_bytes, md->width_bits);
   if (rc) return rc;
   if (row_bytes > IBP_MAX_COMPRESS_ROW_BYTES) return IBP_ERR_UNSUPPORTED;
   if (n_rows == 0) return IBP_OK;
@@ -3884,18 +3979,21 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
     const uintptr_t a = (uintptr_t)src, b = (uintptr_t)slots, len = n_rows * row_bytes;
     if (a != b && a < b + len && b < a + len) return IBP_ERR_INVALID_ARGUMENT;
   }
-  rc = pending_hip_error();
-  if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
+  return IBP_OK;
+}
+
+// Enqueues the compression of one checked tensor (n_rows > 0).
+static void enqueue_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes,
+                             const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
+                             hipStream_t st) {
   // no clearing launch: every row's flag bit is cleared or set by the
-  // kernel that compresses the row (put_flag_bits)
+  // kernel that compresses the row
   if (md->width_bits != 32) {
     if (md->width_bits == 16)
       launch_compress_wide<uint16_t>(md, n_rows, row_bytes, src, slots, flags, row_bits, st);
     else
       launch_compress_wide<uint64_t>(md, n_rows, row_bytes, src, slots, flags, row_bits, st);
-    hipError_t e = hipGetLastError();
-    return e == hipSuccess ? IBP_OK : hip_fail(e);
+    return;
   }
   Codec cd = make_codec(md, row_bytes);
   cd.pad = is_host_memory(slots) ? 0u : 1u;
@@ -3907,6 +4005,62 @@ int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, co
     case 3: launch_compress_nr<3>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
     case 4: launch_compress_nr<4>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
     default: launch_compress_nr<-1>(cd, n_rows, src, slots, flags, row_bits, vec, st); break;
+  }
+}
+
+int ibp_compress(const ibp_metadata* md, uint64_t n_rows, uint64_t row_bytes, const void* src,
+                 void* slots, uint64_t* flags, uint32_t* row_bits, void* stream) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  rc = check_compress(md, n_rows, row_bytes, src, slots, flags, row_bits);
+  if (rc || n_rows == 0) return rc;
+  rc = pending_hip_error();
+  if (rc) return rc;
+  enqueue_compress(md, n_rows, row_bytes, src, slots, flags, row_bits, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? IBP_OK : hip_fail(e);
+}
+
+int ibp_compress_batch(const ibp_metadata* md, const ibp_compress_tensor* tensors,
+                       uint64_t n_tensors, void* stream) {
+  int rc = check_metadata(md);
+  if (rc) return rc;
+  if (n_tensors == 0) return IBP_OK;
+  if (!tensors) return IBP_ERR_INVALID_ARGUMENT;
+  bool work = false;
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    const ibp_compress_tensor& x = tensors[t];
+    rc = check_compress(md, x.n_rows, x.row_bytes, x.src, x.slots, x.flags, x.row_bits);
+    if (rc) return rc;
+    work = work || x.n_rows != 0;
+  }
+  if (!work) return IBP_OK;
+  rc = pending_hip_error();
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  bool done[4] = {false, false, false, false};  // the four row lengths of cwg_row
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    const ibp_compress_tensor& x = tensors[t];
+    if (x.n_rows == 0) continue;
+    const uint64_t n = x.row_bytes / 4;
+    if (md->width_bits != 32 || !cwg_row((uint32_t)n)) {  // tensor by tensor
+      enqueue_compress(md, x.n_rows, x.row_bytes, x.src, x.slots, x.flags, x.row_bits, st);
+      continue;
+    }
+    // the first tensor of each row length of the weight-row kernel gathers
+    // every tensor of that length into shared launches
+    bool& d = done[n == 2048 ? 0 : n == 4096 ? 1 : n == 7168 ? 2 : 3];
+    if (d) continue;
+    d = true;
+    const Codec cd = make_codec(md, x.row_bytes);
+    switch (cd.runs.n) {
+      case 0: compress_wg_batch<0>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      case 1: compress_wg_batch<1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      case 2: compress_wg_batch<2>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      case 3: compress_wg_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      case 4: compress_wg_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      default: compress_wg_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+    }
   }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? IBP_OK : hip_fail(e);

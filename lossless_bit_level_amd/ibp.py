@@ -37,6 +37,16 @@ class ibp_tensor(ctypes.Structure):
                 ("dst", ctypes.c_void_p)]
 
 
+class ibp_compress_tensor(ctypes.Structure):
+    """One tensor of ibp_compress_batch (see include/ibp.h)."""
+    _fields_ = [("n_rows", ctypes.c_uint64),
+                ("row_bytes", ctypes.c_uint64),
+                ("src", ctypes.c_void_p),
+                ("slots", ctypes.c_void_p),
+                ("flags", ctypes.c_void_p),
+                ("row_bits", ctypes.c_void_p)]
+
+
 class ibp_metadata(ctypes.Structure):
     _fields_ = [("width_bits", ctypes.c_uint32),
                 ("invariant_bits", ctypes.c_uint32),
@@ -81,6 +91,7 @@ def lib() -> ctypes.CDLL:
         L.ibp_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, vp]
         L.ibp_gather_decompress.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp]
         L.ibp_decompress_batch.argtypes = [mdp, ctypes.POINTER(ibp_tensor), u64, vp]
+        L.ibp_compress_batch.argtypes = [mdp, ctypes.POINTER(ibp_compress_tensor), u64, vp]
         L.ibp_cache_plan.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, ctypes.POINTER(u64), vp]
         L.ibp_cache_fill.argtypes = [mdp, u64, u64, vp, vp, vp, u64, vp, vp, u64, vp, vp]
         L.ibp_gather_decompress_cached.argtypes = [mdp, u64, u64, vp, vp, vp, vp, vp, u64, vp, vp]
@@ -228,6 +239,40 @@ def ibp_compress(md: ibp_metadata, src: torch.Tensor, slots: torch.Tensor | None
                               row_bits.data_ptr() if row_bits is not None else None,
                               _stream(stream)))
     return slots, flags, row_bits
+
+
+def _compress_batch_args(srcs, outs):
+    arr = (ibp_compress_tensor * max(1, len(srcs)))()
+    for k, (src, (slots, flags, row_bits)) in enumerate(zip(srcs, outs)):
+        n_rows, row_bytes = _rows(src)
+        _need_cuda(flags, "flags")
+        if row_bits is not None:
+            _need_cuda(row_bits, "row_bits")
+        arr[k] = ibp_compress_tensor(n_rows, row_bytes, _dptr(src), _dptr(slots),
+                                     flags.data_ptr(),
+                                     row_bits.data_ptr() if row_bits is not None else None)
+    return arr
+
+
+def ibp_compress_batch(md: ibp_metadata, srcs, outs=None, stream=None):
+    """Compress several tensors sharing `md` (one launch per row length and 16
+    tensors where the library batches them): srcs is a list of tables; outs
+    (optional) the matching (slots, flags, row_bits) buffers.  Returns outs."""
+    srcs = list(srcs)
+    if outs is None:
+        outs = []
+        for src in srcs:
+            n_rows, row_bytes = _rows(src)
+            dev = src.device if src.is_cuda else torch.device("cuda")
+            outs.append((torch.empty((n_rows, row_bytes), dtype=torch.uint8, device=dev),
+                         torch.empty(max(1, ibp_flag_words(n_rows)), dtype=torch.int64, device=dev),
+                         torch.empty(max(1, n_rows), dtype=torch.int32, device=dev)))
+    if len(outs) != len(srcs):
+        raise ValueError("one output per table")
+    arr = _compress_batch_args(srcs, outs)
+    _check("ibp_compress_batch",
+           lib().ibp_compress_batch(ctypes.byref(md), arr, len(srcs), _stream(stream)))
+    return outs
 
 
 def ibp_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,

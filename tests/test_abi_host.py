@@ -108,6 +108,32 @@ def test_batch_validation_before_enqueue(ibp):
     assert L.ibp_decompress_batch(byref(md), empty, 1, None) == ibp.IBP_OK
 
 
+def test_compress_batch_validation_before_enqueue(ibp):
+    """ibp_compress_batch checks every tensor (ibp_compress's rules) before it
+    enqueues anything."""
+    L = ibp.lib()
+    md = _md(ibp)
+    byref = ctypes.byref
+    fake = 0x10000  # never dereferenced
+    T = ibp.ibp_compress_tensor
+    good = T(4, 8192, fake, fake + (1 << 20), fake, None)
+    arr = (T * 3)(good, T(4, 8194, fake, fake, fake, None), good)   # row_bytes % 4
+    assert L.ibp_compress_batch(byref(md), arr, 3, None) == ibp.IBP_ERR_LAYOUT
+    arr = (T * 2)(good, T(4, 8192, fake, fake, None, None))         # null flags
+    assert L.ibp_compress_batch(byref(md), arr, 2, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    arr = (T * 2)(good, T(4, 8192, fake, fake + 8192, fake, None))  # src and slots overlap
+    assert L.ibp_compress_batch(byref(md), arr, 2, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    arr = (T * 2)(good, T(4, 8192, fake, fake + (1 << 20), fake, fake + 2))  # row_bits
+    assert L.ibp_compress_batch(byref(md), arr, 2, None) == ibp.IBP_ERR_LAYOUT
+    big = T(4, (1 << 20) + 4, fake, fake + (1 << 24), fake, None)   # row too long
+    assert L.ibp_compress_batch(byref(md), (T * 1)(big), 1, None) == ibp.IBP_ERR_UNSUPPORTED
+    assert L.ibp_compress_batch(byref(md), None, 1, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress_batch(None, arr, 1, None) == ibp.IBP_ERR_INVALID_ARGUMENT
+    assert L.ibp_compress_batch(byref(md), None, 0, None) == ibp.IBP_OK
+    empty = (T * 1)(T(0, 8192, None, None, None, None))            # empty tensors: no-op
+    assert L.ibp_compress_batch(byref(md), empty, 1, None) == ibp.IBP_OK
+
+
 def test_validation_before_enqueue(ibp):
     L = ibp.lib()
     md = _md(ibp)

@@ -1180,6 +1180,62 @@ def test_decompress_batch(ibp, n_tensors):
     assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("w,mask,bitval", [(32, 0x78007800, 0x38003800), (16, 0x7800, 0x3800)],
+                         ids=["w32", "w16"])
+def test_compress_batch(ibp, w, mask, bitval):
+    """ibp_compress_batch: each tensor's image equals ibp_compress's and, for
+    two tensors, the oracle's.  8 and 28 KiB rows (W = 32: two launches of
+    the weight-row kernel, tensors of several ranges per launch, a ragged
+    one), rows other kernels take (2 KiB, 4100 B), an empty tensor, a tensor
+    compressed in place and one without row_bits."""
+    rng = np.random.default_rng(w + 7)
+    shapes = [(1300, 8192), (64, 8192), (33, 28672), (1283, 28672), (100, 2048), (0, 8192),
+              (50, 4100 if w == 32 else 4096), (70, 8192), (40, 28672)]
+    in_place, no_row_bits = 7, 8
+    md = gmd(ibp, mask, bitval, w=w)
+    xs, srcs, outs = [], [], []
+    for k, (n_rows, S) in enumerate(shapes):
+        x = (make_rows(rng, n_rows, S, mask, bitval, match_p=0.9) if w == 32 else
+             make_rows_w(rng, w, n_rows, S, mask, bitval, 0.9)) if n_rows else \
+            np.zeros((0, S), np.uint8)
+        if n_rows > 2:
+            x[1] = rng.integers(0, 256, S, dtype=np.uint8)           # a raw row
+        xs.append(x)
+        xg = to_gpu(x) if n_rows else torch.empty((0, S), dtype=torch.uint8, device="cuda")
+        srcs.append(xg)
+        nw = max(1, ibp.ibp_flag_words(n_rows))
+        flags = torch.full((nw,), -1, dtype=torch.int64, device="cuda")  # any prior contents
+        slots = xg if k == in_place else torch.empty_like(xg)
+        rb = None if k == no_row_bits else torch.empty(max(1, n_rows), dtype=torch.int32,
+                                                     device="cuda")
+        outs.append((slots, flags, rb))
+    say(f"compress batch W={w} of {len(shapes)} tensors")
+    ibp.ibp_compress_batch(md, srcs, outs)
+    torch.cuda.synchronize()
+    for k, (x, (slots, flags, rb)) in enumerate(zip(xs, outs)):
+        n_rows = x.shape[0]
+        if n_rows == 0:
+            continue
+        s1, f1, r1 = ibp.ibp_compress(md, to_gpu(x))
+        torch.cuda.synchronize()
+        fl = flags_np(flags, n_rows)
+        assert np.array_equal(fl, flags_np(f1, n_rows)), k
+        r1n = r1.cpu().numpy()[:n_rows].view(np.uint32)
+        if rb is not None:
+            assert np.array_equal(rb.cpu().numpy()[:n_rows].view(np.uint32), r1n), k
+        sg, s1n = slots.cpu().numpy(), s1.cpu().numpy()
+        for r in range(n_rows):
+            nb = orc.stored_bytes(x.shape[1], int(r1n[r]), flag_of(fl, r))
+            assert np.array_equal(sg[r, :nb], s1n[r, :nb]), (k, r)
+        assert torch.equal(ibp.ibp_decompress(md, slots, flags), to_gpu(x)), k
+    for k in (1, 2):
+        slots, flags, rb = outs[k]
+        slots_o, flags_o, rb_o = orc.compress(omd(md), xs[k])
+        assert_image_equal(slots.cpu().numpy(), flags_np(flags, xs[k].shape[0]),
+                           rb.cpu().numpy()[:xs[k].shape[0]].view(np.uint32),
+                           slots_o, flags_o, rb_o)
+
+
 @pytest.mark.parametrize("w,shapes,mask,bitval", [
     # 16-bit blocks: rows of 1 and 14 segments, a ragged one (n = 1026), raw
     # rows, a tensor of one row; one batched launch
