@@ -368,7 +368,11 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
         f"({raw_bytes / comp_s / 1e9:.0f} GB/s); ratio {raw_bytes / stored:.4f}")
     compress_rec = {"ms": round(comp_s * 1e3, 3), "GB_per_s_raw_in": round(raw_bytes / comp_s / 1e9, 1),
                     # raw bytes read plus stored bytes written, against the HBM peak
-                    "frac": round((raw_bytes + stored) / comp_s / 1e9 / HBM_PEAK_GBPS, 4)}
+                    "frac": round((raw_bytes + stored) / comp_s / 1e9 / HBM_PEAK_GBPS, 4),
+                    "timed": ("one table, three calls back to back" if wl.n_tables == 1 else
+                              "each layer's tables in one batched call"
+                              if pos_table is None else "each layer's tables back to back") +
+                             ", after a spin kernel; HIP events"}
     common = {
         "desc": wl.desc,
         "compression_ratio": round(raw_bytes / stored, 4),
