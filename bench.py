@@ -312,49 +312,50 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
                                                row_bits=rb)
         return ibp.ibp_compress(md, tg, slots=slots, flags=flags, row_bits=rb)
 
-    def time_compress(calls, batch=False):
-        """GPU seconds of the compress calls (staged table, outputs) back to
-        back on the stream, or with batch of one ibp_compress_batch over them.
-        A spin kernel runs first, so that the calls are queued before the
-        region starts and the host's own per-call work is not timed (the GPU
-        time of a pipeline of such calls)."""
+    def time_compress(groups, batch=False, reps=1):
+        """GPU seconds of compressing the staged tables again into their
+        outputs: each group (a list of (staged table, outputs)) with one
+        ibp_compress_batch, or table by table, back to back on the stream,
+        reps times.  The calls' arguments are converted first, and a spin
+        kernel runs before the region, so that the calls are queued before it
+        starts and the host's own per-call work is not timed (the GPU time of
+        a pipeline of such calls).  No table generator runs meanwhile."""
+        if batch:
+            calls = [ibp.ibp_compress_batch_launcher(md, [tg for tg, _ in g], [o for _, o in g])
+                     for g in groups]
+        else:
+            calls = [(lambda tg=tg, o=o: compress(tg, o)) for g in groups for tg, o in g]
         torch.cuda.synchronize()
         torch.cuda._sleep(COMPRESS_SPIN_CYCLES)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        if batch:
-            ibp.ibp_compress_batch(md, [tg for tg, _ in calls], [out for _, out in calls])
-        else:
-            for tg, out in calls:
-                compress(tg, out)
+        for _ in range(reps):
+            for call in calls:
+                call()
         e1.record(stream)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3
+        return e0.elapsed_time(e1) / 1e3 / reps
 
     # upload and compress every table (out of place from a staging upload),
-    # then time its compression again into the same buffers: the tables of a
-    # layer (up to COMPRESS_GROUP_BYTES of raw input) in one batched call, a
-    # one-table workload three times back to back
+    # keeping the staged tables; then, with no table generator running, time
+    # their compression again into the same buffers: the tables of a layer
+    # (up to COMPRESS_GROUP_BYTES of raw input) in one batched call, layer
+    # after layer, or a one-table workload three times back to back
     images = []          # (slots, flags, stored bytes per row numpy, stored bytes int32 GPU)
     shapes = []
-    comp_s = 0.0
     raw_bytes = stored = bits_total = side_bytes = 0
     t_up = time.perf_counter()
-    group, group_bytes = [], 0
+    groups, group_bytes = [[]], 0
     for i, x in iter_tables(wl, threads):
         tg = torch.from_numpy(x.reshape(x.shape[0], -1).view(np.uint8)).to(dev)
         shapes.append(tuple(tg.shape))
         out = compress(tg)
         slots, flags, rb = out
-        group.append((tg, out))
+        groups[-1].append((tg, out))
         group_bytes += tg.numel()
-        if wl.n_tables == 1:
-            comp_s += time_compress(group * 3) / 3
-            group, group_bytes = [], 0
-        elif group_bytes >= COMPRESS_GROUP_BYTES or i == wl.n_tables - 1:
-            # a layer's tables in one ibp_compress_batch (global metadata)
-            comp_s += time_compress(group, batch=pos_table is None)
-            group, group_bytes = [], 0
+        if group_bytes >= COMPRESS_GROUP_BYTES and i < wl.n_tables - 1:
+            groups.append([])
+            group_bytes = 0
         del tg
         rbn = rb.cpu().numpy()[:shapes[-1][0]]
         sb = stored_bytes_per_row(rbn, shapes[-1][1])
@@ -363,6 +364,10 @@ def measure(wl: Workload, opt: Opts, sources, K: int, W: int, threads: int, dev,
         stored += int(sb.sum())
         side_bytes += 8 * ((shapes[-1][0] + 63) // 64)
         bits_total += int(np.minimum(rbn.astype(np.int64), 8 * shapes[-1][1]).sum())
+    # a layer's tables in one ibp_compress_batch (global metadata)
+    comp_s = time_compress(groups, batch=wl.n_tables > 1 and pos_table is None,
+                           reps=3 if wl.n_tables == 1 else 1)
+    del groups
     log(f"{wl.name}: {len(images)} tables uploaded and compressed in "
         f"{time.perf_counter() - t_up:.1f} s; {md}; compress {comp_s * 1e3:.2f} ms "
         f"({raw_bytes / comp_s / 1e9:.0f} GB/s); ratio {raw_bytes / stored:.4f}")

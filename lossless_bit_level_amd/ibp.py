@@ -275,6 +275,23 @@ def ibp_compress_batch(md: ibp_metadata, srcs, outs=None, stream=None):
     return outs
 
 
+def ibp_compress_batch_launcher(md: ibp_metadata, srcs, outs, stream=None):
+    """ibp_compress_batch with its arguments converted once."""
+    srcs, outs = list(srcs), list(outs)
+    if len(outs) != len(srcs):
+        raise ValueError("one output per table")
+    arr = _compress_batch_args(srcs, outs)
+    fn = lib().ibp_compress_batch
+    args = (ctypes.byref(md), arr, ctypes.c_uint64(len(srcs)), ctypes.c_void_p(_stream(stream)))
+
+    def launch():
+        rc = fn(*args)
+        if rc:
+            raise IBPError("ibp_compress_batch", rc)
+    launch.keep = (arr, srcs, outs)
+    return launch
+
+
 def ibp_decompress(md: ibp_metadata, slots: torch.Tensor, flags: torch.Tensor,
                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Restore every row; `out` defaults to uint8 [n_rows, row_bytes] on the GPU."""
