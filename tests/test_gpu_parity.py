@@ -459,8 +459,9 @@ def test_compress_row_ranges_across_flag_words(ibp, kind):
 
 
 @pytest.mark.parametrize("kind,row_bytes", [
-    ("w32", 128), ("w32", 512), ("w32", 8192), ("w32", 4100), ("w16", 8192), ("w16", 512),
-    ("w64", 2048), ("w64", 4104), ("positional", 512), ("positional", 4100)])
+    ("w32", 128), ("w32", 512), ("w32", 8192), ("w32", 28672), ("w32", 4100), ("w16", 8192),
+    ("w16", 28672), ("w16", 512), ("w64", 2048), ("w64", 4104), ("positional", 512),
+    ("positional", 4100)])
 def test_flags_written_over_any_prior_contents(ibp, kind, row_bytes):
     """Every compression kernel writes each row's flag bit itself (no clearing
     launch): flag words that start as all ones, or as the flags of another
