@@ -186,10 +186,9 @@ typedef struct ibp_compress_tensor {
 /*
  * [IBP] Compression of n_tensors tensors that share the metadata `md` (the
  * weight matrices of a model layer): each tensor's image exactly as
- * ibp_compress would write it.  With W = 32, the tensors whose rows are 8,
- * 16, 28 or 32 KiB (2048, 4096, 7168 or 8192 blocks) are compressed in one
- * launch per row length and 16 tensors; any other tensor is compressed as by
- * ibp_compress.  The descriptor array is host memory and is read before the
+ * ibp_compress would write it.  With W = 32 or 16, the tensors whose rows
+ * are 8, 16, 28 or 32 KiB are compressed in one launch per row length and 16
+ * tensors; any other tensor is compressed as by ibp_compress.  The descriptor array is host memory and is read before the
  * call returns.  Every tensor is checked first (the rules of ibp_compress);
  * on an error nothing is enqueued.  n_tensors == 0 is a no-op.  Tensors must
  * not overlap each other's buffers (each may compress in place).

@@ -1894,14 +1894,23 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
 // workgroup's LDS stream, which is then written with coalesced stores (a raw
 // row straight from the registers).  Three barriers per row.  As in
 // compress_wg_kernel, a workgroup takes a contiguous range of `per_wg` rows
-// (at most 64), loads its next row while it encodes one and writes the
-// range's flag bits once at its end (whole bytes when per_wg is a multiple
-// of 8).  In place is safe: every wave has read its part of the row before
-// the first barrier, and the row loaded ahead is another row.
+// (at most 64), loads its next row while it encodes one, writes the range's
+// flag bits once at its end (whole bytes when per_wg is a multiple of 8) and
+// takes up to kCompressBatchMax tensors of one row length per launch.  In
+// place is safe: every wave has read its part of the row before the first
+// barrier, and the row loaded ahead is another row.
 template <int NR, int CPW>
 __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
-    WideCodec<uint16_t> cd, uint64_t n_rows, const uint32_t* src, uint32_t* slots,
-    unsigned long long* __restrict__ flags, uint32_t* __restrict__ row_bits, uint32_t per_wg) {
+    WideCodec<uint16_t> cd, CompressBatch batch, uint32_t per_wg) {
+  uint32_t t = 0;
+  while (blockIdx.x >= batch.wg_end[t]) ++t;
+  const CompressTensor& ct = batch.t[t];
+  const uint64_t n_rows = ct.n_rows;
+  const uint32_t* src = ct.src;
+  uint32_t* slots = ct.slots;
+  unsigned long long* flags = ct.flags;
+  uint32_t* row_bits = ct.row_bits;
+  const uint32_t wg = blockIdx.x - (t ? batch.wg_end[t - 1] : 0u);  // within the tensor
   constexpr uint32_t nw = (uint32_t)CPW * kWave * kWavesPerBlock;  // words of a row
   constexpr uint32_t n = 2u * nw;                                   // blocks of a row
   __shared__ uint32_t buf[nw + 4];
@@ -1930,7 +1939,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
     }
     return v;
   };
-  const uint64_t r0 = (uint64_t)blockIdx.x * per_wg;
+  const uint64_t r0 = (uint64_t)wg * per_wg;
   const uint64_t r1 = min(n_rows, r0 + per_wg);
   // a row past the range loads as zeros (empty range), never out of bounds
   auto load = [&](uint32_t (&v)[CPW], uint64_t r) {
@@ -2026,7 +2035,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
       for (int c = 0; c < CPW; ++c)
         __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
     } else {
-      const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, cd.pad);
+      const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, ct.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
         const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
@@ -3327,8 +3336,20 @@ uint32_t cwg_rows_per_wg(uint64_t n_rows, uint64_t cap, bool bytes) {
   return (uint32_t)std::min<uint64_t>(64, bytes ? 8 * ((fill + 7) / 8) : fill);
 }
 
-// Row lengths (in blocks) that compress_wg_kernel takes.
+// Row lengths (in 32-bit words) that the weight-row kernels take
+// (compress_wg_kernel, compress_pair_wg_kernel).
 bool cwg_row(uint32_t n) { return n == 2048 || n == 4096 || n == 7168 || n == 8192; }
+
+// Running workgroup counts of a batch at per_wg rows per workgroup; the
+// total is the grid.
+uint32_t set_wg_ends(CompressBatch& b, uint32_t per_wg) {
+  uint32_t wgs = 0;
+  for (uint32_t e = 0; e < b.count; ++e) {
+    wgs += (uint32_t)((b.t[e].n_rows + per_wg - 1) / per_wg);
+    b.wg_end[e] = wgs;
+  }
+  return wgs;
+}
 
 // Rows of one entry of a batched compression launch at most.  Longer
 // tensors (2^29 rows of 8 KiB are 4 TiB) are cut into entries of this many
@@ -3352,11 +3373,7 @@ void launch_compress_wg(const Codec& cd, CompressBatch& b, uint64_t total_rows, 
     constexpr uint32_t per_cu = std::min(32u / WPB, (160u * 1024u) / lds);                  \
     const uint32_t per_wg =                                                                 \
         cwg_rows_per_wg(total_rows, workgroups_per_device(per_cu), BYTES);                  \
-    uint32_t wgs = 0;                                                                       \
-    for (uint32_t e = 0; e < b.count; ++e) {                                                \
-      wgs += (uint32_t)((b.t[e].n_rows + per_wg - 1) / per_wg);                             \
-      b.wg_end[e] = wgs;                                                                    \
-    }                                                                                       \
+    const uint32_t wgs = set_wg_ends(b, per_wg);                                            \
     hipLaunchKernelGGL((compress_wg_kernel<NR, CPW, WPB>), dim3(wgs), dim3(WPB * kWave), 0,  \
                        st, cd, b, per_wg);                                                  \
   }
@@ -3369,21 +3386,22 @@ void launch_compress_wg(const Codec& cd, CompressBatch& b, uint64_t total_rows, 
 #undef IBP_CWG
 }
 
-// Appends the rows of one tensor (rows of cd.n blocks) to a batch of
-// compress_wg_kernel entries, launching whenever the batch is full.
-template <int NR>
-void add_compress_wg(const Codec& cd, CompressBatch& b, uint64_t& total_rows, uint64_t n_rows,
-                     const void* src, void* slots, uint64_t* flags, uint32_t* row_bits,
-                     uint32_t pad, hipStream_t st) {
+// Appends the rows of one tensor (rows of `words` 32-bit words) to a batch of
+// weight-row kernel entries, calling flush(b, total_rows) to launch whenever
+// the batch is full.
+template <typename Flush>
+void add_compress_entries(CompressBatch& b, uint64_t& total_rows, uint32_t words,
+                          uint64_t n_rows, const void* src, void* slots, uint64_t* flags,
+                          uint32_t* row_bits, uint32_t pad, Flush flush) {
   for (uint64_t off = 0; off < n_rows; off += kCompressEntryRows) {
     if (b.count == kCompressBatchMax) {
-      launch_compress_wg<NR>(cd, b, total_rows, st);
+      flush(b, total_rows);
       b.count = 0;
       total_rows = 0;
     }
     CompressTensor& e = b.t[b.count++];
-    e.src = (const uint32_t*)src + off * cd.n;
-    e.slots = (uint32_t*)slots + off * cd.n;
+    e.src = (const uint32_t*)src + off * words;
+    e.slots = (uint32_t*)slots + off * words;
     e.flags = (unsigned long long*)flags + off / 64;
     e.row_bits = row_bits ? row_bits + off : nullptr;
     e.n_rows = std::min(kCompressEntryRows, n_rows - off);
@@ -3391,6 +3409,7 @@ void add_compress_wg(const Codec& cd, CompressBatch& b, uint64_t& total_rows, ui
     total_rows += e.n_rows;
   }
 }
+
 
 template <int NR>
 void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void* slots,
@@ -3407,8 +3426,9 @@ void launch_compress_nr(const Codec& cd, uint64_t n_rows, const void* src, void*
   if (cwg_row(cd.n)) {
     CompressBatch b{};
     uint64_t total = 0;
-    add_compress_wg<NR>(cd, b, total, n_rows, src, slots, flags, row_bits, cd.pad, st);
-    launch_compress_wg<NR>(cd, b, total, st);
+    auto flush = [&](CompressBatch& fb, uint64_t rows) { launch_compress_wg<NR>(cd, fb, rows, st); };
+    add_compress_entries(b, total, cd.n, n_rows, src, slots, flags, row_bits, cd.pad, flush);
+    flush(b, total);
     return;
   }
   // LDS window tiers: the whole row stream (<= n words) lives in LDS
@@ -3555,6 +3575,30 @@ void launch_decode(const Codec& cd, const DecodeArgs& a, hipStream_t st) {
   }
 }
 
+// One launch of compress_pair_wg_kernel over the entries of `b` (rows of
+// cd.nw words, 16-bit blocks), sized as launch_compress_wg.
+template <int NR>
+void launch_compress_pair_wg(const WideCodec<uint16_t>& cd, CompressBatch& b, uint64_t total_rows,
+                             hipStream_t st) {
+#define IBP_PAIR_WG(CPW, BYTES)                                                             \
+  {                                                                                         \
+    constexpr uint32_t lds = (CPW * kWave * kWavesPerBlock + 4u + kWavesPerBlock) * 4u;      \
+    constexpr uint32_t per_cu = std::min(8u, (160u * 1024u) / lds);                         \
+    const uint32_t per_wg =                                                                 \
+        cwg_rows_per_wg(total_rows, workgroups_per_device(per_cu), BYTES);                  \
+    const uint32_t wgs = set_wg_ends(b, per_wg);                                            \
+    hipLaunchKernelGGL((compress_pair_wg_kernel<NR, CPW>), dim3(wgs), dim3(kBlockThreads), 0, \
+                       st, cd, b, per_wg);                                                  \
+  }
+  switch (cd.nw) {
+    case 2048: IBP_PAIR_WG(8, true); return;
+    case 4096: IBP_PAIR_WG(16, true); return;
+    case 7168: IBP_PAIR_WG(28, false); return;
+    default: IBP_PAIR_WG(32, false); return;  // 8192
+  }
+#undef IBP_PAIR_WG
+}
+
 template <typename T, int NR>
 void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void* src,
                              void* slots, uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
@@ -3576,24 +3620,16 @@ void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void
 #undef IBP_PAIR
     // rows of 512 * CPW blocks (the 8 and 28 KiB weight rows): a workgroup
     // per row, ranges of rows per workgroup as for compress_wg_kernel
-#define IBP_PAIR_WG(CPW, BYTES)                                                             \
-  {                                                                                         \
-    constexpr uint32_t lds = (CPW * kWave * kWavesPerBlock + 4u + kWavesPerBlock) * 4u;      \
-    constexpr uint32_t per_cu = std::min(8u, (160u * 1024u) / lds);                         \
-    const uint32_t per_wg = cwg_rows_per_wg(n_rows, workgroups_per_device(per_cu), BYTES);  \
-    hipLaunchKernelGGL((compress_pair_wg_kernel<NR, CPW>),                                  \
-                       dim3(grid_for((n_rows + per_wg - 1) / per_wg)), dim3(kBlockThreads), \
-                       0, st, cd, n_rows, (const uint32_t*)src, (uint32_t*)slots,           \
-                       (unsigned long long*)flags, row_bits, per_wg);                       \
-  }
-    switch (cd.nw) {
-      case 2048: IBP_PAIR_WG(8, true); return;
-      case 4096: IBP_PAIR_WG(16, true); return;
-      case 7168: IBP_PAIR_WG(28, false); return;
-      case 8192: IBP_PAIR_WG(32, false); return;
-      default: break;
+    if (cwg_row(cd.nw)) {
+      CompressBatch b{};
+      uint64_t total = 0;
+      auto flush = [&](CompressBatch& fb, uint64_t rows) {
+        launch_compress_pair_wg<NR>(cd, fb, rows, st);
+      };
+      add_compress_entries(b, total, cd.nw, n_rows, src, slots, flags, row_bits, cd.pad, flush);
+      flush(b, total);
+      return;
     }
-#undef IBP_PAIR_WG
   }
   if constexpr (sizeof(T) == 8) {
     // rows of 64 * NCH 64-bit blocks (512 bytes to 4 KiB): one wave per row
@@ -3798,13 +3834,32 @@ void compress_wg_batch(const Codec& cd, const ibp_compress_tensor* tensors, uint
                        uint64_t row_bytes, hipStream_t st) {
   CompressBatch b{};
   uint64_t total = 0;
+  auto flush = [&](CompressBatch& fb, uint64_t rows) { launch_compress_wg<NR>(cd, fb, rows, st); };
   for (uint64_t t = 0; t < n_tensors; ++t) {
     const ibp_compress_tensor& x = tensors[t];
     if (x.n_rows == 0 || x.row_bytes != row_bytes) continue;
-    add_compress_wg<NR>(cd, b, total, x.n_rows, x.src, x.slots, x.flags, x.row_bits,
-                        is_host_memory(x.slots) ? 0u : 1u, st);
+    add_compress_entries(b, total, cd.n, x.n_rows, x.src, x.slots, x.flags, x.row_bits,
+                         is_host_memory(x.slots) ? 0u : 1u, flush);
   }
-  if (b.count) launch_compress_wg<NR>(cd, b, total, st);
+  if (b.count) flush(b, total);
+}
+
+// The same for 16-bit blocks and compress_pair_wg_kernel.
+template <int NR>
+void compress_pair_batch(const WideCodec<uint16_t>& cd, const ibp_compress_tensor* tensors,
+                         uint64_t n_tensors, uint64_t row_bytes, hipStream_t st) {
+  CompressBatch b{};
+  uint64_t total = 0;
+  auto flush = [&](CompressBatch& fb, uint64_t rows) {
+    launch_compress_pair_wg<NR>(cd, fb, rows, st);
+  };
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    const ibp_compress_tensor& x = tensors[t];
+    if (x.n_rows == 0 || x.row_bytes != row_bytes) continue;
+    add_compress_entries(b, total, cd.nw, x.n_rows, x.src, x.slots, x.flags, x.row_bits,
+                         is_host_memory(x.slots) ? 0u : 1u, flush);
+  }
+  if (b.count) flush(b, total);
 }
 
 }  // namespace
@@ -4042,24 +4097,37 @@ int ibp_compress_batch(const ibp_metadata* md, const ibp_compress_tensor* tensor
   for (uint64_t t = 0; t < n_tensors; ++t) {
     const ibp_compress_tensor& x = tensors[t];
     if (x.n_rows == 0) continue;
-    const uint64_t n = x.row_bytes / 4;
-    if (md->width_bits != 32 || !cwg_row((uint32_t)n)) {  // tensor by tensor
+    const uint64_t n = x.row_bytes / 4;  // words of a row
+    if (md->width_bits == 64 || !cwg_row((uint32_t)n)) {  // tensor by tensor
       enqueue_compress(md, x.n_rows, x.row_bytes, x.src, x.slots, x.flags, x.row_bits, st);
       continue;
     }
-    // the first tensor of each row length of the weight-row kernel gathers
+    // the first tensor of each row length of the weight-row kernels gathers
     // every tensor of that length into shared launches
     bool& d = done[n == 2048 ? 0 : n == 4096 ? 1 : n == 7168 ? 2 : 3];
     if (d) continue;
     d = true;
-    const Codec cd = make_codec(md, x.row_bytes);
-    switch (cd.runs.n) {
-      case 0: compress_wg_batch<0>(cd, tensors, n_tensors, x.row_bytes, st); break;
-      case 1: compress_wg_batch<1>(cd, tensors, n_tensors, x.row_bytes, st); break;
-      case 2: compress_wg_batch<2>(cd, tensors, n_tensors, x.row_bytes, st); break;
-      case 3: compress_wg_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
-      case 4: compress_wg_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
-      default: compress_wg_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+    if (md->width_bits == 32) {
+      const Codec cd = make_codec(md, x.row_bytes);
+      switch (cd.runs.n) {
+        case 0: compress_wg_batch<0>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 1: compress_wg_batch<1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 2: compress_wg_batch<2>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 3: compress_wg_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 4: compress_wg_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        default: compress_wg_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      }
+    } else {
+      const WideCodec<uint16_t> cd = make_wide_codec<uint16_t>(md, x.row_bytes);
+      switch (cd.nruns) {
+        case 0: compress_pair_batch<0>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 1: compress_pair_batch<1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 2: compress_pair_batch<2>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 3: compress_pair_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 4: compress_pair_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 5: compress_pair_batch<5>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        default: compress_pair_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      }
     }
   }
   hipError_t e = hipGetLastError();
