@@ -4575,16 +4575,19 @@ static int decode_positional(const void* table, uint64_t n_rows, uint64_t row_by
       const int64_t* id_p = gather ? ids + off : nullptr;
       uint32_t* out_p = (uint32_t*)dst + off * n;
       // workgroups of 4 waves (8 for 4 KiB rows, whose 32 KiB table is then
-      // shared by more waves); as many as stay resident
+      // shared by more waves); per CU, measured: 6 for rows of 128 and 256
+      // blocks (against 4, 5, 7, 8 and 12), 3 for 512 (against 2, 4, 5, 8),
+      // 2 for 1024 (against 1, 3, 4): fewer workgroups stage the position
+      // table fewer times
 #define IBP_PP(G, NCH, WPB, PER_CU)                                                             \
   hipLaunchKernelGGL((decode_pos_pipe_kernel<G, NCH, WPB>), dim3(row_pipe_grid(cnt, WPB, PER_CU)), \
                      dim3(WPB * kWave), 0, st, (const PosEntry*)table, sl, fl, id_p,           \
                      gather ? n_rows : (uint64_t)cnt, cnt, out_p)
 #define IBP_PP_N(G)                                         \
   switch (n) {                                              \
-    case 128: IBP_PP(G, 2, 4, 8); break;                    \
-    case 256: IBP_PP(G, 4, 4, 8); break;                    \
-    case 512: IBP_PP(G, 8, 4, 5); break;                    \
+    case 128: IBP_PP(G, 2, 4, 6); break;                    \
+    case 256: IBP_PP(G, 4, 4, 6); break;                    \
+    case 512: IBP_PP(G, 8, 4, 3); break;                    \
     default: IBP_PP(G, 16, 8, 2); break;                    \
   }
       if (gather) { IBP_PP_N(true); } else { IBP_PP_N(false); }
