@@ -3007,20 +3007,40 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
     }
     return (n + 32u * n - wave_sum(s_lane) + 31u) >> 5;
   };
+  // Two chunks share one wave scan: chunk c's stripped p in the low half of
+  // a word, chunk c + 1's in the high half (a chunk's sum is at most 64 * 32,
+  // so neither half carries into the other).  The pair's position entries
+  // are read before the scan (the barrier keeps them there) and both stream
+  // words before either deposit, so the LDS reads overlap; the deposit is
+  // computed for every lane and then selected.
   auto decode = [&](uint32_t win, uint32_t* x) {
     uint32_t u = n;
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
-      const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
-      const bool stripped =
-          __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
-      const uint32_t v = stripped ? p_of(c) : 0u;
+    for (int c = 0; c < NCH; c += 2) {
+      const PosEntry e[2] = {entry(c * kWave + lane), entry((c + 1) * kWave + lane)};
+      __builtin_amdgcn_sched_barrier(0);
+      bool st[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * (c + j));
+        const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * (c + j) + 1);
+        st[j] = __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+      }
+      const uint32_t v = (st[0] ? p_of(c) : 0u) | ((st[1] ? p_of(c + 1) : 0u) << 16);
       const uint32_t incl = wave_scan_incl(v);
-      const uint32_t rel = (u + l32) - (incl - v);
-      const uint32_t w = lds_bits(lds, rel);
-      x[c] = stripped ? deposit_pos(w, entry(c * kWave + lane)) : w;
-      u += 32u * kWave - __builtin_amdgcn_readlane(incl, kWave - 1);
+      const uint32_t excl = incl - v;  // per half: no borrow, incl >= v in each
+      const uint32_t tot = __builtin_amdgcn_readlane(incl, kWave - 1);
+      uint32_t w[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        w[j] = lds_bits(lds, (u + l32) - ((excl >> (16 * j)) & 0xffffu));
+        u += 32u * kWave - ((tot >> (16 * j)) & 0xffffu);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t d = deposit_pos(w[j], e[j]);
+        x[c + j] = st[j] ? d : w[j];
+      }
     }
   };
   row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
