@@ -587,13 +587,14 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
         out_sb.append(images[ti][3] if ids is None else
                       torch.from_numpy(sb[ids].astype(np.int32)).to(dev))
 
-    def make_copy(gi, oi, cap, pack):
+    def make_copy(gi, oi, cap, pack, nt):
         parts = []
         for j, k in enumerate(groups[gi]):
             slots = images[steps[k][0]][0]
             n, S = group_shapes[gi][j]
             parts.append((slots, out_sb[k], ids_g[k], out_sets[oi][j].view(-1)[:n * S].view(n, S)))
-        return ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack)
+        return ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack,
+                                            stream_loads=nt)
 
     def launcher(make):
         # every (group, output set) pair the warm-up, the timed region and
@@ -646,25 +647,28 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
             raise SystemExit(f"bench: decompressed rows of {wl.name} differ from the source")
 
     # the gather-copy ceiling on the same ids, images and output rotation:
-    # the best of a few grid sizes (the copy's waves loop over their work)
+    # the best of a few grid sizes (the copy's waves loop over their work),
+    # task shapes and load policies
     ceil_rec = None
     if arena is None:
         best = None
         short = min(s[1] for s in shapes) < 4096
         for pack in ((False, True) if short else (False,)):
-            for per_cu in CEILING_GRIDS:
-                cap = per_cu * cu_count()
-                copy = launcher(lambda gi, oi, c=cap, p=pack: make_copy(gi, oi, c, p))
-                for k in range(W):
-                    copy(k)
-                torch.cuda.synchronize()
-                _, c_region = time_region(stream, copy, K)
-                if best is None or c_region < best[0]:
-                    best = (c_region, per_cu, pack)
-                del copy
+            for nt in (False, True):
+                for per_cu in CEILING_GRIDS:
+                    cap = per_cu * cu_count()
+                    copy = launcher(lambda gi, oi, c=cap, p=pack, t=nt: make_copy(gi, oi, c, p, t))
+                    for k in range(W):
+                        copy(k)
+                    torch.cuda.synchronize()
+                    _, c_region = time_region(stream, copy, K)
+                    if best is None or c_region < best[0]:
+                        best = (c_region, per_cu, pack, nt)
+                    del copy
         c_s = best[0] / K
         ceil_rec = {"kernel": "gather_copy_kernel", "workgroups_per_cu": best[1],
                     "rows_per_task": "4 KiB of rows" if best[2] else "one",
+                    "loads": "non-temporal" if best[3] else "default",
                     "mean_launch_us": round(c_s * 1e6, 3),
                     "achieved": round(a_bytes / c_s / 1e9, 2),
                     "frac_of_peak": round(a_bytes / c_s / 1e9 / HBM_PEAK_GBPS, 4),

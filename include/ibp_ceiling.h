@@ -29,6 +29,10 @@ extern "C" {
 /* Largest number of tensors one ibp_ceiling_gather_copy call takes. */
 #define IBP_CEILING_MAX_TENSORS 16u
 
+/* Flags of ibp_ceiling_gather_copy. */
+#define IBP_CEILING_PACK 1u         /* several short rows per 4 KiB task */
+#define IBP_CEILING_STREAM_LOADS 2u /* non-temporal slot loads */
+
 /*
  * One tensor of a gather copy.
  *   n_rows     rows of the source table (slots)
@@ -63,17 +67,21 @@ typedef struct ibp_copy_tensor {
  * Enqueues one launch on `stream` (a hipStream_t; NULL = the null stream)
  * that copies every tensor as described above, n_tensors <=
  * IBP_CEILING_MAX_TENSORS.  A task is 4 KiB of output: a row or a 4 KiB
- * chunk of a longer row; with pack != 0, rows shorter than 4 KiB whose size
- * is a power of two times 16 bytes go 4 KiB / S to a task instead.
+ * chunk of a longer row; with IBP_CEILING_PACK in flags, rows shorter than
+ * 4 KiB whose size is a power of two times 16 bytes go 4 KiB / S to a task
+ * instead.  With IBP_CEILING_STREAM_LOADS the slot loads are non-temporal
+ * (the cache policy libibp's decoders give the image reads), otherwise they
+ * take the default policy.
  * max_workgroups caps the grid (workgroups of 256 threads; each wave loops
  * over its share of the tasks), 0 = one wave per task.  The result is the
  * same either way.  Asynchronous; allocates nothing.  Returns 0, or -1 (null
  * or misaligned pointer, row_bytes not a multiple of 16 or above 2^26,
- * n_out > n_rows without ids, too many tensors; nothing enqueued) or -5
+ * n_out > n_rows without ids, too many tensors, an unknown flag; nothing
+ * enqueued) or -5
  * (launch failure).  Tensors with n_out == 0 are skipped.
  */
 int ibp_ceiling_gather_copy(const ibp_copy_tensor *tensors, uint64_t n_tensors,
-                            uint32_t max_workgroups, uint32_t pack, void *stream);
+                            uint32_t max_workgroups, uint32_t flags, void *stream);
 
 #ifdef __cplusplus
 }

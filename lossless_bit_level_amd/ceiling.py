@@ -12,6 +12,8 @@ from . import ibp
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libibp_ceiling.so")
 IBP_CEILING_MAX_TENSORS = 16
+IBP_CEILING_PACK = 1
+IBP_CEILING_STREAM_LOADS = 2
 
 
 class ibp_copy_tensor(ctypes.Structure):
@@ -41,13 +43,14 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-def gather_copy_launcher(parts, max_workgroups: int = 0, pack: bool = False, stream=None):
+def gather_copy_launcher(parts, max_workgroups: int = 0, pack: bool = False,
+                         stream_loads: bool = False, stream=None):
     """parts: list of (slots, src_bytes, ids or None, out) with slots a
     [n_rows, S] uint8 tensor (GPU or pinned host), src_bytes an int32 GPU
     tensor of the n_out stored lengths of the output rows' source rows, ids
     an int64 GPU tensor and out a GPU tensor of n_out x S bytes;
     max_workgroups caps the grid (0: none); pack puts several short rows in
-    one 4 KiB task.
+    one 4 KiB task; stream_loads makes the slot loads non-temporal.
     Returns a no-argument callable that enqueues the copy (one launch) on
     the current stream."""
     if not 0 < len(parts) <= IBP_CEILING_MAX_TENSORS:
@@ -69,7 +72,8 @@ def gather_copy_launcher(parts, max_workgroups: int = 0, pack: bool = False, str
     s = ctypes.c_void_p((torch.cuda.current_stream() if stream is None else stream).cuda_stream)
     n = ctypes.c_uint64(len(parts))
     cap = ctypes.c_uint32(max_workgroups)
-    pk = ctypes.c_uint32(1 if pack else 0)
+    pk = ctypes.c_uint32((IBP_CEILING_PACK if pack else 0) |
+                         (IBP_CEILING_STREAM_LOADS if stream_loads else 0))
 
     def launch():
         rc = fn(arr, n, cap, pk, s)

@@ -14,8 +14,9 @@
 // stores.  Packed tasks (rows shorter than 4 KiB whose 16-byte unit count is
 // a power of two) hold 4 KiB / S rows, each lane loading the id and byte
 // count of its own row.  Waves loop over tasks when the caller caps the
-// grid (the benchmark takes the best of a few grids and both task shapes,
-// as a floor should).
+// grid.  The slot loads take the default cache policy or the non-temporal
+// one (the benchmark takes the best of a few grids, both task shapes and
+// both load policies, as a floor should).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -55,6 +56,14 @@ struct CopyBatch {
   CopyTensor t[IBP_CEILING_MAX_TENSORS];
 };
 
+// a 16-byte unit of a slot, with the load policy the launch chose
+template <bool NT>
+__device__ __forceinline__ u32x4 load_unit(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void gather_copy_kernel(CopyBatch b) {
   const uint32_t lane = threadIdx.x % kWave;
   const uint64_t nwaves = (uint64_t)gridDim.x * kWaves;
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void gather_copy_kernel(CopyBatch b) {
         const bool in = id[j] >= 0 && (uint64_t)id[j] < t.n_rows;
         v[j] = u32x4{0u, 0u, 0u, 0u};
         if (in && col[j] < std::min<uint32_t>((lim[j] + 15u) / 16u, t.units))
-          v[j] = t.src[(uint64_t)id[j] * t.units + col[j]];
+          v[j] = load_unit<NT>(t.src + (uint64_t)id[j] * t.units + col[j]);
       }
 #pragma unroll
       for (int j = 0; j < kPerLane; ++j)
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void gather_copy_kernel(CopyBatch b) {
     for (int j = 0; j < kPerLane; ++j) {
       const uint32_t col = chunk * kTaskUnits + (uint32_t)j * kWave + lane;
       v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (col < limit) v[j] = s[col];
+      if (col < limit) v[j] = load_unit<NT>(s + col);
     }
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) {
@@ -123,8 +132,10 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 }  // namespace
 
 extern "C" int ibp_ceiling_gather_copy(const ibp_copy_tensor* tensors, uint64_t n_tensors,
-                                       uint32_t max_workgroups, uint32_t pack, void* stream) {
+                                       uint32_t max_workgroups, uint32_t flags, void* stream) {
   if (n_tensors > IBP_CEILING_MAX_TENSORS || (n_tensors && !tensors)) return -1;
+  if (flags & ~(IBP_CEILING_PACK | IBP_CEILING_STREAM_LOADS)) return -1;
+  const bool pack = flags & IBP_CEILING_PACK;
   CopyBatch b{};
   uint64_t tasks = 0;
   for (uint64_t i = 0; i < n_tensors; ++i) {
@@ -161,6 +172,11 @@ extern "C" int ibp_ceiling_gather_copy(const ibp_copy_tensor* tensors, uint64_t 
   const uint64_t wgs = (tasks + kWaves - 1) / kWaves;
   const uint32_t grid = (uint32_t)std::min<uint64_t>(
       wgs, max_workgroups ? std::min<uint32_t>(max_workgroups, 1u << 20) : 1u << 20);
-  hipLaunchKernelGGL(gather_copy_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream, b);
+  if (flags & IBP_CEILING_STREAM_LOADS)
+    hipLaunchKernelGGL(gather_copy_kernel<true>, dim3(grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, b);
+  else
+    hipLaunchKernelGGL(gather_copy_kernel<false>, dim3(grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, b);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -164,6 +164,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
                                            0x00020000);
 }
 
+// Cache policy (aux operand) of a buffer load of the part of a stream past
+// its first 128 bytes: non-temporal, as stage_window's loads.
+constexpr int kLoadStream = 2;
+
 // Words to write for a compressed row whose stream has `words` words, at slot
 // address row (slots of n words): with pad (device memory), on to the next
 // 64-byte boundary of the address, at most n.  A write that ends inside a
@@ -185,8 +189,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // U is u32x4, words when U is uint32_t).  All loads of a batch of MAXV units
 // per lane are issued before the first LDS write, so that a window costs one
 // memory latency per batch, not one per 64 units (a plain strided loop waits
-// for each load before its LDS write).  cnt is wave-uniform.
-template <int MAXV, typename U>
+// for each load before its LDS write).  With NT the loads are non-temporal.
+// Measured on MI355X: for the bulk of a stream, past the 128-byte window a
+// row's first load takes, that is faster (a weight layer 1% and KV pages
+// 5.5% faster; per-position KV pages 5.5% with the row pipeline's loads of
+// the same part); for the windows themselves, short scattered reads, and
+// for whole short slots read again and again (Zipf ids) it is much slower,
+// so those keep the default policy, as does the cache arena, whose rows are
+// read again.  cnt is wave-uniform.
+template <int MAXV, bool NT = false, typename U>
 __device__ __forceinline__ void stage_window(const U* __restrict__ g, U* l, uint32_t cnt,
                                              uint32_t lane) {
   for (uint32_t j0 = 0; j0 < cnt; j0 += MAXV * kWave) {
@@ -194,7 +205,10 @@ __device__ __forceinline__ void stage_window(const U* __restrict__ g, U* l, uint
 #pragma unroll
     for (int c = 0; c < MAXV; ++c) {
       const uint32_t j = j0 + c * kWave + lane;
-      v[c] = j < cnt ? g[j] : U{};
+      if constexpr (NT)
+        v[c] = j < cnt ? __builtin_nontemporal_load(g + j) : U{};
+      else
+        v[c] = j < cnt ? g[j] : U{};
     }
 #pragma unroll
     for (int c = 0; c < MAXV; ++c) {
@@ -1024,11 +1038,12 @@ __device__ __forceinline__ void decode_segment_task(
   uint32_t base;
   if (vec) {
     base = wa & ~3u;
-    stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
-                    (wb - base + 3u) / 4u, lane);
+    stage_window<5, MODE != kModeCached>(reinterpret_cast<const u32x4*>(src + base),
+                                         reinterpret_cast<u32x4*>(lds), (wb - base + 3u) / 4u,
+                                         lane);
   } else {
     base = wa;
-    stage_window<4>(src + wa, lds, wb - wa, lane);
+    stage_window<4, MODE != kModeCached>(src + wa, lds, wb - wa, lane);
   }
   wave_lds_sync();
 
@@ -1215,11 +1230,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_rows_kernel(
         // one batch: n <= 64 * NCH words (<= 1024 for NCH == 0) past the window
         constexpr int kV = NCH >= 8 ? NCH / 4 : (NCH > 0 ? 1 : 4);
         if (vec)
-          stage_window<kV>(reinterpret_cast<const u32x4*>(src) + spec / 4,
-                           reinterpret_cast<u32x4*>(lds) + spec / 4, (wb + 3u) / 4u - spec / 4,
-                           lane);
+          stage_window<kV, MODE != kModeCached>(
+              reinterpret_cast<const u32x4*>(src) + spec / 4,
+              reinterpret_cast<u32x4*>(lds) + spec / 4, (wb + 3u) / 4u - spec / 4, lane);
         else
-          stage_window<4>(src + spec, lds + spec, wb - spec, lane);
+          stage_window<4, MODE != kModeCached>(src + spec, lds + spec, wb - spec, lane);
       }
       wave_lds_sync();
     }
@@ -1412,7 +1427,8 @@ __device__ __forceinline__ void run_row_pipeline(
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, ((words + 3u) & ~3u) * 4u);
 #pragma unroll
       for (int c = 0; c < RV; ++c)
-        rr[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0, 0);
+        rr[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0,
+                                                      kLoadStream);
     };
 
     // prologue: windows of rows 0 and 1, the stream of row 0
@@ -2208,10 +2224,11 @@ __device__ __forceinline__ void decode_wide_task(
   uint32_t base = wa;
   if (vec) {  // 16-byte loads from the 16-byte unit holding word wa
     base = wa & ~3u;
-    stage_window<5>(reinterpret_cast<const u32x4*>(src + base), reinterpret_cast<u32x4*>(lds),
-                    (wb - base + 3u) / 4u, lane);
+    stage_window<5, MODE != kModeCached>(reinterpret_cast<const u32x4*>(src + base),
+                                         reinterpret_cast<u32x4*>(lds), (wb - base + 3u) / 4u,
+                                         lane);
   } else {
-    stage_window<4>(src + wa, lds, wb - wa, lane);
+    stage_window<4, MODE != kModeCached>(src + wa, lds, wb - wa, lane);
   }
   wave_lds_sync();
   uint32_t u = a - 32u * base;
@@ -2666,10 +2683,10 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
       uint32_t base = wa;
       if (vec) {
         base = wa & ~3u;
-        stage_window<5>(reinterpret_cast<const u32x4*>(src + base),
-                        reinterpret_cast<u32x4*>(lds), (wb - base + 3u) / 4u, lane);
+        stage_window<5, true>(reinterpret_cast<const u32x4*>(src + base),
+                              reinterpret_cast<u32x4*>(lds), (wb - base + 3u) / 4u, lane);
       } else {
-        stage_window<4>(src + wa, lds, wb - wa, lane);
+        stage_window<4, true>(src + wa, lds, wb - wa, lane);
       }
       wave_lds_sync();
       uint32_t u = a - 32u * base;

@@ -70,6 +70,7 @@ def test_ceiling_library_exports_and_validation():
                 T(4, 4096, fake, fake, fake + 4, 4, fake)]:  # misaligned ids
         assert f((T * 1)(bad), 1, 0, 0, None) == -1
     assert f((T * 17)(), 17, 0, 0, None) == -1
+    assert f((T * 1)(T(4, 4096, fake, fake, None, 4, fake)), 1, 0, 4, None) == -1  # unknown flag
 
 
 def test_flag_words_and_status_strings(ibp):

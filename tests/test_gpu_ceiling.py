@@ -43,13 +43,14 @@ def case(rng, n_rows, S, n_ids):
     return table, src_bytes, ids
 
 
-@pytest.mark.parametrize("pack", [False, True])
+@pytest.mark.parametrize("pack,stream_loads", [(False, False), (True, False), (False, True),
+                                               (True, True)])
 @pytest.mark.parametrize("cap", [0, 1, 7])
 @pytest.mark.parametrize("S,n_rows,n_ids", [(512, 3000, 5000), (1024, 700, 4097),
                                             (2048, 513, 1000), (4096, 300, 999),
                                             (16, 100, 77), (8192, 65, None),
                                             (28672, 33, None), (1040, 40, 90)])
-def test_gather_copy_single(ceiling, S, n_rows, n_ids, cap, pack):
+def test_gather_copy_single(ceiling, S, n_rows, n_ids, cap, pack, stream_loads):
     rng = np.random.default_rng(S + n_rows)
     table, sb, ids = case(rng, n_rows, S, n_ids)
     tg = torch.from_numpy(table).cuda()
@@ -57,7 +58,8 @@ def test_gather_copy_single(ceiling, S, n_rows, n_ids, cap, pack):
     idg = torch.from_numpy(ids).cuda() if ids is not None else None
     n_out = len(ids) if ids is not None else n_rows
     out = torch.full((n_out, S), 0xAB, dtype=torch.uint8, device="cuda")
-    ceiling.gather_copy_launcher([(tg, sbg, idg, out)], max_workgroups=cap, pack=pack)()
+    ceiling.gather_copy_launcher([(tg, sbg, idg, out)], max_workgroups=cap, pack=pack,
+                                 stream_loads=stream_loads)()
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy(), expected(table, sb, ids))
 
@@ -75,10 +77,10 @@ def test_gather_copy_batch_and_host_source(ceiling):
         out = torch.full((n_out, S), 0xCD, dtype=torch.uint8, device="cuda")
         parts.append((tg, torch.from_numpy(sb).cuda(), idg, out))
         want.append(expected(table, sb, ids))
-    for cap, pack in ((0, False), (3, False), (0, True), (5, True)):
+    for cap, pack, nt in ((0, False, False), (3, False, True), (0, True, True), (5, True, False)):
         for _, _, _, out in parts:
             out.fill_(0xCD)
-        ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack)()
+        ceiling.gather_copy_launcher(parts, max_workgroups=cap, pack=pack, stream_loads=nt)()
         torch.cuda.synchronize()
         for (_, _, _, out), w in zip(parts, want):
             assert np.array_equal(out.cpu().numpy(), w)
