@@ -24,7 +24,10 @@ Prints one JSON line:
   roofline     algorithmic bytes of one launch / its mean duration (HIP
                events on the launch stream) against the 8 TB/s HBM peak;
                "ceiling": the gather-copy floor of the same transfer, timed
-               the same way on the same ids, images and outputs
+               the same way on the same ids, images and outputs;
+               "device_copy" (headline): a plain contiguous 1 GiB device-to-
+               device copy, read + written bytes per second, the practical
+               rate of a streaming read/write mix on the GPU at hand
   cpu_baseline the CPU oracle on the host cores: full decompress and
                compress of one layer on every thread of the box's share,
                plus single-thread figures on the tiny table and a 256 MiB
@@ -263,6 +266,55 @@ def link_ceiling(dev, stream):
     rate = 3 * (1 << 30) / (e0.elapsed_time(e1) / 1e3) / 1e9
     del h, d
     return rate
+
+
+def device_copy_reference(dev, stream, reps: int = 5):
+    """Read + write bytes per second of a plain contiguous 1 GiB device-to-
+    device copy, the practical rate of a streaming read/write mix on this
+    GPU: torch's copy_ (hipMemcpyAsync) and the gather-copy kernel of
+    libibp_ceiling on the same buffers as 4 KiB rows in order (no ids; the
+    best of a few grids and both load policies).  Context for the headline's
+    roofline fraction, which is against the nominal 8 TB/s."""
+    import torch
+    from lossless_bit_level_amd import ceiling
+    n = 1 << 30
+    a = torch.randint(0, 255, (n,), dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    t_memcpy = timed(lambda: b.copy_(a))
+    rows = a.view(n // 4096, 4096)
+    lens = torch.full((n // 4096,), 4096, dtype=torch.int32, device=dev)
+    best = None
+    for per_cu in (8, 16, 64):
+        for nt in (False, True):
+            fn = ceiling.gather_copy_launcher([(rows, lens, None, b)],
+                                              max_workgroups=per_cu * cu_count(),
+                                              stream_loads=nt)
+            t = timed(fn)
+            if best is None or t < best[0]:
+                best = (t, per_cu, nt)
+    if not torch.equal(a, b):
+        raise SystemExit("bench: the reference copy differs from its source")
+    del a, b, rows, lens
+    r_memcpy = 2 * n / t_memcpy / 1e9
+    r_kernel = 2 * n / best[0] / 1e9
+    return {"what": "contiguous 1 GiB device-to-device copy, read + written bytes per second",
+            "hipMemcpy_GB_per_s": round(r_memcpy, 1),
+            "copy_kernel_GB_per_s": round(r_kernel, 1),
+            "copy_kernel": {"kernel": "gather_copy_kernel", "workgroups_per_cu": best[1],
+                            "loads": "non-temporal" if best[2] else "default"},
+            "best_frac_of_peak": round(max(r_memcpy, r_kernel) / HBM_PEAK_GBPS, 4)}
 
 
 # ------------------------------------------------------------- measure ----
@@ -996,6 +1048,12 @@ def main():
     }
     if "cache" in head:
         res["cache"] = head["cache"]
+    if args.source == "device":
+        ref = device_copy_reference(dev, stream)
+        ref["decode_over_best_copy"] = round(
+            head["roofline"]["achieved"] /
+            max(ref["hipMemcpy_GB_per_s"], ref["copy_kernel_GB_per_s"]), 4)
+        res["roofline"]["device_copy"] = ref
     if link_rate is not None:
         res["host_link_memcpy_GB_per_s"] = round(link_rate, 2)
 
