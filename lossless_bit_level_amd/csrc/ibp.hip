@@ -1423,12 +1423,17 @@ __device__ __forceinline__ void run_row_pipeline(
       if (!fl_of(j)) return n;
       return min(stream_words(win), n);
     };
+    // the rest of a 4 KiB row's stream loads non-temporal (KV pages); rows of
+    // 512 B to 2 KiB keep the default policy: gathers of them under Zipf ids
+    // read hot rows again and again, and non-temporal loads of those made
+    // the 64-bit-block dense feature and embedding gathers 1.6x slower
+    constexpr int kRestPolicy = NCH >= 16 ? kLoadStream : 0;
     auto load_rest = [&](const uint32_t* src, uint32_t words, u32x4* rr) {
       const __amdgpu_buffer_rsrc_t rs = row_rsrc(src, ((words + 3u) & ~3u) * 4u);
 #pragma unroll
       for (int c = 0; c < RV; ++c)
         rr[c] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kWin / 4 + c * kWave + lane) * 16u, 0,
-                                                      kLoadStream);
+                                                      kRestPolicy);
     };
 
     // prologue: windows of rows 0 and 1, the stream of row 0
