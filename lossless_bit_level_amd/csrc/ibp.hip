@@ -2256,23 +2256,33 @@ __device__ __forceinline__ void decode_wide_task(
     // source bit), so a raw half or the bits past a payload cannot leak.
     const uint32_t bv2 = (uint32_t)cd.bitval * 0x10001u;
     const uint32_t sh = 2u * (lane & 15u);
+    const uint32_t sh1 = sh + 1u;
     const uint32_t hsel = 4u * (lane >> 4);
-    const uint32_t l32 = 32u * lane;
+    // the lane's bit cursor, u plus 32 bits per lane below it, kept in a
+    // vector register and advanced once per step
+    uint32_t ul = u + 32u * lane;
     uint32_t* out_w = reinterpret_cast<uint32_t*>(out);
     auto pair = [&](uint32_t k0, bool ragged) {
       // the lane's header word, q + l/16, from the lane of hw holding it
       const uint32_t q = (k0 - lo) / 32;
       const uint32_t hs = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(4u * q + hsel), (int)hw);
-      const uint32_t b2 = __builtin_amdgcn_ubfe(hs, sh, 2);
-      const bool s0 = (b2 & 1u) != 0u, s1 = b2 > 1u;
+      // all ones / zero: the first / second block of the pair stripped
+      const uint32_t m0 = (uint32_t)__builtin_amdgcn_sbfe((int)hs, sh, 1);
+      const uint32_t m1 = (uint32_t)__builtin_amdgcn_sbfe((int)hs, sh1, 1);
+      const bool s0 = m0 != 0u, s1 = m1 != 0u;
       const unsigned long long e = __ballot(s0), o = __ballot(s1);
       const bool valid = !ragged || k0 + 2u * lane < hi;
       const uint32_t below = bits_below_lane_acc((uint32_t)o, (uint32_t)(o >> 32),
                                                  bits_below_lane((uint32_t)e, (uint32_t)(e >> 32)));
-      const uint32_t rel = valid ? (uint32_t)__mul24(negp, (int)below) + (u + l32) : 0u;
-      const uint32_t v = lds_bits(lds, rel);
-      const uint32_t l0 = s0 ? 16u - cd.p : 16u;
-      const uint32_t y = (v & 0xFFFFu) | ((v >> l0) << 16);
+      const uint32_t rel = valid ? (uint32_t)__mul24(negp, (int)below) + ul : 0u;
+      // the window word index as an opaque value: its LDS address is then one
+      // shift-add on it, not a shift, an and and an add on rel
+      uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
+      asm volatile("" : "+v"(wi));
+      const uint32_t v = __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], rel & 31u);
+      // low half: the first payload; high half: the second one, which starts
+      // 16 - p bits on when the first block is stripped, else 16
+      const uint32_t y = select_bits(0xFFFFu, v, v << (cd.p & m0));
       uint32_t dep = bv2;
       if constexpr (NR >= 0) {
 #pragma unroll
@@ -2281,9 +2291,13 @@ __device__ __forceinline__ void decode_wide_task(
         for (uint32_t j = 0; j < cd.nruns; ++j)
           dep |= (y << cd.shift[j]) & ((uint32_t)cd.place[j] * 0x10001u);
       }
-      const uint32_t sel = (s0 ? 0x0000FFFFu : 0u) | (s1 ? 0xFFFF0000u : 0u);
+      const uint32_t sel = select_bits(0xFFFFu, m0, m1);
       if (valid) __builtin_nontemporal_store(select_bits(sel, dep, y), out_w + k0 / 2 + lane);
-      u += 16u * 2u * kWave - cd.p * (uint32_t)(__popcll(e) + __popcll(o));
+      // the step's advance is scalar work; kept opaque so that it is one
+      // vector add, not a subtract and an add of a constant
+      uint32_t adv = 16u * 2u * kWave - cd.p * (uint32_t)(__popcll(e) + __popcll(o));
+      asm volatile("" : "+s"(adv));
+      ul += adv;
     };
     if (hi - lo == kFull && seg == kFull) {
 #pragma unroll
