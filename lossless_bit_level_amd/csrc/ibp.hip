@@ -1053,13 +1053,28 @@ __device__ __forceinline__ void decode_segment_task(
   uint32_t u = n + 32u * lo - cd.p * carry - 32u * base;
   const uint32_t l32 = lane * 32u;
   const int negp = -(int)cd.p;
+  // the lane's bit cursor (u plus 32 bits per lane below it) in a vector
+  // register, advanced by one add per chunk
+  uint32_t ul = u + l32;
   auto chunk = [&](uint32_t k0) {  // a whole 64-block chunk
     const uint32_t q = (k0 - lo) / 32;
     const uint32_t h_lo = __builtin_amdgcn_readlane(hw, q);
     const uint32_t h_hi = __builtin_amdgcn_readlane(hw, q + 1);
-    const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
-    __builtin_nontemporal_store(decode_block<NR>(lds, rel, h_lo, h_hi, cd), out + k0 + lane);
-    u += 32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+    const uint32_t rel = (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + ul;
+    // the window word index as an opaque value: its LDS address is one
+    // shift-add on it, not a shift, an and and an add on rel
+    uint32_t wi = __builtin_amdgcn_ubfe(rel, 5, 27);
+    asm volatile("" : "+v"(wi));
+    const uint32_t v = __builtin_amdgcn_alignbit(lds[wi + 1], lds[wi], rel & 31u);
+    const bool stripped =
+        __builtin_amdgcn_inverse_ballot_w64(((unsigned long long)h_hi << 32) | h_lo);
+    const uint32_t x = stripped ? deposit_kept<NR>(v, cd.runs, cd.bitval) : v;
+    __builtin_nontemporal_store(x, out + k0 + lane);
+    uint32_t adv =
+        32u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
+    asm volatile("" : "+s"(adv));
+    ul += adv;
+    u += adv;
   };
   const uint32_t full_hi = lo + ((hi - lo) & ~(uint32_t)(kWave - 1));
   uint32_t k0 = lo;
