@@ -677,8 +677,14 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, Comp
   unsigned long long* flags = ct.flags;
   uint32_t* row_bits = ct.row_bits;
   const uint32_t wg = blockIdx.x - (t ? batch.wg_end[t - 1] : 0u);  // within the tensor
-  __shared__ uint32_t buf[n + 4];
-  __shared__ uint32_t wtot[WPB];  // the waves' match totals
+  // the row's stream and the waves' match totals; with two of each (rows of
+  // 8 KiB, whose two streams fit beside the other resident workgroups'),
+  // consecutive rows alternate between them and a row needs no barrier
+  // after its stores: the next use of a buffer is two rows on, past both
+  // barriers of the row between
+  constexpr int NB = CPW == 8 ? 2 : 1;
+  __shared__ uint32_t buf_all[NB][n + 4];
+  __shared__ uint32_t wtot_all[NB][WPB];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   const uint32_t c0 = wave * CPW;  // the wave's first chunk
@@ -712,6 +718,8 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, Comp
   unsigned long long fl = 0;  // bit j: row r0 + j is stored compressed
   for (uint64_t row = r0; row < r1; ++row) {
     uint32_t* s_row = slots + row * n;
+    uint32_t* buf = buf_all[NB == 2 ? (uint32_t)(row - r0) & 1u : 0u];
+    uint32_t* wtot = wtot_all[NB == 2 ? (uint32_t)(row - r0) & 1u : 0u];
     uint32_t y[CPW];  // the next row, in flight
     load(y, row + 1);
     uint32_t mw = 0;
@@ -815,7 +823,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, Comp
     for (int c = 0; c < CPW; ++c) x[c] = y[c];
     // the LDS stream is reused only by a next row; after the last one the
     // workgroup ends without waiting for its stores (a barrier would)
-    if (row + 1 < r1) __syncthreads();
+    if (NB == 1 && row + 1 < r1) __syncthreads();
   }
   if (wave == 0 && r0 < r1) {
     const uint32_t k = (uint32_t)(r1 - r0);
@@ -3440,7 +3448,7 @@ template <int NR>
 void launch_compress_wg(const Codec& cd, CompressBatch& b, uint64_t total_rows, hipStream_t st) {
 #define IBP_CWG(CPW, WPB, BYTES)                                                           \
   {                                                                                         \
-    constexpr uint32_t lds = (CPW * kWave * WPB + 4u + WPB) * 4u;                           \
+    constexpr uint32_t lds = (CPW == 8 ? 2u : 1u) * (CPW * kWave * WPB + 4u + WPB) * 4u;    \
     constexpr uint32_t per_cu = std::min(32u / WPB, (160u * 1024u) / lds);                  \
     const uint32_t per_wg =                                                                 \
         cwg_rows_per_wg(total_rows, workgroups_per_device(per_cu), BYTES);                  \
