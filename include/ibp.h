@@ -54,6 +54,10 @@
  * synchronise.  The W = 32 decodes ask HIP (hipPointerGetAttributes) whether
  * `slots` is host memory, and then cut rows of 1024 or more blocks into
  * smaller tasks, which suits the host link; the result is the same.
+ * The same holds for ibp_compress_batch and the per-position compress and
+ * decompress calls; none of these clears memory with a memset (the flag
+ * words are written by the compression kernels), so a caller may capture
+ * them in a HIP graph and replay it.
  * ibp_build_metadata is synchronous.  The library keeps no state between
  * calls apart from the last HIP error code of the calling thread, the
  * compute-unit count of each device (read once per device, to size
