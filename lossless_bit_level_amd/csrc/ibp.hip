@@ -2184,6 +2184,158 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
   });
 }
 
+// [IBP] Compression with 64-bit blocks of the long weight rows (1024, 2048,
+// 3584 or 4096 blocks: 8, 16, 28 and 32 KiB), a workgroup of four waves per
+// row, the scheme of compress_wg_kernel: each wave holds CPW chunks of the
+// row in registers (one block per lane each), so the row is read once; the
+// chunk ballots are the header word pairs (placed in their lanes with lane
+// writes); the waves' match totals meet in LDS and give each wave its carry;
+// a payload of up to 64 bits is ORed into the workgroup's LDS stream in up to
+// three words, and the stream is written with coalesced stores (a raw row
+// straight from the registers).  A workgroup takes a contiguous range of
+// `per_wg` rows with the next row in flight and writes the range's flag bits
+// once (whole bytes when per_wg is a multiple of 8).  In place is safe as in
+// compress_wg_kernel.  One launch takes up to kCompressBatchMax tensors of
+// one row length.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+template <int NR, int CPW>
+__global__ __launch_bounds__(kBlockThreads) void compress_w64_wg_kernel(
+    WideCodec<uint64_t> cd, CompressBatch batch, uint32_t per_wg) {
+  uint32_t t = 0;
+  while (blockIdx.x >= batch.wg_end[t]) ++t;
+  const CompressTensor& ct = batch.t[t];
+  const uint64_t n_rows = ct.n_rows;
+  const uint32_t* src = ct.src;
+  uint32_t* slots = ct.slots;
+  unsigned long long* flags = ct.flags;
+  uint32_t* row_bits = ct.row_bits;
+  const uint32_t wg = blockIdx.x - (t ? batch.wg_end[t - 1] : 0u);  // within the tensor
+  constexpr uint32_t nb = (uint32_t)CPW * kWave * kWavesPerBlock;  // blocks of a row
+  constexpr uint32_t nw = 2u * nb;                                  // words of a row
+  __shared__ uint32_t buf[nw + 4];
+  __shared__ uint32_t wtot[kWavesPerBlock];  // the waves' match totals
+  const uint32_t lane = lane_id();
+  const uint32_t wave = uniform(threadIdx.x / kWave);
+  const uint32_t c0 = wave * CPW;                        // the wave's first chunk
+  const uint32_t lane_byte = (c0 * kWave + lane) * 8u;   // its first block's byte
+  const int negp = -(int)cd.p;
+  const uint64_t r0 = (uint64_t)wg * per_wg;
+  const uint64_t r1 = min(n_rows, r0 + per_wg);
+  // a row past the range loads as zeros (empty range), never out of bounds
+  auto load = [&](uint64_t (&v)[CPW], uint64_t r) {
+    const __amdgpu_buffer_rsrc_t in =
+        row_rsrc(src + (r < r1 ? r : r0) * nw, r < r1 ? nw * 4u : 0u);
+    uint32_t lb = lane_byte;  // opaque: the chunks' offsets are immediates on it
+    asm volatile("" : "+v"(lb));
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(in, lb + c * kWave * 8u, 0, 0);
+      v[c] = ((uint64_t)w.y << 32) | w.x;
+    }
+  };
+  uint64_t x[CPW];
+  load(x, r0);
+  unsigned long long fl = 0;  // bit j: row r0 + j is stored compressed
+  for (uint64_t row = r0; row < r1; ++row) {
+    uint32_t* s_row = slots + row * nw;
+    uint64_t y[CPW];  // the next row, in flight
+    load(y, row + 1);
+    // the payload part of the stream starts zeroed; header words are whole
+    for (uint32_t j = nb / 32 + threadIdx.x; j < nw + 4; j += kBlockThreads) buf[j] = 0u;
+    uint32_t mw = 0;
+    uint32_t hword = 0;  // lane 2c / 2c + 1: low / high half of chunk c's ballot
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const unsigned long long h = __ballot((x[c] & cd.mask) == cd.bitval);
+      mw += (uint32_t)__popcll(h);
+      hword = (uint32_t)lane_write((int)(uint32_t)h, 2 * c, (int)hword);
+      hword = (uint32_t)lane_write((int)(uint32_t)(h >> 32), 2 * c + 1, (int)hword);
+    }
+    if (lane < 2u * CPW) buf[2u * c0 + lane] = hword;
+    if (lane == 0) wtot[wave] = mw;
+    __syncthreads();
+    uint32_t carry = 0, m = 0;
+#pragma unroll
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      const uint32_t tw = wtot[w];
+      carry += (uint32_t)w < wave ? tw : 0u;
+      m += tw;
+    }
+    const uint32_t c_bits = nb + 64u * nb - cd.p * m;
+    const bool flag = c_bits < 64u * nb;
+    fl |= (unsigned long long)flag << (row - r0);
+    if (flag) {
+      // the lane's first payload offset less the carry: the stream's nb
+      // header bits, then 64 bits per block before it (opaque, as in
+      // compress_wg_kernel)
+      uint32_t ob = nb + 8u * lane_byte;
+      asm volatile("" : "+v"(ob));
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        const bool match = (x[c] & cd.mask) == cd.bitval;
+        const unsigned long long h = __ballot(match);
+        const uint32_t below = bits_below_lane((uint32_t)h, (uint32_t)(h >> 32));
+        uint32_t tc = (uint32_t)(c * kWave * 64) - cd.p * carry;
+        asm volatile("" : "+s"(tc));
+        const uint32_t off = (uint32_t)mul_i24((int)below, negp) + ob + tc;
+        const uint32_t sh = off & 31u, wi = off >> 5;
+        if constexpr (NR != 0) {
+          // p < 64: every block has a payload of 64 - p or 64 bits; its
+          // first two stream words get their bits with no branch
+          const uint64_t pay = match ? extract_wide<uint64_t, NR>(x[c], cd) : x[c];
+          const uint32_t len = match ? 64u - cd.p : 64u;
+          const uint64_t placed = pay << sh;
+          atomicOr(&buf[wi], (uint32_t)placed);
+          atomicOr(&buf[wi + 1u], (uint32_t)(placed >> 32));
+          if (sh + len > 64u) atomicOr(&buf[wi + 2u], (uint32_t)(pay >> (64u - sh)));
+        } else {
+          // p = 64: a stripped block has no payload
+          if (!match) {
+            const uint64_t placed = x[c] << sh;
+            atomicOr(&buf[wi], (uint32_t)placed);
+            atomicOr(&buf[wi + 1u], (uint32_t)(placed >> 32));
+            if (sh) atomicOr(&buf[wi + 2u], (uint32_t)(x[c] >> (64u - sh)));
+          }
+        }
+        carry += (uint32_t)__popcll(h);
+      }
+    }
+    __syncthreads();
+    if (!flag) {
+      const __amdgpu_buffer_rsrc_t out = row_rsrc(s_row, nw * 4u);
+      uint32_t lb = lane_byte;
+      asm volatile("" : "+v"(lb));
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)x[c], (uint32_t)(x[c] >> 32)},
+                                              out, lb + c * kWave * 8u, 0, 0);
+    } else {
+      const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, ct.pad);
+      uint32_t j0 = 0;
+      if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
+        const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
+        u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
+        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) o4[j] = b4[j];
+        j0 = nwc & ~3u;
+      }
+      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
+    }
+    if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) x[c] = y[c];
+    // the LDS stream is reused only by a next row; after the last one the
+    // workgroup ends without waiting for its stores (a barrier would)
+    if (row + 1 < r1) __syncthreads();
+  }
+  if (wave == 0 && r0 < r1) {
+    const uint32_t k = (uint32_t)(r1 - r0);
+    if (per_wg % 8u == 0)
+      put_flag_bytes(flags, r0, k, fl, n_rows, lane);
+    else if (lane == 0)
+      put_flag_bits(flags, r0, k, fl, n_rows);
+  }
+}
+
 // Blocks per decode task for W = 16 / 64: a segment's stream stays within
 // the LDS window of a 32-bit segment (seg * W / 32 <= kSegBlocks words).
 template <typename T>
@@ -3678,6 +3830,31 @@ void launch_compress_pair_wg(const WideCodec<uint16_t>& cd, CompressBatch& b, ui
 #undef IBP_PAIR_WG
 }
 
+// One launch of compress_w64_wg_kernel over the entries of `b` (64-bit blocks
+// in rows of 8, 16, 28 or 32 KiB), grid and rows per workgroup as for
+// compress_wg_kernel.
+template <int NR>
+void launch_compress_w64_wg(const WideCodec<uint64_t>& cd, CompressBatch& b,
+                            uint64_t total_rows, hipStream_t st) {
+#define IBP_W64_WG(CPW, BYTES)                                                              \
+  {                                                                                         \
+    constexpr uint32_t lds = (2u * CPW * kWave * kWavesPerBlock + 4u + kWavesPerBlock) * 4u; \
+    constexpr uint32_t per_cu = std::min(8u, (160u * 1024u) / lds);                         \
+    const uint32_t per_wg =                                                                 \
+        cwg_rows_per_wg(total_rows, workgroups_per_device(per_cu), BYTES);                  \
+    const uint32_t wgs = set_wg_ends(b, per_wg);                                            \
+    hipLaunchKernelGGL((compress_w64_wg_kernel<NR, CPW>), dim3(wgs), dim3(kBlockThreads), 0, \
+                       st, cd, b, per_wg);                                                  \
+  }
+  switch (cd.nw) {
+    case 2048: IBP_W64_WG(4, true); return;
+    case 4096: IBP_W64_WG(8, true); return;
+    case 7168: IBP_W64_WG(14, false); return;
+    default: IBP_W64_WG(16, false); return;  // 8192
+  }
+#undef IBP_W64_WG
+}
+
 template <typename T, int NR>
 void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void* src,
                              void* slots, uint64_t* flags, uint32_t* row_bits, hipStream_t st) {
@@ -3726,6 +3903,18 @@ void launch_compress_wide_nr(const WideCodec<T>& cd, uint64_t n_rows, const void
       default: break;
     }
 #undef IBP_W64
+    // rows of 256 * CPW blocks (the 8 and 28 KiB weight rows): a workgroup
+    // per row, ranges of rows per workgroup as for compress_wg_kernel
+    if (cwg_row(cd.nw)) {
+      CompressBatch b{};
+      uint64_t total = 0;
+      auto flush = [&](CompressBatch& fb, uint64_t rows) {
+        launch_compress_w64_wg<NR>(cd, fb, rows, st);
+      };
+      add_compress_entries(b, total, cd.nw, n_rows, src, slots, flags, row_bits, cd.pad, flush);
+      flush(b, total);
+      return;
+    }
   }
 #define IBP_WIDE(MAXW)                                                                    \
   hipLaunchKernelGGL((compress_wide_kernel<T, NR, MAXW>), dim3(grid_for(n_rows)),         \
@@ -3931,6 +4120,23 @@ void compress_pair_batch(const WideCodec<uint16_t>& cd, const ibp_compress_tenso
   uint64_t total = 0;
   auto flush = [&](CompressBatch& fb, uint64_t rows) {
     launch_compress_pair_wg<NR>(cd, fb, rows, st);
+  };
+  for (uint64_t t = 0; t < n_tensors; ++t) {
+    const ibp_compress_tensor& x = tensors[t];
+    if (x.n_rows == 0 || x.row_bytes != row_bytes) continue;
+    add_compress_entries(b, total, cd.nw, x.n_rows, x.src, x.slots, x.flags, x.row_bits,
+                         is_host_memory(x.slots) ? 0u : 1u, flush);
+  }
+  if (b.count) flush(b, total);
+}
+
+template <int NR>
+void compress_w64_batch(const WideCodec<uint64_t>& cd, const ibp_compress_tensor* tensors,
+                        uint64_t n_tensors, uint64_t row_bytes, hipStream_t st) {
+  CompressBatch b{};
+  uint64_t total = 0;
+  auto flush = [&](CompressBatch& fb, uint64_t rows) {
+    launch_compress_w64_wg<NR>(cd, fb, rows, st);
   };
   for (uint64_t t = 0; t < n_tensors; ++t) {
     const ibp_compress_tensor& x = tensors[t];
@@ -4177,7 +4383,7 @@ int ibp_compress_batch(const ibp_metadata* md, const ibp_compress_tensor* tensor
     const ibp_compress_tensor& x = tensors[t];
     if (x.n_rows == 0) continue;
     const uint64_t n = x.row_bytes / 4;  // words of a row
-    if (md->width_bits == 64 || !cwg_row((uint32_t)n)) {  // tensor by tensor
+    if (!cwg_row((uint32_t)n)) {  // tensor by tensor
       enqueue_compress(md, x.n_rows, x.row_bytes, x.src, x.slots, x.flags, x.row_bits, st);
       continue;
     }
@@ -4195,6 +4401,17 @@ int ibp_compress_batch(const ibp_metadata* md, const ibp_compress_tensor* tensor
         case 3: compress_wg_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
         case 4: compress_wg_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
         default: compress_wg_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+      }
+    } else if (md->width_bits == 64) {
+      const WideCodec<uint64_t> cd = make_wide_codec<uint64_t>(md, x.row_bytes);
+      switch (cd.nruns) {
+        case 0: compress_w64_batch<0>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 1: compress_w64_batch<1>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 2: compress_w64_batch<2>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 3: compress_w64_batch<3>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 4: compress_w64_batch<4>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        case 5: compress_w64_batch<5>(cd, tensors, n_tensors, x.row_bytes, st); break;
+        default: compress_w64_batch<-1>(cd, tensors, n_tensors, x.row_bytes, st); break;
       }
     } else {
       const WideCodec<uint16_t> cd = make_wide_codec<uint16_t>(md, x.row_bytes);

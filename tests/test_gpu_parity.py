@@ -460,7 +460,8 @@ def test_compress_row_ranges_across_flag_words(ibp, kind):
 
 @pytest.mark.parametrize("kind,row_bytes", [
     ("w32", 128), ("w32", 512), ("w32", 8192), ("w32", 28672), ("w32", 4100), ("w16", 8192),
-    ("w16", 28672), ("w16", 512), ("w64", 2048), ("w64", 4104), ("positional", 512),
+    ("w16", 28672), ("w16", 512), ("w64", 2048), ("w64", 4104), ("w64", 8192), ("w64", 28672),
+    ("positional", 512),
     ("positional", 4100)])
 def test_flags_written_over_any_prior_contents(ibp, kind, row_bytes):
     """Every compression kernel writes each row's flag bit itself (no clearing
@@ -571,6 +572,15 @@ WIDE_CASES = [
     (64, 30, 512, 0x5555555555555555, 0x1111111111111111, 0.9),     # 32 runs
     (64, 3, 98304, 0x7FF0000000000000, 0x3FF0000000000000, 0.9),    # largest row
     (64, 48, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 512 blocks, wave per row
+    # rows of 1024, 2048, 3584 and 4096 blocks: workgroup per row
+    (64, 20, 8192, 0x7800780078007800, 0x3800380038003800, 0.9),    # bf16 weight quads
+    (64, 9, 28672, 0x7C007C007C007C00, 0x3C003C003C003C00, 0.9),    # 3584 blocks
+    (64, 5, 16384, 0x5555555555555555, 0x1111111111111111, 0.9),    # 32 runs (generic path)
+    (64, 6, 32768, 0xFFFFFFFFFFFFFFFF, 0x0, 0.995),                 # p = 64: empty payloads
+    (64, 6, 8192, 0x0, 0x0, 0.0),                                   # p = 0: raw rows from registers
+    # more rows than stay resident: ranges of several rows per workgroup
+    (64, 2600, 8192, 0x7800780078007800, 0x3800380038003800, 0.9),  # flag bytes owned
+    (64, 1300, 28672, 0x7800780078007800, 0x3800380038003800, 0.9), # flag atomics per range
 ]
 
 
@@ -1181,14 +1191,15 @@ def test_decompress_batch(ibp, n_tensors):
     assert np.array_equal(outs[1][torch.from_numpy(ids).cuda()].cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("w,mask,bitval", [(32, 0x78007800, 0x38003800), (16, 0x7800, 0x3800)],
-                         ids=["w32", "w16"])
+@pytest.mark.parametrize("w,mask,bitval", [(32, 0x78007800, 0x38003800), (16, 0x7800, 0x3800),
+                                           (64, 0x7800780078007800, 0x3800380038003800)],
+                         ids=["w32", "w16", "w64"])
 def test_compress_batch(ibp, w, mask, bitval):
     """ibp_compress_batch: each tensor's image equals ibp_compress's and, for
-    two tensors, the oracle's.  8 and 28 KiB rows (W = 32: two launches of
-    the weight-row kernel, tensors of several ranges per launch, a ragged
-    one), rows other kernels take (2 KiB, 4100 B), an empty tensor, a tensor
-    compressed in place and one without row_bits."""
+    two tensors, the oracle's.  8 and 28 KiB rows (two launches of the
+    weight-row kernel of the width, tensors of several ranges per launch, a
+    ragged one), rows other kernels take (2 KiB, 4100 or 4096 B), an empty
+    tensor, a tensor compressed in place and one without row_bits."""
     rng = np.random.default_rng(w + 7)
     shapes = [(1300, 8192), (64, 8192), (33, 28672), (1283, 28672), (100, 2048), (0, 8192),
               (50, 4100 if w == 32 else 4096), (70, 8192), (40, 28672)]
