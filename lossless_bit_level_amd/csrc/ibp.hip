@@ -1532,7 +1532,7 @@ __device__ __forceinline__ void run_row_pipeline(
 // flight.  Same bookkeeping and id rules as run_row_pipeline.
 //   decode(hdr, x): the row's n words from the LDS copy of its slot, x[c] =
 //                   word c * 64 + lane; hdr holds header word q in lane q
-template <int NCH, bool GATHER, typename Decode>
+template <int NCH, bool GATHER, int Q = 1, typename Decode>
 __device__ __forceinline__ void run_slot_pipeline(
     const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
     const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
@@ -1582,18 +1582,22 @@ __device__ __forceinline__ void run_slot_pipeline(
       for (int c = 0; c < FV; ++c) l4[c * kWave + lane] = cur[c];
       wave_lds_sync();
       load_slot(2, src_of(k + 2), nxt);
-      uint32_t x[NCH];
+      // NCH / Q words of Q * 32 bits per lane (Q = 2: 64-bit blocks)
+      using XT = std::conditional_t<Q == 2, unsigned long long, uint32_t>;
+      constexpr int NX = NCH / Q;
+      XT x[NX];
       if (!ok_of(0)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) x[c] = 0u;
+        for (int c = 0; c < NX; ++c) x[c] = 0u;
       } else if (!fl_of(0)) {
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) x[c] = lds[c * kWave + lane];
+        for (int c = 0; c < NX; ++c) x[c] = reinterpret_cast<const XT*>(lds)[c * kWave + lane];
       } else {
         decode(lds[lane], x);
       }
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], out + c * kWave + lane);
+      for (int c = 0; c < NX; ++c)
+        __builtin_nontemporal_store(x[c], reinterpret_cast<XT*>(out) + c * kWave + lane);
       __builtin_amdgcn_sched_barrier(0);
       wave_lds_sync();
       ++k;
@@ -1621,17 +1625,18 @@ __device__ __forceinline__ void run_slot_pipeline(
 }
 
 // The row pipeline of a kernel: whole slots (SLOT) or window + rest.
-template <int NCH, bool GATHER, bool SLOT, typename StreamWords, typename Decode>
+template <int NCH, bool GATHER, bool SLOT, int Q = 1, typename StreamWords, typename Decode>
 __device__ __forceinline__ void row_pipeline(
     const uint32_t* __restrict__ slots, const unsigned long long* __restrict__ flags,
     const int64_t* __restrict__ ids, uint64_t n_rows, uint32_t n_out,
     uint32_t* __restrict__ dst, uint32_t* lds, uint32_t i, uint32_t stride,
     StreamWords stream_words, Decode decode) {
   if constexpr (SLOT)
-    run_slot_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride, decode);
+    run_slot_pipeline<NCH, GATHER, Q>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                      decode);
   else
-    run_row_pipeline<NCH, GATHER>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
-                                  stream_words, decode);
+    run_row_pipeline<NCH, GATHER, Q>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
+                                     stream_words, decode);
 }
 
 // [IBP] Decompression of rows of 64 * NCH blocks with one global Mask/Bitval
@@ -2570,11 +2575,11 @@ __global__ __launch_bounds__(kBlockThreads) void decode_wide_batch_kernel(WideCo
 
 // [IBP] Decompression with 64-bit blocks of rows of 512 bytes to 2 KiB (32 * NCH
 // blocks, NCH = 2, 4, 8), 16-byte aligned: the row pipeline of the 32-bit
-// decoder with 64-bit stores.  A compressed row's stream is nb + 64 nb - p m
+// decoder with 64-bit stores (SLOT: the whole-slot pipeline, for p <= 16).  A compressed row's stream is nb + 64 nb - p m
 // bits (nb blocks, m stripped); per 64-block chunk a lane's payload starts at
 // u + 64 lane - p * (stripped blocks of the chunk below the lane) and is read
 // from three LDS words with two funnel shifts.
-template <int MODE, int NR, int NCH>
+template <int MODE, int NR, int NCH, bool SLOT = false>
 __global__ __launch_bounds__(kBlockThreads) void decode_pipe64_kernel(
     WideCodec<uint64_t> cd, const uint32_t* __restrict__ slots,
     const unsigned long long* __restrict__ flags, const int64_t* __restrict__ ids,
@@ -2582,7 +2587,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe64_kernel(
   using P = RowPipe<NCH>;
   constexpr uint32_t n = P::n;   // words of a row
   constexpr uint32_t nb = n / 2;  // 64-bit blocks of a row
-  __shared__ __attribute__((aligned(16))) uint32_t lds_all[kWavesPerBlock][P::kLdsWords];
+  __shared__ __attribute__((aligned(16)))
+  uint32_t lds_all[kWavesPerBlock][SLOT ? (NCH >= 4 ? n : 256u) + 4u : P::kLdsWords];
   const uint32_t lane = lane_id();
   const uint32_t wave = uniform(threadIdx.x / kWave);
   uint32_t* lds = lds_all[wave];
@@ -2609,8 +2615,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_pipe64_kernel(
       u += 64u * kWave - cd.p * (uint32_t)__popcll(((unsigned long long)h_hi << 32) | h_lo);
     }
   };
-  run_row_pipeline<NCH, MODE == kModeGather, 2>(slots, flags, ids, n_rows, n_out, dst, lds, i,
-                                                stride, stream_words, decode);
+  row_pipeline<NCH, MODE == kModeGather, SLOT, 2>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                                  stride, stream_words, decode);
 }
 
 // ---------------------------------------------------- per-position metadata --
@@ -3961,14 +3967,26 @@ void launch_decode_wide_nr(const WideCodec<T>& cd, const DecodeArgs& a, hipStrea
         }
         const int64_t* id_p = MODE != kModeTable ? a.ids + off : a.ids;
         uint32_t* out_p = (uint32_t*)a.dst + off * cd.nw;
-        const uint32_t grid = row_pipe_grid(cnt, kWavesPerBlock, 8);
-#define IBP_P64(NCH)                                                                          \
-  hipLaunchKernelGGL((decode_pipe64_kernel<MODE, NR, NCH>), dim3(grid), dim3(kBlockThreads), 0, \
-                     st, cd, sl, fl, id_p, a.n_rows, cnt, out_p)
-        switch (cd.nw) {
-          case 128: IBP_P64(2); break;
-          case 256: IBP_P64(4); break;
-          default: IBP_P64(8); break;
+        // at most 16 invariant bits of 64 (a stored row is at least about
+        // three quarters of its slot): whole slots, as the 32-bit decoder
+        // fetches them for p <= 8
+        const bool slot_pipe = cd.p <= 2u * kSlotPipeMaxP;
+        const uint32_t grid = row_pipe_grid(cnt, kWavesPerBlock, slot_pipe ? 6u : 8u);
+#define IBP_P64(NCH, SLOT)                                                                    \
+  hipLaunchKernelGGL((decode_pipe64_kernel<MODE, NR, NCH, SLOT>), dim3(grid),                 \
+                     dim3(kBlockThreads), 0, st, cd, sl, fl, id_p, a.n_rows, cnt, out_p)
+        if (slot_pipe) {
+          switch (cd.nw) {
+            case 128: IBP_P64(2, true); break;
+            case 256: IBP_P64(4, true); break;
+            default: IBP_P64(8, true); break;
+          }
+        } else {
+          switch (cd.nw) {
+            case 128: IBP_P64(2, false); break;
+            case 256: IBP_P64(4, false); break;
+            default: IBP_P64(8, false); break;
+          }
         }
 #undef IBP_P64
       }
