@@ -29,7 +29,7 @@ Prints one JSON line:
                device copy, read + written bytes per second, the practical
                rate of a streaming read/write mix on the GPU at hand
   cpu_baseline the CPU oracle on the host cores: full decompress and
-               compress of one layer on every thread of the box's share,
+               compress of one layer on every host thread of this GPU's share,
                plus single-thread figures on the tiny table and a 256 MiB
                slice of the model
 """
@@ -68,8 +68,8 @@ def log(*a):
 
 def cpu_threads():
     """(threads to use, CPUs the affinity mask allows): the affinity mask,
-    capped at the share OMP_NUM_THREADS announces (a GPU machine gives one GPU
-    16 host threads whatever the mask shows)."""
+    capped at the share OMP_NUM_THREADS announces (a host may give one GPU
+    a share of its threads smaller than the mask shows)."""
     allowed = len(os.sched_getaffinity(0))
     share = int(os.environ.get("OMP_NUM_THREADS") or allowed)
     return max(1, min(allowed, share)), allowed
@@ -816,8 +816,9 @@ def measure_decode(wl, opt, images, shapes, md, pos_table, K, W, dev, stream, ho
 
 
 def measure_tiny(dev, reps: int = 50):
-    """Cfg 1, reported and not judged: compress, full decompress and the
-    round trip of the 2 MiB table, each the median of `reps` calls."""
+    """The tiny dense table (4096 x 128 fp32), reported only: compress, full
+    decompress and the round trip of the 2 MiB table, each the median of
+    `reps` calls."""
     import torch
     from lossless_bit_level_amd import ibp
     import synthetic as syn
@@ -848,7 +849,7 @@ def measure_tiny(dev, reps: int = 50):
     sb = stored_bytes_per_row(rb.cpu().numpy()[:x.shape[0]], 512)
     nb = x.nbytes
     return {"desc": "tiny dense 4096 x 128 fp32 N(0, 0.1^2): compress, full decompress, round "
-                    "trip (2 MiB: launch- and cache-bound; reported, not judged)",
+                    "trip (2 MiB: launch- and cache-bound; reported only)",
             "compress_us": round(c * 1e6, 2), "compress_GB_per_s": round(nb / c / 1e9, 1),
             "decompress_us": round(d * 1e6, 2), "decompress_GB_per_s": round(nb / d / 1e9, 1),
             "round_trip_us": round(r * 1e6, 2), "round_trip_GB_per_s": round(nb / r / 1e9, 1),

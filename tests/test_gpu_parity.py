@@ -5,7 +5,7 @@ every image byte that belongs to the image, every decompressed byte).  The
 full-size workloads run in the launch configuration the benchmark times: the
 whole image of every table (every row's stored words, flag and C) is
 compared with the oracle's, which compresses the table on every host thread
-of the box's share, and every gather batch or layer decode is compared with
+of the host's share, and every gather batch or layer decode is compared with
 the source rows; closed-form row sizes are checked independently of both.
 """
 import os
