@@ -3181,6 +3181,55 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
         row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i, stride,
                                          stream_words, decode);
       } else {
+        // the kept bits ~m0 as runs, at most two taken (sign and mantissa
+        // around an exponent field): then the deposit is a shift and an
+        // and-or per run, as in the global decoder; more runs keep the five
+        // shift-and-select steps of the position entries
+        uint32_t rsh[2] = {0u, 0u}, rpl[2] = {0u, 0u};
+        uint32_t nruns = 0;
+        {
+          uint32_t keep = ~m0, at = 0;
+          while (keep != 0u && nruns < 3u) {
+            const uint32_t b = (uint32_t)__builtin_ctz(keep);
+            const uint32_t rest = ~(keep >> b);
+            const uint32_t len = rest == 0u ? 32u - b : (uint32_t)__builtin_ctz(rest);
+            const uint32_t place = (len >= 32u ? ~0u : ((1u << len) - 1u)) << b;
+            if (nruns < 2u) {
+              rsh[nruns] = b - at;
+              rpl[nruns] = place;
+            }
+            at += len;
+            keep &= ~place;
+            ++nruns;
+          }
+        }
+        if (nruns <= 2u) {
+          const uint32_t sh0 = uniform(rsh[0]), sh1 = uniform(rsh[1]);
+          const uint32_t pl0 = uniform(rpl[0]), pl1 = uniform(rpl[1]);
+          auto decode = [&](uint32_t win, uint32_t* x) {
+            uint32_t u = n;
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+              const uint32_t h_lo = __builtin_amdgcn_readlane(win, 2 * c);
+              const uint32_t h_hi = __builtin_amdgcn_readlane(win, 2 * c + 1);
+              const unsigned long long h = ((unsigned long long)h_hi << 32) | h_lo;
+              const uint32_t rel =
+                  (uint32_t)__mul24(negp, (int)bits_below_lane(h_lo, h_hi)) + (u + l32);
+              const uint32_t w = lds_bits(lds, rel);
+              const uint32_t d = b0 | ((w << sh0) & pl0) | ((w << sh1) & pl1);
+              x[c] = __builtin_amdgcn_inverse_ballot_w64(h) ? d : w;
+              u += 32u * kWave - p * (uint32_t)__popcll(h);
+            }
+          };
+          // few invariant bits: whole slots, as the global decoder fetches them
+          if (p <= kSlotPipeMaxP)
+            row_pipeline<NCH, GATHER, true>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                            stride, stream_words, decode);
+          else
+            row_pipeline<NCH, GATHER, false>(slots, flags, ids, n_rows, n_out, dst, lds, i,
+                                             stride, stream_words, decode);
+          return;
+        }
         PosEntry e = pos_entry<n>(tf, 0);
         e.mask = m0;
         e.bitval = b0;
