@@ -2913,6 +2913,30 @@ __global__ __launch_bounds__(kBlockThreads) void decode_positional_kernel(
   }
 }
 
+// The first two runs of kept bits (~mask) of a uniform mask, as make_codec
+// cuts them on the host: run j moves payload bits down by sh[j] into the
+// positions place[j].  Returns the number of runs, 3 meaning three or more
+// (then sh/place hold only the first two).  Scalar work, once per workgroup.
+__device__ __forceinline__ uint32_t kept_runs2(uint32_t mask, uint32_t (&sh)[2],
+                                               uint32_t (&place)[2]) {
+  sh[0] = sh[1] = place[0] = place[1] = 0u;
+  uint32_t keep = ~mask, at = 0, nr = 0;
+  while (keep != 0u && nr < 3u) {
+    const uint32_t b = (uint32_t)__builtin_ctz(keep);
+    const uint32_t rest = ~(keep >> b);
+    const uint32_t len = rest == 0u ? 32u - b : (uint32_t)__builtin_ctz(rest);
+    const uint32_t pl = (len >= 32u ? ~0u : ((1u << len) - 1u)) << b;
+    if (nr < 2u) {
+      sh[nr] = b - at;
+      place[nr] = pl;
+    }
+    at += len;
+    keep &= ~pl;
+    ++nr;
+  }
+  return nr;
+}
+
 // The position entries of rows of n blocks staged into LDS field by field
 // (tf[0] Mask, tf[1] Bitval, tf[2..6] the five parallel-suffix masks), so
 // that a wave reads one field of 64 consecutive positions without bank
@@ -2992,6 +3016,14 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
       e.bitval = b0;
 #pragma unroll
       for (int j = 0; j < 5; ++j) e.sfx[j] = uniform(e.sfx[j]);
+      // with at most two runs of kept bits, the extract is a shift and an
+      // and-or per run (as compress_rows_kernel's), else the five steps of
+      // the position entries
+      uint32_t rsh[2], rpl[2];
+      const uint32_t nruns = kept_runs2(m0, rsh, rpl);
+      const uint32_t sh0 = uniform(rsh[0]), sh1 = uniform(rsh[1]);
+      const uint32_t kp0 = uniform(rpl[0] >> rsh[0]), kp1 = uniform(rpl[1] >> rsh[1]);
+      auto encode = [&](auto extract) {
       compress_row_range(n_rows, wave, WPB, 32u * n, flags, row_bits, [&](uint64_t row) {
         const uint32_t* x_row = src + row * n;
         uint32_t* s_row = slots + row * n;
@@ -3031,7 +3063,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
             const uint32_t off =
                 n + 32u * (c * kWave + lane) - __umul24(p, carry + bits_below_lane(lo, hi));
             const uint32_t len = match ? 32u - p : 32u;
-            const uint32_t pay = match ? extract_pos(x[c], e) : x[c];
+            const uint32_t pay = match ? extract(x[c]) : x[c];
             if (len) {
               const uint32_t sh = off & 31u, wi = off >> 5;
               atomicOr(&buf[wi], pay << sh);
@@ -3045,6 +3077,11 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
         }
         return c_bits;
       });
+      };
+      if (nruns <= 2u)
+        encode([&](uint32_t v) { return ((v >> sh0) & kp0) | ((v >> sh1) & kp1); });
+      else
+        encode([&](uint32_t v) { return extract_pos(v, e); });
       return;
     }
   }
@@ -3185,24 +3222,8 @@ __global__ __launch_bounds__(WPB * kWave) void decode_pos_pipe_kernel(
         // around an exponent field): then the deposit is a shift and an
         // and-or per run, as in the global decoder; more runs keep the five
         // shift-and-select steps of the position entries
-        uint32_t rsh[2] = {0u, 0u}, rpl[2] = {0u, 0u};
-        uint32_t nruns = 0;
-        {
-          uint32_t keep = ~m0, at = 0;
-          while (keep != 0u && nruns < 3u) {
-            const uint32_t b = (uint32_t)__builtin_ctz(keep);
-            const uint32_t rest = ~(keep >> b);
-            const uint32_t len = rest == 0u ? 32u - b : (uint32_t)__builtin_ctz(rest);
-            const uint32_t place = (len >= 32u ? ~0u : ((1u << len) - 1u)) << b;
-            if (nruns < 2u) {
-              rsh[nruns] = b - at;
-              rpl[nruns] = place;
-            }
-            at += len;
-            keep &= ~place;
-            ++nruns;
-          }
-        }
+        uint32_t rsh[2], rpl[2];
+        const uint32_t nruns = kept_runs2(m0, rsh, rpl);
         if (nruns <= 2u) {
           const uint32_t sh0 = uniform(rsh[0]), sh1 = uniform(rsh[1]);
           const uint32_t pl0 = uniform(rpl[0]), pl1 = uniform(rpl[1]);

@@ -625,7 +625,9 @@ def test_codec_parity_other_widths(ibp, case):
     (16, 8192, 0x7800, 0x3800, "host"),
     (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000, "device"),
     (64, 1024, 0x7FF0000000000000, 0x3FF0000000000000, "host"),
-    (64, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00, "device")])
+    (64, 4096, 0x7C007C007C007C00, 0x3C003C003C003C00, "device"),
+    (64, 8192, 0x7800780078007800, 0x3800380038003800, "host"),
+    (64, 28672, 0x7800780078007800, 0x3800380038003800, "device")])
 def test_compress_in_place_other_widths(ibp, w, row_bytes, mask, bitval, where):
     """16- and 64-bit blocks compressed in place (each row into its own
     buffer, in device or pinned host memory): flags, sizes and image bytes
