@@ -1335,6 +1335,39 @@ def test_full_llm_weights(ibp, llm_metadata, first_layer):
             del images, sources, outs
 
 
+def test_full_llm_weights_width64(ibp):
+    """Two layers of the 32-layer model (the first and the last) at full size
+    with 64-bit blocks, four bf16 values per block: metadata from the same
+    sample agrees with the oracle's; each layer's seven matrices compressed
+    in one ibp_compress_batch call (one launch per row length) and every
+    image compared whole with the oracle's; the layer decoded in one batched
+    launch and compared with the source."""
+    sample = np.concatenate([syn.llm_weight(0, 0).reshape(-1), syn.llm_weight(0, 1).reshape(-1)])
+    s64 = sample.view(np.uint64)
+    md, ones = ibp.ibp_build_metadata(to_gpu(sample[None]), width_bits=64, n_blocks=1 << 23)
+    md_o, ones_o = orc.build_metadata(s64[:1 << 23], 64)
+    assert (md.mask, md.bitval) == (md_o.mask, md_o.bitval)
+    assert (md.mask, md.bitval) == (0x7800780078007800, 0x3800380038003800)
+    assert np.array_equal(np.array(ones, np.uint64), ones_o)
+    with ThreadPoolExecutor(syn.LLM_MATRICES) as ex:
+        for layer in (0, syn.LLM_LAYERS - 1):
+            mats = list(ex.map(lambda j: syn.llm_weight(layer, j), range(syn.LLM_MATRICES)))
+            srcs = [to_gpu(w) for w in mats]
+            imgs = ibp.ibp_compress_batch(md, srcs)
+            torch.cuda.synchronize()
+            for j, (w, (slots, flags, rb)) in enumerate(zip(mats, imgs)):
+                slots_o, flags_o, rb_o = oracle_image(omd(md), w.view(np.uint8))
+                assert_images_equal(f"W=64 layer {layer} matrix {j}", slots.cpu().numpy(),
+                                    flags_np(flags, w.shape[0]), rb.cpu().numpy()[:w.shape[0]],
+                                    slots_o, flags_o, rb_o)
+            outs = ibp.ibp_decompress_batch(md, [(sl, fl) for sl, fl, _ in imgs])
+            torch.cuda.synchronize()
+            for j, (out, wg) in enumerate(zip(outs, srcs)):
+                assert torch.equal(out, wg), f"W=64 layer {layer} matrix {j}"
+            say(f"W=64 layer {layer}: 7 matrices bit-exact")
+            del srcs, imgs, outs
+
+
 def test_full_sparse_gnn_cache_of_whole_table(ibp):
     """The sparse feature table cached whole in GPU memory (its packed arena
     is ~1/24 of the raw table) and the image in pinned host memory: every
