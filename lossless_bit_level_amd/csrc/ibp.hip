@@ -168,6 +168,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* p, uint32
 // its first 128 bytes: non-temporal, as stage_window's loads.
 constexpr int kLoadStream = 2;
 
+// Cache policy of the compressors' row loads and stores: non-temporal (a raw
+// row is read once and a stored row written once).
+constexpr int kRowLoad = 2;
+constexpr int kRowStore = 2;
+
 // Words to write for a compressed row whose stream has `words` words, at slot
 // address row (slots of n words): with pad (device memory), on to the next
 // 64-byte boundary of the address, at most n.  A write that ends inside a
@@ -614,7 +619,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_kernel(
       }
       __syncthreads();
       const uint32_t nw = (c_bits + 31u) >> 5;
-      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = threadIdx.x; j < nw; j += kBlockThreads) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0) {
       put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
@@ -711,7 +716,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, Comp
     asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
-      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, kRowLoad);
   };
   uint32_t x[CPW];
   load(x, r0);
@@ -806,17 +811,17 @@ __global__ __launch_bounds__(WPB * kWave) void compress_wg_kernel(Codec cd, Comp
       asm volatile("" : "+v"(lb));
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
-        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, kRowStore);
     } else {
       const uint32_t nw = store_words(s_row, (c_bits + 31u) >> 5, n, ct.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
         const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
         u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
-        for (uint32_t j = threadIdx.x; j < nw / 4; j += WPB * kWave) o4[j] = b4[j];
+        for (uint32_t j = threadIdx.x; j < nw / 4; j += WPB * kWave) __builtin_nontemporal_store(b4[j], &o4[j]);
         j0 = nw & ~3u;
       }
-      for (uint32_t j = j0 + threadIdx.x; j < nw; j += WPB * kWave) s_row[j] = buf[j];
+      for (uint32_t j = j0 + threadIdx.x; j < nw; j += WPB * kWave) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
 #pragma unroll
@@ -897,7 +902,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
       asm volatile("" : "+v"(lb));
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+        x[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, kRowLoad);
     }
     uint32_t m = 0;
     uint32_t hword = 0;  // lane 2c / 2c + 1: low / high half of chunk c's ballot
@@ -959,7 +964,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_rows_kernel(
     asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
-      __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, kRowStore);
     wave_lds_sync();
     return c_bits;
   });
@@ -1817,7 +1822,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_wide_kernel(
       }
       __syncthreads();
       const uint32_t words = (c_bits + 31u) >> 5;
-      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0) {
       put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
@@ -1869,7 +1874,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
     unsigned long long e[NWL], o[NWL];
 #pragma unroll
     for (int t = 0; t < NWL; ++t)
-      x[t] = __builtin_amdgcn_raw_buffer_load_b32(in, (t * kWave + lane) * 4u, 0, 0);
+      x[t] = __builtin_amdgcn_raw_buffer_load_b32(in, (t * kWave + lane) * 4u, 0, kRowLoad);
     uint32_t m = 0;
 #pragma unroll
     for (int t = 0; t < NWL; ++t) {
@@ -1927,7 +1932,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_rows_kernel(
     const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * nw, nwc * 4u);
 #pragma unroll
     for (int t = 0; t < NWL; ++t)
-      __builtin_amdgcn_raw_buffer_store_b32(x[t], out, (t * kWave + lane) * 4u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(x[t], out, (t * kWave + lane) * 4u, 0, kRowStore);
     wave_lds_sync();
     return c_bits;
   });
@@ -1998,7 +2003,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
     asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int c = 0; c < CPW; ++c)
-      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, 0);
+      v[c] = __builtin_amdgcn_raw_buffer_load_b32(in, lb + c * kWave * 4u, 0, kRowLoad);
   };
   uint32_t x[CPW];
   load(x, r0);
@@ -2082,17 +2087,17 @@ __global__ __launch_bounds__(kBlockThreads) void compress_pair_wg_kernel(
       asm volatile("" : "+v"(lb));
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
-        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(x[c], out, lb + c * kWave * 4u, 0, kRowStore);
     } else {
       const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, ct.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
         const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
         u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
-        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) o4[j] = b4[j];
+        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) __builtin_nontemporal_store(b4[j], &o4[j]);
         j0 = nwc & ~3u;
       }
-      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
 #pragma unroll
@@ -2132,7 +2137,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
     uint64_t x[NCH];
     unsigned long long h[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+    for (int c = 0; c < NCH; ++c) x[c] = __builtin_nontemporal_load(&x_row[c * kWave + lane]);
     uint32_t m = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -2143,7 +2148,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
     const bool flag = c_bits < 64u * nb;
     if (!flag) {
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) s_row64[c * kWave + lane] = x[c];
+      for (int c = 0; c < NCH; ++c) __builtin_nontemporal_store(x[c], &s_row64[c * kWave + lane]);
     } else {
       const uint32_t nwc = store_words(slots + row * nw, (c_bits + 31u) >> 5, nw, cd.pad);
       for (uint32_t j = nb / 32 + lane; j < nwc + 2; j += kWave) buf[j] = 0u;
@@ -2182,7 +2187,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_rows_kernel(
       const __amdgpu_buffer_rsrc_t out = row_rsrc(slots + row * nw, nwc * 4u);
 #pragma unroll
       for (int t = 0; t < 2 * NCH; ++t)
-        __builtin_amdgcn_raw_buffer_store_b32(v[t], out, (t * kWave + lane) * 4u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(v[t], out, (t * kWave + lane) * 4u, 0, kRowStore);
       wave_lds_sync();
     }
     return c_bits;
@@ -2234,7 +2239,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_wg_kernel(
     asm volatile("" : "+v"(lb));
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(in, lb + c * kWave * 8u, 0, 0);
+      const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(in, lb + c * kWave * 8u, 0, kRowLoad);
       v[c] = ((uint64_t)w.y << 32) | w.x;
     }
   };
@@ -2313,17 +2318,17 @@ __global__ __launch_bounds__(kBlockThreads) void compress_w64_wg_kernel(
 #pragma unroll
       for (int c = 0; c < CPW; ++c)
         __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)x[c], (uint32_t)(x[c] >> 32)},
-                                              out, lb + c * kWave * 8u, 0, 0);
+                                              out, lb + c * kWave * 8u, 0, kRowStore);
     } else {
       const uint32_t nwc = store_words(s_row, (c_bits + 31u) >> 5, nw, ct.pad);
       uint32_t j0 = 0;
       if ((reinterpret_cast<uintptr_t>(s_row) & 15u) == 0) {  // whole 16-byte units
         const u32x4* b4 = reinterpret_cast<const u32x4*>(buf);
         u32x4* o4 = reinterpret_cast<u32x4*>(s_row);
-        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) o4[j] = b4[j];
+        for (uint32_t j = threadIdx.x; j < nwc / 4; j += kBlockThreads) __builtin_nontemporal_store(b4[j], &o4[j]);
         j0 = nwc & ~3u;
       }
-      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = j0 + threadIdx.x; j < nwc; j += kBlockThreads) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0 && row_bits) row_bits[row] = c_bits;
 #pragma unroll
@@ -2793,7 +2798,7 @@ __global__ __launch_bounds__(kBlockThreads) void compress_positional_kernel(
       }
       __syncthreads();
       const uint32_t words = (c_bits + 31u) >> 5;
-      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) s_row[j] = buf[j];
+      for (uint32_t j = threadIdx.x; j < words; j += kBlockThreads) __builtin_nontemporal_store(buf[j], &s_row[j]);
     }
     if (threadIdx.x == 0) {
       put_flag_bits(flags, row, 1u, flag ? 1ull : 0ull, n_rows);
@@ -3030,7 +3035,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
         uint32_t x[NCH];
         unsigned long long h[NCH];
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+        for (int c = 0; c < NCH; ++c) x[c] = __builtin_nontemporal_load(&x_row[c * kWave + lane]);
         uint32_t m = 0;
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
@@ -3072,7 +3077,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
             carry += (uint32_t)__popcll(h[c]);
           }
           wave_lds_sync();
-          for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+          for (uint32_t j = lane; j < nw; j += kWave) __builtin_nontemporal_store(buf[j], &s_row[j]);
           wave_lds_sync();
         }
         return c_bits;
@@ -3092,7 +3097,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
     uint32_t x[NCH];
     unsigned long long h[NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) x[c] = x_row[c * kWave + lane];
+    for (int c = 0; c < NCH; ++c) x[c] = __builtin_nontemporal_load(&x_row[c * kWave + lane]);
     uint32_t s_lane = 0;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -3137,7 +3142,7 @@ __global__ __launch_bounds__(WPB * kWave) void compress_pos_rows_kernel(
         carry += __builtin_amdgcn_readlane(incl, kWave - 1);
       }
       wave_lds_sync();
-      for (uint32_t j = lane; j < nw; j += kWave) s_row[j] = buf[j];
+      for (uint32_t j = lane; j < nw; j += kWave) __builtin_nontemporal_store(buf[j], &s_row[j]);
       wave_lds_sync();
     }
     return c_bits;
