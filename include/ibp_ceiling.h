@@ -15,7 +15,9 @@
  * the stored length, streaming row writes) on the machine at hand.
  *
  * It is not part of the compression method: the benchmark times it beside
- * the decompression on the same ids, images and outputs.
+ * the decompression on the same ids, images and outputs.  A plain contiguous
+ * copy (ibp_ceiling_copy) gives the practical rate of a streaming read/write
+ * mix on the GPU, against which the nominal HBM peak is put in context.
  */
 #ifndef IBP_CEILING_H_
 #define IBP_CEILING_H_
@@ -82,6 +84,19 @@ typedef struct ibp_copy_tensor {
  */
 int ibp_ceiling_gather_copy(const ibp_copy_tensor *tensors, uint64_t n_tensors,
                             uint32_t max_workgroups, uint32_t flags, void *stream);
+
+/*
+ * Enqueues one launch on `stream` that copies n_bytes from src to dst (both
+ * device memory, 16-byte aligned, not overlapping; n_bytes a multiple of 16):
+ * workgroups of 256 threads stride over 16 KiB tiles, every load and store
+ * 16 bytes and non-temporal.  max_workgroups caps the grid, 0 = one
+ * workgroup per tile (at most 2^20).  Asynchronous; allocates nothing.
+ * Returns 0 (n_bytes == 0: nothing enqueued), -1 (null or misaligned
+ * pointer, n_bytes not a multiple of 16; nothing enqueued) or -5 (launch
+ * failure).
+ */
+int ibp_ceiling_copy(const void *src, void *dst, uint64_t n_bytes, uint32_t max_workgroups,
+                     void *stream);
 
 #ifdef __cplusplus
 }

@@ -1,5 +1,6 @@
 """ctypes binding of libibp_ceiling (include/ibp_ceiling.h): the gather-copy
-floor the benchmark times beside each decompression.  Argument marshalling
+floor the benchmark times beside each decompression, and a plain contiguous
+copy.  Argument marshalling
 only; raises if the library has not been built."""
 from __future__ import annotations
 
@@ -39,6 +40,9 @@ def lib() -> ctypes.CDLL:
         L.ibp_ceiling_gather_copy.argtypes = [ctypes.POINTER(ibp_copy_tensor), ctypes.c_uint64,
                                               ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
         L.ibp_ceiling_gather_copy.restype = ctypes.c_int
+        L.ibp_ceiling_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.c_uint32, ctypes.c_void_p]
+        L.ibp_ceiling_copy.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -80,4 +84,28 @@ def gather_copy_launcher(parts, max_workgroups: int = 0, pack: bool = False,
         if rc:
             raise RuntimeError(f"ibp_ceiling_gather_copy failed ({rc})")
     launch.keep = (arr, parts)
+    return launch
+
+
+def copy_launcher(src, dst, max_workgroups: int = 0, stream=None):
+    """A plain contiguous copy of src into dst (GPU tensors of the same byte
+    size, 16-byte aligned, a multiple of 16 bytes): workgroups stride over 16
+    KiB tiles with non-temporal 16-byte loads and stores; max_workgroups caps
+    the grid (0: one workgroup per tile).  Returns a no-argument callable
+    that enqueues the copy (one launch) on the current stream."""
+    ibp._need_cuda(src, "src")
+    ibp._need_cuda(dst, "dst")
+    n = src.numel() * src.element_size()
+    ibp._need_size(src, n, "src")
+    ibp._need_size(dst, n, "dst")
+    fn = lib().ibp_ceiling_copy
+    s = ctypes.c_void_p((torch.cuda.current_stream() if stream is None else stream).cuda_stream)
+    a, b = ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr())
+    nb, cap = ctypes.c_uint64(n), ctypes.c_uint32(max_workgroups)
+
+    def launch():
+        rc = fn(a, b, nb, cap, s)
+        if rc:
+            raise RuntimeError(f"ibp_ceiling_copy failed ({rc})")
+    launch.keep = (src, dst)
     return launch

@@ -17,6 +17,12 @@
 // grid.  The slot loads take the default cache policy or the non-temporal
 // one (the benchmark takes the best of a few grids, both task shapes and
 // both load policies, as a floor should).
+//
+// ibp_ceiling_copy is the plain contiguous copy the benchmark quotes as the
+// practical rate of a streaming read/write mix: workgroups stride over 16 KiB
+// tiles, each lane loading four 16-byte units (one per 4 KiB quarter of the
+// tile, so that each load instruction of the workgroup covers 4 KiB in a
+// row) and then storing them, loads and stores non-temporal.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -127,6 +133,28 @@ __global__ __launch_bounds__(kThreads) void gather_copy_kernel(CopyBatch b) {
   }
 }
 
+constexpr uint32_t kTileUnits = kThreads * kPerLane;  // 16-byte units of a copy tile
+
+__global__ __launch_bounds__(kThreads) void tile_copy_kernel(const u32x4* __restrict__ src,
+                                                             u32x4* __restrict__ dst,
+                                                             uint64_t n_units) {
+  const uint64_t tiles = (n_units + kTileUnits - 1) / kTileUnits;
+  for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+    const uint64_t b = t * kTileUnits + threadIdx.x;
+    u32x4 v[kPerLane];
+    if (t * kTileUnits + kTileUnits <= n_units) {  // a whole tile
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) v[j] = __builtin_nontemporal_load(src + b + j * kThreads);
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) __builtin_nontemporal_store(v[j], dst + b + j * kThreads);
+    } else {  // the last, partial tile
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j)
+        if (b + j * kThreads < n_units) dst[b + j * kThreads] = src[b + j * kThreads];
+    }
+  }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 }  // namespace
@@ -178,5 +206,18 @@ extern "C" int ibp_ceiling_gather_copy(const ibp_copy_tensor* tensors, uint64_t 
   else
     hipLaunchKernelGGL(gather_copy_kernel<false>, dim3(grid), dim3(kThreads), 0,
                        (hipStream_t)stream, b);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int ibp_ceiling_copy(const void* src, void* dst, uint64_t n_bytes,
+                                uint32_t max_workgroups, void* stream) {
+  if (n_bytes == 0) return 0;
+  if (!src || !dst || n_bytes % 16 || !aligned16(src) || !aligned16(dst)) return -1;
+  const uint64_t n_units = n_bytes / 16;
+  const uint64_t tiles = (n_units + kTileUnits - 1) / kTileUnits;
+  const uint32_t grid = (uint32_t)std::min<uint64_t>(
+      tiles, max_workgroups ? std::min<uint32_t>(max_workgroups, 1u << 20) : 1u << 20);
+  hipLaunchKernelGGL(tile_copy_kernel, dim3(grid), dim3(kThreads), 0, (hipStream_t)stream,
+                     (const u32x4*)src, (u32x4*)dst, n_units);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -53,7 +53,7 @@ def test_ceiling_library_exports_and_validation():
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "ibp_ceiling.h")).read(),
                   flags=re.S)
     names = sorted(set(re.findall(r"\b(ibp_[a-z_]+)\s*\(", text)))
-    assert names == ["ibp_ceiling_gather_copy"]
+    assert names == ["ibp_ceiling_copy", "ibp_ceiling_gather_copy"]
     L = ctypes.CDLL(lib)
     for n in names:
         assert hasattr(L, n), n
@@ -71,6 +71,12 @@ def test_ceiling_library_exports_and_validation():
         assert f((T * 1)(bad), 1, 0, 0, None) == -1
     assert f((T * 17)(), 17, 0, 0, None) == -1
     assert f((T * 1)(T(4, 4096, fake, fake, None, 4, fake)), 1, 0, 4, None) == -1  # unknown flag
+    c = ceiling.lib().ibp_ceiling_copy
+    assert c(None, None, 0, 0, None) == 0                   # nothing to copy
+    assert c(fake, fake + 4096, 40, 0, None) == -1          # not a multiple of 16 bytes
+    assert c(fake + 8, fake + 4096, 64, 0, None) == -1      # misaligned src
+    assert c(fake, fake + 4100, 64, 0, None) == -1          # misaligned dst
+    assert c(None, fake, 64, 0, None) == -1                 # null src
 
 
 def test_flag_words_and_status_strings(ibp):

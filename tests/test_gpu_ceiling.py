@@ -3,7 +3,8 @@ row i = the first src_bytes[i] bytes (rounded up to 16) of slot ids[i],
 zeros after; an id outside the table gives a zero row.  Rows of 16 B to
 4 KiB (one task each), chunked rows (8 and 28 KiB), several tensors in one
 launch, a capped grid, a pinned host source.  The benchmark times this copy as the floor of each
-decompression, so it has to read and write exactly that."""
+decompression, so it has to read and write exactly that.  The plain tile
+copy (ibp_ceiling_copy) equals its source and writes nothing past it."""
 import numpy as np
 import pytest
 
@@ -84,3 +85,18 @@ def test_gather_copy_batch_and_host_source(ceiling):
         torch.cuda.synchronize()
         for (_, _, _, out), w in zip(parts, want):
             assert np.array_equal(out.cpu().numpy(), w)
+
+
+@pytest.mark.parametrize("cap", [0, 1, 5])
+@pytest.mark.parametrize("n_bytes", [16, 16368, 16384, 16400, 37 * 16384 + 80, (64 << 20) + 48])
+def test_tile_copy(ceiling, n_bytes, cap):
+    """The plain contiguous copy the benchmark quotes as the practical
+    read/write rate: whole 16 KiB tiles, a partial last tile, a capped grid
+    (workgroups looping over tiles); nothing is written past n_bytes."""
+    rng = np.random.default_rng(n_bytes + cap)
+    src = torch.from_numpy(rng.integers(0, 256, n_bytes, dtype=np.uint8)).cuda()
+    dst = torch.full((n_bytes + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    ceiling.copy_launcher(src, dst[:n_bytes], max_workgroups=cap)()
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n_bytes], src)
+    assert bool((dst[n_bytes:] == 0xA5).all())
